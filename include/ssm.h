@@ -1,0 +1,159 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) causal selective-SSM hot path.
+ *
+ * Three operations, named after the operators of the Mamba adaptation in
+ * "feat(llama.cu): 适配 mamba 模型" (InfiniLM-Rust PR #48, section 2.1 lists
+ * causal-conv1d, selective-scan, silu and element-mul; section 3.1 places the
+ * per-request mamba-cache reads and writes at the conv and scan operators) and
+ * after the decode call of "[XPU] Add tuned Mamba SSU configs for Intel Arc Pro
+ * B70" (vLLM PR #50534 report, section "关键源码片段":
+ * selective_state_update(state, x, dt, A, B, C, D=D, z=None, dt_bias=dt_bias,
+ * dt_softplus=True, out=out)).  The pages name the operators without writing
+ * their equations; the equations below are the standard selective SSM that
+ * those operator names and arguments describe.
+ *
+ * Common conventions
+ * ------------------
+ *  - Every tensor argument is a pointer to DEVICE memory owned by the caller.
+ *    The library allocates nothing, frees nothing, keeps no state between
+ *    calls and never synchronises: each call validates its arguments on the
+ *    host, enqueues its kernels on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns.  Calls can be captured into a HIP graph.
+ *  - Tensors are dense row-major with the shapes given per call (element
+ *    strides implied by the shape); pointers must be aligned to their element
+ *    size.  Outputs must not overlap inputs.
+ *  - dtype codes (ssm_dtype): SSM_F32, SSM_F16 (IEEE binary16), SSM_BF16.
+ *    "io dtype" covers x/u, dt, B, C, z, out and the conv cache; A, D, dt_bias,
+ *    conv weight and conv bias are always float32.  All arithmetic is float32;
+ *    narrowing to f16/bf16 rounds to nearest, ties to even.
+ *  - Slots: slot_idx (int32 [batch], may be NULL) maps request b to cache row
+ *    slot_idx[b]; NULL means slot b.  A negative index marks a padded request:
+ *    nothing of it is read or written (its out rows keep their contents).
+ *    Non-negative indices must be < nslots and distinct within a call
+ *    (duplicates race; this is not checked on the device).
+ *  - batch == 0 or seqlen == 0 is a no-op returning SSM_OK.
+ *  - Errors are returned synchronously, before anything is enqueued, as
+ *    ssm_status codes; asynchronous device faults surface at the caller's
+ *    next synchronisation, as with any HIP launch.  Nothing is thrown.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum ssm_dtype {
+    SSM_F32 = 0,
+    SSM_F16 = 1,
+    SSM_BF16 = 2
+} ssm_dtype;
+
+typedef enum ssm_status {
+    SSM_OK = 0,
+    SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL                     */
+    SSM_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree       */
+    SSM_ERR_DTYPE = 3,       /* unknown dtype code                             */
+    SSM_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size   */
+    SSM_ERR_UNSUPPORTED = 5, /* a size beyond what the kernels are built for   */
+    SSM_ERR_HIP = 6          /* the HIP runtime refused a launch               */
+} ssm_status;
+
+/*
+ * ssm_causal_conv1d -- causal depthwise conv1d + bias + optional SiLU, with an
+ * optional per-request conv cache (the causal-conv1d and silu operators and
+ * the cache of InfiniLM-Rust PR #48, sections 2.1 and 3.1).
+ *
+ *   x, out      io dtype [batch, channels, seqlen]   (time innermost)
+ *   weight      f32 [channels, width]; tap width-1 multiplies the newest sample
+ *   bias        f32 [channels] or NULL
+ *   conv_state  io dtype [nslots, channels, width-1] or NULL; oldest sample
+ *               first.  In: the history before x[...,0] when
+ *               has_initial_state (else the history is zeros).  Out: the last
+ *               width-1 samples of history||x, copied bit-exactly.
+ *
+ *   out[b,c,t] = act(bias[c] + sum_{k<width} weight[c,k] * xh(t-width+1+k))
+ *   xh(s) = x[b,c,s] for s >= 0, history for s < 0; act = SiLU or identity.
+ *
+ * seqlen == 1 with has_initial_state is the decode update (one output, window
+ * shifted by one); prefill writes the tail a later decode step starts from.
+ * Limits: 1 <= width <= 4.
+ */
+int ssm_causal_conv1d(const void *x, const float *weight, const float *bias,
+                      void *conv_state, const int32_t *slot_idx, void *out,
+                      int batch, int channels, int seqlen, int width,
+                      int nslots, int dtype, int has_initial_state,
+                      int apply_silu, void *stream);
+
+/*
+ * ssm_selective_scan -- selective scan over a whole sequence (prefill): the
+ * selective-scan operator with its silu(z) element-mul gate (InfiniLM-Rust PR
+ * #48, section 2.1), final state stored to the request's cache slot (3.1).
+ *
+ *   u, z, out   io dtype [batch, nheads*headdim, seqlen]; z may be NULL
+ *   dt          io dtype [batch, nheads, seqlen]
+ *   dt_bias     f32 [nheads] or NULL;  D  f32 [nheads] or NULL
+ *   A           f32 [nheads, dstate] when a_per_state (Mamba-1: one decay per
+ *               channel and state, headdim 1), else f32 [nheads] (Mamba-2:
+ *               one decay per head)
+ *   B, C        io dtype [batch, ngroups, dstate, seqlen]; head h reads group
+ *               h / (nheads/ngroups)
+ *   ssm_state   state dtype [nslots, nheads, headdim, dstate] or NULL; in: the
+ *               initial state when has_initial_state (else zeros); out: the
+ *               state after the last token
+ *
+ *   delta_t = softplus(dt_t + dt_bias) (or dt_t + dt_bias if !dt_softplus)
+ *   h_t[n]  = exp(delta_t*A[n]) * h_{t-1}[n] + delta_t * B_t[n] * u_t
+ *   out_t   = (sum_n C_t[n] h_t[n] + D u_t) * silu(z_t)
+ *
+ * Limits: nheads % ngroups == 0; 1 <= dstate <= 256.
+ */
+int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias,
+                       const float *A, const void *B, const void *C,
+                       const float *D, const void *z, void *ssm_state,
+                       const int32_t *slot_idx, void *out, int batch,
+                       int seqlen, int nheads, int headdim, int dstate,
+                       int ngroups, int nslots, int io_dtype, int state_dtype,
+                       int a_per_state, int dt_softplus, int has_initial_state,
+                       void *stream);
+
+/*
+ * ssm_state_update -- one-token selective state update (decode) in place on a
+ * slot-indexed state cache: the selective_state_update call of the vLLM PR
+ * #50534 report ("关键源码片段"), same argument set.
+ *
+ *   state       state dtype [nslots, nheads, headdim, dstate], read-modify-
+ *               written in place for the named slots only
+ *   x, z, out   io dtype [batch, nheads, headdim]; z may be NULL
+ *   dt          io dtype [batch, nheads]
+ *   dt_bias, D  f32 [nheads] or NULL
+ *   A           f32 [nheads, dstate] (a_per_state) or f32 [nheads]
+ *   B, C        io dtype [batch, ngroups, dstate]
+ *
+ *   h' = exp(delta*A) * h + delta * B * x;  out = (C.h' + D x) * silu(z)
+ * The readout uses the float32 h'; the cache receives h' rounded to the state
+ * dtype.  Limits: nheads % ngroups == 0; 1 <= dstate <= 512.
+ */
+int ssm_state_update(void *state, const int32_t *slot_idx, const void *x,
+                     const void *dt, const float *dt_bias, const float *A,
+                     const void *B, const void *C, const float *D,
+                     const void *z, void *out, int batch, int nheads,
+                     int headdim, int dstate, int ngroups, int nslots,
+                     int io_dtype, int state_dtype, int a_per_state,
+                     int dt_softplus, void *stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char *ssm_status_string(int status);
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

@@ -1,0 +1,179 @@
+"""Python binding of the gfx950 causal selective-SSM library (libssm_hip.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/ssm.h``.  PyTorch supplies device memory
+(tensors are passed as raw pointers) and the current stream.  There is no CPU
+fallback: if the library is missing or the tensors are not on the GPU the
+calls raise.
+
+Layouts (dense, row-major, time innermost for prefill):
+    prefill  u/x/z/out [batch, channels, seqlen], dt [batch, nheads, seqlen],
+             B/C [batch, ngroups, dstate, seqlen]
+    decode   x/z/out [batch, nheads, headdim], dt [batch, nheads],
+             B/C [batch, ngroups, dstate]
+    caches   conv_state [nslots, channels, width-1], ssm_state
+             [nslots, nheads, headdim, dstate]
+    params   A [nheads, dstate] (one decay per channel and state) or [nheads]
+             (one decay per head), D/dt_bias [nheads], conv weight
+             [channels, width], conv bias [channels] -- all float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm_hip.so")
+
+SSM_F32, SSM_F16, SSM_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: SSM_BF16}
+
+EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_state_update",
+            "ssm_status_string", "ssm_abi_version")
+
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE",
+          4: "SSM_ERR_ALIGN", 5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_HIP"}
+
+
+class SsmError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """dlopen the HIP library and declare the C signatures (no device call)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: the HIP extension has not been built "
+            "(run __graft_entry__.build() or python state_space_model_causal_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.ssm_causal_conv1d.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.ssm_causal_conv1d.restype = I
+    lib.ssm_selective_scan.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
+                                       I, I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_selective_scan.restype = I
+    lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
+                                     I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_state_update.restype = I
+    lib.ssm_status_string.argtypes = [I]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_abi_version.restype = I
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SsmError(fn, status, load_library().ssm_status_string(status).decode())
+
+
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _code(t, name):
+    try:
+        return _DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise TypeError(f"{name}: unsupported dtype {t.dtype}") from None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _same_io(name_dtype, *pairs):
+    for t, n in pairs:
+        if t is not None and t.dtype != name_dtype:
+            raise TypeError(f"{n} must have the io dtype {name_dtype} (got {t.dtype})")
+
+
+def causal_conv1d(x, weight, bias=None, conv_state=None, slot_idx=None, out=None,
+                  has_initial_state=False, apply_silu=True, stream=None):
+    """ssm_causal_conv1d: x [batch, channels, seqlen] -> out (same shape/dtype)."""
+    batch, channels, seqlen = x.shape
+    width = weight.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    _same_io(x.dtype, (out, "out"), (conv_state, "conv_state"))
+    nslots = conv_state.shape[0] if conv_state is not None else 0
+    st = load_library().ssm_causal_conv1d(
+        _ptr(x, "x"), _ptr(weight, "weight", torch.float32), _ptr(bias, "bias", torch.float32),
+        _ptr(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32), _ptr(out, "out"),
+        batch, channels, seqlen, width, nslots, _code(x, "x"), int(bool(has_initial_state)),
+        int(bool(apply_silu)), _stream(stream))
+    _check("ssm_causal_conv1d", st)
+    return out
+
+
+def selective_scan(u, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
+                   ssm_state=None, slot_idx=None, has_initial_state=False, out=None,
+                   stream=None):
+    """ssm_selective_scan: u [batch, nheads*headdim, seqlen] -> out."""
+    batch, channels, seqlen = u.shape
+    nheads = dt.shape[1]
+    headdim = channels // nheads
+    ngroups, dstate = B.shape[1], B.shape[2]
+    a_per_state = 1 if A.dim() == 2 else 0
+    if out is None:
+        out = torch.empty_like(u)
+    _same_io(u.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
+    nslots = ssm_state.shape[0] if ssm_state is not None else 0
+    sd = _code(ssm_state, "ssm_state") if ssm_state is not None else SSM_F32
+    st = load_library().ssm_selective_scan(
+        _ptr(u, "u"), _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32),
+        _ptr(A, "A", torch.float32), _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32),
+        _ptr(z, "z"), _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+        _ptr(out, "out"), batch, seqlen, nheads, headdim, dstate, ngroups, nslots,
+        _code(u, "u"), sd, a_per_state, int(bool(dt_softplus)), int(bool(has_initial_state)),
+        _stream(stream))
+    _check("ssm_selective_scan", st)
+    return out
+
+
+def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
+                 slot_idx=None, out=None, stream=None):
+    """ssm_state_update: one token per request, state cache updated in place."""
+    nslots, nheads, headdim, dstate = state.shape
+    batch = x.shape[0]
+    ngroups = B.shape[1]
+    a_per_state = 1 if A.dim() == 2 else 0
+    if out is None:
+        out = torch.empty_like(x)
+    _same_io(x.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
+    st = load_library().ssm_state_update(
+        _ptr(state, "state"), _ptr(slot_idx, "slot_idx", torch.int32), _ptr(x, "x"),
+        _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32),
+        _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32), _ptr(z, "z"), _ptr(out, "out"),
+        batch, nheads, headdim, dstate, ngroups, nslots, _code(x, "x"), _code(state, "state"),
+        a_per_state, int(bool(dt_softplus)), _stream(stream))
+    _check("ssm_state_update", st)
+    return out
+
+
+__all__ = ["causal_conv1d", "selective_scan", "state_update", "load_library", "SsmError",
+           "SSM_F32", "SSM_F16", "SSM_BF16", "EXPORTED", "LIB_PATH"]

@@ -1,0 +1,170 @@
+// conv1d.hip -- causal depthwise conv1d + bias + SiLU with a per-request conv
+// cache, on gfx950.
+//
+// Operation: the causal-conv1d and silu operators of "feat(llama.cu): 适配
+// mamba 模型" (InfiniLM-Rust PR #48, section 2.1), with the cache handling of
+// section 3.1 (the conv operator reads the request's cached history and leaves
+// the newest width-1 samples behind for the next call):
+//     out[b,c,t] = silu(bias[c] + sum_{k<W} w[c,k] * xh[b,c,t-W+1+k])
+// where xh is x preceded by the cached history (or zeros).
+//
+// Prefill kernel: one 256-lane workgroup per (b, c) row walks the row in
+// tiles of 256*VEC samples (VEC = one 128-bit load per lane).  The tile plus
+// its W-1 history is staged in LDS so each lane reads its neighbours' samples
+// without re-fetching them from memory; the history of the next tile is kept
+// in LDS, and the row's final W-1 samples go to the cache at the end.  HBM
+// traffic: x read once, out written once.
+//
+// Decode kernel (seqlen == 1): one lane per (b, c): gather the window from the
+// slot, one output, shift the window by one in place (bit-exact copies).
+#include "ssm_device.hpp"
+#include "ssm_kernels.hpp"
+
+namespace ssm {
+
+template <typename T, int W, bool VEC>
+__global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
+{
+    constexpr int E = 16 / StorageSize<T>::value;  // samples per 128-bit access
+    constexpr int TILE = 256 * E;
+    constexpr int H = W - 1;
+    constexpr int OFF = 4;                          // history sits in xs[OFF-H, OFF)
+    __shared__ float xs[OFF + TILE];
+    __shared__ float hist[4];
+
+    const int64_t row = xcd_block_order(blockIdx.x, gridDim.x);  // b*channels + c
+    const int b = (int)(row / a.channels), c = (int)(row % a.channels);
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0)
+        return;  // padded request (uniform over the workgroup)
+    const int tid = threadIdx.x;
+
+    float w[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+        w[k] = a.weight[(int64_t)c * W + k];
+    const float bias = a.bias ? a.bias[c] : 0.0f;
+
+    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
+    if (tid < H)
+        hist[tid] = (a.has_initial_state && cs) ? to_f32(cs[tid]) : 0.0f;
+
+    const T *xr = static_cast<const T *>(a.x) + row * a.seqlen;
+    T *orow = static_cast<T *>(a.out) + row * a.seqlen;
+
+    for (int t0 = 0; t0 < a.seqlen; t0 += TILE) {
+        const int t = t0 + tid * E;
+        const int len = min(TILE, a.seqlen - t0);
+        float v[E];
+        if (VEC && t + E <= a.seqlen) {
+            load_vec<T, E>(xr + t, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                v[i] = (t + i < a.seqlen) ? to_f32(xr[t + i]) : 0.0f;
+        }
+        __syncthreads();  // hist written / previous tile's readers finished
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            xs[OFF + tid * E + i] = v[i];
+        if (tid < H)
+            xs[OFF - H + tid] = hist[tid];
+        __syncthreads();
+        float o[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            float acc = bias;
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                acc = fmaf(w[k], xs[OFF + tid * E + i - H + k], acc);
+            o[i] = a.apply_silu ? silu_f32(acc) : acc;
+        }
+        if (VEC && t + E <= a.seqlen) {
+            store_vec<T, E>(orow + t, o);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                if (t + i < a.seqlen)
+                    orow[t + i] = from_f32<T>(o[i]);
+        }
+        // history of the next tile: the last H samples of history||tile
+        if (tid < H)
+            hist[tid] = xs[OFF + len - H + tid];
+    }
+    __syncthreads();
+    if (cs && tid < H)
+        cs[tid] = from_f32<T>(hist[tid]);  // exact: the values came from T
+}
+
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_decode_kernel(ConvArgs a)
+{
+    constexpr int H = W - 1;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)a.batch * a.channels)
+        return;
+    const int b = (int)(i / a.channels), c = (int)(i % a.channels);
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0)
+        return;
+    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
+    const T xv_raw = static_cast<const T *>(a.x)[i];
+    T win[H > 0 ? H : 1];
+    float acc = a.bias ? a.bias[c] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        win[k] = cs ? cs[k] : T{};
+        const float hv = (a.has_initial_state && cs) ? to_f32(win[k]) : 0.0f;
+        acc = fmaf(a.weight[(int64_t)c * W + k], hv, acc);
+    }
+    acc = fmaf(a.weight[(int64_t)c * W + H], to_f32(xv_raw), acc);
+    static_cast<T *>(a.out)[i] = from_f32<T>(a.apply_silu ? silu_f32(acc) : acc);
+    if (cs) {
+        // shift the window by one; without an initial state the history is
+        // zeros, so the new window is (0, ..., 0, x)
+#pragma unroll
+        for (int k = 0; k + 1 < H; ++k)
+            cs[k] = a.has_initial_state ? win[k + 1] : from_f32<T>(0.0f);
+        if (H > 0)
+            cs[H - 1] = xv_raw;
+    }
+}
+
+template <typename T, int W>
+static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
+{
+    if (a.seqlen == 1) {
+        const int64_t n = (int64_t)a.batch * a.channels;
+        hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, a);
+    } else {
+        const dim3 grid((unsigned)((int64_t)a.batch * a.channels));
+        if (a.vec)
+            hipLaunchKernelGGL((conv_prefill_kernel<T, W, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((conv_prefill_kernel<T, W, false>), grid, dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_conv_t(const ConvArgs &a, hipStream_t stream)
+{
+    switch (a.width) {
+    case 1: return launch_conv_tw<T, 1>(a, stream);
+    case 2: return launch_conv_tw<T, 2>(a, stream);
+    case 3: return launch_conv_tw<T, 3>(a, stream);
+    default: return launch_conv_tw<T, 4>(a, stream);
+    }
+}
+
+hipError_t launch_conv(const ConvArgs &a, hipStream_t stream)
+{
+    switch (a.dtype) {
+    case 0: return launch_conv_t<float>(a, stream);
+    case 1: return launch_conv_t<f16>(a, stream);
+    default: return launch_conv_t<bf16>(a, stream);
+    }
+}
+
+} // namespace ssm

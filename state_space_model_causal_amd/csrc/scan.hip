@@ -1,0 +1,325 @@
+// scan.hip -- chunked selective scan (prefill) on gfx950.
+//
+// Operation: the selective-scan operator of "feat(llama.cu): 适配 mamba 模型"
+// (InfiniLM-Rust PR #48, section 2.1) with its silu(z) element-mul gate, and
+// the final state stored to the request's cache slot (section 3.1):
+//     delta_t = softplus(dt_t + dt_bias)
+//     h_t[n]  = exp(delta_t A[n]) h_{t-1}[n] + delta_t B_t[n] u_t
+//     out_t   = (sum_n C_t[n] h_t[n] + D u_t) * silu(z_t)
+//
+// Work decomposition
+//   * Workgroup = 256 lanes = 16 channels x 16 lanes ("a row": one DPP row).
+//     All 16 channels belong to one (request, group), so they share one B/C
+//     stream, which is staged once per tile in LDS and read by all of them.
+//   * The sequence is walked in tiles of 256 timesteps; lane r of a channel
+//     owns timesteps [16r, 16r+16) of the tile (two or four 128-bit loads of
+//     u, dt and z).
+//   * For each state n, every lane reduces its 16 steps to one affine map
+//     h -> a*h + b (a = product of decays, b = local state from zero), the 16
+//     maps of a row are combined by an inclusive Hillis-Steele scan with DPP
+//     row shifts (4 steps), and each lane then re-runs its 16 steps from the
+//     exact incoming state, accumulating C_t[n] h_t[n] into its outputs.  The
+//     tile-end state of each channel (lane 15's scan result, rotated into lane
+//     0) carries to the next tile through LDS.
+//   * Mamba-2 (one decay per head, a_per_state == 0): the decays and their
+//     row scan are state-independent and are computed once per tile.
+// All arithmetic is float32; the state never leaves the chip until the final
+// write to the cache slot.
+#include "ssm_device.hpp"
+#include "ssm_kernels.hpp"
+
+namespace ssm {
+
+namespace {
+constexpr int R = 16;        // lanes per channel
+constexpr int K = 16;        // timesteps per lane per tile
+constexpr int T = R * K;     // timesteps per tile
+constexpr int CPB = 256 / R; // channels per workgroup
+constexpr int NC = 16;       // states per LDS chunk of B/C
+} // namespace
+
+// Load timesteps [tl, tl+K) of one row (zeros past the end of the sequence).
+template <typename TI, bool VEC, bool STREAM>
+__device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, int L, float (&dst)[K])
+{
+    constexpr int E = 16 / StorageSize<TI>::value;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int v = 0; v < K / E; ++v) {
+            float part[E];
+            if (tl + (v + 1) * E <= L) {
+                if constexpr (STREAM)
+                    load_vec<TI, E>(row + tl + v * E, part);
+                else
+                    load_vec_cached<TI, E>(row + tl + v * E, part);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    part[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                dst[v * E + e] = part[e];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            dst[i] = (tl + i < L) ? to_f32(row[tl + i]) : 0.0f;
+    }
+}
+
+template <typename TI, bool VEC>
+__device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int L, const float (&src)[K])
+{
+    constexpr int E = 16 / StorageSize<TI>::value;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int v = 0; v < K / E; ++v) {
+            if (tl + (v + 1) * E <= L) {
+                float part[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    part[e] = src[v * E + e];
+                store_vec<TI, E>(row + tl + v * E, part);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            if (tl + i < L)
+                row[tl + i] = from_f32<TI>(src[i]);
+    }
+}
+
+template <typename TI, typename TS, bool A_PER_STATE, bool VEC, int NCAP>
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
+{
+    constexpr int E = 16 / StorageSize<TI>::value;
+    // B/C chunk in a lane-interleaved layout: the float4 holding timesteps
+    // [16r + 4q, 16r + 4q + 4) of local state nl sits at (nl*(K/4) + q)*R + r,
+    // so the 16 lanes of a row read 16 consecutive float4s (no bank conflict).
+    __shared__ float4 lds_b[NC * T / 4];
+    __shared__ float4 lds_c[NC * T / 4];
+    __shared__ float lds_carry[CPB][NCAP];
+
+    const int L = a.seqlen, N = a.dstate, P = a.headdim;
+    const int cpg = a.heads_per_group * P;  // channels per group (contiguous)
+    const int nblk_g = (cpg + CPB - 1) / CPB;
+    const uint32_t lb = xcd_block_order(blockIdx.x, gridDim.x);
+    const int cb = (int)(lb % nblk_g);
+    const int bg = (int)(lb / nblk_g);
+    const int g = bg % a.ngroups, b = bg / a.ngroups;
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0)
+        return;  // padded request (uniform over the workgroup)
+
+    const int tid = threadIdx.x, ch = tid / R, r = tid % R;
+    const int cig = cb * CPB + ch;
+    const bool active = cig < cpg;
+    const int c = g * cpg + (active ? cig : 0);  // inactive lanes shadow a valid channel
+    const int h = c / P, p = c % P;
+    const int Cn = a.nheads * P;
+
+    const TI *urow = static_cast<const TI *>(a.u) + ((int64_t)b * Cn + c) * L;
+    const TI *dtrow = static_cast<const TI *>(a.dt) + ((int64_t)b * a.nheads + h) * L;
+    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + ((int64_t)b * Cn + c) * L : nullptr;
+    TI *orow = static_cast<TI *>(a.out) + ((int64_t)b * Cn + c) * L;
+    const TI *Bg = static_cast<const TI *>(a.B) + ((int64_t)b * a.ngroups + g) * N * L;
+    const TI *Cg = static_cast<const TI *>(a.C) + ((int64_t)b * a.ngroups + g) * N * L;
+    TS *srow = a.state ? static_cast<TS *>(a.state) + (((int64_t)slot * a.nheads + h) * P + p) * N : nullptr;
+
+    const float bias_h = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float D_h = a.D ? a.D[h] : 0.0f;
+    const float A2_h = A_PER_STATE ? 0.0f : a.A[h] * kLog2e;
+
+    for (int n = r; n < N; n += R)
+        lds_carry[ch][n] = (srow && a.has_initial_state) ? to_f32(srow[n]) : 0.0f;
+
+    for (int t0 = 0; t0 < L; t0 += T) {
+        const int tl = t0 + r * K;
+        float dl[K], du[K], y[K];
+        {
+            float uu[K], dd[K];
+            load_steps<TI, VEC, true>(urow, tl, L, uu);
+            load_steps<TI, VEC, true>(dtrow, tl, L, dd);
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const float v = dd[i] + bias_h;
+                float d = a.dt_softplus ? softplus_f32(v) : v;
+                d = (tl + i < L) ? d : 0.0f;  // identity step past the end
+                dl[i] = d;
+                du[i] = d * uu[i];
+                y[i] = D_h * uu[i];
+            }
+        }
+        float sdl = 0.0f;
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            sdl += dl[i];
+
+        // Mamba-2: decays and their row scan do not depend on the state.
+        float am[A_PER_STATE ? 1 : K];
+        float acum[A_PER_STATE ? 1 : 4];
+        if constexpr (!A_PER_STATE) {
+#pragma unroll
+            for (int i = 0; i < K; ++i)
+                am[i] = exp2_hw(dl[i] * A2_h);
+            float ag = exp2_hw(sdl * A2_h);
+            acum[0] = ag;
+            ag *= dpp_move<DPP_ROW_SHR1>(1.0f, ag);
+            acum[1] = ag;
+            ag *= dpp_move<DPP_ROW_SHR2>(1.0f, ag);
+            acum[2] = ag;
+            ag *= dpp_move<DPP_ROW_SHR4>(1.0f, ag);
+            acum[3] = ag;
+        }
+
+        for (int n0 = 0; n0 < N; n0 += NC) {
+            __syncthreads();  // previous chunk's readers are done with the LDS tiles
+            for (int m = tid; m < NC * T / E; m += 256) {
+                const int nl = m / (T / E), tc = (m % (T / E)) * E;
+                const int n = n0 + nl, t = t0 + tc;
+                float vb[E], vc[E];
+                if (VEC && n < N && t + E <= L) {
+                    load_vec_cached<TI, E>(Bg + (int64_t)n * L + t, vb);
+                    load_vec_cached<TI, E>(Cg + (int64_t)n * L + t, vc);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const bool ok = n < N && t + e < L;
+                        vb[e] = ok ? to_f32(Bg[(int64_t)n * L + t + e]) : 0.0f;
+                        vc[e] = ok ? to_f32(Cg[(int64_t)n * L + t + e]) : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int e4 = 0; e4 < E / 4; ++e4) {
+                    const int tt = tc + 4 * e4;
+                    const int idx = (nl * (K / 4) + (tt % K) / 4) * R + tt / K;
+                    lds_b[idx] = make_float4(vb[4 * e4], vb[4 * e4 + 1], vb[4 * e4 + 2], vb[4 * e4 + 3]);
+                    lds_c[idx] = make_float4(vc[4 * e4], vc[4 * e4 + 1], vc[4 * e4 + 2], vc[4 * e4 + 3]);
+                }
+            }
+            __syncthreads();
+            const int nc = min(NC, N - n0);
+            for (int nl = 0; nl < nc; ++nl) {
+                const int n = n0 + nl;
+                float Bv[K], Cv[K];
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q) {
+                    const float4 vb = lds_b[(nl * (K / 4) + q) * R + r];
+                    const float4 vc = lds_c[(nl * (K / 4) + q) * R + r];
+                    Bv[4 * q] = vb.x; Bv[4 * q + 1] = vb.y; Bv[4 * q + 2] = vb.z; Bv[4 * q + 3] = vb.w;
+                    Cv[4 * q] = vc.x; Cv[4 * q + 1] = vc.y; Cv[4 * q + 2] = vc.z; Cv[4 * q + 3] = vc.w;
+                }
+                float av[K], bx[K];
+                float aagg, bagg = 0.0f;
+                if constexpr (A_PER_STATE) {
+                    const float A2 = a.A[(int64_t)h * N + n] * kLog2e;
+#pragma unroll
+                    for (int i = 0; i < K; ++i)
+                        av[i] = exp2_hw(dl[i] * A2);
+                    aagg = exp2_hw(sdl * A2);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < K; ++i)
+                        av[i] = am[i];
+                    aagg = acum[0];
+                }
+#pragma unroll
+                for (int i = 0; i < K; ++i) {
+                    bx[i] = du[i] * Bv[i];
+                    bagg = fmaf(av[i], bagg, bx[i]);
+                }
+                const float carry = (r == 0) ? lds_carry[ch][n] : 0.0f;
+                bagg = fmaf(aagg, carry, bagg);  // lane 0 starts from the incoming state
+                // inclusive scan of the affine maps over the 16 lanes of the row
+                if constexpr (A_PER_STATE) {
+                    float bp, ap;
+                    bp = dpp_move<DPP_ROW_SHR1>(0.0f, bagg); ap = dpp_move<DPP_ROW_SHR1>(1.0f, aagg);
+                    bagg = fmaf(aagg, bp, bagg); aagg *= ap;
+                    bp = dpp_move<DPP_ROW_SHR2>(0.0f, bagg); ap = dpp_move<DPP_ROW_SHR2>(1.0f, aagg);
+                    bagg = fmaf(aagg, bp, bagg); aagg *= ap;
+                    bp = dpp_move<DPP_ROW_SHR4>(0.0f, bagg); ap = dpp_move<DPP_ROW_SHR4>(1.0f, aagg);
+                    bagg = fmaf(aagg, bp, bagg); aagg *= ap;
+                    bp = dpp_move<DPP_ROW_SHR8>(0.0f, bagg);
+                    bagg = fmaf(aagg, bp, bagg);
+                } else {
+                    bagg = fmaf(acum[0], dpp_move<DPP_ROW_SHR1>(0.0f, bagg), bagg);
+                    bagg = fmaf(acum[1], dpp_move<DPP_ROW_SHR2>(0.0f, bagg), bagg);
+                    bagg = fmaf(acum[2], dpp_move<DPP_ROW_SHR4>(0.0f, bagg), bagg);
+                    bagg = fmaf(acum[3], dpp_move<DPP_ROW_SHR8>(0.0f, bagg), bagg);
+                }
+                // lane r >= 1 starts from lane r-1's end state; lane 0 from the
+                // carry, and receives lane 15's end state as the next carry
+                const float rot = dpp_move<DPP_ROW_ROR1>(0.0f, bagg);
+                float hh = (r == 0) ? carry : rot;
+                if (r == 0)
+                    lds_carry[ch][n] = rot;
+#pragma unroll
+                for (int i = 0; i < K; ++i) {
+                    hh = fmaf(av[i], hh, bx[i]);
+                    y[i] = fmaf(Cv[i], hh, y[i]);
+                }
+            }
+        }
+        if (zrow) {
+            float zz[K];
+            load_steps<TI, VEC, true>(zrow, tl, L, zz);
+#pragma unroll
+            for (int i = 0; i < K; ++i)
+                y[i] *= silu_f32(zz[i]);
+        }
+        if (active)
+            store_steps<TI, VEC>(orow, tl, L, y);
+    }
+    __syncthreads();
+    if (srow && active)
+        for (int n = r; n < N; n += R)
+            srow[n] = from_f32<TS>(lds_carry[ch][n]);
+}
+
+template <typename TI, typename TS, bool A_PER_STATE, bool VEC>
+static void launch_scan_v(const ScanArgs &a, dim3 grid, hipStream_t stream)
+{
+    if (a.dstate <= 16)
+        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, 16>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, kMaxScanDstate>), grid, dim3(256), 0, stream, a);
+}
+
+template <typename TI, typename TS>
+static hipError_t launch_scan_ts(const ScanArgs &a, hipStream_t stream)
+{
+    const int cpg = a.heads_per_group * a.headdim;
+    const int64_t nblocks = (int64_t)a.batch * a.ngroups * ((cpg + CPB - 1) / CPB);
+    const dim3 grid((unsigned)nblocks);
+    if (a.a_per_state) {
+        if (a.vec) launch_scan_v<TI, TS, true, true>(a, grid, stream);
+        else launch_scan_v<TI, TS, true, false>(a, grid, stream);
+    } else {
+        if (a.vec) launch_scan_v<TI, TS, false, true>(a, grid, stream);
+        else launch_scan_v<TI, TS, false, false>(a, grid, stream);
+    }
+    return hipGetLastError();
+}
+
+template <typename TI>
+static hipError_t launch_scan_t(const ScanArgs &a, hipStream_t stream)
+{
+    switch (a.state_dtype) {
+    case 0: return launch_scan_ts<TI, float>(a, stream);
+    case 1: return launch_scan_ts<TI, f16>(a, stream);
+    default: return launch_scan_ts<TI, bf16>(a, stream);
+    }
+}
+
+hipError_t launch_scan(const ScanArgs &a, hipStream_t stream)
+{
+    switch (a.io_dtype) {
+    case 0: return launch_scan_t<float>(a, stream);
+    case 1: return launch_scan_t<f16>(a, stream);
+    default: return launch_scan_t<bf16>(a, stream);
+    }
+}
+
+} // namespace ssm

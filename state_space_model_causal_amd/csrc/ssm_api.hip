@@ -1,0 +1,212 @@
+// ssm_api.hip -- the C ABI declared in include/ssm.h: host-side argument
+// validation, launch-geometry choice and dispatch to the gfx950 kernels.
+// Everything here runs on the host before any HIP call; a rejected call
+// enqueues nothing.
+#include "ssm.h"
+#include "ssm_kernels.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+bool valid_dtype(int d) { return d == SSM_F32 || d == SSM_F16 || d == SSM_BF16; }
+int dtype_size(int d) { return d == SSM_F32 ? 4 : 2; }
+
+bool aligned(const void *p, uintptr_t n) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
+
+// Slot arguments: with a cache, explicit indices need nslots >= 1; implicit
+// (slot = b) needs nslots >= batch.
+bool slots_ok(const void *cache, const int32_t *slot_idx, int nslots, int batch)
+{
+    if (!cache)
+        return true;
+    if (nslots < 1)
+        return false;
+    return slot_idx != nullptr || nslots >= batch;
+}
+
+} // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char *ssm_status_string(int status)
+{
+    switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL_ARG: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case SSM_ERR_DTYPE: return "unknown dtype code";
+    case SSM_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case SSM_ERR_UNSUPPORTED: return "a size beyond what the kernels are built for";
+    case SSM_ERR_HIP: return "the HIP runtime refused a launch";
+    default: return "unknown status";
+    }
+}
+
+int ssm_causal_conv1d(const void *x, const float *weight, const float *bias, void *conv_state,
+                      const int32_t *slot_idx, void *out, int batch, int channels, int seqlen,
+                      int width, int nslots, int dtype, int has_initial_state, int apply_silu,
+                      void *stream)
+{
+    if (!x || !weight || !out)
+        return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(dtype))
+        return SSM_ERR_DTYPE;
+    if (batch < 0 || seqlen < 0 || channels < 1 || width < 1)
+        return SSM_ERR_SHAPE;
+    if (width > ssm::kMaxConvWidth)
+        return SSM_ERR_UNSUPPORTED;
+    if (!slots_ok(conv_state, slot_idx, nslots, batch))
+        return SSM_ERR_SHAPE;
+    const int es = dtype_size(dtype);
+    if (!aligned(x, es) || !aligned(out, es) || !aligned(conv_state, es) || !aligned(weight, 4) ||
+        !aligned(bias, 4) || !aligned(slot_idx, 4))
+        return SSM_ERR_ALIGN;
+    if ((int64_t)batch * channels > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
+    if (batch == 0 || seqlen == 0)
+        return SSM_OK;
+    ssm::ConvArgs a;
+    a.x = x;
+    a.weight = weight;
+    a.bias = bias;
+    a.conv_state = conv_state;
+    a.slot_idx = slot_idx;
+    a.out = out;
+    a.batch = batch;
+    a.channels = channels;
+    a.seqlen = seqlen;
+    a.width = width;
+    a.nslots = nslots;
+    a.dtype = dtype;
+    a.has_initial_state = has_initial_state ? 1 : 0;
+    a.apply_silu = apply_silu ? 1 : 0;
+    a.vec = (seqlen % 8 == 0) && aligned(x, 16) && aligned(out, 16);
+    return status_of(ssm::launch_conv(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias, const float *A,
+                       const void *B, const void *C, const float *D, const void *z, void *ssm_state,
+                       const int32_t *slot_idx, void *out, int batch, int seqlen, int nheads,
+                       int headdim, int dstate, int ngroups, int nslots, int io_dtype,
+                       int state_dtype, int a_per_state, int dt_softplus, int has_initial_state,
+                       void *stream)
+{
+    if (!u || !dt || !A || !B || !C || !out)
+        return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
+        return SSM_ERR_DTYPE;
+    if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1 ||
+        nheads % ngroups != 0)
+        return SSM_ERR_SHAPE;
+    if (dstate > ssm::kMaxScanDstate)
+        return SSM_ERR_UNSUPPORTED;
+    if (!slots_ok(ssm_state, slot_idx, nslots, batch))
+        return SSM_ERR_SHAPE;
+    const int es = dtype_size(io_dtype);
+    if (!aligned(u, es) || !aligned(dt, es) || !aligned(B, es) || !aligned(C, es) ||
+        !aligned(z, es) || !aligned(out, es) || !aligned(ssm_state, dtype_size(state_dtype)) ||
+        !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(slot_idx, 4))
+        return SSM_ERR_ALIGN;
+    const int64_t channels = (int64_t)nheads * headdim;
+    const int64_t cpg = channels / ngroups;
+    const int64_t nblocks = (int64_t)batch * ngroups * ((cpg + 15) / 16);
+    if (channels > INT32_MAX || nblocks > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
+    if (batch == 0 || seqlen == 0)
+        return SSM_OK;
+    ssm::ScanArgs a;
+    a.u = u;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.z = z;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.D = D;
+    a.state = ssm_state;
+    a.slot_idx = slot_idx;
+    a.out = out;
+    a.batch = batch;
+    a.seqlen = seqlen;
+    a.nheads = nheads;
+    a.headdim = headdim;
+    a.dstate = dstate;
+    a.ngroups = ngroups;
+    a.nslots = nslots;
+    a.heads_per_group = nheads / ngroups;
+    a.io_dtype = io_dtype;
+    a.state_dtype = state_dtype;
+    a.a_per_state = a_per_state ? 1 : 0;
+    a.dt_softplus = dt_softplus ? 1 : 0;
+    a.has_initial_state = has_initial_state ? 1 : 0;
+    a.vec = (seqlen % 8 == 0) && aligned(u, 16) && aligned(dt, 16) && aligned(B, 16) &&
+            aligned(C, 16) && aligned(z, 16) && aligned(out, 16);
+    return status_of(ssm::launch_scan(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const void *dt,
+                     const float *dt_bias, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, void *out, int batch, int nheads, int headdim,
+                     int dstate, int ngroups, int nslots, int io_dtype, int state_dtype,
+                     int a_per_state, int dt_softplus, void *stream)
+{
+    if (!state || !x || !dt || !A || !B || !C || !out)
+        return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
+        return SSM_ERR_DTYPE;
+    if (batch < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1 ||
+        nheads % ngroups != 0)
+        return SSM_ERR_SHAPE;
+    if (dstate > ssm::kMaxSsuDstate)
+        return SSM_ERR_UNSUPPORTED;
+    if (!slots_ok(state, slot_idx, nslots, batch))
+        return SSM_ERR_SHAPE;
+    const int es = dtype_size(io_dtype), ss = dtype_size(state_dtype);
+    if (!aligned(state, ss) || !aligned(x, es) || !aligned(dt, es) || !aligned(B, es) ||
+        !aligned(C, es) || !aligned(z, es) || !aligned(out, es) || !aligned(A, 4) ||
+        !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(slot_idx, 4))
+        return SSM_ERR_ALIGN;
+    // lanes per (b,h,p) row: ceil(dstate/8) rounded up to a power of two (<= 64)
+    int lanes = (dstate + 7) / 8, lg = 0;
+    while ((1 << lg) < lanes)
+        ++lg;
+    const int64_t nrows = (int64_t)batch * nheads * headdim;
+    if (((nrows << lg) + 255) / 256 > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
+    if (batch == 0)
+        return SSM_OK;
+    ssm::SsuArgs a;
+    a.state = state;
+    a.slot_idx = slot_idx;
+    a.x = x;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.z = z;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.D = D;
+    a.out = out;
+    a.nrows = nrows;
+    a.batch = batch;
+    a.nheads = nheads;
+    a.headdim = headdim;
+    a.dstate = dstate;
+    a.ngroups = ngroups;
+    a.nslots = nslots;
+    a.heads_per_group = nheads / ngroups;
+    a.lanes_per_row_log2 = lg;
+    a.io_dtype = io_dtype;
+    a.state_dtype = state_dtype;
+    a.a_per_state = a_per_state ? 1 : 0;
+    a.dt_softplus = dt_softplus ? 1 : 0;
+    a.vec = (dstate % 8 == 0) && aligned(state, 16) && aligned(B, 16) && aligned(C, 16);
+    return status_of(ssm::launch_ssu(a, static_cast<hipStream_t>(stream)));
+}
+
+} // extern "C"

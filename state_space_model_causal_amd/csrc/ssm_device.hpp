@@ -1,0 +1,222 @@
+// ssm_device.hpp -- device-side helpers shared by the gfx950 kernels:
+// storage conversions, 128-bit vector access, the float32 transcendental
+// pieces of the selective SSM (softplus of the step size, SiLU gate, exp of
+// the decay), DPP lane moves and the XCD-aware block order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// ---------------------------------------------------------------- storage
+// Three storage formats; arithmetic is always float32.
+using f16 = _Float16;
+struct bf16 {
+    uint16_t bits;
+};
+
+template <typename T> struct StorageSize;
+template <> struct StorageSize<float> { static constexpr int value = 4; };
+template <> struct StorageSize<f16> { static constexpr int value = 2; };
+template <> struct StorageSize<bf16> { static constexpr int value = 2; };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.bits << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// v_cvt_f16_f32 rounds to nearest even in the default mode.
+template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }
+// Round to nearest even on the bit pattern; NaN stays a quiet NaN.
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    bf16 r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+        r.bits = (uint16_t)((u >> 16) | 0x40u);
+    } else {
+        u += 0x7fffu + ((u >> 16) & 1u);
+        r.bits = (uint16_t)(u >> 16);
+    }
+    return r;
+}
+
+// Unpack one 32-bit word holding 1 (f32) or 2 (f16/bf16) elements.
+__device__ __forceinline__ void unpack_word(uint32_t w, float *dst, float) { dst[0] = __uint_as_float(w); }
+__device__ __forceinline__ void unpack_word(uint32_t w, float *dst, f16)
+{
+    union { uint32_t u; f16 h[2]; } c;
+    c.u = w;
+    dst[0] = (float)c.h[0];
+    dst[1] = (float)c.h[1];
+}
+__device__ __forceinline__ void unpack_word(uint32_t w, float *dst, bf16)
+{
+    dst[0] = __uint_as_float(w << 16);
+    dst[1] = __uint_as_float(w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint32_t pack_word(const float *src, float) { return __float_as_uint(src[0]); }
+__device__ __forceinline__ uint32_t pack_word(const float *src, f16)
+{
+    union { uint32_t u; f16 h[2]; } c;
+    c.h[0] = (f16)src[0];
+    c.h[1] = (f16)src[1];
+    return c.u;
+}
+__device__ __forceinline__ uint32_t pack_word(const float *src, bf16)
+{
+    return (uint32_t)from_f32<bf16>(src[0]).bits | ((uint32_t)from_f32<bf16>(src[1]).bits << 16);
+}
+
+template <typename T> struct PerWord { static constexpr int value = 4 / StorageSize<T>::value; };
+
+// 128-bit access unit (a native vector type, usable with the nontemporal
+// builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Load K consecutive elements (K * sizeof(T) a multiple of 16 bytes, p 16-byte
+// aligned) with 128-bit loads and widen them to float.
+template <typename T, int K>
+__device__ __forceinline__ void load_vec(const T *__restrict__ p, float (&dst)[K])
+{
+    constexpr int PW = PerWord<T>::value;
+    constexpr int NV = K * StorageSize<T>::value / 16;
+    static_assert(NV * 16 == K * StorageSize<T>::value, "K elements must fill whole 16-byte vectors");
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        u32x4 w = __builtin_nontemporal_load(q + v);
+        unpack_word(w.x, &dst[(4 * v + 0) * PW], T{});
+        unpack_word(w.y, &dst[(4 * v + 1) * PW], T{});
+        unpack_word(w.z, &dst[(4 * v + 2) * PW], T{});
+        unpack_word(w.w, &dst[(4 * v + 3) * PW], T{});
+    }
+}
+
+// Same, with ordinary (cached) loads: for data read by several workgroups.
+template <typename T, int K>
+__device__ __forceinline__ void load_vec_cached(const T *__restrict__ p, float (&dst)[K])
+{
+    constexpr int PW = PerWord<T>::value;
+    constexpr int NV = K * StorageSize<T>::value / 16;
+    static_assert(NV * 16 == K * StorageSize<T>::value, "K elements must fill whole 16-byte vectors");
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        u32x4 w = q[v];
+        unpack_word(w.x, &dst[(4 * v + 0) * PW], T{});
+        unpack_word(w.y, &dst[(4 * v + 1) * PW], T{});
+        unpack_word(w.z, &dst[(4 * v + 2) * PW], T{});
+        unpack_word(w.w, &dst[(4 * v + 3) * PW], T{});
+    }
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void store_vec(T *__restrict__ p, const float (&src)[K])
+{
+    constexpr int PW = PerWord<T>::value;
+    constexpr int NV = K * StorageSize<T>::value / 16;
+    static_assert(NV * 16 == K * StorageSize<T>::value, "K elements must fill whole 16-byte vectors");
+    u32x4 *q = reinterpret_cast<u32x4 *>(p);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        u32x4 w;
+        w.x = pack_word(&src[(4 * v + 0) * PW], T{});
+        w.y = pack_word(&src[(4 * v + 1) * PW], T{});
+        w.z = pack_word(&src[(4 * v + 2) * PW], T{});
+        w.w = pack_word(&src[(4 * v + 3) * PW], T{});
+        __builtin_nontemporal_store(w, q + v);
+    }
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void store_vec_cached(T *__restrict__ p, const float (&src)[K])
+{
+    constexpr int PW = PerWord<T>::value;
+    constexpr int NV = K * StorageSize<T>::value / 16;
+    static_assert(NV * 16 == K * StorageSize<T>::value, "K elements must fill whole 16-byte vectors");
+    u32x4 *q = reinterpret_cast<u32x4 *>(p);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        u32x4 w;
+        w.x = pack_word(&src[(4 * v + 0) * PW], T{});
+        w.y = pack_word(&src[(4 * v + 1) * PW], T{});
+        w.z = pack_word(&src[(4 * v + 2) * PW], T{});
+        w.w = pack_word(&src[(4 * v + 3) * PW], T{});
+        q[v] = w;
+    }
+}
+
+// ------------------------------------------------------------ math pieces
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x on the hardware exponential unit (v_exp_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the hardware unit (v_log_f32).
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log1p(e) for e in [0, 1], accurate to a few ulp.  w = 1 + e is rounded; the
+// factor e / (w - 1) corrects the rounding of w exactly to first order
+// (Goldberg, "What every computer scientist should know about floating-point
+// arithmetic", 1991, Theorem 4).
+__device__ __forceinline__ float log1p_unit(float e)
+{
+    const float w = 1.0f + e;
+    const float d = w - 1.0f;
+    return d == 0.0f ? e : log2_hw(w) * kLn2 * (e / d);
+}
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^{-|v|}); for v > 20 the
+// second term is below 2.1e-9 and v alone is returned.
+__device__ __forceinline__ float softplus_f32(float v)
+{
+    if (v > 20.0f)
+        return v;
+    const float e = exp2_hw(-fabsf(v) * kLog2e);
+    return fmaxf(v, 0.0f) + log1p_unit(e);
+}
+
+// SiLU(v) = v / (1 + e^{-v}).
+__device__ __forceinline__ float silu_f32(float v)
+{
+    return v * rcp_hw(1.0f + exp2_hw(-v * kLog2e));
+}
+
+// ---------------------------------------------------------------- lane moves
+// DPP controls (GCN/CDNA encoding).
+enum : int {
+    DPP_ROW_SHR1 = 0x111,
+    DPP_ROW_SHR2 = 0x112,
+    DPP_ROW_SHR4 = 0x114,
+    DPP_ROW_SHR8 = 0x118,
+    DPP_ROW_ROR1 = 0x121,
+};
+
+// Read `src` from another lane of the same 16-lane row; lanes whose source
+// falls outside the row receive `old`.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float old, float src)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL,
+                                                      0xf, 0xf, false));
+}
+
+// ---------------------------------------------------------------- block order
+// MI355X hands consecutive workgroups to its 8 XCDs round-robin.  Renumber so
+// that each XCD receives one contiguous range of logical blocks: neighbours
+// that share operands (B/C of one request, one head's parameters) then share
+// one XCD's L2.
+__device__ __forceinline__ uint32_t xcd_block_order(uint32_t i, uint32_t nblocks)
+{
+    constexpr uint32_t kXcd = 8;
+    const uint32_t xcd = i % kXcd, local = i / kXcd;
+    const uint32_t per = nblocks / kXcd, rem = nblocks % kXcd;
+    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+} // namespace ssm

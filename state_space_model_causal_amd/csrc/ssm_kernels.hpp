@@ -1,0 +1,61 @@
+// ssm_kernels.hpp -- argument blocks and launchers of the gfx950 kernels.
+// The C-ABI layer (ssm_api.hip) validates the caller's arguments, fills one
+// of these blocks (pointers + sizes, already checked) and calls a launcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct ConvArgs {
+    const void *x;
+    const float *weight;
+    const float *bias;        // may be null
+    void *conv_state;         // may be null
+    const int32_t *slot_idx;  // may be null
+    void *out;
+    int batch, channels, seqlen, width, nslots;
+    int dtype;                // 0 f32, 1 f16, 2 bf16
+    int has_initial_state, apply_silu;
+    int vec;                  // rows 16-byte aligned and seqlen a multiple of 8
+};
+
+struct ScanArgs {
+    const void *u, *dt, *B, *C, *z;  // z may be null
+    const float *dt_bias, *A, *D;    // dt_bias, D may be null
+    void *state;                     // may be null
+    const int32_t *slot_idx;         // may be null
+    void *out;
+    int batch, seqlen, nheads, headdim, dstate, ngroups, nslots;
+    int heads_per_group;
+    int io_dtype, state_dtype;
+    int a_per_state, dt_softplus, has_initial_state;
+    int vec;                         // rows 16-byte aligned and seqlen a multiple of 8
+};
+
+struct SsuArgs {
+    void *state;
+    const int32_t *slot_idx;         // may be null
+    const void *x, *dt, *B, *C, *z;  // z may be null
+    const float *dt_bias, *A, *D;    // dt_bias, D may be null
+    void *out;
+    int64_t nrows;                   // batch * nheads * headdim
+    int batch, nheads, headdim, dstate, ngroups, nslots;
+    int heads_per_group;
+    int lanes_per_row_log2;          // lanes per (b,h,p) row = 2^this
+    int io_dtype, state_dtype;
+    int a_per_state, dt_softplus;
+    int vec;                         // dstate % 8 == 0 and 16-byte aligned bases
+};
+
+hipError_t launch_conv(const ConvArgs &a, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs &a, hipStream_t stream);
+hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
+
+// Limits the kernels are built for.
+constexpr int kMaxConvWidth = 4;
+constexpr int kMaxScanDstate = 256;
+constexpr int kMaxSsuDstate = 512;
+
+} // namespace ssm

@@ -1,0 +1,128 @@
+"""C-ABI library checks that need no GPU: the library loads, exports every
+function include/ssm.h declares, and rejects bad arguments on the host before
+anything is enqueued (fake device pointers are never dereferenced: every call
+here fails validation or is a documented no-op)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import state_space_model_causal_amd as ssm
+
+    if not os.path.exists(ssm.LIB_PATH):
+        from state_space_model_causal_amd import build
+
+        build.build()
+    return ssm.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_state_update"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import state_space_model_causal_amd as ssm
+
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(ssm.EXPORTED) <= set(header_functions())
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define SSM_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.ssm_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.ssm_status_string(code)
+    assert lib.ssm_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def conv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, b=None, cs=None, idx=None, out=FAKE, batch=2, ch=8, L=16, W=4,
+             S=0, dt=1, init=0, silu=1)
+    a.update(kw)
+    return lib.ssm_causal_conv1d(a["x"], a["w"], a["b"], a["cs"], a["idx"], a["out"], a["batch"],
+                                 a["ch"], a["L"], a["W"], a["S"], a["dt"], a["init"], a["silu"], None)
+
+
+def scan(lib, **kw):
+    a = dict(u=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, st=None,
+             idx=None, out=FAKE, batch=2, L=16, H=8, P=1, N=16, G=1, S=0, io=1, sd=0, aps=1, sp=1,
+             init=0)
+    a.update(kw)
+    return lib.ssm_selective_scan(a["u"], a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"],
+                                  a["z"], a["st"], a["idx"], a["out"], a["batch"], a["L"], a["H"],
+                                  a["P"], a["N"], a["G"], a["S"], a["io"], a["sd"], a["aps"],
+                                  a["sp"], a["init"], None)
+
+
+def ssu(lib, **kw):
+    a = dict(st=FAKE, idx=None, x=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None,
+             z=None, out=FAKE, batch=2, H=8, P=4, N=16, G=1, S=2, io=1, sd=0, aps=0, sp=1)
+    a.update(kw)
+    return lib.ssm_state_update(a["st"], a["idx"], a["x"], a["dt"], a["bias"], a["A"], a["B"],
+                                a["C"], a["D"], a["z"], a["out"], a["batch"], a["H"], a["P"],
+                                a["N"], a["G"], a["S"], a["io"], a["sd"], a["aps"], a["sp"], None)
+
+
+NULL, SHAPE, DTYPE, ALIGN, UNSUP = 1, 2, 3, 4, 5
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL),
+    (dict(dt=7), DTYPE), (dict(batch=-1), SHAPE), (dict(ch=0), SHAPE), (dict(W=0), SHAPE),
+    (dict(W=5), UNSUP), (dict(cs=FAKE, S=0), SHAPE), (dict(cs=FAKE, S=1, batch=2), SHAPE),
+    (dict(x=FAKE + 1), ALIGN), (dict(w=FAKE + 2, dt=1), ALIGN), (dict(idx=FAKE + 2), ALIGN),
+    (dict(batch=0), 0), (dict(L=0), 0),
+])
+def test_conv_validation(lib, kw, code):
+    assert conv(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), NULL), (dict(A=None), NULL), (dict(B=None), NULL), (dict(out=None), NULL),
+    (dict(io=3), DTYPE), (dict(sd=-1), DTYPE), (dict(H=6, G=4), SHAPE), (dict(N=0), SHAPE),
+    (dict(N=257), UNSUP), (dict(P=0), SHAPE), (dict(st=FAKE, S=1), SHAPE),
+    (dict(u=FAKE + 1), ALIGN), (dict(st=FAKE + 2, S=4, sd=0), ALIGN), (dict(A=FAKE + 1), ALIGN),
+    (dict(batch=0), 0), (dict(L=0), 0),
+])
+def test_scan_validation(lib, kw, code):
+    assert scan(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(st=None), NULL), (dict(x=None), NULL), (dict(C=None), NULL),
+    (dict(io=9), DTYPE), (dict(H=8, G=3), SHAPE), (dict(N=513), UNSUP), (dict(S=1), SHAPE),
+    (dict(S=0, idx=FAKE), SHAPE), (dict(x=FAKE + 1), ALIGN), (dict(st=FAKE + 2, sd=0), ALIGN),
+    (dict(batch=0), 0),
+])
+def test_ssu_validation(lib, kw, code):
+    assert ssu(lib, **kw) == code
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import state_space_model_causal_amd as ssm
+
+    x = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.causal_conv1d(x, torch.zeros(4, 4))

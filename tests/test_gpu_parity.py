@@ -1,0 +1,342 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle,
+element by element, on the same seeded inputs.  Sizes keep the oracle to
+seconds while spanning several workgroups, several 256-step tiles and ragged
+tails; the full-size workloads are in test_gpu_fullsize.py.
+
+Output tolerance: |g - o| <= rtol * s + ulp/2 (tests/_parity.py), rtol 1e-5
+for float32 I/O and 3e-3 for float16/bfloat16 I/O.  Cache rows: same metric in
+the cache dtype; unnamed slots, padded requests and conv tails bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests._parity import RTOL, check, to_f64 as f
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import state_space_model_causal_amd as ssm
+
+    ssm.load_library()  # fail loudly if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    import state_space_model_causal_amd as m
+
+    return m
+
+
+def _pad(idx: torch.Tensor, every: int) -> torch.Tensor:
+    idx = idx.clone()
+    if every:
+        idx[::every] = -1
+    return idx
+
+
+def _named(idx_np):
+    return idx_np[idx_np >= 0]
+
+
+# ------------------------------------------------------------------ conv1d
+CONV_CASES = [
+    # (label, spec kwargs, has_initial_state, pad_every)
+    ("tiny_f32", dict(), False, 0),
+    ("tiny_f32_init", dict(), True, 0),
+    ("f16_L1_decode_like", dict(seqlen=1, io="f16", nheads=300, batch=5, nslots=9,
+                                random_slots=True), True, 2),
+    ("f16_L3", dict(seqlen=3, io="f16", nheads=40, batch=3, nslots=5, random_slots=True), True, 0),
+    ("bf16_L7", dict(seqlen=7, io="bf16", nheads=33, batch=2), True, 0),
+    ("f16_L65_w2", dict(seqlen=65, io="f16", nheads=17, width=2, batch=2), False, 0),
+    ("f32_L513_w3", dict(seqlen=513, io="f32", nheads=9, width=3, batch=3, nslots=4,
+                         random_slots=True), True, 3),
+    ("f16_L2048", dict(seqlen=2048, io="f16", nheads=24, batch=2), False, 0),
+    ("bf16_L2049_w1", dict(seqlen=2049, io="bf16", nheads=5, width=1, batch=2), True, 0),
+    ("f16_L4104", dict(seqlen=4104, io="f16", nheads=6, batch=1), True, 0),
+]
+
+
+@pytest.mark.parametrize("label,kw,init,pad", CONV_CASES, ids=[c[0] for c in CONV_CASES])
+def test_conv1d_parity(dev, ssm, oracle, label, kw, init, pad):
+    spec = W.tiny(**kw)
+    t = W.make(spec, dev)
+    x = t["x"].view(spec.batch, spec.channels, spec.seqlen)
+    idx = _pad(t["slot_idx"], pad)
+    cs0 = t["conv_state"].clone()
+    out0 = torch.full_like(x, 7.0)
+    out = ssm.causal_conv1d(x, t["conv_w"], t["conv_b"], conv_state=t["conv_state"], slot_idx=idx,
+                            out=out0.clone(), has_initial_state=init)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    o, s, cs = oracle.causal_conv1d(f(x), f(t["conv_w"]), f(t["conv_b"]), f(cs0), idx_np,
+                                    has_initial_state=init, out=f(out0))
+    check(out, o, s, RTOL[spec.io], spec.io, f"conv {label} out")
+    # cache: tails are exact copies, other slots untouched
+    np.testing.assert_array_equal(f(t["conv_state"]), cs)
+
+
+def test_conv1d_no_bias_no_silu(dev, ssm, oracle):
+    spec = W.tiny(seqlen=100, io="f32", nheads=20)
+    t = W.make(spec, dev)
+    out = ssm.causal_conv1d(t["x"], t["conv_w"], None, apply_silu=False)
+    torch.cuda.synchronize()
+    o, s, _ = oracle.causal_conv1d(f(t["x"]), f(t["conv_w"]), None, None, None, apply_silu=False)
+    check(out, o, s, 1e-5, "f32", "conv no bias/silu")
+
+
+# ------------------------------------------------------------------- scan
+SCAN_CASES = [
+    # (label, spec kwargs, options)
+    ("tiny_f32", dict(), {}),
+    ("tiny_f32_idx", dict(index_sensitive=True), {}),
+    ("tiny_f32_init_state", dict(index_sensitive=True, nslots=3, random_slots=True),
+     dict(init=True)),
+    ("m1_f16_L1", dict(io="f16", seqlen=1, nheads=40, batch=2), dict(init=True)),
+    ("m1_f16_L3", dict(io="f16", seqlen=3, nheads=40, batch=2), {}),
+    ("m1_bf16_L7", dict(io="bf16", seqlen=7, nheads=24, batch=2, index_sensitive=True), {}),
+    ("m1_f16_L65", dict(io="f16", seqlen=65, nheads=40, batch=2, index_sensitive=True), {}),
+    ("m1_f32_L513", dict(io="f32", seqlen=513, nheads=20, batch=2, index_sensitive=True,
+                         nslots=5, random_slots=True), dict(init=True, pad=2)),
+    ("m1_f16_L2049", dict(io="f16", seqlen=2049, nheads=18, batch=1, index_sensitive=True), {}),
+    ("m1_f16_L2048_stf16", dict(io="f16", state="f16", seqlen=2048, nheads=32, batch=2,
+                                index_sensitive=True), dict(init=True)),
+    ("m1_f32_N5", dict(io="f32", seqlen=100, nheads=12, dstate=5, index_sensitive=True),
+     dict(init=True)),
+    ("m1_f32_N20", dict(io="f32", seqlen=77, nheads=12, dstate=20, index_sensitive=True), {}),
+    ("m1_hd4", dict(io="f32", seqlen=50, nheads=6, headdim=4, index_sensitive=True), {}),
+    ("m1_noz_noD_nobias", dict(io="f32", seqlen=300, nheads=16, index_sensitive=True),
+     dict(z=False, D=False, bias=False)),
+    ("m1_no_softplus", dict(io="f32", seqlen=64, nheads=16, index_sensitive=True),
+     dict(softplus=False, bias=False)),
+    ("m2_bf16_N256", dict(io="bf16", state="bf16", seqlen=300, nheads=2, headdim=64,
+                          dstate=256, a_per_state=False, index_sensitive=True), dict(init=True)),
+    ("m2_f16_N128_G8", dict(io="f16", state="f32", seqlen=129, nheads=16, headdim=4,
+                            dstate=128, ngroups=8, a_per_state=False, index_sensitive=True,
+                            batch=2), {}),
+    ("m2_f32_N16_G2", dict(io="f32", state="f32", seqlen=258, nheads=4, headdim=8, dstate=16,
+                           ngroups=2, a_per_state=False, index_sensitive=True, nslots=4,
+                           random_slots=True, batch=3), dict(init=True, pad=3)),
+    ("m2_bf16_L4096_N256", dict(io="bf16", state="f32", seqlen=4096, nheads=1, headdim=16,
+                                dstate=256, a_per_state=False, index_sensitive=True), {}),
+]
+
+
+def run_scan(ssm, oracle, dev, spec, opts, label, t=None):
+    t = t or W.make(spec, dev)
+    u = t["x"].view(spec.batch, spec.channels, spec.seqlen)
+    dt = t["dt"].view(spec.batch, spec.nheads, spec.seqlen)
+    Bm = t["B"].view(spec.batch, spec.ngroups, spec.dstate, spec.seqlen)
+    Cm = t["C"].view(spec.batch, spec.ngroups, spec.dstate, spec.seqlen)
+    z = t["z"].view(spec.batch, spec.channels, spec.seqlen) if opts.get("z", True) else None
+    D = t["D"] if opts.get("D", True) else None
+    bias = t["dt_bias"] if opts.get("bias", True) else None
+    sp = opts.get("softplus", True)
+    init = opts.get("init", False)
+    idx = _pad(t["slot_idx"], opts.get("pad", 0))
+    st0 = t["ssm_state"].clone()
+    out0 = torch.full_like(u, 5.0)
+    out = ssm.selective_scan(u, dt, t["A"], Bm, Cm, D=D, z=z, dt_bias=bias, dt_softplus=sp,
+                             ssm_state=t["ssm_state"], slot_idx=idx, has_initial_state=init,
+                             out=out0.clone())
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    o, s, st, sts = oracle.selective_scan(
+        f(u), f(dt), f(t["A"]), f(Bm), f(Cm), D=None if D is None else f(D),
+        z=None if z is None else f(z), dt_bias=None if bias is None else f(bias),
+        dt_softplus=sp, state=f(st0), slot_idx=idx_np, has_initial_state=init, out=f(out0))
+    check(out, o, s, RTOL[spec.io], spec.io, f"scan {label} out")
+    named = _named(idx_np)
+    gst = f(t["ssm_state"])
+    check(gst[named], st[named], sts[named], RTOL[spec.io], spec.state, f"scan {label} state")
+    others = np.setdiff1d(np.arange(spec.slots), named)
+    np.testing.assert_array_equal(gst[others], f(st0)[others])
+    return t, out
+
+
+@pytest.mark.parametrize("label,kw,opts", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_selective_scan_parity(dev, ssm, oracle, label, kw, opts):
+    spec = W.tiny(**kw)
+    t = W.make(spec, dev)
+    if not opts.get("softplus", True):
+        # raw steps (no softplus, no bias): keep them positive, |dt| + 0.01
+        t["dt"].abs_().add_(0.01)
+    run_scan(ssm, oracle, dev, spec, opts, label, t=t)
+
+
+def test_scan_no_state_cache(dev, ssm, oracle):
+    spec = W.tiny(io="f16", seqlen=200, nheads=16, index_sensitive=True)
+    t = W.make(spec, dev)
+    out = ssm.selective_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             dt_bias=t["dt_bias"])
+    torch.cuda.synchronize()
+    o, s, _, _ = oracle.selective_scan(f(t["x"]), f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
+                                       D=f(t["D"]), z=f(t["z"]), dt_bias=f(t["dt_bias"]))
+    check(out, o, s, 3e-3, "f16", "scan without cache")
+
+
+# -------------------------------------------------------------------- SSU
+SSU_CASES = [
+    # (label, spec kwargs, options)
+    ("m1_N16_f32", dict(seqlen=1, nheads=300, dstate=16, io="f16", state="f32", batch=7,
+                        nslots=20, random_slots=True, index_sensitive=True), dict(pad=3)),
+    ("m1_N16_f16", dict(seqlen=1, nheads=64, dstate=16, io="f16", state="f16", batch=5,
+                        nslots=6, random_slots=True, index_sensitive=True), {}),
+    ("m2_hd64_N128_f16", dict(seqlen=1, nheads=80, headdim=64, dstate=128, io="f16", state="f16",
+                              a_per_state=False, batch=3, index_sensitive=True), {}),
+    ("m2_hd64_N128_G8_f32", dict(seqlen=1, nheads=80, headdim=64, dstate=128, ngroups=8, io="f16",
+                                 state="f32", a_per_state=False, batch=2, index_sensitive=True),
+     {}),
+    ("m2_hd128_N256_bf16", dict(seqlen=1, nheads=8, headdim=128, dstate=256, io="bf16",
+                                state="bf16", a_per_state=False, batch=3, nslots=11,
+                                random_slots=True, index_sensitive=True), dict(pad=2)),
+    ("m2_hd128_N256_f32io", dict(seqlen=1, nheads=4, headdim=128, dstate=256, io="f32",
+                                 state="f32", a_per_state=False, batch=2, index_sensitive=True),
+     {}),
+    ("N5_scalar_path", dict(seqlen=1, nheads=6, headdim=3, dstate=5, io="f32", state="f32",
+                            a_per_state=False, batch=2, index_sensitive=True), {}),
+    ("N24_pad_lanes", dict(seqlen=1, nheads=6, headdim=3, dstate=24, io="f32", state="f16",
+                           a_per_state=True, batch=2, index_sensitive=True), {}),
+    ("N512", dict(seqlen=1, nheads=2, headdim=4, dstate=512, io="bf16", state="f32",
+                  a_per_state=False, batch=2, index_sensitive=True), {}),
+    ("hd1_noz_noD", dict(seqlen=1, nheads=50, dstate=16, io="f32", state="f32", batch=3,
+                         index_sensitive=True), dict(z=False, D=False, bias=False)),
+]
+
+
+def run_ssu(ssm, oracle, dev, spec, opts, label, t=None):
+    t = t or W.make(spec, dev)
+    z = t["z"] if opts.get("z", True) else None
+    D = t["D"] if opts.get("D", True) else None
+    bias = t["dt_bias"] if opts.get("bias", True) else None
+    idx = _pad(t["slot_idx"], opts.get("pad", 0))
+    st0 = t["ssm_state"].clone()
+    out0 = torch.full_like(t["x"], 3.0)
+    out = ssm.state_update(t["ssm_state"], t["x"], t["dt"], t["A"], t["B"], t["C"], D=D, z=z,
+                           dt_bias=bias, slot_idx=idx, out=out0.clone())
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    o, s, st, sts = oracle.state_update(
+        f(st0), f(t["x"]), f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
+        D=None if D is None else f(D), z=None if z is None else f(z),
+        dt_bias=None if bias is None else f(bias), slot_idx=idx_np, out=f(out0))
+    check(out, o, s, RTOL[spec.io], spec.io, f"ssu {label} out")
+    named = _named(idx_np)
+    gst = f(t["ssm_state"])
+    check(gst[named], st[named], sts[named], RTOL[spec.io], spec.state, f"ssu {label} state")
+    others = np.setdiff1d(np.arange(spec.slots), named)
+    np.testing.assert_array_equal(gst[others], f(st0)[others])
+
+
+@pytest.mark.parametrize("label,kw,opts", SSU_CASES, ids=[c[0] for c in SSU_CASES])
+def test_state_update_parity(dev, ssm, oracle, label, kw, opts):
+    run_ssu(ssm, oracle, dev, W.tiny(**kw), opts, label)
+
+
+# ------------------------------------------------------------- invariants
+def test_scan_equals_chained_gpu_updates(dev, ssm):
+    """A GPU scan over L tokens equals L chained GPU state updates (float32
+    state, float32 I/O): both from the same cached initial state."""
+    spec = W.tiny(io="f32", state="f32", seqlen=37, nheads=4, headdim=8, dstate=32,
+                  a_per_state=False, index_sensitive=True, batch=2, nslots=3, random_slots=True)
+    t = W.make(spec, dev)
+    st_chain = t["ssm_state"].clone()
+    out = ssm.selective_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             dt_bias=t["dt_bias"], ssm_state=t["ssm_state"],
+                             slot_idx=t["slot_idx"], has_initial_state=True)
+    outs = []
+    for s in range(spec.seqlen):
+        x = t["x"][:, :, s].contiguous().view(2, 4, 8)
+        z = t["z"][:, :, s].contiguous().view(2, 4, 8)
+        y = ssm.state_update(st_chain, x, t["dt"][:, :, s].contiguous(), t["A"],
+                             t["B"][..., s].contiguous(), t["C"][..., s].contiguous(), D=t["D"],
+                             z=z, dt_bias=t["dt_bias"], slot_idx=t["slot_idx"])
+        outs.append(y.view(2, 32))
+    torch.cuda.synchronize()
+    chain = torch.stack(outs, dim=2)
+    err = (chain - out).abs().max().item()
+    scale = out.abs().max().item()
+    assert err <= 2e-5 * scale, (err, scale)
+    serr = (st_chain - t["ssm_state"]).abs().max().item()
+    assert serr <= 2e-5 * t["ssm_state"].abs().max().item()
+
+
+def test_prefill_then_decode_resumes(dev, ssm, oracle):
+    """Prefill writes the final state and conv tail to the slot; decode steps
+    continue from them (checked against one oracle pass over the whole
+    sequence)."""
+    L1, L2 = 40, 3
+    spec = W.tiny(io="f32", seqlen=L1 + L2, nheads=24, index_sensitive=True, nslots=4,
+                  random_slots=True, batch=2)
+    t = W.make(spec, dev)
+    x = t["x"]
+    cs, ss = t["conv_state"], t["ssm_state"]
+    idx = t["slot_idx"]
+    u1 = ssm.causal_conv1d(x[..., :L1].contiguous(), t["conv_w"], t["conv_b"], conv_state=cs,
+                           slot_idx=idx, has_initial_state=False)
+    y1 = ssm.selective_scan(u1, t["dt"][..., :L1].contiguous(), t["A"],
+                            t["B"][..., :L1].contiguous(), t["C"][..., :L1].contiguous(),
+                            D=t["D"], z=t["z"][..., :L1].contiguous(), dt_bias=t["dt_bias"],
+                            ssm_state=ss, slot_idx=idx, has_initial_state=False)
+    ys = []
+    for s in range(L1, L1 + L2):
+        u = ssm.causal_conv1d(x[..., s:s + 1].contiguous(), t["conv_w"], t["conv_b"],
+                              conv_state=cs, slot_idx=idx, has_initial_state=True)
+        y = ssm.state_update(ss, u.view(2, 24, 1), t["dt"][..., s].contiguous(), t["A"],
+                             t["B"][..., s].contiguous(), t["C"][..., s].contiguous(), D=t["D"],
+                             z=t["z"][..., s].contiguous().view(2, 24, 1), dt_bias=t["dt_bias"],
+                             slot_idx=idx)
+        ys.append(y.view(2, 24, 1))
+    torch.cuda.synchronize()
+    got = torch.cat([y1] + ys, dim=2)
+    uo, _, _ = oracle.causal_conv1d(f(x), f(t["conv_w"]), f(t["conv_b"]), None, None)
+    o, sc, _, _ = oracle.selective_scan(uo, f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
+                                        D=f(t["D"]), z=f(t["z"]), dt_bias=f(t["dt_bias"]))
+    check(got, o, sc, 1e-5, "f32", "prefill+decode resume")
+
+
+def test_graph_replay_matches_eager(dev, ssm):
+    """The entry points are capturable: a HIP graph of conv + scan + update,
+    replayed several times with eager work in between, matches eager runs."""
+    spec = W.tiny(io="f16", seqlen=128, nheads=32, index_sensitive=True)
+    t = W.make(spec, dev)
+    d = W.make(W.decode(batch=3, nslots=5, nheads=64, seed=21), dev)
+    out_u = torch.empty_like(t["x"])
+    out_y = torch.empty_like(t["x"])
+    out_d = torch.empty_like(d["x"])
+
+    def body():
+        ssm.causal_conv1d(t["x"], t["conv_w"], t["conv_b"], out=out_u)
+        ssm.selective_scan(out_u, t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           dt_bias=t["dt_bias"], out=out_y)
+        ssm.state_update(d["ssm_state"], d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"],
+                         z=d["z"], dt_bias=d["dt_bias"], slot_idx=d["slot_idx"], out=out_d)
+
+    st_init = d["ssm_state"].clone()
+    refs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            body()
+            refs.append((out_y.clone(), out_d.clone(), d["ssm_state"].clone()))
+    torch.cuda.current_stream().wait_stream(s)
+    d["ssm_state"].copy_(st_init)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    d["ssm_state"].copy_(st_init)
+    for k in range(3):
+        out_y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_y, refs[k][0])
+        assert torch.equal(out_d, refs[k][1])
+        assert torch.equal(d["ssm_state"], refs[k][2])
+        _ = (t["x"].float() * 2).sum().item()  # eager work between replays

@@ -22,10 +22,14 @@ def test_softplus_special_values(oracle):
     assert oracle.softplus(0.0) == pytest.approx(math.log(2.0), rel=1e-15)
     for v in np.linspace(-30, 30, 61):
         assert oracle.softplus(v) - oracle.softplus(-v) == pytest.approx(v, abs=1e-12)
-    assert oracle.softplus(-40.0) == pytest.approx(math.exp(-40.0), rel=1e-15)
+    # (absolute tolerance 0: the naive log(1 + e^v) returns 0 at v = -40)
+    assert oracle.softplus(-40.0) == pytest.approx(math.exp(-40.0), rel=1e-15, abs=0)
     assert oracle.softplus(-12.0) == pytest.approx(math.exp(-12.0) - math.exp(-24.0) / 2
-                                                   + math.exp(-36.0) / 3, rel=1e-15)
+                                                   + math.exp(-36.0) / 3, rel=1e-15, abs=0)
+    for v in (-25.0, -18.0, -9.5):
+        assert oracle.softplus(v) == pytest.approx(math.log1p(math.exp(v)), rel=1e-15, abs=0)
     assert oracle.softplus(700.0) == 700.0
+    assert oracle.softplus(710.0) == 710.0
 
 
 def test_silu_special_values(oracle):
@@ -36,6 +40,7 @@ def test_silu_special_values(oracle):
     assert oracle.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
     assert oracle.silu(50.0) == pytest.approx(50.0, rel=1e-15)
     assert abs(oracle.silu(-50.0)) < 1e-19
+    assert oracle.silu(-30.0) == pytest.approx(-30.0 * math.exp(-30.0), rel=1e-12, abs=0)
 
 
 # ----------------------------------------------------------- rounding helpers
