@@ -20,7 +20,7 @@
 //     row shifts (4 steps), and each lane then re-runs its 16 steps from the
 //     exact incoming state, accumulating C_t[n] h_t[n] into its outputs.  The
 //     tile-end state of each channel (lane 15's scan result, rotated into lane
-//     0) carries to the next tile through LDS.
+//     0) carries to the next tile in registers (through LDS when dstate > 16).
 //   * Mamba-2 (one decay per head, a_per_state == 0): the decays and their
 //     row scan are state-independent and are computed once per tile.
 // All arithmetic is float32; the state never leaves the chip until the final
@@ -91,7 +91,7 @@ __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int L,
     }
 }
 
-template <typename TI, typename TS, bool A_PER_STATE, bool VEC, int NCAP>
+template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
 {
     constexpr int E = 16 / StorageSize<TI>::value;
@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
     // so the 16 lanes of a row read 16 consecutive float4s (no bank conflict).
     __shared__ float4 lds_b[NC * T / 4];
     __shared__ float4 lds_c[NC * T / 4];
-    __shared__ float lds_carry[CPB][NCAP];
+    // states beyond the first chunk keep their carries here between tiles
+    __shared__ float lds_carry[ONE_CHUNK ? 1 : CPB][ONE_CHUNK ? 1 : kMaxScanDstate];
 
     const int L = a.seqlen, N = a.dstate, P = a.headdim;
     const int cpg = a.heads_per_group * P;  // channels per group (contiguous)
@@ -127,13 +128,25 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
     const TI *Bg = static_cast<const TI *>(a.B) + ((int64_t)b * a.ngroups + g) * N * L;
     const TI *Cg = static_cast<const TI *>(a.C) + ((int64_t)b * a.ngroups + g) * N * L;
     TS *srow = a.state ? static_cast<TS *>(a.state) + (((int64_t)slot * a.nheads + h) * P + p) * N : nullptr;
+    const bool load_init = srow && a.has_initial_state;
 
     const float bias_h = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float D_h = a.D ? a.D[h] : 0.0f;
     const float A2_h = A_PER_STATE ? 0.0f : a.A[h] * kLog2e;
 
-    for (int n = r; n < N; n += R)
-        lds_carry[ch][n] = (srow && a.has_initial_state) ? to_f32(srow[n]) : 0.0f;
+    // carry[nl]: on lane 0 of the row, the state entering the current tile of
+    // state n0+nl (zero on the other lanes); A2[nl] = A[h, n0+nl] * log2(e)
+    float carry[NC], A2[NC];
+    if constexpr (ONE_CHUNK) {
+#pragma unroll
+        for (int nl = 0; nl < NC; ++nl) {
+            carry[nl] = (r == 0 && load_init && nl < N) ? to_f32(srow[nl]) : 0.0f;
+            A2[nl] = A_PER_STATE ? ((nl < N) ? a.A[(int64_t)h * N + nl] * kLog2e : 0.0f) : A2_h;
+        }
+    } else {
+        for (int n = r; n < N; n += R)
+            lds_carry[ch][n] = load_init ? to_f32(srow[n]) : 0.0f;
+    }
 
     for (int t0 = 0; t0 < L; t0 += T) {
         const int tl = t0 + r * K;
@@ -166,11 +179,11 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                 am[i] = exp2_hw(dl[i] * A2_h);
             float ag = exp2_hw(sdl * A2_h);
             acum[0] = ag;
-            ag *= dpp_move<DPP_ROW_SHR1>(1.0f, ag);
+            ag *= dpp_move_zero<DPP_ROW_SHR1>(ag);
             acum[1] = ag;
-            ag *= dpp_move<DPP_ROW_SHR2>(1.0f, ag);
+            ag *= dpp_move_zero<DPP_ROW_SHR2>(ag);
             acum[2] = ag;
-            ag *= dpp_move<DPP_ROW_SHR4>(1.0f, ag);
+            ag *= dpp_move_zero<DPP_ROW_SHR4>(ag);
             acum[3] = ag;
         }
 
@@ -199,10 +212,23 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                     lds_c[idx] = make_float4(vc[4 * e4], vc[4 * e4 + 1], vc[4 * e4 + 2], vc[4 * e4 + 3]);
                 }
             }
+            if constexpr (!ONE_CHUNK) {
+#pragma unroll
+                for (int nl = 0; nl < NC; ++nl) {
+                    const int n = min(n0 + nl, N - 1);
+                    A2[nl] = A_PER_STATE ? a.A[(int64_t)h * N + n] * kLog2e : A2_h;
+                }
+            }
             __syncthreads();
-            const int nc = min(NC, N - n0);
-            for (int nl = 0; nl < nc; ++nl) {
-                const int n = n0 + nl;
+            if constexpr (!ONE_CHUNK) {
+#pragma unroll
+                for (int nl = 0; nl < NC; ++nl)
+                    carry[nl] = (r == 0 && n0 + nl < N) ? lds_carry[ch][n0 + nl] : 0.0f;
+            }
+#pragma unroll
+            for (int nl = 0; nl < NC; ++nl) {
+                if (n0 + nl >= N)
+                    break;
                 float Bv[K], Cv[K];
 #pragma unroll
                 for (int q = 0; q < K / 4; ++q) {
@@ -214,11 +240,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                 float av[K], bx[K];
                 float aagg, bagg = 0.0f;
                 if constexpr (A_PER_STATE) {
-                    const float A2 = a.A[(int64_t)h * N + n] * kLog2e;
 #pragma unroll
                     for (int i = 0; i < K; ++i)
-                        av[i] = exp2_hw(dl[i] * A2);
-                    aagg = exp2_hw(sdl * A2);
+                        av[i] = exp2_hw(dl[i] * A2[nl]);
+                    aagg = exp2_hw(sdl * A2[nl]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < K; ++i)
@@ -230,35 +255,43 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                     bx[i] = du[i] * Bv[i];
                     bagg = fmaf(av[i], bagg, bx[i]);
                 }
-                const float carry = (r == 0) ? lds_carry[ch][n] : 0.0f;
-                bagg = fmaf(aagg, carry, bagg);  // lane 0 starts from the incoming state
-                // inclusive scan of the affine maps over the 16 lanes of the row
+                bagg = fmaf(aagg, carry[nl], bagg);  // lane 0 starts from the incoming state
+                // inclusive scan of the affine maps over the 16 lanes of the row.
+                // Lanes whose source lies before lane 0 read 0: the b term then
+                // adds nothing, and the decay products they corrupt belong to
+                // segments that start at lane 0, which no later step multiplies
+                // into a valid combine (nothing precedes lane 0).
                 if constexpr (A_PER_STATE) {
-                    float bp, ap;
-                    bp = dpp_move<DPP_ROW_SHR1>(0.0f, bagg); ap = dpp_move<DPP_ROW_SHR1>(1.0f, aagg);
-                    bagg = fmaf(aagg, bp, bagg); aagg *= ap;
-                    bp = dpp_move<DPP_ROW_SHR2>(0.0f, bagg); ap = dpp_move<DPP_ROW_SHR2>(1.0f, aagg);
-                    bagg = fmaf(aagg, bp, bagg); aagg *= ap;
-                    bp = dpp_move<DPP_ROW_SHR4>(0.0f, bagg); ap = dpp_move<DPP_ROW_SHR4>(1.0f, aagg);
-                    bagg = fmaf(aagg, bp, bagg); aagg *= ap;
-                    bp = dpp_move<DPP_ROW_SHR8>(0.0f, bagg);
-                    bagg = fmaf(aagg, bp, bagg);
+                    bagg = fmaf(aagg, dpp_move_zero<DPP_ROW_SHR1>(bagg), bagg);
+                    aagg *= dpp_move_zero<DPP_ROW_SHR1>(aagg);
+                    bagg = fmaf(aagg, dpp_move_zero<DPP_ROW_SHR2>(bagg), bagg);
+                    aagg *= dpp_move_zero<DPP_ROW_SHR2>(aagg);
+                    bagg = fmaf(aagg, dpp_move_zero<DPP_ROW_SHR4>(bagg), bagg);
+                    aagg *= dpp_move_zero<DPP_ROW_SHR4>(aagg);
+                    bagg = fmaf(aagg, dpp_move_zero<DPP_ROW_SHR8>(bagg), bagg);
                 } else {
-                    bagg = fmaf(acum[0], dpp_move<DPP_ROW_SHR1>(0.0f, bagg), bagg);
-                    bagg = fmaf(acum[1], dpp_move<DPP_ROW_SHR2>(0.0f, bagg), bagg);
-                    bagg = fmaf(acum[2], dpp_move<DPP_ROW_SHR4>(0.0f, bagg), bagg);
-                    bagg = fmaf(acum[3], dpp_move<DPP_ROW_SHR8>(0.0f, bagg), bagg);
+                    bagg = fmaf(acum[0], dpp_move_zero<DPP_ROW_SHR1>(bagg), bagg);
+                    bagg = fmaf(acum[1], dpp_move_zero<DPP_ROW_SHR2>(bagg), bagg);
+                    bagg = fmaf(acum[2], dpp_move_zero<DPP_ROW_SHR4>(bagg), bagg);
+                    bagg = fmaf(acum[3], dpp_move_zero<DPP_ROW_SHR8>(bagg), bagg);
                 }
                 // lane r >= 1 starts from lane r-1's end state; lane 0 from the
                 // carry, and receives lane 15's end state as the next carry
-                const float rot = dpp_move<DPP_ROW_ROR1>(0.0f, bagg);
-                float hh = (r == 0) ? carry : rot;
-                if (r == 0)
-                    lds_carry[ch][n] = rot;
+                const float rot = dpp_move_zero<DPP_ROW_ROR1>(bagg);
+                float hh = (r == 0) ? carry[nl] : rot;
+                carry[nl] = (r == 0) ? rot : 0.0f;
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
                     hh = fmaf(av[i], hh, bx[i]);
                     y[i] = fmaf(Cv[i], hh, y[i]);
+                }
+            }
+            if constexpr (!ONE_CHUNK) {
+                if (r == 0) {
+#pragma unroll
+                    for (int nl = 0; nl < NC; ++nl)
+                        if (n0 + nl < N)
+                            lds_carry[ch][n0 + nl] = carry[nl];
                 }
             }
         }
@@ -272,19 +305,28 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
         if (active)
             store_steps<TI, VEC>(orow, tl, L, y);
     }
-    __syncthreads();
-    if (srow && active)
-        for (int n = r; n < N; n += R)
-            srow[n] = from_f32<TS>(lds_carry[ch][n]);
+    if constexpr (ONE_CHUNK) {
+        if (srow && active && r == 0) {
+#pragma unroll
+            for (int nl = 0; nl < NC; ++nl)
+                if (nl < N)
+                    srow[nl] = from_f32<TS>(carry[nl]);
+        }
+    } else {
+        __syncthreads();
+        if (srow && active)
+            for (int n = r; n < N; n += R)
+                srow[n] = from_f32<TS>(lds_carry[ch][n]);
+    }
 }
 
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC>
 static void launch_scan_v(const ScanArgs &a, dim3 grid, hipStream_t stream)
 {
-    if (a.dstate <= 16)
-        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, 16>), grid, dim3(256), 0, stream, a);
+    if (a.dstate <= NC)
+        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, kMaxScanDstate>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false>), grid, dim3(256), 0, stream, a);
 }
 
 template <typename TI, typename TS>

@@ -163,22 +163,22 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 // log1p(e) for e in [0, 1], accurate to a few ulp.  w = 1 + e is rounded; the
 // factor e / (w - 1) corrects the rounding of w exactly to first order
 // (Goldberg, "What every computer scientist should know about floating-point
-// arithmetic", 1991, Theorem 4).
+// arithmetic", 1991, Theorem 4).  Branch-free.
 __device__ __forceinline__ float log1p_unit(float e)
 {
     const float w = 1.0f + e;
     const float d = w - 1.0f;
-    return d == 0.0f ? e : log2_hw(w) * kLn2 * (e / d);
+    const float l = log2_hw(w) * kLn2 * (e * rcp_hw(d));
+    return d == 0.0f ? e : l;
 }
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^{-|v|}); for v > 20 the
-// second term is below 2.1e-9 and v alone is returned.
+// second term is below 2.1e-9 and v alone is returned.  Branch-free.
 __device__ __forceinline__ float softplus_f32(float v)
 {
-    if (v > 20.0f)
-        return v;
     const float e = exp2_hw(-fabsf(v) * kLog2e);
-    return fmaxf(v, 0.0f) + log1p_unit(e);
+    const float r = fmaxf(v, 0.0f) + log1p_unit(e);
+    return v > 20.0f ? v : r;
 }
 
 // SiLU(v) = v / (1 + e^{-v}).
@@ -204,6 +204,15 @@ __device__ __forceinline__ float dpp_move(float old, float src)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL,
                                                       0xf, 0xf, false));
+}
+
+// Same, but lanes whose source falls outside the row read 0 (bound_ctrl).  No
+// "old" operand has to be materialised, so the move can fold into the VALU
+// instruction that consumes it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move_zero(float src)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(src), CTRL, 0xf, 0xf, true));
 }
 
 // ---------------------------------------------------------------- block order

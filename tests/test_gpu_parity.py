@@ -340,3 +340,27 @@ def test_graph_replay_matches_eager(dev, ssm):
         assert torch.equal(out_d, refs[k][1])
         assert torch.equal(d["ssm_state"], refs[k][2])
         _ = (t["x"].float() * 2).sum().item()  # eager work between replays
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_softplus_step_accuracy(dev, ssm, oracle, io):
+    """The step size alone: a one-step scan with B = C = u = 1, D = 0, no gate
+    and a single state returns delta = softplus(dt + bias) itself, over raw
+    values from -30 to 25 (both exp tails and the log1p-sensitive middle)."""
+    nv = 2048
+    v = torch.linspace(-30.0, 25.0, nv, dtype=torch.float64)
+    dtype = W.DTYPES[io]
+    dt = v.to(dtype).view(1, nv, 1).to(dev)
+    one = torch.ones(1, nv, 1, dtype=dtype, device=dev)
+    Bm = torch.ones(1, 1, 1, 1, dtype=dtype, device=dev)
+    A = -torch.ones(nv, 1, dtype=torch.float32, device=dev)
+    out = ssm.selective_scan(one, dt, A, Bm, Bm.clone(), D=None, z=None, dt_bias=None)
+    torch.cuda.synchronize()
+    want = np.array([oracle.softplus(x) for x in f(dt).ravel()])
+    got = f(out).ravel()
+    # float32: a few ulp, plus the rounding of the exponent argument |v|*log2(e)
+    # (about |v| * 6e-8 relative); the bf16 store adds half an ulp
+    x = np.abs(f(dt).ravel())
+    tol = (4e-7 + 1e-7 * x) * np.abs(want) + (0.5 * 2.0 ** -7 * np.abs(want) if io == "bf16" else 0.0)
+    bad = np.abs(got - want) > tol
+    assert not bad.any(), (f(dt).ravel()[bad][:5], got[bad][:5], want[bad][:5])
