@@ -39,7 +39,7 @@ constexpr int NC = 16;       // states per LDS chunk of B/C
 } // namespace
 
 // Load timesteps [tl, tl+K) of one row (zeros past the end of the sequence).
-template <typename TI, bool VEC, bool STREAM>
+template <typename TI, bool VEC>
 __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, int L, float (&dst)[K])
 {
     constexpr int E = 16 / StorageSize<TI>::value;
@@ -48,10 +48,7 @@ __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, i
         for (int v = 0; v < K / E; ++v) {
             float part[E];
             if (tl + (v + 1) * E <= L) {
-                if constexpr (STREAM)
-                    load_vec<TI, E>(row + tl + v * E, part);
-                else
-                    load_vec_cached<TI, E>(row + tl + v * E, part);
+                load_vec_cached<TI, E>(row + tl + v * E, part);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
@@ -80,7 +77,7 @@ __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int L,
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     part[e] = src[v * E + e];
-                store_vec<TI, E>(row + tl + v * E, part);
+                store_vec_cached<TI, E>(row + tl + v * E, part);
             }
         }
     } else {
@@ -153,8 +150,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
         float dl[K], du[K], y[K];
         {
             float uu[K], dd[K];
-            load_steps<TI, VEC, true>(urow, tl, L, uu);
-            load_steps<TI, VEC, true>(dtrow, tl, L, dd);
+            load_steps<TI, VEC>(urow, tl, L, uu);
+            load_steps<TI, VEC>(dtrow, tl, L, dd);
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 const float v = dd[i] + bias_h;
@@ -225,7 +222,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                 for (int nl = 0; nl < NC; ++nl)
                     carry[nl] = (r == 0 && n0 + nl < N) ? lds_carry[ch][n0 + nl] : 0.0f;
             }
-#pragma unroll
+#pragma unroll 1
             for (int nl = 0; nl < NC; ++nl) {
                 if (n0 + nl >= N)
                     break;
@@ -297,7 +294,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
         }
         if (zrow) {
             float zz[K];
-            load_steps<TI, VEC, true>(zrow, tl, L, zz);
+            load_steps<TI, VEC>(zrow, tl, L, zz);
 #pragma unroll
             for (int i = 0; i < K; ++i)
                 y[i] *= silu_f32(zz[i]);

@@ -171,8 +171,11 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const 
         !aligned(C, es) || !aligned(z, es) || !aligned(out, es) || !aligned(A, 4) ||
         !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(slot_idx, 4))
         return SSM_ERR_ALIGN;
-    // lanes per (b,h,p) row: ceil(dstate/8) rounded up to a power of two (<= 64)
-    int lanes = (dstate + 7) / 8, lg = 0;
+    // states per lane: 16 for rows of >= 32 states that are a multiple of 16
+    // (more bytes in flight per lane), else 8; lanes per (b,h,p) row:
+    // ceil(dstate/V) rounded up to a power of two (<= 64)
+    const int V = (dstate % 16 == 0 && dstate >= 32) ? 16 : 8;
+    int lanes = (dstate + V - 1) / V, lg = 0;
     while ((1 << lg) < lanes)
         ++lg;
     const int64_t nrows = (int64_t)batch * nheads * headdim;
@@ -201,11 +204,13 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const 
     a.nslots = nslots;
     a.heads_per_group = nheads / ngroups;
     a.lanes_per_row_log2 = lg;
+    a.states_per_lane = V;
     a.io_dtype = io_dtype;
     a.state_dtype = state_dtype;
     a.a_per_state = a_per_state ? 1 : 0;
     a.dt_softplus = dt_softplus ? 1 : 0;
-    a.vec = (dstate % 8 == 0) && aligned(state, 16) && aligned(B, 16) && aligned(C, 16);
+    a.vec = (dstate % 8 == 0) && aligned(state, 16) && aligned(B, 16) && aligned(C, 16) &&
+            aligned(A, 16);
     return status_of(ssm::launch_ssu(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -10,18 +10,17 @@
 // with h' written back to state[s,h,p,n] in the cache dtype.
 //
 // Design: the kernel is bound by streaming the state cache once (read +
-// write).  One lane owns 8 consecutive states of one (b,h,p) row, so a row of
-// dstate states is dstate/8 lanes (rounded up to a power of two that divides
-// 64) and a wave covers 64*8 consecutive states: 2 KiB (f32) or 1 KiB
-// (f16/bf16) of contiguous cache per wave, read and written with 128-bit
-// accesses.  The readout sum over states is a butterfly across the row's
-// lanes.  No LDS, no barriers.
+// write).  One lane owns V (8 or 16) consecutive states of one (b,h,p) row, so
+// a row of dstate states is dstate/V lanes (rounded up to a power of two that
+// divides 64) and a wave covers 64*V consecutive states of the cache, read and
+// written with 128-bit accesses.  The readout sum over states is a butterfly
+// across the row's lanes.  No LDS, no barriers.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
 namespace ssm {
 
-template <typename TS, typename TI, bool A_PER_STATE, bool VEC>
+template <typename TS, typename TI, bool A_PER_STATE, bool VEC, int V>
 __global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
 {
     const int lpr_log2 = a.lanes_per_row_log2;
@@ -38,7 +37,7 @@ __global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
     if (slot < 0)
         return;  // padded request: nothing read or written
     const int g = h / a.heads_per_group;
-    const int n0 = j * 8;
+    const int n0 = j * V;
 
     const TI *dtp = static_cast<const TI *>(a.dt);
     const TI *xp = static_cast<const TI *>(a.x);
@@ -53,14 +52,14 @@ __global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
         const int64_t bc_off = ((int64_t)b * a.ngroups + g) * a.dstate + n0;
         const TI *Bp = static_cast<const TI *>(a.B) + bc_off;
         const TI *Cp = static_cast<const TI *>(a.C) + bc_off;
-        float hs[8], bv[8], cv[8];
+        float hs[V], bv[V], cv[V];
         if constexpr (VEC) {
-            load_vec_cached<TS, 8>(sp, hs);
-            load_vec_cached<TI, 8>(Bp, bv);
-            load_vec_cached<TI, 8>(Cp, cv);
+            load_vec_cached<TS, V>(sp, hs);
+            load_vec_cached<TI, V>(Bp, bv);
+            load_vec_cached<TI, V>(Cp, cv);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < V; ++i) {
                 const bool ok = n0 + i < a.dstate;
                 hs[i] = ok ? to_f32(sp[i]) : 0.0f;
                 bv[i] = ok ? to_f32(Bp[i]) : 0.0f;
@@ -68,27 +67,34 @@ __global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
             }
         }
         if constexpr (A_PER_STATE) {
+            float an[V];
             const float *Ap = a.A + (int64_t)h * a.dstate + n0;
+            if constexpr (VEC) {
+                load_vec_cached<float, V>(Ap, an);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float an = (VEC || n0 + i < a.dstate) ? Ap[i] : 0.0f;
-                const float dA = exp2_hw(delta * (an * kLog2e));
+                for (int i = 0; i < V; ++i)
+                    an[i] = (n0 + i < a.dstate) ? Ap[i] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const float dA = exp2_hw(delta * (an[i] * kLog2e));
                 hs[i] = fmaf(dA, hs[i], dx * bv[i]);
                 y = fmaf(cv[i], hs[i], y);
             }
         } else {
             const float dA = exp2_hw(delta * (a.A[h] * kLog2e));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < V; ++i) {
                 hs[i] = fmaf(dA, hs[i], dx * bv[i]);
                 y = fmaf(cv[i], hs[i], y);
             }
         }
         if constexpr (VEC) {
-            store_vec_cached<TS, 8>(sp, hs);
+            store_vec_cached<TS, V>(sp, hs);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < V; ++i)
                 if (n0 + i < a.dstate)
                     sp[i] = from_f32<TS>(hs[i]);
         }
@@ -110,17 +116,22 @@ static hipError_t launch_ssu_t(const SsuArgs &a, hipStream_t stream)
 {
     const int64_t threads = a.nrows << a.lanes_per_row_log2;
     const dim3 grid((unsigned)((threads + 255) / 256));
-    if (a.a_per_state) {
-        if (a.vec)
-            hipLaunchKernelGGL((ssu_kernel<TS, TI, true, true>), grid, dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((ssu_kernel<TS, TI, true, false>), grid, dim3(256), 0, stream, a);
+#define SSU_LAUNCH(APS, VEC, V) \
+    hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V>), grid, dim3(256), 0, stream, a)
+    if (a.states_per_lane == 16) {
+        if (a.a_per_state) {
+            if (a.vec) SSU_LAUNCH(true, true, 16); else SSU_LAUNCH(true, false, 16);
+        } else {
+            if (a.vec) SSU_LAUNCH(false, true, 16); else SSU_LAUNCH(false, false, 16);
+        }
     } else {
-        if (a.vec)
-            hipLaunchKernelGGL((ssu_kernel<TS, TI, false, true>), grid, dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((ssu_kernel<TS, TI, false, false>), grid, dim3(256), 0, stream, a);
+        if (a.a_per_state) {
+            if (a.vec) SSU_LAUNCH(true, true, 8); else SSU_LAUNCH(true, false, 8);
+        } else {
+            if (a.vec) SSU_LAUNCH(false, true, 8); else SSU_LAUNCH(false, false, 8);
+        }
     }
+#undef SSU_LAUNCH
     return hipGetLastError();
 }
 
