@@ -32,7 +32,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+# fp32 vector FMA rate without packed-FP32 forms: 256 CUs x 4 SIMDs x 16 lanes
+# x 2 flop x 2.4 GHz (the published 157.3 TFLOP/s counts packed FP32)
+VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp"],
+                  "state_update": ["ssu.hip", "ssm_device.hpp"],
+                  "conv1d_prefill": ["conv1d.hip", "ssm_device.hpp"],
+                  "conv1d_decode": ["conv1d.hip", "ssm_device.hpp"]}
+# rocprofv3 kernel names of each kernel in the benchmarked configuration
+KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "state_update": "ssu_kernel",
+                  "conv1d_prefill": "conv_prefill_kernel", "conv1d_decode": "conv_decode_kernel"}
 
 
 def parse():
@@ -47,7 +57,135 @@ def parse():
                    help="only run a plain 1 GiB device copy (for counter calibration)")
     p.add_argument("--only", choices=["prefill", "decode"], default=None,
                    help="run only one half of the step (for profiling)")
+    p.add_argument("--profile-script", metavar="OUTDIR",
+                   help="print the rocprofv3 commands whose output --summarize-profile reads")
+    p.add_argument("--summarize-profile", metavar="OUTDIR",
+                   help="turn rocprofv3 CSV output under OUTDIR into profiles/ summaries")
     return p.parse_args()
+
+
+SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+               "SQ_WAIT_INST_ANY SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT")
+
+
+def profile_commands(out):
+    """The rocprofv3 runs behind the committed profiles: a kernel trace with
+    stats, then one counter per pass (FETCH_SIZE, WRITE_SIZE) on the step and
+    on a plain 1 GiB device copy (the calibration), and the SQ counters of the
+    prefill half."""
+    b = "python -u bench.py --no-cpu-baseline"
+    pmc = "timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d {o}/{n} -o run -- {cmd}"
+    return [
+        ("trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d {out}/trace "
+                  f"-o run -- {b} --steps 20 --warmup 5"),
+        ("fetch", pmc.format(c="FETCH_SIZE", o=out, n="fetch", cmd=f"{b} --steps 3 --warmup 1")),
+        ("write", pmc.format(c="WRITE_SIZE", o=out, n="write", cmd=f"{b} --steps 3 --warmup 1")),
+        ("copy_fetch", pmc.format(c="FETCH_SIZE", o=out, n="copy_fetch",
+                                  cmd="python -u bench.py --copy-calibration")),
+        ("copy_write", pmc.format(c="WRITE_SIZE", o=out, n="copy_write",
+                                  cmd="python -u bench.py --copy-calibration")),
+        ("sq", pmc.format(c=SQ_COUNTERS, o=out, n="sq",
+                          cmd=f"{b} --steps 3 --warmup 1 --only prefill")),
+    ]
+
+
+def _read_counters(path):
+    import collections
+    import csv
+
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def _match(agg, symbol):
+    """Counters of the kernels whose name contains symbol, all instantiations
+    pooled: {counter: mean per dispatch}."""
+    vals = {}
+    for name, d in agg.items():
+        if symbol in name:
+            for c, v in d.items():
+                vals.setdefault(c, []).extend(v)
+    return {c: sum(v) / len(v) for c, v in vals.items()}, sum(len(v) for v in vals.values())
+
+
+def summarize_profile(out):
+    """Write profiles/<kernel>_traffic.json and profiles/*.md from the CSVs of
+    the runs listed by profile_commands()."""
+    import csv
+    import glob
+
+    os.makedirs(PROFILES, exist_ok=True)
+    cmds = dict(profile_commands(out))
+    import workloads as W
+
+    pb, db = W.algorithmic_bytes(W.prefill()), W.algorithmic_bytes(W.decode())
+    alg = {"conv1d_prefill": pb["conv"], "selective_scan": pb["scan"],
+           "conv1d_decode": db["conv"], "state_update": db["ssu"]}
+    copy_bytes = 1 << 30
+    cf, _ = _match(_read_counters(glob.glob(f"{out}/copy_fetch/*counter_collection.csv")[0]),
+                   "copyBuffer")
+    cw, _ = _match(_read_counters(glob.glob(f"{out}/copy_write/*counter_collection.csv")[0]),
+                   "copyBuffer")
+    f_factor = copy_bytes / (cf["FETCH_SIZE"] * 1024)
+    w_factor = copy_bytes / (cw["WRITE_SIZE"] * 1024)
+    fetch = _read_counters(glob.glob(f"{out}/fetch/*counter_collection.csv")[0])
+    write = _read_counters(glob.glob(f"{out}/write/*counter_collection.csv")[0])
+    stats = list(csv.DictReader(open(glob.glob(f"{out}/trace/*kernel_stats.csv")[0])))
+    # source hashes of the kernels as profiled: from the benchmark line the
+    # traced run printed (not from the tree as it is now)
+    profiled_sha = {}
+    with open(f"{out}/trace.log") as f:
+        for ln in f:
+            if ln.startswith("{") and '"kernels"' in ln:
+                profiled_sha = {k: v.get("kernel_source_sha")
+                                for k, v in json.loads(ln)["kernels"].items()}
+
+    lines = ["# Kernel trace and HBM traffic: Mamba-1 2.8B layer step", "",
+             "Workload: prefill conv1d+scan, batch 4 x L 2048, d_inner 5120, d_state 16, f16 "
+             "I/O, f32 state; decode conv update + state update, 245 requests from a 512-slot "
+             "cache.", "", "Commands (run from the repository root on the MI355X):", ""]
+    for n, c in profile_commands(out):
+        lines.append(f"    {c}")
+    lines += ["", f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE = {cf['FETCH_SIZE']:.0f} "
+              f"KiB and WRITE_SIZE = {cw['WRITE_SIZE']:.0f} KiB per dispatch, so HBM bytes = "
+              f"FETCH_SIZE x 1024 x {f_factor:.3f} + WRITE_SIZE x 1024 x {w_factor:.3f}.", "",
+              "| kernel | calls | avg us | min us | max us | algorithmic MB | counter read MB | "
+              "counter write MB | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|---|"]
+    for k, sym in KERNEL_SYMBOLS.items():
+        rows = [r for r in stats if sym in r["Name"]]
+        calls = sum(int(r["Calls"]) for r in rows)
+        tot = sum(float(r["TotalDurationNs"]) for r in rows)
+        avg = tot / calls / 1e3 if calls else float("nan")
+        mn = min(float(r["MinNs"]) for r in rows) / 1e3 if rows else float("nan")
+        mx = max(float(r["MaxNs"]) for r in rows) / 1e3 if rows else float("nan")
+        fr, _ = _match(fetch, sym)
+        wr, _ = _match(write, sym)
+        rb = fr.get("FETCH_SIZE", float("nan")) * 1024 * f_factor
+        wb = wr.get("WRITE_SIZE", float("nan")) * 1024 * w_factor
+        lines.append(f"| {k} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {alg[k] / 1e6:.1f} | "
+                     f"{rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / alg[k]:.3f} |")
+        rec = {"kernel": k, "kernel_source_sha": profiled_sha.get(k),
+               "fetch_kib_per_dispatch": fr.get("FETCH_SIZE"),
+               "write_kib_per_dispatch": wr.get("WRITE_SIZE"),
+               "fetch_factor": f_factor, "write_factor": w_factor,
+               "hbm_bytes_per_launch": rb + wb, "algorithmic_bytes_per_launch": alg[k],
+               "avg_launch_us_trace": avg, "commands": [cmds["fetch"], cmds["write"],
+                                                       cmds["copy_fetch"], cmds["copy_write"]]}
+        with open(os.path.join(PROFILES, f"{k}_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    sq = _read_counters(glob.glob(f"{out}/sq/*counter_collection.csv")[0])
+    lines += ["", "SQ counters of the selective scan (mean per dispatch; command above, `sq`):", ""]
+    v, _ = _match(sq, KERNEL_SYMBOLS["selective_scan"])
+    for c in sorted(v):
+        lines.append(f"- {c}: {v[c]:.0f}")
+    if v.get("SQ_WAVES"):
+        lines.append(f"- VALU instructions per wave: {v['SQ_INSTS_VALU'] / v['SQ_WAVES']:.0f}")
+    with open(os.path.join(PROFILES, "mamba1_layer_step_kernels.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def kernel_source_sha(names):
@@ -73,6 +211,13 @@ def load_traffic(kernel: str, sha: str, launches_per_step: int = 1):
 
 def main():
     args = parse()
+    if args.profile_script:
+        for n, c in profile_commands(args.profile_script):
+            print(f'echo "step: {n}" && {c} > {args.profile_script}/{n}.log 2>&1 || exit 1')
+        return
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -198,7 +343,8 @@ def main():
         "conv1d_decode": {"bytes": dbytes.get("conv"), "us": k_ms[2] * 1e3},
         "state_update": {"bytes": dbytes.get("ssu"), "us": k_ms[3] * 1e3},
     }
-    for v in kernels.values():
+    for k, v in kernels.items():
+        v["kernel_source_sha"] = kernel_source_sha(KERNEL_SOURCES[k])
         v["GBps"] = gbps(v["bytes"], v["us"] * 1e-3) if v["bytes"] else None
         v["frac_hbm_peak"] = v["GBps"] / HBM_PEAK_GBPS if v["GBps"] else None
 
@@ -208,24 +354,27 @@ def main():
     # dominant kernel: the one with the largest share of the step
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
-    src = {"selective_scan": ["scan.hip", "ssm_device.hpp"],
-           "state_update": ["ssu.hip", "ssm_device.hpp"],
-           "conv1d_prefill": ["conv1d.hip", "ssm_device.hpp"],
-           "conv1d_decode": ["conv1d.hip", "ssm_device.hpp"]}[dom]
-    sha = kernel_source_sha(src)
+    sha = kernel_source_sha(KERNEL_SOURCES[dom])
     traffic = load_traffic(dom, sha)
-    roofline = {
-        "kernel": dom,
-        "bound": "hbm",
-        "achieved": dk["GBps"],
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": dk["frac_hbm_peak"],
-        "traffic": traffic,
-        "algorithmic_bytes_per_launch": dk["bytes"],
-        "avg_launch_us": dk["us"],
-        "kernel_source_sha": sha,
-    }
+    if dom == "selective_scan":
+        # The Mamba-1 scan is bound by float32 VALU work, not by HBM: one
+        # exponential (half-rate on gfx950) and four other VALU operations per
+        # (time, channel, state) element against 8 bytes of HBM traffic per
+        # (time, channel).  Its roofline is the non-packed fp32 FMA rate.
+        flops = W.algorithmic_flops(pspec)
+        achieved = flops / (dk["us"] * 1e-6) / 1e12
+        roofline = {"kernel": dom, "bound": "alu", "achieved": achieved,
+                    "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / VALU_PEAK_TFLOPS, "traffic": traffic,
+                    "algorithmic_flops_per_launch": flops,
+                    "algorithmic_bytes_per_launch": dk["bytes"],
+                    "hbm_GBps": dk["GBps"], "hbm_frac": dk["frac_hbm_peak"]}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": dk["frac_hbm_peak"], "traffic": traffic,
+                    "algorithmic_bytes_per_launch": dk["bytes"]}
+    roofline["avg_launch_us"] = dk["us"]
+    roofline["kernel_source_sha"] = sha
 
     cpu = None
     if not args.no_cpu_baseline:

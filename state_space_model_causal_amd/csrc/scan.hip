@@ -28,6 +28,8 @@
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
+#include <type_traits>
+
 namespace ssm {
 
 namespace {
@@ -39,29 +41,70 @@ constexpr int NC = 16;       // states per LDS chunk of B/C
 } // namespace
 
 // Load timesteps [tl, tl+K) of one row (zeros past the end of the sequence).
+// Every load is issued unconditionally from a clamped, in-bounds address and
+// the out-of-range values are replaced afterwards, so all loads of a lane are
+// in flight together instead of each waiting behind its own branch.
 template <typename TI, bool VEC>
 __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, int L, float (&dst)[K])
 {
     constexpr int E = 16 / StorageSize<TI>::value;
     if constexpr (VEC) {
+        // VEC: L is a positive multiple of 8 (>= E), so offset 0 is a valid vector
 #pragma unroll
         for (int v = 0; v < K / E; ++v) {
+            const int off = tl + v * E;
+            const bool ok = off + E <= L;
             float part[E];
-            if (tl + (v + 1) * E <= L) {
-                load_vec_cached<TI, E>(row + tl + v * E, part);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    part[e] = 0.0f;
-            }
+            load_vec_cached<TI, E>(row + (ok ? off : 0), part);
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                dst[v * E + e] = part[e];
+                dst[v * E + e] = ok ? part[e] : 0.0f;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < K; ++i)
-            dst[i] = (tl + i < L) ? to_f32(row[tl + i]) : 0.0f;
+        for (int i = 0; i < K; ++i) {
+            const bool ok = tl + i < L;
+            const float x = to_f32(row[ok ? tl + i : 0]);
+            dst[i] = ok ? x : 0.0f;
+        }
+    }
+}
+
+// Raw 128-bit loads of timesteps [tl, tl+K) of one row (VEC rows only),
+// issued back to back; widen() converts them once they are needed.
+template <typename TI>
+struct RawSteps {
+    static constexpr int E = 16 / StorageSize<TI>::value;
+    static constexpr int NV = K / E;
+    u32x4 w[NV];
+    bool ok[NV];
+};
+
+template <typename TI>
+__device__ __forceinline__ void load_raw(RawSteps<TI> &r, const TI *__restrict__ row, int tl, int L)
+{
+#pragma unroll
+    for (int v = 0; v < RawSteps<TI>::NV; ++v) {
+        const int off = tl + v * RawSteps<TI>::E;
+        r.ok[v] = off + RawSteps<TI>::E <= L;
+        r.w[v] = *reinterpret_cast<const u32x4 *>(row + (r.ok[v] ? off : 0));
+    }
+}
+
+template <typename TI>
+__device__ __forceinline__ void widen(const RawSteps<TI> &r, float (&dst)[K])
+{
+    constexpr int E = RawSteps<TI>::E, PW = PerWord<TI>::value;
+#pragma unroll
+    for (int v = 0; v < RawSteps<TI>::NV; ++v) {
+        float part[E];
+        unpack_word(r.w[v].x, &part[0 * PW], TI{});
+        unpack_word(r.w[v].y, &part[1 * PW], TI{});
+        unpack_word(r.w[v].z, &part[2 * PW], TI{});
+        unpack_word(r.w[v].w, &part[3 * PW], TI{});
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            dst[v * E + e] = r.ok[v] ? part[e] : 0.0f;
     }
 }
 
@@ -88,8 +131,19 @@ __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int L,
     }
 }
 
+// Register budget: the float16 vector paths (except per-state decays over
+// several state chunks) fit three waves per SIMD (at most 168 VGPRs) without
+// spilling; the other variants are allowed two.
+template <typename TI, bool VEC, bool A_PER_STATE, bool ONE_CHUNK>
+constexpr int scan_waves_per_simd()
+{
+    return (std::is_same<TI, f16>::value && VEC && (ONE_CHUNK || !A_PER_STATE)) ? 3 : 2;
+}
+
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, VEC, A_PER_STATE, ONE_CHUNK>())))
+void scan_kernel(ScanArgs a)
 {
     constexpr int E = 16 / StorageSize<TI>::value;
     // B/C chunk in a lane-interleaved layout: the float4 holding timesteps
@@ -135,10 +189,17 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
     // state n0+nl (zero on the other lanes); A2[nl] = A[h, n0+nl] * log2(e)
     float carry[NC], A2[NC];
     if constexpr (ONE_CHUNK) {
+        // unconditional loads from clamped indices (see load_steps)
+        const TS *sinit = load_init ? srow : static_cast<const TS *>(nullptr);
 #pragma unroll
         for (int nl = 0; nl < NC; ++nl) {
-            carry[nl] = (r == 0 && load_init && nl < N) ? to_f32(srow[nl]) : 0.0f;
-            A2[nl] = A_PER_STATE ? ((nl < N) ? a.A[(int64_t)h * N + nl] * kLog2e : 0.0f) : A2_h;
+            const int n = min(nl, N - 1);
+            const float s0 = sinit ? to_f32(sinit[n]) : 0.0f;
+            carry[nl] = (r == 0 && nl < N) ? s0 : 0.0f;
+            if constexpr (A_PER_STATE)
+                A2[nl] = a.A[(int64_t)h * N + n] * kLog2e;
+            else
+                A2[nl] = A2_h;
         }
     } else {
         for (int n = r; n < N; n += R)
@@ -148,14 +209,27 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
     for (int t0 = 0; t0 < L; t0 += T) {
         const int tl = t0 + r * K;
         float dl[K], du[K], y[K];
+        RawSteps<TI> rz;  // the gate's loads are issued with the others
         {
             float uu[K], dd[K];
-            load_steps<TI, VEC>(urow, tl, L, uu);
-            load_steps<TI, VEC>(dtrow, tl, L, dd);
+            if constexpr (VEC) {
+                RawSteps<TI> ru, rd;
+                load_raw(ru, urow, tl, L);
+                load_raw(rd, dtrow, tl, L);
+                // 2-byte gates are fetched early (8 VGPRs); 4-byte ones at the end
+                if (zrow && StorageSize<TI>::value == 2)
+                    load_raw(rz, zrow, tl, L);
+                widen(ru, uu);
+                widen(rd, dd);
+            } else {
+                load_steps<TI, VEC>(urow, tl, L, uu);
+                load_steps<TI, VEC>(dtrow, tl, L, dd);
+            }
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 const float v = dd[i] + bias_h;
-                float d = a.dt_softplus ? softplus_f32(v) : v;
+                const float sp = softplus_f32(v);
+                float d = a.dt_softplus ? sp : v;
                 d = (tl + i < L) ? d : 0.0f;  // identity step past the end
                 dl[i] = d;
                 du[i] = d * uu[i];
@@ -190,15 +264,25 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                 const int nl = m / (T / E), tc = (m % (T / E)) * E;
                 const int n = n0 + nl, t = t0 + tc;
                 float vb[E], vc[E];
-                if (VEC && n < N && t + E <= L) {
-                    load_vec_cached<TI, E>(Bg + (int64_t)n * L + t, vb);
-                    load_vec_cached<TI, E>(Cg + (int64_t)n * L + t, vc);
+                if constexpr (VEC) {
+                    // clamped address, unconditional load, then select
+                    const bool ok = n < N && t + E <= L;
+                    const int64_t off = ok ? (int64_t)n * L + t : 0;
+                    load_vec_cached<TI, E>(Bg + off, vb);
+                    load_vec_cached<TI, E>(Cg + off, vc);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        vb[e] = ok ? vb[e] : 0.0f;
+                        vc[e] = ok ? vc[e] : 0.0f;
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
                         const bool ok = n < N && t + e < L;
-                        vb[e] = ok ? to_f32(Bg[(int64_t)n * L + t + e]) : 0.0f;
-                        vc[e] = ok ? to_f32(Cg[(int64_t)n * L + t + e]) : 0.0f;
+                        const int64_t off = ok ? (int64_t)n * L + t + e : 0;
+                        const float xb = to_f32(Bg[off]), xc = to_f32(Cg[off]);
+                        vb[e] = ok ? xb : 0.0f;
+                        vc[e] = ok ? xc : 0.0f;
                     }
                 }
 #pragma unroll
@@ -294,7 +378,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
         }
         if (zrow) {
             float zz[K];
-            load_steps<TI, VEC>(zrow, tl, L, zz);
+            if constexpr (VEC && StorageSize<TI>::value == 2)
+                widen(rz, zz);
+            else
+                load_steps<TI, VEC>(zrow, tl, L, zz);
 #pragma unroll
             for (int i = 0; i < K; ++i)
                 y[i] *= silu_f32(zz[i]);

@@ -225,3 +225,20 @@ def algorithmic_bytes(spec: Spec) -> dict:
                       + (H * N if spec.a_per_state else H) * 4 + 2 * H * 4
                       + Bt * 4)                        # slot_idx
     return out
+
+
+def algorithmic_flops(spec: Spec) -> float:
+    """Floating-point operations the recurrence needs, counting an exponential
+    as one operation and an FMA as two: per (batch, channel, time, state)
+    element, Mamba-1 takes delta*A (1), exp (1), (delta*u)*B (1), the state FMA
+    (2) and the readout FMA (2); Mamba-2 shares delta*A and exp across states
+    (per head and time: 2) and keeps 5 per element.  Per (batch, channel, time)
+    another 14: softplus (6), delta*u (1), D*u plus add (2), SiLU (4), gate (1).
+    """
+    Bt, L, H, P, N = spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate
+    Cn = H * P
+    per_elem = 7 if spec.a_per_state else 5
+    flops = Bt * Cn * L * N * per_elem + Bt * Cn * L * 14
+    if not spec.a_per_state:
+        flops += Bt * H * L * 2
+    return float(flops)
