@@ -433,17 +433,23 @@ def cpu_baseline(target_s, pspec, dspec):
 
     oracle.build(force=False)
     f = W.to_f64
-    t = W.make(W.prefill(batch=1), "cpu")
-    L, N = pspec.seqlen, pspec.dstate
+    t = W.make(pspec, "cpu")
+    L, N, Cn = pspec.seqlen, pspec.dstate, pspec.channels
 
-    def run_prefill(nch):
-        x = f(t["x"][:, :nch])
-        u, _, _ = oracle.causal_conv1d(x, f(t["conv_w"][:nch]), f(t["conv_b"][:nch]),
-                                       np.zeros((1, nch, 3)), None)
-        u = oracle.round_to(u, oracle.F16)
-        oracle.selective_scan(u, f(t["dt"][:, :nch]), f(t["A"][:nch]), f(t["B"]), f(t["C"]),
-                              D=f(t["D"][:nch]), z=f(t["z"][:, :nch]),
-                              dt_bias=f(t["dt_bias"][:nch]), state=np.zeros((1, nch, 1, N)))
+    def run_prefill(nrows):
+        # rows are (request, channel) pairs taken request by request
+        for b in range(pspec.batch):
+            nch = min(Cn, nrows - b * Cn)
+            if nch <= 0:
+                break
+            x = f(t["x"][b:b + 1, :nch])
+            u, _, _ = oracle.causal_conv1d(x, f(t["conv_w"][:nch]), f(t["conv_b"][:nch]),
+                                           np.zeros((1, nch, 3)), None)
+            u = oracle.round_to(u, oracle.F16)
+            oracle.selective_scan(u, f(t["dt"][b:b + 1, :nch]), f(t["A"][:nch]),
+                                  f(t["B"][b:b + 1]), f(t["C"][b:b + 1]), D=f(t["D"][:nch]),
+                                  z=f(t["z"][b:b + 1, :nch]), dt_bias=f(t["dt_bias"][:nch]),
+                                  state=np.zeros((1, nch, 1, N)))
 
     t0 = time.perf_counter()
     run_prefill(32)
@@ -460,7 +466,7 @@ def cpu_baseline(target_s, pspec, dspec):
                         f(d["A"]), f(d["B"]), f(d["C"]), D=f(d["D"]), z=f(d["z"]),
                         dt_bias=f(d["dt_bias"]), slot_idx=idx)
     t_dec = time.perf_counter() - t0
-    nch = int(max(32, min(pspec.channels, (target_s - t_dec) / max(per_ch, 1e-9))))
+    nch = int(max(32, min(pspec.batch * Cn, (target_s - t_dec) / max(per_ch, 1e-9))))
     t0 = time.perf_counter()
     run_prefill(nch)
     t_pre = time.perf_counter() - t0

@@ -19,7 +19,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
-_LIB = os.path.join(_HERE, "libssm_oracle.so")
+# SSM_ORACLE_LIB points the wrapper at another build of ssm_oracle.c (the
+# mutation test uses it to check that the pins reject planted mistakes).
+_LIB = os.environ.get("SSM_ORACLE_LIB") or os.path.join(_HERE, "libssm_oracle.so")
 _lib = None
 
 F32, F16, BF16 = 0, 1, 2  # rounding kinds of oracle_round
