@@ -38,11 +38,12 @@ VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp"],
                   "state_update": ["ssu.hip", "ssm_device.hpp"],
+                  "decode_step": ["ssu.hip", "ssm_device.hpp"],
                   "conv1d_prefill": ["conv1d.hip", "ssm_device.hpp"],
                   "conv1d_decode": ["conv1d.hip", "ssm_device.hpp"]}
 # rocprofv3 kernel names of each kernel in the benchmarked configuration
-KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "state_update": "ssu_kernel",
-                  "conv1d_prefill": "conv_prefill_kernel", "conv1d_decode": "conv_decode_kernel"}
+KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "decode_step": "ssu_kernel",
+                  "conv1d_prefill": "conv_prefill_kernel"}
 
 
 def parse():
@@ -57,6 +58,9 @@ def parse():
                    help="only run a plain 1 GiB device copy (for counter calibration)")
     p.add_argument("--only", choices=["prefill", "decode"], default=None,
                    help="run only one half of the step (for profiling)")
+    p.add_argument("--unfused-decode", action="store_true",
+                   help="decode with the separate conv-update and state-update calls instead "
+                        "of the fused decode step")
     p.add_argument("--profile-script", metavar="OUTDIR",
                    help="print the rocprofv3 commands whose output --summarize-profile reads")
     p.add_argument("--summarize-profile", metavar="OUTDIR",
@@ -122,8 +126,9 @@ def summarize_profile(out):
     import workloads as W
 
     pb, db = W.algorithmic_bytes(W.prefill()), W.algorithmic_bytes(W.decode())
+    dspec = W.decode()
     alg = {"conv1d_prefill": pb["conv"], "selective_scan": pb["scan"],
-           "conv1d_decode": db["conv"], "state_update": db["ssu"]}
+           "decode_step": db["conv"] + db["ssu"] - 2 * dspec.batch * dspec.channels * 2}
     copy_bytes = 1 << 30
     cf, _ = _match(_read_counters(glob.glob(f"{out}/copy_fetch/*counter_collection.csv")[0]),
                    "copyBuffer")
@@ -145,8 +150,9 @@ def summarize_profile(out):
 
     lines = ["# Kernel trace and HBM traffic: Mamba-1 2.8B layer step", "",
              "Workload: prefill conv1d+scan, batch 4 x L 2048, d_inner 5120, d_state 16, f16 "
-             "I/O, f32 state; decode conv update + state update, 245 requests from a 512-slot "
-             "cache.", "", "Commands (run from the repository root on the MI355X):", ""]
+             "I/O, f32 state; one decode step (fused conv update + state update, "
+             "`decode_step`), 245 requests from a 512-slot cache.", "",
+             "Commands (run from the repository root on the MI355X):", ""]
     for n, c in profile_commands(out):
         lines.append(f"    {c}")
     lines += ["", f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE = {cf['FETCH_SIZE']:.0f} "
@@ -277,8 +283,11 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    fused = not args.unfused_decode
+
     def step(i, ev=None):
-        # ev: list of 5 events bracketing conv, scan, conv update, state update
+        # ev: 5 events bracketing prefill conv, prefill scan, then either the
+        # fused decode step (3 -> 4) or conv update (2 -> 3) + state update (3 -> 4)
         def rec(j):
             if ev is not None:
                 ev[j].record(stream)
@@ -298,14 +307,21 @@ def main():
         rec(2)
         if dsets:
             t = dsets[i % ND]
-            ssm.causal_conv1d(t["x3"], t["conv_w"], t["conv_b"], conv_state=t["conv_state"],
-                              slot_idx=t["slot_idx"], out=t["u"], has_initial_state=True,
-                              stream=stream)
-            rec(3)
-            ssm.state_update(t["ssm_state"], t["u"].view(dspec.batch, dspec.nheads, 1),
-                             t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                             dt_bias=t["dt_bias"], slot_idx=t["slot_idx"], out=t["out"],
-                             stream=stream)
+            if fused:
+                rec(3)
+                ssm.decode_step(t["ssm_state"], t["conv_state"], t["x"], t["conv_w"], t["dt"],
+                                t["A"], t["B"], t["C"], conv_bias=t["conv_b"], D=t["D"],
+                                z=t["z"], dt_bias=t["dt_bias"], slot_idx=t["slot_idx"],
+                                out=t["out"], stream=stream)
+            else:
+                ssm.causal_conv1d(t["x3"], t["conv_w"], t["conv_b"], conv_state=t["conv_state"],
+                                  slot_idx=t["slot_idx"], out=t["u"], has_initial_state=True,
+                                  stream=stream)
+                rec(3)
+                ssm.state_update(t["ssm_state"], t["u"].view(dspec.batch, dspec.nheads, 1),
+                                 t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                 dt_bias=t["dt_bias"], slot_idx=t["slot_idx"], out=t["out"],
+                                 stream=stream)
         else:
             rec(3)
         rec(4)
@@ -330,8 +346,10 @@ def main():
     ms_per_step = total_ms / K
     k_ms = per.mean(axis=0)
 
+    # the fused decode step moves the conv cache and the state, not u
+    fused_bytes = dbytes["conv"] + dbytes["ssu"] - 2 * dspec.batch * dspec.channels * 2
     step_bytes = ((pbytes["conv"] + pbytes["scan"]) if psets else 0) + \
-                 ((dbytes["conv"] + dbytes["ssu"]) if dsets else 0)
+                 (((fused_bytes if fused else dbytes["conv"] + dbytes["ssu"])) if dsets else 0)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     def gbps(b, ms):
@@ -340,15 +358,18 @@ def main():
     kernels = {
         "conv1d_prefill": {"bytes": pbytes.get("conv"), "us": k_ms[0] * 1e3},
         "selective_scan": {"bytes": pbytes.get("scan"), "us": k_ms[1] * 1e3},
-        "conv1d_decode": {"bytes": dbytes.get("conv"), "us": k_ms[2] * 1e3},
-        "state_update": {"bytes": dbytes.get("ssu"), "us": k_ms[3] * 1e3},
     }
+    if fused:
+        kernels["decode_step"] = {"bytes": fused_bytes, "us": k_ms[3] * 1e3}
+    else:
+        kernels["conv1d_decode"] = {"bytes": dbytes.get("conv"), "us": k_ms[2] * 1e3}
+        kernels["state_update"] = {"bytes": dbytes.get("ssu"), "us": k_ms[3] * 1e3}
     for k, v in kernels.items():
         v["kernel_source_sha"] = kernel_source_sha(KERNEL_SOURCES[k])
         v["GBps"] = gbps(v["bytes"], v["us"] * 1e-3) if v["bytes"] else None
         v["frac_hbm_peak"] = v["GBps"] / HBM_PEAK_GBPS if v["GBps"] else None
 
-    decode_ms = k_ms[2] + k_ms[3]
+    decode_ms = k_ms[2] + k_ms[3]  # conv update + state update, or the fused step
     decode_tps = dspec.batch / (decode_ms * 1e-3) if dsets else None
 
     # dominant kernel: the one with the largest share of the step
@@ -396,12 +417,12 @@ def main():
         "data": "synthetic (seeded; Mamba-2.8B layer shapes, random parameters)",
         "config": {
             "workload": "mamba1-2.8B layer: prefill conv1d+scan batch 4 x L 2048, d_inner 5120, "
-                        "d_state 16, conv 4, f16 io / f32 state; + decode conv update + state "
-                        "update, 245 requests from a 512-slot cache",
+                        "d_state 16, conv 4, f16 io / f32 state; + one decode step (conv update "
+                        "+ state update), 245 requests from a 512-slot cache",
             "prefill": {"batch": pspec.batch, "seqlen": pspec.seqlen, "d_inner": pspec.channels,
                         "d_state": pspec.dstate, "conv_width": pspec.width},
             "decode": {"batch": dspec.batch, "nslots": dspec.nslots, "d_inner": dspec.channels,
-                       "d_state": dspec.dstate},
+                       "d_state": dspec.dstate, "fused_conv_update": fused},
             "step_bytes": step_bytes,
             "buffer_sets": {"prefill": NP, "decode": ND},
             "only": args.only,

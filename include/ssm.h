@@ -146,6 +146,36 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x,
                      int io_dtype, int state_dtype, int a_per_state,
                      int dt_softplus, void *stream);
 
+/*
+ * ssm_decode_step -- one decode token per request: the conv update followed by
+ * the state update, in one kernel (the causal-conv1d and silu operators of
+ * InfiniLM-Rust PR #48 section 2.1 at seqlen 1, feeding the
+ * selective_state_update call of the vLLM PR #50534 report).
+ *
+ *   x           io dtype [batch, nheads, headdim]: the token's input to the
+ *               conv (channel c = h*headdim + p)
+ *   conv_state  io dtype [nslots, nheads*headdim, conv_width-1], in/out: the
+ *               window before the token, shifted by one on return
+ *   conv_weight f32 [nheads*headdim, conv_width]; conv_bias f32 or NULL
+ *   u_out       io dtype [batch, nheads, headdim] or NULL: the conv output
+ *   every other argument as in ssm_state_update
+ *
+ *   u = silu(conv_bias + sum_k conv_weight[c,k] * window_k (newest = x))
+ *   then ssm_state_update with x := u.
+ * Equals ssm_causal_conv1d (seqlen 1, has_initial_state) followed by
+ * ssm_state_update, except that u is passed to the update in float32 instead
+ * of being rounded to the io dtype in between.  Limits: conv_width == 4, plus
+ * those of ssm_state_update.
+ */
+int ssm_decode_step(void *state, void *conv_state, const int32_t *slot_idx,
+                    const void *x, const float *conv_weight,
+                    const float *conv_bias, int conv_width, const void *dt,
+                    const float *dt_bias, const float *A, const void *B,
+                    const void *C, const float *D, const void *z, void *out,
+                    void *u_out, int batch, int nheads, int headdim, int dstate,
+                    int ngroups, int nslots, int io_dtype, int state_dtype,
+                    int a_per_state, int dt_softplus, void *stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *ssm_status_string(int status);
 

@@ -31,7 +31,7 @@ SSM_F32, SSM_F16, SSM_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: SSM_BF16}
 
 EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_state_update",
-            "ssm_status_string", "ssm_abi_version")
+            "ssm_decode_step", "ssm_status_string", "ssm_abi_version")
 
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE",
           4: "SSM_ERR_ALIGN", 5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_HIP"}
@@ -65,6 +65,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
                                      I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_state_update.restype = I
+    lib.ssm_decode_step.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P,
+                                    I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_decode_step.restype = I
     lib.ssm_status_string.argtypes = [I]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -175,5 +178,31 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplu
     return out
 
 
-__all__ = ["causal_conv1d", "selective_scan", "state_update", "load_library", "SsmError",
+def decode_step(state, conv_state, x, conv_weight, dt, A, B, C, conv_bias=None, D=None, z=None,
+                dt_bias=None, dt_softplus=True, slot_idx=None, out=None, u_out=None,
+                stream=None):
+    """ssm_decode_step: conv update + state update for one token per request.
+    x [batch, nheads, headdim] is the conv input; returns out."""
+    nslots, nheads, headdim, dstate = state.shape
+    batch = x.shape[0]
+    ngroups = B.shape[1]
+    a_per_state = 1 if A.dim() == 2 else 0
+    if out is None:
+        out = torch.empty_like(x)
+    _same_io(x.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"),
+             (conv_state, "conv_state"), (u_out, "u_out"))
+    st = load_library().ssm_decode_step(
+        _ptr(state, "state"), _ptr(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+        _ptr(x, "x"), _ptr(conv_weight, "conv_weight", torch.float32),
+        _ptr(conv_bias, "conv_bias", torch.float32), conv_weight.shape[1], _ptr(dt, "dt"),
+        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32), _ptr(B, "B"),
+        _ptr(C, "C"), _ptr(D, "D", torch.float32), _ptr(z, "z"), _ptr(out, "out"),
+        _ptr(u_out, "u_out"), batch, nheads, headdim, dstate, ngroups, nslots, _code(x, "x"),
+        _code(state, "state"), a_per_state, int(bool(dt_softplus)), _stream(stream))
+    _check("ssm_decode_step", st)
+    return out
+
+
+__all__ = ["causal_conv1d", "selective_scan", "state_update", "decode_step", "load_library",
+           "SsmError",
            "SSM_F32", "SSM_F16", "SSM_BF16", "EXPORTED", "LIB_PATH"]

@@ -15,8 +15,10 @@
 // in LDS, and the row's final W-1 samples go to the cache at the end.  HBM
 // traffic: x read once, out written once.
 //
-// Decode kernel (seqlen == 1): one lane per (b, c): gather the window from the
-// slot, one output, shift the window by one in place (bit-exact copies).
+// Decode kernels (seqlen == 1): gather the window from the slot, one output,
+// shift the window by one in place.  The vector kernel gives each lane 8
+// channels with 128-bit accesses; the scalar kernel (any channel count or
+// alignment) gives each lane one channel.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -130,10 +132,76 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(ConvArgs a)
     }
 }
 
+// Decode with 128-bit accesses: one lane per 8 consecutive channels of one
+// request (channels % 8 == 0, 16-byte aligned tensors).  The 8 windows of
+// width-1 samples are contiguous in the cache row, so a lane reads and writes
+// them as whole vectors; the window values pass through float32 unchanged.
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
+{
+    constexpr int H = W - 1, G = 8;
+    const int groups = a.channels / G;
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gi >= (int64_t)a.batch * groups)
+        return;
+    const int b = (int)(gi / groups), c0 = (int)(gi % groups) * G;
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0)
+        return;
+    const int64_t xo = (int64_t)b * a.channels + c0;
+    float xv[G], w[G * W], bias[G];
+    load_vec_cached<T, G>(static_cast<const T *>(a.x) + xo, xv);
+    load_vec_cached<float, G * W>(a.weight + (int64_t)c0 * W, w);
+    if (a.bias)
+        load_vec_cached<float, G>(a.bias + c0, bias);
+    else
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            bias[g] = 0.0f;
+    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c0) * H : nullptr;
+    float win[G * H > 0 ? G * H : 1];
+    if constexpr (H > 0) {
+        if (cs && a.has_initial_state)
+            load_vec_cached<T, G * H>(cs, win);
+        else
+#pragma unroll
+            for (int k = 0; k < G * H; ++k)
+                win[k] = 0.0f;
+    }
+    float o[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float acc = bias[g];
+#pragma unroll
+        for (int k = 0; k < H; ++k)
+            acc = fmaf(w[g * W + k], win[g * H + k], acc);
+        acc = fmaf(w[g * W + H], xv[g], acc);
+        o[g] = a.apply_silu ? silu_f32(acc) : acc;
+    }
+    store_vec_cached<T, G>(static_cast<T *>(a.out) + xo, o);
+    if constexpr (H > 0) {
+        if (cs) {
+            float nw[G * H];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+#pragma unroll
+                for (int k = 0; k + 1 < H; ++k)
+                    nw[g * H + k] = win[g * H + k + 1];
+                nw[g * H + H - 1] = xv[g];
+            }
+            store_vec_cached<T, G * H>(cs, nw);
+        }
+    }
+}
+
 template <typename T, int W>
 static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
 {
-    if (a.seqlen == 1) {
+    if (a.seqlen == 1 && a.vec_decode) {
+        const int64_t n = (int64_t)a.batch * (a.channels / 8);
+        hipLaunchKernelGGL((conv_decode_vec_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, a);
+    } else if (a.seqlen == 1) {
         const int64_t n = (int64_t)a.batch * a.channels;
         hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            stream, a);

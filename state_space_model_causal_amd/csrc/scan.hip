@@ -91,6 +91,10 @@ __device__ __forceinline__ void load_raw(RawSteps<TI> &r, const TI *__restrict__
     }
 }
 
+// Values past the end of the sequence are not masked here: they came from
+// clamped in-bounds addresses (finite data of the same row), and the step size
+// of those timesteps is zeroed, which makes them identity steps (decay 1,
+// input 0) whose outputs are never stored.
 template <typename TI>
 __device__ __forceinline__ void widen(const RawSteps<TI> &r, float (&dst)[K])
 {
@@ -104,7 +108,7 @@ __device__ __forceinline__ void widen(const RawSteps<TI> &r, float (&dst)[K])
         unpack_word(r.w[v].w, &part[3 * PW], TI{});
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            dst[v * E + e] = r.ok[v] ? part[e] : 0.0f;
+            dst[v * E + e] = part[e];
     }
 }
 
@@ -151,8 +155,12 @@ void scan_kernel(ScanArgs a)
     // so the 16 lanes of a row read 16 consecutive float4s (no bank conflict).
     __shared__ float4 lds_b[NC * T / 4];
     __shared__ float4 lds_c[NC * T / 4];
-    // states beyond the first chunk keep their carries here between tiles
-    __shared__ float lds_carry[ONE_CHUNK ? 1 : CPB][ONE_CHUNK ? 1 : kMaxScanDstate];
+    // per channel and state: the state entering the current tile (the carry)
+    // and A*log2(e); lane 0 of the row reads and rewrites the carry once per
+    // tile, all 16 lanes read A*log2(e) (an LDS broadcast)
+    constexpr int NCAP = ONE_CHUNK ? NC : kMaxScanDstate;
+    __shared__ float lds_carry[CPB][NCAP];
+    __shared__ float lds_a2[A_PER_STATE ? CPB : 1][A_PER_STATE ? NCAP : 1];
 
     const int L = a.seqlen, N = a.dstate, P = a.headdim;
     const int cpg = a.heads_per_group * P;  // channels per group (contiguous)
@@ -185,25 +193,10 @@ void scan_kernel(ScanArgs a)
     const float D_h = a.D ? a.D[h] : 0.0f;
     const float A2_h = A_PER_STATE ? 0.0f : a.A[h] * kLog2e;
 
-    // carry[nl]: on lane 0 of the row, the state entering the current tile of
-    // state n0+nl (zero on the other lanes); A2[nl] = A[h, n0+nl] * log2(e)
-    float carry[NC], A2[NC];
-    if constexpr (ONE_CHUNK) {
-        // unconditional loads from clamped indices (see load_steps)
-        const TS *sinit = load_init ? srow : static_cast<const TS *>(nullptr);
-#pragma unroll
-        for (int nl = 0; nl < NC; ++nl) {
-            const int n = min(nl, N - 1);
-            const float s0 = sinit ? to_f32(sinit[n]) : 0.0f;
-            carry[nl] = (r == 0 && nl < N) ? s0 : 0.0f;
-            if constexpr (A_PER_STATE)
-                A2[nl] = a.A[(int64_t)h * N + n] * kLog2e;
-            else
-                A2[nl] = A2_h;
-        }
-    } else {
-        for (int n = r; n < N; n += R)
-            lds_carry[ch][n] = load_init ? to_f32(srow[n]) : 0.0f;
+    for (int n = r; n < N; n += R) {
+        lds_carry[ch][n] = load_init ? to_f32(srow[n]) : 0.0f;
+        if constexpr (A_PER_STATE)
+            lds_a2[ch][n] = a.A[(int64_t)h * N + n] * kLog2e;
     }
 
     for (int t0 = 0; t0 < L; t0 += T) {
@@ -293,23 +286,12 @@ void scan_kernel(ScanArgs a)
                     lds_c[idx] = make_float4(vc[4 * e4], vc[4 * e4 + 1], vc[4 * e4 + 2], vc[4 * e4 + 3]);
                 }
             }
-            if constexpr (!ONE_CHUNK) {
-#pragma unroll
-                for (int nl = 0; nl < NC; ++nl) {
-                    const int n = min(n0 + nl, N - 1);
-                    A2[nl] = A_PER_STATE ? a.A[(int64_t)h * N + n] * kLog2e : A2_h;
-                }
-            }
             __syncthreads();
-            if constexpr (!ONE_CHUNK) {
-#pragma unroll
-                for (int nl = 0; nl < NC; ++nl)
-                    carry[nl] = (r == 0 && n0 + nl < N) ? lds_carry[ch][n0 + nl] : 0.0f;
-            }
 #pragma unroll 1
             for (int nl = 0; nl < NC; ++nl) {
                 if (n0 + nl >= N)
                     break;
+                const int n = n0 + nl;
                 float Bv[K], Cv[K];
 #pragma unroll
                 for (int q = 0; q < K / 4; ++q) {
@@ -318,13 +300,16 @@ void scan_kernel(ScanArgs a)
                     Bv[4 * q] = vb.x; Bv[4 * q + 1] = vb.y; Bv[4 * q + 2] = vb.z; Bv[4 * q + 3] = vb.w;
                     Cv[4 * q] = vc.x; Cv[4 * q + 1] = vc.y; Cv[4 * q + 2] = vc.z; Cv[4 * q + 3] = vc.w;
                 }
+                const float cin = lds_carry[ch][n];
+                const float carry = (r == 0) ? cin : 0.0f;
                 float av[K], bx[K];
-                float aagg, bagg = 0.0f;
+                float aagg, bagg;
                 if constexpr (A_PER_STATE) {
+                    const float A2 = lds_a2[ch][n];
 #pragma unroll
                     for (int i = 0; i < K; ++i)
-                        av[i] = exp2_hw(dl[i] * A2[nl]);
-                    aagg = exp2_hw(sdl * A2[nl]);
+                        av[i] = exp2_hw(dl[i] * A2);
+                    aagg = exp2_hw(sdl * A2);
                 } else {
 #pragma unroll
                     for (int i = 0; i < K; ++i)
@@ -334,9 +319,9 @@ void scan_kernel(ScanArgs a)
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
                     bx[i] = du[i] * Bv[i];
-                    bagg = fmaf(av[i], bagg, bx[i]);
+                    bagg = (i == 0) ? bx[0] : fmaf(av[i], bagg, bx[i]);
                 }
-                bagg = fmaf(aagg, carry[nl], bagg);  // lane 0 starts from the incoming state
+                bagg = fmaf(aagg, carry, bagg);  // lane 0 starts from the incoming state
                 // inclusive scan of the affine maps over the 16 lanes of the row.
                 // Lanes whose source lies before lane 0 read 0: the b term then
                 // adds nothing, and the decay products they corrupt belong to
@@ -359,20 +344,13 @@ void scan_kernel(ScanArgs a)
                 // lane r >= 1 starts from lane r-1's end state; lane 0 from the
                 // carry, and receives lane 15's end state as the next carry
                 const float rot = dpp_move_zero<DPP_ROW_ROR1>(bagg);
-                float hh = (r == 0) ? carry[nl] : rot;
-                carry[nl] = (r == 0) ? rot : 0.0f;
+                float hh = (r == 0) ? carry : rot;
+                if (r == 0)
+                    lds_carry[ch][n] = rot;
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
                     hh = fmaf(av[i], hh, bx[i]);
                     y[i] = fmaf(Cv[i], hh, y[i]);
-                }
-            }
-            if constexpr (!ONE_CHUNK) {
-                if (r == 0) {
-#pragma unroll
-                    for (int nl = 0; nl < NC; ++nl)
-                        if (n0 + nl < N)
-                            lds_carry[ch][n0 + nl] = carry[nl];
                 }
             }
         }
@@ -389,19 +367,10 @@ void scan_kernel(ScanArgs a)
         if (active)
             store_steps<TI, VEC>(orow, tl, L, y);
     }
-    if constexpr (ONE_CHUNK) {
-        if (srow && active && r == 0) {
-#pragma unroll
-            for (int nl = 0; nl < NC; ++nl)
-                if (nl < N)
-                    srow[nl] = from_f32<TS>(carry[nl]);
-        }
-    } else {
-        __syncthreads();
-        if (srow && active)
-            for (int n = r; n < N; n += R)
-                srow[n] = from_f32<TS>(lds_carry[ch][n]);
-    }
+    __syncthreads();
+    if (srow && active)
+        for (int n = r; n < N; n += R)
+            srow[n] = from_f32<TS>(lds_carry[ch][n]);
 }
 
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC>

@@ -86,6 +86,8 @@ int ssm_causal_conv1d(const void *x, const float *weight, const float *bias, voi
     a.has_initial_state = has_initial_state ? 1 : 0;
     a.apply_silu = apply_silu ? 1 : 0;
     a.vec = (seqlen % 8 == 0) && aligned(x, 16) && aligned(out, 16);
+    a.vec_decode = (seqlen == 1) && (channels % 8 == 0) && aligned(x, 16) && aligned(out, 16) &&
+                   aligned(conv_state, 16) && aligned(weight, 16) && aligned(bias, 16);
     return status_of(ssm::launch_conv(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -149,11 +151,17 @@ int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias, cons
     return status_of(ssm::launch_scan(a, static_cast<hipStream_t>(stream)));
 }
 
-int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const void *dt,
-                     const float *dt_bias, const float *A, const void *B, const void *C,
-                     const float *D, const void *z, void *out, int batch, int nheads, int headdim,
-                     int dstate, int ngroups, int nslots, int io_dtype, int state_dtype,
-                     int a_per_state, int dt_softplus, void *stream)
+} // extern "C"
+
+namespace {
+
+// Validation and launch geometry shared by ssm_state_update and
+// ssm_decode_step; fills `a` and returns SSM_OK, or an error status.
+int prepare_ssu(ssm::SsuArgs &a, void *state, const int32_t *slot_idx, const void *x,
+                const void *dt, const float *dt_bias, const float *A, const void *B,
+                const void *C, const float *D, const void *z, void *out, int batch, int nheads,
+                int headdim, int dstate, int ngroups, int nslots, int io_dtype, int state_dtype,
+                int a_per_state, int dt_softplus)
 {
     if (!state || !x || !dt || !A || !B || !C || !out)
         return SSM_ERR_NULL_ARG;
@@ -181,9 +189,7 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const 
     const int64_t nrows = (int64_t)batch * nheads * headdim;
     if (((nrows << lg) + 255) / 256 > INT32_MAX)
         return SSM_ERR_UNSUPPORTED;
-    if (batch == 0)
-        return SSM_OK;
-    ssm::SsuArgs a;
+    a = ssm::SsuArgs{};
     a.state = state;
     a.slot_idx = slot_idx;
     a.x = x;
@@ -211,6 +217,63 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const 
     a.dt_softplus = dt_softplus ? 1 : 0;
     a.vec = (dstate % 8 == 0) && aligned(state, 16) && aligned(B, 16) && aligned(C, 16) &&
             aligned(A, 16);
+    // a request's lanes fill whole waves: the slot index is then wave-uniform
+    a.wave_per_request = ((((int64_t)nheads * headdim) << lg) % 64) == 0;
+    a.conv_width = 0;
+    return SSM_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const void *dt,
+                     const float *dt_bias, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, void *out, int batch, int nheads, int headdim,
+                     int dstate, int ngroups, int nslots, int io_dtype, int state_dtype,
+                     int a_per_state, int dt_softplus, void *stream)
+{
+    ssm::SsuArgs a;
+    const int st = prepare_ssu(a, state, slot_idx, x, dt, dt_bias, A, B, C, D, z, out, batch,
+                               nheads, headdim, dstate, ngroups, nslots, io_dtype, state_dtype,
+                               a_per_state, dt_softplus);
+    if (st != SSM_OK)
+        return st;
+    if (batch == 0)
+        return SSM_OK;
+    return status_of(ssm::launch_ssu(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_decode_step(void *state, void *conv_state, const int32_t *slot_idx, const void *x,
+                    const float *conv_weight, const float *conv_bias, int conv_width,
+                    const void *dt, const float *dt_bias, const float *A, const void *B,
+                    const void *C, const float *D, const void *z, void *out, void *u_out,
+                    int batch, int nheads, int headdim, int dstate, int ngroups, int nslots,
+                    int io_dtype, int state_dtype, int a_per_state, int dt_softplus, void *stream)
+{
+    ssm::SsuArgs a;
+    const int st = prepare_ssu(a, state, slot_idx, x, dt, dt_bias, A, B, C, D, z, out, batch,
+                               nheads, headdim, dstate, ngroups, nslots, io_dtype, state_dtype,
+                               a_per_state, dt_softplus);
+    if (st != SSM_OK)
+        return st;
+    if (!conv_state || !conv_weight)
+        return SSM_ERR_NULL_ARG;
+    if (conv_width < 1)
+        return SSM_ERR_SHAPE;
+    if (conv_width != ssm::kFusedConvWidth)
+        return SSM_ERR_UNSUPPORTED;
+    const int es = dtype_size(io_dtype);
+    if (!aligned(conv_state, es) || !aligned(u_out, es) || !aligned(conv_weight, 4) ||
+        !aligned(conv_bias, 4))
+        return SSM_ERR_ALIGN;
+    if (batch == 0)
+        return SSM_OK;
+    a.conv_state = conv_state;
+    a.conv_weight = conv_weight;
+    a.conv_bias = conv_bias;
+    a.u_out = u_out;
+    a.conv_width = conv_width;
     return status_of(ssm::launch_ssu(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -19,6 +19,7 @@ struct ConvArgs {
     int dtype;                // 0 f32, 1 f16, 2 bf16
     int has_initial_state, apply_silu;
     int vec;                  // rows 16-byte aligned and seqlen a multiple of 8
+    int vec_decode;           // seqlen 1, channels % 8 == 0, 16-byte aligned tensors
 };
 
 struct ScanArgs {
@@ -48,6 +49,13 @@ struct SsuArgs {
     int io_dtype, state_dtype;
     int a_per_state, dt_softplus;
     int vec;                         // dstate % 8 == 0 and 16-byte aligned bases
+    int wave_per_request;            // every wave's rows belong to one request
+    // fused decode step (conv update in front of the state update); width 0 = none
+    void *conv_state;                // [nslots, nheads*headdim, width-1], io dtype
+    const float *conv_weight;        // [nheads*headdim, width]
+    const float *conv_bias;          // [nheads*headdim] or null
+    void *u_out;                     // optional: the conv output, io dtype
+    int conv_width;
 };
 
 hipError_t launch_conv(const ConvArgs &a, hipStream_t stream);
@@ -58,5 +66,6 @@ hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
 constexpr int kMaxConvWidth = 4;
 constexpr int kMaxScanDstate = 256;
 constexpr int kMaxSsuDstate = 512;
+constexpr int kFusedConvWidth = 4;  // the conv width the fused decode step is built for
 
 } // namespace ssm

@@ -20,7 +20,7 @@
 
 namespace ssm {
 
-template <typename TS, typename TI, bool A_PER_STATE, bool VEC, int V>
+template <typename TS, typename TI, bool A_PER_STATE, bool VEC, int V, bool WAVE_REQ, int CW>
 __global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
 {
     const int lpr_log2 = a.lanes_per_row_log2;
@@ -32,7 +32,9 @@ __global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
     const int p = (int)(row % a.headdim);
     const int64_t bh = row / a.headdim;
     const int h = (int)(bh % a.nheads);
-    const int b = (int)(bh / a.nheads);
+    int b = (int)(bh / a.nheads);
+    if constexpr (WAVE_REQ)
+        b = __builtin_amdgcn_readfirstlane(b);  // one request per wave: scalar slot load
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0)
         return;  // padded request: nothing read or written
@@ -43,7 +45,34 @@ __global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
     const TI *xp = static_cast<const TI *>(a.x);
     float v = to_f32(dtp[bh]) + (a.dt_bias ? a.dt_bias[h] : 0.0f);
     const float delta = a.dt_softplus ? softplus_f32(v) : v;
-    const float xv = to_f32(xp[row]);
+    float xv = to_f32(xp[row]);
+    if constexpr (CW > 0) {
+        // fused conv update of channel c: every lane of the row computes the
+        // (cheap) conv; lane 0 shifts the cached window after its own loads
+        // of the old window have returned (the stored values depend on them)
+        constexpr int HW = CW - 1;
+        const int64_t c = (int64_t)h * a.headdim + p;
+        TI *cw = static_cast<TI *>(a.conv_state) + ((int64_t)slot * a.nheads * a.headdim + c) * HW;
+        float acc = a.conv_bias ? a.conv_bias[c] : 0.0f;
+        float win[HW > 0 ? HW : 1];
+#pragma unroll
+        for (int k = 0; k < HW; ++k) {
+            win[k] = to_f32(cw[k]);
+            acc = fmaf(a.conv_weight[c * CW + k], win[k], acc);
+        }
+        acc = fmaf(a.conv_weight[c * CW + HW], xv, acc);
+        const float u = silu_f32(acc);
+        if (j == 0) {
+#pragma unroll
+            for (int k = 0; k + 1 < HW; ++k)
+                cw[k] = from_f32<TI>(win[k + 1]);
+            if (HW > 0)
+                cw[HW - 1] = xp[row];
+            if (a.u_out)
+                static_cast<TI *>(a.u_out)[row] = from_f32<TI>(u);
+        }
+        xv = u;  // the update reads the float32 conv output
+    }
     const float dx = delta * xv;
 
     float y = 0.0f;
@@ -116,8 +145,20 @@ static hipError_t launch_ssu_t(const SsuArgs &a, hipStream_t stream)
 {
     const int64_t threads = a.nrows << a.lanes_per_row_log2;
     const dim3 grid((unsigned)((threads + 255) / 256));
-#define SSU_LAUNCH(APS, VEC, V) \
-    hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V>), grid, dim3(256), 0, stream, a)
+#define SSU_LAUNCH_CW(APS, VEC, V, CW)                                                             \
+    do {                                                                                           \
+        if (a.wave_per_request)                                                                    \
+            hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V, true, CW>), grid, dim3(256), 0, stream, a);  \
+        else                                                                                       \
+            hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V, false, CW>), grid, dim3(256), 0, stream, a); \
+    } while (0)
+#define SSU_LAUNCH(APS, VEC, V)                                                                    \
+    do {                                                                                           \
+        if (a.conv_width == kFusedConvWidth)                                                       \
+            SSU_LAUNCH_CW(APS, VEC, V, kFusedConvWidth);                                           \
+        else                                                                                       \
+            SSU_LAUNCH_CW(APS, VEC, V, 0);                                                         \
+    } while (0)
     if (a.states_per_lane == 16) {
         if (a.a_per_state) {
             if (a.vec) SSU_LAUNCH(true, true, 16); else SSU_LAUNCH(true, false, 16);
@@ -132,6 +173,7 @@ static hipError_t launch_ssu_t(const SsuArgs &a, hipStream_t stream)
         }
     }
 #undef SSU_LAUNCH
+#undef SSU_LAUNCH_CW
     return hipGetLastError();
 }
 

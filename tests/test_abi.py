@@ -126,3 +126,24 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError, match="GPU"):
         ssm.causal_conv1d(x, torch.zeros(4, 4))
+
+
+def dstep(lib, **kw):
+    a = dict(st=FAKE, cs=FAKE, idx=None, x=FAKE, w=FAKE, cb=None, W=4, dt=FAKE, bias=None, A=FAKE,
+             B=FAKE, C=FAKE, D=None, z=None, out=FAKE, uo=None, batch=2, H=8, P=4, N=16, G=1,
+             S=2, io=1, sd=0, aps=0, sp=1)
+    a.update(kw)
+    return lib.ssm_decode_step(a["st"], a["cs"], a["idx"], a["x"], a["w"], a["cb"], a["W"],
+                               a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                               a["out"], a["uo"], a["batch"], a["H"], a["P"], a["N"], a["G"],
+                               a["S"], a["io"], a["sd"], a["aps"], a["sp"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), NULL), (dict(w=None), NULL), (dict(st=None), NULL), (dict(W=3), UNSUP),
+    (dict(W=0), SHAPE), (dict(N=513), UNSUP), (dict(cs=FAKE + 1), ALIGN),
+    (dict(uo=FAKE + 1), ALIGN), (dict(w=FAKE + 2), ALIGN), (dict(H=8, G=3), SHAPE),
+    (dict(batch=0), 0),
+])
+def test_decode_step_validation(lib, kw, code):
+    assert dstep(lib, **kw) == code

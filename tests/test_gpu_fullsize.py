@@ -170,3 +170,31 @@ def test_mamba2_prefill_full(dev, ssm, oracle, state):
         slot = int(t["slot_idx"][b])
         gst = t["ssm_state"][slot][hi][:, pi]
         check(gst, st[0], sts[0], RTOL[spec.io], spec.state, f"m2 prefill state b={b}")
+
+
+def test_mamba1_decode_step_fused_full(dev, ssm, oracle):
+    """The decode workload through the fused conv-update + state-update entry
+    point (the configuration the benchmark times)."""
+    spec = W.decode()
+    t = W.make(spec, dev)
+    cs0, ss0 = t["conv_state"].clone(), t["ssm_state"].clone()
+    y = ssm.decode_step(t["ssm_state"], t["conv_state"], t["x"], t["conv_w"], t["dt"], t["A"],
+                        t["B"], t["C"], conv_bias=t["conv_b"], D=t["D"], z=t["z"],
+                        dt_bias=t["dt_bias"], slot_idx=t["slot_idx"])
+    torch.cuda.synchronize()
+    idx = t["slot_idx"].cpu().numpy()
+    for b in (0, 3, 128, 244):
+        s = int(idx[b])
+        uo, _, cso = oracle.causal_conv1d(f(t["x"][b:b + 1]).reshape(1, 5120, 1), f(t["conv_w"]),
+                                          f(t["conv_b"]), f(cs0[s:s + 1]),
+                                          np.array([0], np.int32), has_initial_state=True)
+        np.testing.assert_array_equal(f(t["conv_state"][s:s + 1]), cso)
+        o, so, st, sts = oracle.state_update(
+            f(ss0[s:s + 1]), uo.reshape(1, 5120, 1), f(t["dt"][b:b + 1]), f(t["A"]),
+            f(t["B"][b:b + 1]), f(t["C"][b:b + 1]), D=f(t["D"]), z=f(t["z"][b:b + 1]),
+            dt_bias=f(t["dt_bias"]), slot_idx=np.array([0], np.int32))
+        check(y[b:b + 1], o, so, RTOL["f16"], "f16", f"fused decode out b={b}")
+        check(t["ssm_state"][s:s + 1], st, sts, RTOL["f16"], "f32", f"fused decode state b={b}")
+    others = torch.as_tensor(np.setdiff1d(np.arange(512), idx), device=dev)
+    assert torch.equal(t["ssm_state"][others], ss0[others])
+    assert torch.equal(t["conv_state"][others], cs0[others])

@@ -60,6 +60,13 @@ CONV_CASES = [
     ("f16_L2048", dict(seqlen=2048, io="f16", nheads=24, batch=2), False, 0),
     ("bf16_L2049_w1", dict(seqlen=2049, io="bf16", nheads=5, width=1, batch=2), True, 0),
     ("f16_L4104", dict(seqlen=4104, io="f16", nheads=6, batch=1), True, 0),
+    # decode through the 8-channels-per-lane vector kernel (channels % 8 == 0)
+    ("f16_L1_vec", dict(seqlen=1, io="f16", nheads=512, batch=7, nslots=11, random_slots=True),
+     True, 3),
+    ("bf16_L1_vec_w2", dict(seqlen=1, io="bf16", nheads=64, width=2, batch=6, nslots=9,
+                            random_slots=True), True, 2),
+    ("f32_L1_vec_w3_noinit", dict(seqlen=1, io="f32", nheads=40, width=3, batch=3), False, 0),
+    ("f16_L1_vec_w1", dict(seqlen=1, io="f16", nheads=16, width=1, batch=2), True, 0),
 ]
 
 
@@ -364,3 +371,88 @@ def test_softplus_step_accuracy(dev, ssm, oracle, io):
     tol = (4e-7 + 1e-7 * x) * np.abs(want) + (0.5 * 2.0 ** -7 * np.abs(want) if io == "bf16" else 0.0)
     bad = np.abs(got - want) > tol
     assert not bad.any(), (f(dt).ravel()[bad][:5], got[bad][:5], want[bad][:5])
+
+
+# ------------------------------------------------------- fused decode step
+DECODE_CASES = [
+    ("m1_f16_f32state", dict(seqlen=1, nheads=300, dstate=16, io="f16", state="f32", batch=7,
+                             nslots=20, random_slots=True, index_sensitive=True), dict(pad=3)),
+    ("m1_bf16_bf16state", dict(seqlen=1, nheads=64, dstate=16, io="bf16", state="bf16", batch=5,
+                               nslots=6, random_slots=True, index_sensitive=True), {}),
+    ("m1_f32_noz_noD", dict(seqlen=1, nheads=40, dstate=16, io="f32", state="f32", batch=3,
+                            index_sensitive=True), dict(z=False, D=False, bias=False)),
+    ("m2_hd64_N128_G8", dict(seqlen=1, nheads=16, headdim=64, dstate=128, ngroups=8, io="f16",
+                             state="f16", a_per_state=False, batch=3, index_sensitive=True), {}),
+    ("m2_hd128_N256_bf16", dict(seqlen=1, nheads=4, headdim=128, dstate=256, io="bf16",
+                                state="f32", a_per_state=False, batch=2, nslots=5,
+                                random_slots=True, index_sensitive=True), dict(pad=2)),
+]
+
+
+def run_decode_step(ssm, oracle, spec, t, opts, label):
+    z = t["z"] if opts.get("z", True) else None
+    D = t["D"] if opts.get("D", True) else None
+    bias = t["dt_bias"] if opts.get("bias", True) else None
+    idx = _pad(t["slot_idx"], opts.get("pad", 0))
+    st0, cs0 = t["ssm_state"].clone(), t["conv_state"].clone()
+    out0 = torch.full_like(t["x"], 3.0)
+    u_out = torch.full_like(t["x"], 9.0)
+    out = ssm.decode_step(t["ssm_state"], t["conv_state"], t["x"], t["conv_w"], t["dt"], t["A"],
+                          t["B"], t["C"], conv_bias=t["conv_b"], D=D, z=z, dt_bias=bias,
+                          slot_idx=idx, out=out0.clone(), u_out=u_out)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    Bt, Cn = spec.batch, spec.channels
+    x3 = f(t["x"]).reshape(Bt, Cn, 1)
+    uo, uso, cso = oracle.causal_conv1d(x3, f(t["conv_w"]), f(t["conv_b"]), f(cs0), idx_np,
+                                        has_initial_state=True, out=f(u_out).reshape(Bt, Cn, 1))
+    shp = (Bt, spec.nheads, spec.headdim)
+    # the fused step hands the float32 conv output to the update (no rounding)
+    o, so, st, sts = oracle.state_update(
+        f(st0), uo.reshape(shp), f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
+        D=None if D is None else f(D), z=None if z is None else f(z),
+        dt_bias=None if bias is None else f(bias), slot_idx=idx_np, out=f(out0))
+    check(out, o, so, RTOL[spec.io], spec.io, f"decode_step {label} out")
+    check(u_out.reshape(Bt, Cn, 1), uo, uso, RTOL[spec.io], spec.io, f"decode_step {label} u")
+    np.testing.assert_array_equal(f(t["conv_state"]), cso)
+    named = _named(idx_np)
+    gst = f(t["ssm_state"])
+    check(gst[named], st[named], sts[named], RTOL[spec.io], spec.state, f"decode_step {label} state")
+    others = np.setdiff1d(np.arange(spec.slots), named)
+    np.testing.assert_array_equal(gst[others], f(st0)[others])
+
+
+@pytest.mark.parametrize("label,kw,opts", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_step_parity(dev, ssm, oracle, label, kw, opts):
+    spec = W.tiny(**kw)
+    run_decode_step(ssm, oracle, spec, W.make(spec, dev), opts, label)
+
+
+def test_decode_step_chain_matches_prefill(dev, ssm, oracle):
+    """Prefill the first tokens, then run fused decode steps: the outputs
+    continue the one-pass oracle sequence (conv tail and state from slots)."""
+    L1, L2 = 30, 4
+    spec = W.tiny(io="f32", seqlen=L1 + L2, nheads=24, index_sensitive=True, nslots=4,
+                  random_slots=True, batch=2)
+    t = W.make(spec, dev)
+    idx = t["slot_idx"]
+    u1 = ssm.causal_conv1d(t["x"][..., :L1].contiguous(), t["conv_w"], t["conv_b"],
+                           conv_state=t["conv_state"], slot_idx=idx)
+    y1 = ssm.selective_scan(u1, t["dt"][..., :L1].contiguous(), t["A"],
+                            t["B"][..., :L1].contiguous(), t["C"][..., :L1].contiguous(),
+                            D=t["D"], z=t["z"][..., :L1].contiguous(), dt_bias=t["dt_bias"],
+                            ssm_state=t["ssm_state"], slot_idx=idx)
+    ys = [y1]
+    for s in range(L1, L1 + L2):
+        y = ssm.decode_step(t["ssm_state"], t["conv_state"],
+                            t["x"][..., s].contiguous().view(2, 24, 1), t["conv_w"],
+                            t["dt"][..., s].contiguous(), t["A"], t["B"][..., s].contiguous(),
+                            t["C"][..., s].contiguous(), conv_bias=t["conv_b"], D=t["D"],
+                            z=t["z"][..., s].contiguous().view(2, 24, 1), dt_bias=t["dt_bias"],
+                            slot_idx=idx)
+        ys.append(y.view(2, 24, 1))
+    torch.cuda.synchronize()
+    uo, _, _ = oracle.causal_conv1d(f(t["x"]), f(t["conv_w"]), f(t["conv_b"]), None, None)
+    o, sc, _, _ = oracle.selective_scan(uo, f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
+                                        D=f(t["D"]), z=f(t["z"]), dt_bias=f(t["dt_bias"]))
+    check(torch.cat(ys, dim=2), o, sc, 1e-5, "f32", "prefill + fused decode")
