@@ -28,7 +28,8 @@
  *    narrowing to f16/bf16 rounds to nearest, ties to even.
  *  - Slots: slot_idx (int32 [batch], may be NULL) maps request b to cache row
  *    slot_idx[b]; NULL means slot b.  A negative index marks a padded request:
- *    nothing of it is read or written (its out rows keep their contents).
+ *    nothing is written for it (its out rows keep their contents) and its
+ *    inputs affect no output.
  *    Non-negative indices must be < nslots and distinct within a call
  *    (duplicates race; this is not checked on the device).
  *  - batch == 0 or seqlen == 0 is a no-op returning SSM_OK.
