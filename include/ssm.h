@@ -177,6 +177,61 @@ int ssm_decode_step(void *state, void *conv_state, const int32_t *slot_idx,
                     int ngroups, int nslots, int io_dtype, int state_dtype,
                     int a_per_state, int dt_softplus, void *stream);
 
+/*
+ * Packed variable-length batches (continuous batching).  Several sequences of
+ * different lengths are prefilled in one call, each with its own cache slot
+ * and its own initial-state flag: the serving pattern of InfiniLM-Rust PR #48
+ * (section 3.1 keeps one mamba cache per request; section 4.2, Fig. 2, serves
+ * 245 concurrent requests), where requests that already hold a state continue
+ * from it.  The pages describe no varlen kernel; the packing is this
+ * library's.  The sequences are concatenated along time:
+ *
+ *   cu_seqlens  int32 [nseq+1], DEVICE memory: sequence s is columns
+ *               [cu_seqlens[s], cu_seqlens[s+1]) of every row; the table must
+ *               be non-decreasing from 0 to total_len (entries are clamped to
+ *               [0, total_len] on the device, so a bad table cannot address
+ *               outside the tensors, but overlapping sequences race).  A
+ *               sequence of length 0 reads and writes nothing.
+ *   slot_idx    int32 [nseq] or NULL (slot s); negative = padded sequence
+ *   has_initial_state  int32 [nseq], DEVICE memory, or NULL (none): nonzero =
+ *               the sequence continues from the state in its slot
+ *
+ * Each sequence gives exactly the result of the dense call on that sequence
+ * alone (batch 1, seqlen = its length, has_initial_state = its flag).
+ */
+
+/*
+ * ssm_causal_conv1d_varlen -- ssm_causal_conv1d over a packed batch.
+ *   x, out      io dtype [channels, total_len]
+ *   other arguments as in ssm_causal_conv1d; the conv cache of each sequence
+ *   receives the last width-1 samples of its history || its samples.
+ */
+int ssm_causal_conv1d_varlen(const void *x, const float *weight, const float *bias,
+                             void *conv_state, const int32_t *slot_idx,
+                             const int32_t *has_initial_state,
+                             const int32_t *cu_seqlens, void *out, int nseq,
+                             int channels, int total_len, int width, int nslots,
+                             int dtype, int apply_silu, void *stream);
+
+/*
+ * ssm_selective_scan_varlen -- ssm_selective_scan over a packed batch.
+ *   u, z, out   io dtype [nheads*headdim, total_len]
+ *   dt          io dtype [nheads, total_len]
+ *   B, C        io dtype [ngroups, dstate, total_len]
+ *   other arguments as in ssm_selective_scan; each sequence's final state goes
+ *   to its slot.
+ */
+int ssm_selective_scan_varlen(const void *u, const void *dt, const float *dt_bias,
+                              const float *A, const void *B, const void *C,
+                              const float *D, const void *z, void *ssm_state,
+                              const int32_t *slot_idx,
+                              const int32_t *has_initial_state,
+                              const int32_t *cu_seqlens, void *out, int nseq,
+                              int total_len, int nheads, int headdim, int dstate,
+                              int ngroups, int nslots, int io_dtype,
+                              int state_dtype, int a_per_state, int dt_softplus,
+                              void *stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *ssm_status_string(int status);
 

@@ -204,3 +204,68 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplu
     if rc != 0:
         raise ValueError("oracle_state_update rejected its arguments")
     return o, sc, st, sts
+
+
+def _seq_bounds(cu_seqlens):
+    cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+    return [(cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
+
+
+def causal_conv1d_varlen(x, weight, cu_seqlens, bias=None, conv_state=None, slot_idx=None,
+                         has_initial_state=None, apply_silu=True, out=None):
+    """Packed variable-length batch of the conv: x [channels, total_len] holds
+    the sequences at columns [cu_seqlens[s], cu_seqlens[s+1]).  By definition
+    each sequence is one independent dense call (batch 1) on its own columns,
+    with its own slot and initial-state flag (one mamba cache per request,
+    InfiniLM-Rust PR #48 section 3.1); padded (slot < 0) and empty sequences
+    are skipped.  No arithmetic of its own: it slices and calls
+    causal_conv1d.  Returns (out, out_scale, conv_state_after)."""
+    x = _f64(x)
+    cs = None if conv_state is None else np.array(conv_state, dtype=np.float64, copy=True, order="C")
+    o = np.zeros_like(x) if out is None else np.array(out, dtype=np.float64, copy=True, order="C")
+    sc = np.zeros_like(x)
+    for s, (tb, te) in enumerate(_seq_bounds(cu_seqlens)):
+        slot = s if slot_idx is None else int(slot_idx[s])
+        if slot < 0 or te == tb:
+            continue
+        init = bool(has_initial_state[s]) if has_initial_state is not None else False
+        os_, ss_, cs = causal_conv1d(x[None, :, tb:te], weight, bias, conv_state=cs,
+                                     slot_idx=None if cs is None else [slot],
+                                     has_initial_state=init, apply_silu=apply_silu)
+        o[:, tb:te] = os_[0]
+        sc[:, tb:te] = ss_[0]
+    return o, sc, cs
+
+
+def selective_scan_varlen(u, dt, A, B, C, cu_seqlens, D=None, z=None, dt_bias=None,
+                          dt_softplus=True, state=None, slot_idx=None, has_initial_state=None,
+                          out=None):
+    """Packed variable-length batch of the scan: u, z [nheads*headdim,
+    total_len], dt [nheads, total_len], B, C [ngroups, dstate, total_len].
+    Each sequence is one independent dense call (batch 1) on its columns,
+    starting from its slot's state when its flag is set and leaving its final
+    state in the slot; padded and empty sequences are skipped.  No arithmetic
+    of its own: it slices and calls selective_scan.
+    Returns (out, out_scale, state_after, state_scale)."""
+    u, dt, B, C = _f64(u), _f64(dt), _f64(B), _f64(C)
+    z = _f64(z)
+    st = None if state is None else np.array(state, dtype=np.float64, copy=True, order="C")
+    sts = None if st is None else np.zeros_like(st)
+    o = np.zeros_like(u) if out is None else np.array(out, dtype=np.float64, copy=True, order="C")
+    sc = np.zeros_like(u)
+    for s, (tb, te) in enumerate(_seq_bounds(cu_seqlens)):
+        slot = s if slot_idx is None else int(slot_idx[s])
+        if slot < 0 or te == tb:
+            continue
+        init = bool(has_initial_state[s]) if has_initial_state is not None else False
+        os_, ss_, st_new, sts_new = selective_scan(
+            u[None, :, tb:te], dt[None, :, tb:te], A, B[None, :, :, tb:te], C[None, :, :, tb:te],
+            D=D, z=None if z is None else z[None, :, tb:te], dt_bias=dt_bias,
+            dt_softplus=dt_softplus, state=st, slot_idx=None if st is None else [slot],
+            has_initial_state=init)
+        o[:, tb:te] = os_[0]
+        sc[:, tb:te] = ss_[0]
+        if st is not None:
+            st = st_new
+            sts[slot] = sts_new[slot]
+    return o, sc, st, sts

@@ -11,6 +11,9 @@ Layouts (dense, row-major, time innermost for prefill):
              B/C [batch, ngroups, dstate, seqlen]
     decode   x/z/out [batch, nheads, headdim], dt [batch, nheads],
              B/C [batch, ngroups, dstate]
+    varlen   sequences packed along time: x/u/z/out [channels, total_len],
+             dt [nheads, total_len], B/C [ngroups, dstate, total_len];
+             cu_seqlens int32 [nseq+1] on the GPU
     caches   conv_state [nslots, channels, width-1], ssm_state
              [nslots, nheads, headdim, dstate]
     params   A [nheads, dstate] (one decay per channel and state) or [nheads]
@@ -31,7 +34,8 @@ SSM_F32, SSM_F16, SSM_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: SSM_BF16}
 
 EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_state_update",
-            "ssm_decode_step", "ssm_status_string", "ssm_abi_version")
+            "ssm_decode_step", "ssm_causal_conv1d_varlen", "ssm_selective_scan_varlen",
+            "ssm_status_string", "ssm_abi_version")
 
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE",
           4: "SSM_ERR_ALIGN", 5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_HIP"}
@@ -68,6 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_decode_step.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P,
                                     I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_decode_step.restype = I
+    lib.ssm_causal_conv1d_varlen.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.ssm_causal_conv1d_varlen.restype = I
+    lib.ssm_selective_scan_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                              I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_selective_scan_varlen.restype = I
     lib.ssm_status_string.argtypes = [I]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -203,6 +212,56 @@ def decode_step(state, conv_state, x, conv_weight, dt, A, B, C, conv_bias=None, 
     return out
 
 
-__all__ = ["causal_conv1d", "selective_scan", "state_update", "decode_step", "load_library",
+def causal_conv1d_varlen(x, weight, cu_seqlens, bias=None, conv_state=None, slot_idx=None,
+                         has_initial_state=None, out=None, apply_silu=True, stream=None):
+    """ssm_causal_conv1d_varlen: x [channels, total_len] holding len(cu_seqlens)-1
+    sequences; has_initial_state int32 [nseq] (on the GPU) or None."""
+    channels, total_len = x.shape
+    nseq = cu_seqlens.shape[0] - 1
+    width = weight.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    _same_io(x.dtype, (out, "out"), (conv_state, "conv_state"))
+    nslots = conv_state.shape[0] if conv_state is not None else 0
+    st = load_library().ssm_causal_conv1d_varlen(
+        _ptr(x, "x"), _ptr(weight, "weight", torch.float32), _ptr(bias, "bias", torch.float32),
+        _ptr(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+        _ptr(has_initial_state, "has_initial_state", torch.int32),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32), _ptr(out, "out"), nseq, channels,
+        total_len, width, nslots, _code(x, "x"), int(bool(apply_silu)), _stream(stream))
+    _check("ssm_causal_conv1d_varlen", st)
+    return out
+
+
+def selective_scan_varlen(u, dt, A, B, C, cu_seqlens, D=None, z=None, dt_bias=None,
+                          dt_softplus=True, ssm_state=None, slot_idx=None,
+                          has_initial_state=None, out=None, stream=None):
+    """ssm_selective_scan_varlen: u [nheads*headdim, total_len] holding
+    len(cu_seqlens)-1 sequences -> out."""
+    channels, total_len = u.shape
+    nheads = dt.shape[0]
+    headdim = channels // nheads
+    ngroups, dstate = B.shape[0], B.shape[1]
+    nseq = cu_seqlens.shape[0] - 1
+    a_per_state = 1 if A.dim() == 2 else 0
+    if out is None:
+        out = torch.empty_like(u)
+    _same_io(u.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
+    nslots = ssm_state.shape[0] if ssm_state is not None else 0
+    sd = _code(ssm_state, "ssm_state") if ssm_state is not None else SSM_F32
+    st = load_library().ssm_selective_scan_varlen(
+        _ptr(u, "u"), _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32),
+        _ptr(A, "A", torch.float32), _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32),
+        _ptr(z, "z"), _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+        _ptr(has_initial_state, "has_initial_state", torch.int32),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32), _ptr(out, "out"), nseq, total_len, nheads,
+        headdim, dstate, ngroups, nslots, _code(u, "u"), sd, a_per_state,
+        int(bool(dt_softplus)), _stream(stream))
+    _check("ssm_selective_scan_varlen", st)
+    return out
+
+
+__all__ = ["causal_conv1d", "selective_scan", "state_update", "decode_step",
+           "causal_conv1d_varlen", "selective_scan_varlen", "load_library",
            "SsmError",
            "SSM_F32", "SSM_F16", "SSM_BF16", "EXPORTED", "LIB_PATH"]

@@ -8,12 +8,16 @@
 //     out[b,c,t] = silu(bias[c] + sum_{k<W} w[c,k] * xh[b,c,t-W+1+k])
 // where xh is x preceded by the cached history (or zeros).
 //
-// Prefill kernel: one 256-lane workgroup per (b, c) row walks the row in
-// tiles of 256*VEC samples (VEC = one 128-bit load per lane).  The tile plus
-// its W-1 history is staged in LDS so each lane reads its neighbours' samples
-// without re-fetching them from memory; the history of the next tile is kept
-// in LDS, and the row's final W-1 samples go to the cache at the end.  HBM
-// traffic: x read once, out written once.
+// Prefill kernel: one 256-lane workgroup per (sequence, channel) row walks
+// the row in tiles of 256*E samples (E = one 128-bit load per lane).  The tile
+// plus its W-1 history is staged in LDS so each lane reads its neighbours'
+// samples without re-fetching them from memory; the history of the next tile
+// is kept in LDS, and the sequence's final W-1 samples go to the cache at the
+// end.  The same kernel serves a dense batch and a packed variable-length
+// batch (sequences of different lengths concatenated along time, each with
+// its own slot and initial-state flag); the tiles are aligned to 128-bit
+// vectors whatever column a sequence starts at.  HBM traffic: x read once,
+// out written once.
 //
 // Decode kernels (seqlen == 1): gather the window from the slot, one output,
 // shift the window by one in place.  The vector kernel gives each lane 8
@@ -32,14 +36,17 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
     constexpr int H = W - 1;
     constexpr int OFF = 4;                          // history sits in xs[OFF-H, OFF)
     __shared__ float xs[OFF + TILE];
-    __shared__ float hist[4];
+    __shared__ float hist[4];   // the H samples in front of the current tile
+    __shared__ float init[4];   // the sequence's history (cache or zeros)
 
     const int64_t row = xcd_block_order(blockIdx.x, gridDim.x);  // b*channels + c
     const int b = (int)(row / a.channels), c = (int)(row % a.channels);
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.has_init_seq, b, a.seqlen, a.has_initial_state);
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
-    if (slot < 0)
-        return;  // padded request (uniform over the workgroup)
+    if (slot < 0 || sp.len == 0)
+        return;  // padded or empty sequence (uniform over the workgroup)
     const int tid = threadIdx.x;
+    const int len = sp.len;
 
     float w[W];
 #pragma unroll
@@ -49,21 +56,43 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
 
     T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
     if (tid < H)
-        hist[tid] = (a.has_initial_state && cs) ? to_f32(cs[tid]) : 0.0f;
+        init[tid] = (sp.init && cs) ? to_f32(cs[tid]) : 0.0f;
 
-    const T *xr = static_cast<const T *>(a.x) + row * a.seqlen;
-    T *orow = static_cast<T *>(a.out) + row * a.seqlen;
+    // The row is walked in tiles aligned to 128-bit vectors: column j of the
+    // walk is sequence step j - m, where m places the sequence's first sample
+    // inside its vector.  Samples outside the sequence are replaced by the
+    // history (before it) or by zeros (after it) and never stored.
+    const int64_t first = (sp.block * a.channels + c) * a.seqlen + sp.begin;
+    const int m = VEC ? (int)(first % E) : 0;
+    const T *xr = static_cast<const T *>(a.x) + (first - m);
+    T *orow = static_cast<T *>(a.out) + (first - m);
+    const int64_t room = a.x_elems - (first - m);  // elements of x from xr on
 
-    for (int t0 = 0; t0 < a.seqlen; t0 += TILE) {
+    __syncthreads();  // init visible
+    if (tid < H) {
+        // columns -H..-1 of the first tile are steps -m-H..-m-1
+        const int tau = tid - H - m;
+        hist[tid] = tau >= -H ? init[H + tau] : 0.0f;
+    }
+    for (int t0 = 0; t0 < m + len; t0 += TILE) {
         const int t = t0 + tid * E;
-        const int len = min(TILE, a.seqlen - t0);
         float v[E];
-        if (VEC && t + E <= a.seqlen) {
+        if (VEC && t < m + len && t + E <= room) {
             load_vec<T, E>(xr + t, v);
         } else {
 #pragma unroll
-            for (int i = 0; i < E; ++i)
-                v[i] = (t + i < a.seqlen) ? to_f32(xr[t + i]) : 0.0f;
+            for (int i = 0; i < E; ++i) {
+                const int j = t + i;
+                v[i] = (j >= m && j < m + len) ? to_f32(xr[j]) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const int tau = t + i - m;
+            if (tau < 0)
+                v[i] = tau >= -H ? init[H + tau] : 0.0f;
+            else if (tau >= len)
+                v[i] = 0.0f;
         }
         __syncthreads();  // hist written / previous tile's readers finished
 #pragma unroll
@@ -81,21 +110,23 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
                 acc = fmaf(w[k], xs[OFF + tid * E + i - H + k], acc);
             o[i] = a.apply_silu ? silu_f32(acc) : acc;
         }
-        if (VEC && t + E <= a.seqlen) {
+        if (VEC && t >= m && t + E <= m + len) {
             store_vec<T, E>(orow + t, o);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i)
-                if (t + i < a.seqlen)
+                if (t + i >= m && t + i < m + len)
                     orow[t + i] = from_f32<T>(o[i]);
         }
-        // history of the next tile: the last H samples of history||tile
         if (tid < H)
-            hist[tid] = xs[OFF + len - H + tid];
+            hist[tid] = xs[OFF + TILE - H + tid];
     }
-    __syncthreads();
-    if (cs && tid < H)
-        cs[tid] = from_f32<T>(hist[tid]);  // exact: the values came from T
+    __syncthreads();  // every lane has read init and the cache row
+    if (cs && tid < H) {
+        // the new tail: the last H samples of history || sequence, copied
+        const int tau = len - H + tid;
+        cs[tid] = tau >= 0 ? xr[m + tau] : from_f32<T>(init[H + tau]);
+    }
 }
 
 template <typename T, int W>
@@ -197,11 +228,11 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
 template <typename T, int W>
 static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
 {
-    if (a.seqlen == 1 && a.vec_decode) {
+    if (!a.cu_seqlens && a.seqlen == 1 && a.vec_decode) {
         const int64_t n = (int64_t)a.batch * (a.channels / 8);
         hipLaunchKernelGGL((conv_decode_vec_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            stream, a);
-    } else if (a.seqlen == 1) {
+    } else if (!a.cu_seqlens && a.seqlen == 1) {
         const int64_t n = (int64_t)a.batch * a.channels;
         hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            stream, a);

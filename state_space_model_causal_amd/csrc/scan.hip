@@ -40,31 +40,35 @@ constexpr int CPB = 256 / R; // channels per workgroup
 constexpr int NC = 16;       // states per LDS chunk of B/C
 } // namespace
 
-// Load timesteps [tl, tl+K) of one row (zeros past the end of the sequence).
-// Every load is issued unconditionally from a clamped, in-bounds address and
-// the out-of-range values are replaced afterwards, so all loads of a lane are
-// in flight together instead of each waiting behind its own branch.
+// Columns of a row: the walk over a sequence covers columns [0, hi) of its
+// rows, the sequence itself being columns [lo, hi) (lo > 0 only when a vector
+// row starts the sequence in the middle of a 128-bit vector).
+
+// Load columns [tl, tl+K) of one row, zeros outside [lo, hi).  Every load is
+// issued unconditionally from a clamped, in-bounds address and the
+// out-of-range values are replaced afterwards, so all loads of a lane are in
+// flight together instead of each waiting behind its own branch.
 template <typename TI, bool VEC>
-__device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, int L, float (&dst)[K])
+__device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, int lo, int hi, float (&dst)[K])
 {
     constexpr int E = 16 / StorageSize<TI>::value;
     if constexpr (VEC) {
-        // VEC: L is a positive multiple of 8 (>= E), so offset 0 is a valid vector
+        // a vector that starts before hi ends inside the row (rows are a
+        // multiple of 8 long and 16-byte aligned), and column 0 is a valid vector
 #pragma unroll
         for (int v = 0; v < K / E; ++v) {
             const int off = tl + v * E;
-            const bool ok = off + E <= L;
             float part[E];
-            load_vec_cached<TI, E>(row + (ok ? off : 0), part);
+            load_vec_cached<TI, E>(row + (off < hi ? off : 0), part);
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                dst[v * E + e] = ok ? part[e] : 0.0f;
+                dst[v * E + e] = (off + e >= lo && off + e < hi) ? part[e] : 0.0f;
         }
     } else {
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-            const bool ok = tl + i < L;
-            const float x = to_f32(row[ok ? tl + i : 0]);
+            const bool ok = tl + i >= lo && tl + i < hi;
+            const float x = to_f32(row[ok ? tl + i : lo]);
             dst[i] = ok ? x : 0.0f;
         }
     }
@@ -81,20 +85,20 @@ struct RawSteps {
 };
 
 template <typename TI>
-__device__ __forceinline__ void load_raw(RawSteps<TI> &r, const TI *__restrict__ row, int tl, int L)
+__device__ __forceinline__ void load_raw(RawSteps<TI> &r, const TI *__restrict__ row, int tl, int hi)
 {
 #pragma unroll
     for (int v = 0; v < RawSteps<TI>::NV; ++v) {
         const int off = tl + v * RawSteps<TI>::E;
-        r.ok[v] = off + RawSteps<TI>::E <= L;
+        r.ok[v] = off < hi;
         r.w[v] = *reinterpret_cast<const u32x4 *>(row + (r.ok[v] ? off : 0));
     }
 }
 
-// Values past the end of the sequence are not masked here: they came from
-// clamped in-bounds addresses (finite data of the same row), and the step size
-// of those timesteps is zeroed, which makes them identity steps (decay 1,
-// input 0) whose outputs are never stored.
+// Values outside the sequence are not masked here: they came from clamped
+// in-bounds addresses, and the caller zeroes the step size and the input of
+// those columns, which makes them identity steps (decay 1, input 0) whose
+// outputs are never stored.
 template <typename TI>
 __device__ __forceinline__ void widen(const RawSteps<TI> &r, float (&dst)[K])
 {
@@ -112,25 +116,34 @@ __device__ __forceinline__ void widen(const RawSteps<TI> &r, float (&dst)[K])
     }
 }
 
+// Store columns [tl, tl+K) that lie in [lo, hi): whole vectors where the
+// sequence covers them, single elements at its two ends (the neighbouring
+// columns belong to other sequences).
 template <typename TI, bool VEC>
-__device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int L, const float (&src)[K])
+__device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int lo, int hi, const float (&src)[K])
 {
     constexpr int E = 16 / StorageSize<TI>::value;
     if constexpr (VEC) {
 #pragma unroll
         for (int v = 0; v < K / E; ++v) {
-            if (tl + (v + 1) * E <= L) {
+            const int off = tl + v * E;
+            if (off >= lo && off + E <= hi) {
                 float part[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     part[e] = src[v * E + e];
-                store_vec_cached<TI, E>(row + tl + v * E, part);
+                store_vec_cached<TI, E>(row + off, part);
+            } else if (off + E > lo && off < hi) {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (off + e >= lo && off + e < hi)
+                        row[off + e] = from_f32<TI>(src[v * E + e]);
             }
         }
     } else {
 #pragma unroll
         for (int i = 0; i < K; ++i)
-            if (tl + i < L)
+            if (tl + i >= lo && tl + i < hi)
                 row[tl + i] = from_f32<TI>(src[i]);
     }
 }
@@ -162,16 +175,21 @@ void scan_kernel(ScanArgs a)
     __shared__ float lds_carry[CPB][NCAP];
     __shared__ float lds_a2[A_PER_STATE ? CPB : 1][A_PER_STATE ? NCAP : 1];
 
-    const int L = a.seqlen, N = a.dstate, P = a.headdim;
+    const int L = a.seqlen, N = a.dstate, P = a.headdim;  // L: row length
     const int cpg = a.heads_per_group * P;  // channels per group (contiguous)
     const int nblk_g = (cpg + CPB - 1) / CPB;
     const uint32_t lb = xcd_block_order(blockIdx.x, gridDim.x);
     const int cb = (int)(lb % nblk_g);
     const int bg = (int)(lb / nblk_g);
     const int g = bg % a.ngroups, b = bg / a.ngroups;
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.has_init_seq, b, L, a.has_initial_state);
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
-    if (slot < 0)
-        return;  // padded request (uniform over the workgroup)
+    if (slot < 0 || sp.len == 0)
+        return;  // padded or empty sequence (uniform over the workgroup)
+    // the walk starts at the 128-bit vector holding the sequence's first step
+    // (every row of the sequence starts at the same offset within a vector)
+    const int lo = VEC ? sp.begin % E : 0, hi = lo + sp.len;
+    const int64_t col0 = sp.begin - lo;
 
     const int tid = threadIdx.x, ch = tid / R, r = tid % R;
     const int cig = cb * CPB + ch;
@@ -180,14 +198,15 @@ void scan_kernel(ScanArgs a)
     const int h = c / P, p = c % P;
     const int Cn = a.nheads * P;
 
-    const TI *urow = static_cast<const TI *>(a.u) + ((int64_t)b * Cn + c) * L;
-    const TI *dtrow = static_cast<const TI *>(a.dt) + ((int64_t)b * a.nheads + h) * L;
-    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + ((int64_t)b * Cn + c) * L : nullptr;
-    TI *orow = static_cast<TI *>(a.out) + ((int64_t)b * Cn + c) * L;
-    const TI *Bg = static_cast<const TI *>(a.B) + ((int64_t)b * a.ngroups + g) * N * L;
-    const TI *Cg = static_cast<const TI *>(a.C) + ((int64_t)b * a.ngroups + g) * N * L;
+    const int64_t blk = sp.block;
+    const TI *urow = static_cast<const TI *>(a.u) + (blk * Cn + c) * L + col0;
+    const TI *dtrow = static_cast<const TI *>(a.dt) + (blk * a.nheads + h) * L + col0;
+    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + (blk * Cn + c) * L + col0 : nullptr;
+    TI *orow = static_cast<TI *>(a.out) + (blk * Cn + c) * L + col0;
+    const TI *Bg = static_cast<const TI *>(a.B) + (blk * a.ngroups + g) * N * L + col0;
+    const TI *Cg = static_cast<const TI *>(a.C) + (blk * a.ngroups + g) * N * L + col0;
     TS *srow = a.state ? static_cast<TS *>(a.state) + (((int64_t)slot * a.nheads + h) * P + p) * N : nullptr;
-    const bool load_init = srow && a.has_initial_state;
+    const bool load_init = srow && sp.init;
 
     const float bias_h = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float D_h = a.D ? a.D[h] : 0.0f;
@@ -199,7 +218,7 @@ void scan_kernel(ScanArgs a)
             lds_a2[ch][n] = a.A[(int64_t)h * N + n] * kLog2e;
     }
 
-    for (int t0 = 0; t0 < L; t0 += T) {
+    for (int t0 = 0; t0 < hi; t0 += T) {
         const int tl = t0 + r * K;
         float dl[K], du[K], y[K];
         RawSteps<TI> rz;  // the gate's loads are issued with the others
@@ -207,26 +226,28 @@ void scan_kernel(ScanArgs a)
             float uu[K], dd[K];
             if constexpr (VEC) {
                 RawSteps<TI> ru, rd;
-                load_raw(ru, urow, tl, L);
-                load_raw(rd, dtrow, tl, L);
+                load_raw(ru, urow, tl, hi);
+                load_raw(rd, dtrow, tl, hi);
                 // 2-byte gates are fetched early (8 VGPRs); 4-byte ones at the end
                 if (zrow && StorageSize<TI>::value == 2)
-                    load_raw(rz, zrow, tl, L);
+                    load_raw(rz, zrow, tl, hi);
                 widen(ru, uu);
                 widen(rd, dd);
             } else {
-                load_steps<TI, VEC>(urow, tl, L, uu);
-                load_steps<TI, VEC>(dtrow, tl, L, dd);
+                load_steps<TI, VEC>(urow, tl, lo, hi, uu);
+                load_steps<TI, VEC>(dtrow, tl, lo, hi, dd);
             }
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 const float v = dd[i] + bias_h;
-                const float sp = softplus_f32(v);
-                float d = a.dt_softplus ? sp : v;
-                d = (tl + i < L) ? d : 0.0f;  // identity step past the end
+                const float spv = softplus_f32(v);
+                const bool in = tl + i >= lo && tl + i < hi;
+                // identity step outside the sequence (decay 1, input 0)
+                const float d = in ? (a.dt_softplus ? spv : v) : 0.0f;
+                const float uv = in ? uu[i] : 0.0f;
                 dl[i] = d;
-                du[i] = d * uu[i];
-                y[i] = D_h * uu[i];
+                du[i] = d * uv;
+                y[i] = D_h * uv;
             }
         }
         float sdl = 0.0f;
@@ -259,20 +280,21 @@ void scan_kernel(ScanArgs a)
                 float vb[E], vc[E];
                 if constexpr (VEC) {
                     // clamped address, unconditional load, then select
-                    const bool ok = n < N && t + E <= L;
+                    const bool ok = n < N && t < hi;
                     const int64_t off = ok ? (int64_t)n * L + t : 0;
                     load_vec_cached<TI, E>(Bg + off, vb);
                     load_vec_cached<TI, E>(Cg + off, vc);
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
-                        vb[e] = ok ? vb[e] : 0.0f;
-                        vc[e] = ok ? vc[e] : 0.0f;
+                        const bool in = ok && t + e >= lo && t + e < hi;
+                        vb[e] = in ? vb[e] : 0.0f;
+                        vc[e] = in ? vc[e] : 0.0f;
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
-                        const bool ok = n < N && t + e < L;
-                        const int64_t off = ok ? (int64_t)n * L + t + e : 0;
+                        const bool ok = n < N && t + e >= lo && t + e < hi;
+                        const int64_t off = ok ? (int64_t)n * L + t + e : lo;
                         const float xb = to_f32(Bg[off]), xc = to_f32(Cg[off]);
                         vb[e] = ok ? xb : 0.0f;
                         vc[e] = ok ? xc : 0.0f;
@@ -359,13 +381,13 @@ void scan_kernel(ScanArgs a)
             if constexpr (VEC && StorageSize<TI>::value == 2)
                 widen(rz, zz);
             else
-                load_steps<TI, VEC>(zrow, tl, L, zz);
+                load_steps<TI, VEC>(zrow, tl, lo, hi, zz);
 #pragma unroll
             for (int i = 0; i < K; ++i)
                 y[i] *= silu_f32(zz[i]);
         }
         if (active)
-            store_steps<TI, VEC>(orow, tl, L, y);
+            store_steps<TI, VEC>(orow, tl, lo, hi, y);
     }
     __syncthreads();
     if (srow && active)

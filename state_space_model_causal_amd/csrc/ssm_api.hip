@@ -27,6 +27,120 @@ bool slots_ok(const void *cache, const int32_t *slot_idx, int nslots, int batch)
     return slot_idx != nullptr || nslots >= batch;
 }
 
+// Dense batch (cu_seqlens null): x [batch, channels, seqlen].  Packed batch:
+// x [channels, seqlen] holding batch sequences at the columns cu_seqlens gives.
+int conv_call(const void *x, const float *weight, const float *bias, void *conv_state,
+              const int32_t *slot_idx, const int32_t *cu_seqlens, const int32_t *has_init_seq,
+              void *out, int batch, int channels, int seqlen, int width, int nslots, int dtype,
+              int has_initial_state, int apply_silu, void *stream)
+{
+    if (!x || !weight || !out)
+        return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(dtype))
+        return SSM_ERR_DTYPE;
+    if (batch < 0 || seqlen < 0 || channels < 1 || width < 1)
+        return SSM_ERR_SHAPE;
+    if (width > ssm::kMaxConvWidth)
+        return SSM_ERR_UNSUPPORTED;
+    if (!slots_ok(conv_state, slot_idx, nslots, batch))
+        return SSM_ERR_SHAPE;
+    const int es = dtype_size(dtype);
+    if (!aligned(x, es) || !aligned(out, es) || !aligned(conv_state, es) || !aligned(weight, 4) ||
+        !aligned(bias, 4) || !aligned(slot_idx, 4) || !aligned(cu_seqlens, 4) ||
+        !aligned(has_init_seq, 4))
+        return SSM_ERR_ALIGN;
+    if ((int64_t)batch * channels > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
+    if (batch == 0 || seqlen == 0)
+        return SSM_OK;
+    ssm::ConvArgs a;
+    a.x = x;
+    a.weight = weight;
+    a.bias = bias;
+    a.conv_state = conv_state;
+    a.slot_idx = slot_idx;
+    a.out = out;
+    a.cu_seqlens = cu_seqlens;
+    a.has_init_seq = has_init_seq;
+    a.x_elems = (int64_t)(cu_seqlens ? 1 : batch) * channels * seqlen;
+    a.batch = batch;
+    a.channels = channels;
+    a.seqlen = seqlen;
+    a.width = width;
+    a.nslots = nslots;
+    a.dtype = dtype;
+    a.has_initial_state = has_initial_state ? 1 : 0;
+    a.apply_silu = apply_silu ? 1 : 0;
+    a.vec = aligned(x, 16) && aligned(out, 16);
+    a.vec_decode = (seqlen == 1) && (channels % 8 == 0) && aligned(x, 16) && aligned(out, 16) &&
+                   aligned(conv_state, 16) && aligned(weight, 16) && aligned(bias, 16);
+    return status_of(ssm::launch_conv(a, static_cast<hipStream_t>(stream)));
+}
+
+// Dense batch (cu_seqlens null) or packed batch, as for conv_call.
+int scan_call(const void *u, const void *dt, const float *dt_bias, const float *A, const void *B,
+              const void *C, const float *D, const void *z, void *ssm_state,
+              const int32_t *slot_idx, const int32_t *cu_seqlens, const int32_t *has_init_seq,
+              void *out, int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+              int nslots, int io_dtype, int state_dtype, int a_per_state, int dt_softplus,
+              int has_initial_state, void *stream)
+{
+    if (!u || !dt || !A || !B || !C || !out)
+        return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
+        return SSM_ERR_DTYPE;
+    if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1 ||
+        nheads % ngroups != 0)
+        return SSM_ERR_SHAPE;
+    if (dstate > ssm::kMaxScanDstate)
+        return SSM_ERR_UNSUPPORTED;
+    if (!slots_ok(ssm_state, slot_idx, nslots, batch))
+        return SSM_ERR_SHAPE;
+    const int es = dtype_size(io_dtype);
+    if (!aligned(u, es) || !aligned(dt, es) || !aligned(B, es) || !aligned(C, es) ||
+        !aligned(z, es) || !aligned(out, es) || !aligned(ssm_state, dtype_size(state_dtype)) ||
+        !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(slot_idx, 4) ||
+        !aligned(cu_seqlens, 4) || !aligned(has_init_seq, 4))
+        return SSM_ERR_ALIGN;
+    const int64_t channels = (int64_t)nheads * headdim;
+    const int64_t cpg = channels / ngroups;
+    const int64_t nblocks = (int64_t)batch * ngroups * ((cpg + 15) / 16);
+    if (channels > INT32_MAX || nblocks > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
+    if (batch == 0 || seqlen == 0)
+        return SSM_OK;
+    ssm::ScanArgs a;
+    a.u = u;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.z = z;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.D = D;
+    a.state = ssm_state;
+    a.slot_idx = slot_idx;
+    a.out = out;
+    a.cu_seqlens = cu_seqlens;
+    a.has_init_seq = has_init_seq;
+    a.batch = batch;
+    a.seqlen = seqlen;
+    a.nheads = nheads;
+    a.headdim = headdim;
+    a.dstate = dstate;
+    a.ngroups = ngroups;
+    a.nslots = nslots;
+    a.heads_per_group = nheads / ngroups;
+    a.io_dtype = io_dtype;
+    a.state_dtype = state_dtype;
+    a.a_per_state = a_per_state ? 1 : 0;
+    a.dt_softplus = dt_softplus ? 1 : 0;
+    a.has_initial_state = has_initial_state ? 1 : 0;
+    a.vec = (seqlen % 8 == 0) && aligned(u, 16) && aligned(dt, 16) && aligned(B, 16) &&
+            aligned(C, 16) && aligned(z, 16) && aligned(out, 16);
+    return status_of(ssm::launch_scan(a, static_cast<hipStream_t>(stream)));
+}
+
 } // namespace
 
 extern "C" {
@@ -52,43 +166,20 @@ int ssm_causal_conv1d(const void *x, const float *weight, const float *bias, voi
                       int width, int nslots, int dtype, int has_initial_state, int apply_silu,
                       void *stream)
 {
-    if (!x || !weight || !out)
+    return conv_call(x, weight, bias, conv_state, slot_idx, nullptr, nullptr, out, batch, channels,
+                     seqlen, width, nslots, dtype, has_initial_state, apply_silu, stream);
+}
+
+int ssm_causal_conv1d_varlen(const void *x, const float *weight, const float *bias,
+                             void *conv_state, const int32_t *slot_idx,
+                             const int32_t *has_initial_state, const int32_t *cu_seqlens,
+                             void *out, int nseq, int channels, int total_len, int width,
+                             int nslots, int dtype, int apply_silu, void *stream)
+{
+    if (!cu_seqlens)
         return SSM_ERR_NULL_ARG;
-    if (!valid_dtype(dtype))
-        return SSM_ERR_DTYPE;
-    if (batch < 0 || seqlen < 0 || channels < 1 || width < 1)
-        return SSM_ERR_SHAPE;
-    if (width > ssm::kMaxConvWidth)
-        return SSM_ERR_UNSUPPORTED;
-    if (!slots_ok(conv_state, slot_idx, nslots, batch))
-        return SSM_ERR_SHAPE;
-    const int es = dtype_size(dtype);
-    if (!aligned(x, es) || !aligned(out, es) || !aligned(conv_state, es) || !aligned(weight, 4) ||
-        !aligned(bias, 4) || !aligned(slot_idx, 4))
-        return SSM_ERR_ALIGN;
-    if ((int64_t)batch * channels > INT32_MAX)
-        return SSM_ERR_UNSUPPORTED;
-    if (batch == 0 || seqlen == 0)
-        return SSM_OK;
-    ssm::ConvArgs a;
-    a.x = x;
-    a.weight = weight;
-    a.bias = bias;
-    a.conv_state = conv_state;
-    a.slot_idx = slot_idx;
-    a.out = out;
-    a.batch = batch;
-    a.channels = channels;
-    a.seqlen = seqlen;
-    a.width = width;
-    a.nslots = nslots;
-    a.dtype = dtype;
-    a.has_initial_state = has_initial_state ? 1 : 0;
-    a.apply_silu = apply_silu ? 1 : 0;
-    a.vec = (seqlen % 8 == 0) && aligned(x, 16) && aligned(out, 16);
-    a.vec_decode = (seqlen == 1) && (channels % 8 == 0) && aligned(x, 16) && aligned(out, 16) &&
-                   aligned(conv_state, 16) && aligned(weight, 16) && aligned(bias, 16);
-    return status_of(ssm::launch_conv(a, static_cast<hipStream_t>(stream)));
+    return conv_call(x, weight, bias, conv_state, slot_idx, cu_seqlens, has_initial_state, out,
+                     nseq, channels, total_len, width, nslots, dtype, 0, apply_silu, stream);
 }
 
 int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias, const float *A,
@@ -98,57 +189,24 @@ int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias, cons
                        int state_dtype, int a_per_state, int dt_softplus, int has_initial_state,
                        void *stream)
 {
-    if (!u || !dt || !A || !B || !C || !out)
+    return scan_call(u, dt, dt_bias, A, B, C, D, z, ssm_state, slot_idx, nullptr, nullptr, out,
+                     batch, seqlen, nheads, headdim, dstate, ngroups, nslots, io_dtype,
+                     state_dtype, a_per_state, dt_softplus, has_initial_state, stream);
+}
+
+int ssm_selective_scan_varlen(const void *u, const void *dt, const float *dt_bias,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const void *z, void *ssm_state, const int32_t *slot_idx,
+                              const int32_t *has_initial_state, const int32_t *cu_seqlens,
+                              void *out, int nseq, int total_len, int nheads, int headdim,
+                              int dstate, int ngroups, int nslots, int io_dtype, int state_dtype,
+                              int a_per_state, int dt_softplus, void *stream)
+{
+    if (!cu_seqlens)
         return SSM_ERR_NULL_ARG;
-    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
-        return SSM_ERR_DTYPE;
-    if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1 ||
-        nheads % ngroups != 0)
-        return SSM_ERR_SHAPE;
-    if (dstate > ssm::kMaxScanDstate)
-        return SSM_ERR_UNSUPPORTED;
-    if (!slots_ok(ssm_state, slot_idx, nslots, batch))
-        return SSM_ERR_SHAPE;
-    const int es = dtype_size(io_dtype);
-    if (!aligned(u, es) || !aligned(dt, es) || !aligned(B, es) || !aligned(C, es) ||
-        !aligned(z, es) || !aligned(out, es) || !aligned(ssm_state, dtype_size(state_dtype)) ||
-        !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(slot_idx, 4))
-        return SSM_ERR_ALIGN;
-    const int64_t channels = (int64_t)nheads * headdim;
-    const int64_t cpg = channels / ngroups;
-    const int64_t nblocks = (int64_t)batch * ngroups * ((cpg + 15) / 16);
-    if (channels > INT32_MAX || nblocks > INT32_MAX)
-        return SSM_ERR_UNSUPPORTED;
-    if (batch == 0 || seqlen == 0)
-        return SSM_OK;
-    ssm::ScanArgs a;
-    a.u = u;
-    a.dt = dt;
-    a.B = B;
-    a.C = C;
-    a.z = z;
-    a.dt_bias = dt_bias;
-    a.A = A;
-    a.D = D;
-    a.state = ssm_state;
-    a.slot_idx = slot_idx;
-    a.out = out;
-    a.batch = batch;
-    a.seqlen = seqlen;
-    a.nheads = nheads;
-    a.headdim = headdim;
-    a.dstate = dstate;
-    a.ngroups = ngroups;
-    a.nslots = nslots;
-    a.heads_per_group = nheads / ngroups;
-    a.io_dtype = io_dtype;
-    a.state_dtype = state_dtype;
-    a.a_per_state = a_per_state ? 1 : 0;
-    a.dt_softplus = dt_softplus ? 1 : 0;
-    a.has_initial_state = has_initial_state ? 1 : 0;
-    a.vec = (seqlen % 8 == 0) && aligned(u, 16) && aligned(dt, 16) && aligned(B, 16) &&
-            aligned(C, 16) && aligned(z, 16) && aligned(out, 16);
-    return status_of(ssm::launch_scan(a, static_cast<hipStream_t>(stream)));
+    return scan_call(u, dt, dt_bias, A, B, C, D, z, ssm_state, slot_idx, cu_seqlens,
+                     has_initial_state, out, nseq, total_len, nheads, headdim, dstate, ngroups,
+                     nslots, io_dtype, state_dtype, a_per_state, dt_softplus, 0, stream);
 }
 
 } // extern "C"

@@ -15,10 +15,16 @@ struct ConvArgs {
     void *conv_state;         // may be null
     const int32_t *slot_idx;  // may be null
     void *out;
+    // Packed variable-length batch: sequence b occupies columns
+    // [cu_seqlens[b], cu_seqlens[b+1]) of every channel row of length seqlen
+    // (the packed token count); null = dense batch [batch, channels, seqlen].
+    const int32_t *cu_seqlens;
+    const int32_t *has_init_seq;  // varlen: per-sequence flag, null = none
     int batch, channels, seqlen, width, nslots;
     int dtype;                // 0 f32, 1 f16, 2 bf16
     int has_initial_state, apply_silu;
-    int vec;                  // rows 16-byte aligned and seqlen a multiple of 8
+    int64_t x_elems;          // elements of x (bounds the last vector load)
+    int vec;                  // x and out 16-byte aligned
     int vec_decode;           // seqlen 1, channels % 8 == 0, 16-byte aligned tensors
 };
 
@@ -28,12 +34,46 @@ struct ScanArgs {
     void *state;                     // may be null
     const int32_t *slot_idx;         // may be null
     void *out;
+    // varlen as in ConvArgs: sequence b is columns [cu_seqlens[b],
+    // cu_seqlens[b+1]) of rows of length seqlen; null = dense batch
+    const int32_t *cu_seqlens;
+    const int32_t *has_init_seq;     // varlen: per-sequence flag, null = none
     int batch, seqlen, nheads, headdim, dstate, ngroups, nslots;
     int heads_per_group;
     int io_dtype, state_dtype;
     int a_per_state, dt_softplus, has_initial_state;
-    int vec;                         // rows 16-byte aligned and seqlen a multiple of 8
+    int vec;                         // 16-byte aligned bases and seqlen a multiple of 8
 };
+
+// Where sequence b lies: columns [begin, begin+len) of the rows of row block
+// `block` (b for a dense batch, 0 for a packed one, whose sequences share
+// rows), rows being seqlen long.
+struct SeqSpan {
+    int64_t block;
+    int begin, len;
+    bool init;
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const int32_t *cu, const int32_t *has_init_seq, int b,
+                                            int seqlen, int dense_init)
+{
+    SeqSpan sp;
+    if (cu) {
+        // clamped: a malformed table cannot address columns outside the rows
+        const int tb = min(max(cu[b], 0), seqlen);
+        const int te = min(max(cu[b + 1], tb), seqlen);
+        sp.block = 0;
+        sp.begin = tb;
+        sp.len = te - tb;
+        sp.init = has_init_seq ? has_init_seq[b] != 0 : false;
+    } else {
+        sp.block = b;
+        sp.begin = 0;
+        sp.len = seqlen;
+        sp.init = dense_init != 0;
+    }
+    return sp;
+}
 
 struct SsuArgs {
     void *state;

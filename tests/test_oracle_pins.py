@@ -407,3 +407,88 @@ def test_state_update_gathers_named_slot(oracle):
                                        slot_idx=inv[idx].astype(np.int32))
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(s1, s2[inv])
+
+
+# ------------------------------------------------------ packed variable length
+def _pack(a):
+    # dense [batch, rows..., L] -> packed [rows..., batch*L] (sequence b at
+    # columns [b*L, (b+1)*L)), written with explicit loops
+    batch, L = a.shape[0], a.shape[-1]
+    out = np.zeros(a.shape[1:-1] + (batch * L,))
+    for b in range(batch):
+        for t in range(L):
+            out[..., b * L + t] = a[b, ..., t]
+    return out
+
+
+def test_varlen_equal_lengths_equals_dense(oracle):
+    # sequences of one length packed side by side == the dense batch call
+    # (catches a wrong column slice, a wrong slot or a dropped initial state)
+    c = _scan_case(60, batch=3, seqlen=11, nheads=4, headdim=2, dstate=3, ngroups=2,
+                   a_per_state=False)
+    idx = np.array([3, 0, 2], dtype=np.int32)
+    cu = np.array([0, 11, 22, 33], dtype=np.int32)
+    dense = oracle.selective_scan(c["u"], c["dt"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"],
+                                  dt_bias=c["dt_bias"], state=c["state"], slot_idx=idx,
+                                  has_initial_state=True)
+    packed = oracle.selective_scan_varlen(
+        _pack(c["u"]), _pack(c["dt"]), c["A"], _pack(c["B"]), _pack(c["C"]), cu, D=c["D"],
+        z=_pack(c["z"]), dt_bias=c["dt_bias"], state=c["state"], slot_idx=idx,
+        has_initial_state=np.ones(3, dtype=np.int32))
+    np.testing.assert_array_equal(packed[0], _pack(dense[0]))
+    np.testing.assert_array_equal(packed[2], dense[2])
+    x, w, b, cs = _conv_case(61, batch=3, seqlen=11)
+    cs = np.concatenate([cs, cs[:1] + 1.0])  # 4 slots
+    dense = oracle.causal_conv1d(x, w, b, cs, idx, has_initial_state=True)
+    packed = oracle.causal_conv1d_varlen(_pack(x), w, cu, b, cs, idx,
+                                         has_initial_state=np.ones(3, dtype=np.int32))
+    np.testing.assert_array_equal(packed[0], _pack(dense[0]))
+    np.testing.assert_array_equal(packed[2], dense[2])
+
+
+def test_varlen_split_sequence_resumes(oracle):
+    # a sequence cut across two packed calls (the second continuing from the
+    # slot) == one dense call over the whole sequence; the other sequences of
+    # the calls do not disturb it (catches a flag applied to the wrong
+    # sequence or a state written to the wrong slot)
+    r = rng(62)
+    H, N, L1, L2 = 3, 4, 6, 9
+    c = _scan_case(63, batch=1, seqlen=L1 + L2, nheads=H, dstate=N)
+    state0 = np.zeros((4, H, 1, N))
+    full = oracle.selective_scan(c["u"], c["dt"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"],
+                                 dt_bias=c["dt_bias"], state=state0, slot_idx=[2])
+
+    def packed_call(cols, other_len, init, state):
+        # the piece of sequence 0 as the second of two packed sequences; the
+        # first is unrelated data of other_len steps bound to slot 1
+        o = {k: r.standard_normal(c[k].shape[1:-1] + (other_len,)) for k in ("u", "z", "dt", "B", "C")}
+        cat = {k: np.concatenate([o[k], c[k][0][..., cols]], axis=-1) for k in o}
+        cu = np.array([0, other_len, other_len + cols.stop - cols.start], np.int32)
+        res = oracle.selective_scan_varlen(cat["u"], cat["dt"], c["A"], cat["B"], cat["C"], cu,
+                                           D=c["D"], z=cat["z"], dt_bias=c["dt_bias"],
+                                           state=state, slot_idx=np.array([1, 2], np.int32),
+                                           has_initial_state=np.array([1, init], np.int32))
+        return res[0][:, other_len:], res[2]
+
+    y1, st1 = packed_call(slice(0, L1), 5, 0, state0)
+    y2, st2 = packed_call(slice(L1, L1 + L2), 3, 1, st1)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), full[0][0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st2[2], full[2][2], rtol=1e-12, atol=1e-13)
+
+
+def test_varlen_padded_and_empty_sequences(oracle):
+    # a padded sequence leaves its columns and every slot alone; an empty
+    # sequence leaves its slot alone
+    x, w, b, cs = _conv_case(64, batch=1, seqlen=10)
+    cs = np.concatenate([cs, cs + 1.0, cs + 2.0])  # 3 slots
+    packed = x[0]
+    cu = np.array([0, 4, 4, 10], dtype=np.int32)   # lengths 4, 0, 6
+    idx = np.array([0, 1, -1], dtype=np.int32)
+    sentinel = np.full(packed.shape, 5.0)
+    out, _, cs_new = oracle.causal_conv1d_varlen(packed, w, cu, b, cs, idx,
+                                                 has_initial_state=np.array([1, 1, 1], np.int32),
+                                                 out=sentinel)
+    np.testing.assert_array_equal(out[:, 4:], sentinel[:, 4:])
+    np.testing.assert_array_equal(cs_new[1], cs[1])
+    np.testing.assert_array_equal(cs_new[2], cs[2])
+    assert not np.array_equal(cs_new[0], cs[0])

@@ -184,6 +184,75 @@ def make(spec: Spec, device="cpu") -> dict:
     return t
 
 
+def varlen_lengths(seed: int, nseq: int, total: int, lo: int = 1) -> list:
+    """A seeded mix of nseq sequence lengths summing to total: log-uniform
+    draws between lo and total (short requests next to long ones, as in a
+    continuous-batching prefill), rescaled to the total.  Lengths are not
+    rounded to any multiple."""
+    g = torch.Generator().manual_seed(int(seed) * 7_368_787 + 11)
+    u = torch.rand(nseq, generator=g, dtype=torch.float64)
+    raw = torch.exp(math.log(lo) + u * (math.log(max(total, lo + 1)) - math.log(lo)))
+    lens = [max(lo, int(v)) for v in (raw / raw.sum() * total)]
+    lens[int(torch.argmax(raw))] += total - sum(lens)
+    return lens
+
+
+def make_varlen(spec: Spec, lengths, device="cpu", init_every: int = 2) -> dict:
+    """Draw a packed variable-length prefill: the sequences of `lengths`
+    concatenated along time, x/z [channels, T], dt [nheads, T], B/C [ngroups,
+    dstate, T] (T = sum of lengths), with the parameters and caches of `spec`
+    (spec.batch is ignored: one sequence per length).  Every init_every-th
+    sequence (from the first) continues from its slot's state; slots are the
+    first len(lengths) entries of a permutation of the cache."""
+    io = DTYPES[spec.io]
+    st = DTYPES[spec.state]
+    d = _Draw(spec.seed, device)
+    H, P, N, G = spec.nheads, spec.headdim, spec.dstate, spec.ngroups
+    Cn, nseq = spec.channels, len(lengths)
+    S = max(spec.nslots, nseq)
+    T = int(sum(lengths))
+    t = {}
+    t["x"] = d.normal((Cn, T), io)
+    t["z"] = d.normal((Cn, T), io)
+    t["dt"] = d.normal((H, T), io)
+    t["dt_bias"] = d.uniform((H,), math.log(1e-3), math.log(1e-1))
+    if spec.a_per_state:
+        t["A"] = -d.uniform((H, N), 0.5, N + 0.5)
+    else:
+        t["A"] = -d.uniform((H,), 1.0, 16.0)
+    t["B"] = d.normal((G, N, T), io)
+    t["C"] = d.normal((G, N, T), io)
+    t["D"] = d.uniform((H,), 0.5, 1.5)
+    t["conv_w"] = d.uniform((Cn, spec.width), -0.5, 0.5)
+    t["conv_b"] = d.uniform((Cn,), -0.5, 0.5)
+    t["conv_state"] = d.normal((S, Cn, spec.width - 1), io)
+    t["ssm_state"] = d.normal((S, H, P, N), st)
+    t["slot_idx"] = d.perm(S)[:nseq].to(torch.int32).contiguous()
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    t["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=d.device)
+    t["has_init"] = torch.tensor([1 if (init_every and s % init_every == 0) else 0
+                                  for s in range(nseq)], dtype=torch.int32, device=d.device)
+    return t
+
+
+def varlen_bytes(spec: Spec, lengths, n_init: int) -> dict:
+    """Algorithmic bytes of a packed prefill: the dense formula with the
+    token count T in place of batch x seqlen, plus each sequence's cache
+    rows (read when it continues from its slot, always written)."""
+    isz = {"f32": 4, "f16": 2, "bf16": 2}
+    io, st = isz[spec.io], isz[spec.state]
+    T, nseq = int(sum(lengths)), len(lengths)
+    H, P, N, G, W = spec.nheads, spec.headdim, spec.dstate, spec.ngroups, spec.width
+    Cn = H * P
+    conv = 2 * Cn * T * io + Cn * W * 4 + Cn * 4 + (nseq + n_init) * Cn * (W - 1) * io + (nseq + 1) * 4
+    scan = (2 * Cn * T * io + H * T * io + 2 * G * N * T * io + Cn * T * io
+            + (H * N if spec.a_per_state else H) * 4 + 2 * H * 4
+            + (nseq + n_init) * H * P * N * st + (nseq + 1) * 4)
+    return {"conv": conv, "scan": scan}
+
+
 def to_f64(a) -> np.ndarray:
     """Exact float64 widening of a stored tensor (any of f32/f16/bf16/ints)."""
     if a is None:
