@@ -8,16 +8,17 @@
 //     out[b,c,t] = silu(bias[c] + sum_{k<W} w[c,k] * xh[b,c,t-W+1+k])
 // where xh is x preceded by the cached history (or zeros).
 //
-// Prefill kernel: one 256-lane workgroup per (sequence, channel) row walks
-// the row in tiles of 256*E samples (E = one 128-bit load per lane).  The tile
-// plus its W-1 history is staged in LDS so each lane reads its neighbours'
-// samples without re-fetching them from memory; the history of the next tile
-// is kept in LDS, and the sequence's final W-1 samples go to the cache at the
-// end.  The same kernel serves a dense batch and a packed variable-length
-// batch (sequences of different lengths concatenated along time, each with
-// its own slot and initial-state flag); the tiles are aligned to 128-bit
-// vectors whatever column a sequence starts at.  HBM traffic: x read once,
-// out written once.
+// Dense prefill kernel: one 256-lane workgroup per (b, c) row walks the row
+// in tiles of 256*E samples (E = one 128-bit load per lane).  The tile plus
+// its W-1 history is staged in LDS so each lane reads its neighbours' samples
+// without re-fetching them from memory; the history of the next tile is kept
+// in LDS, and the row's final W-1 samples go to the cache at the end.  HBM
+// traffic: x read once, out written once.
+//
+// Packed variable-length batches (sequences of different lengths side by side
+// along time, each with its own slot and initial-state flag) use a row-tiled
+// kernel whose workgroups each take one tile of a packed channel row, plus a
+// tail kernel that updates the caches afterwards.
 //
 // Decode kernels (seqlen == 1): gather the window from the slot, one output,
 // shift the window by one in place.  The vector kernel gives each lane 8
@@ -36,17 +37,14 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
     constexpr int H = W - 1;
     constexpr int OFF = 4;                          // history sits in xs[OFF-H, OFF)
     __shared__ float xs[OFF + TILE];
-    __shared__ float hist[4];   // the H samples in front of the current tile
-    __shared__ float init[4];   // the sequence's history (cache or zeros)
+    __shared__ float hist[4];
 
     const int64_t row = xcd_block_order(blockIdx.x, gridDim.x);  // b*channels + c
     const int b = (int)(row / a.channels), c = (int)(row % a.channels);
-    const SeqSpan sp = seq_span(a.cu_seqlens, a.has_init_seq, b, a.seqlen, a.has_initial_state);
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
-    if (slot < 0 || sp.len == 0)
-        return;  // padded or empty sequence (uniform over the workgroup)
+    if (slot < 0)
+        return;  // padded request (uniform over the workgroup)
     const int tid = threadIdx.x;
-    const int len = sp.len;
 
     float w[W];
 #pragma unroll
@@ -56,43 +54,21 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
 
     T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
     if (tid < H)
-        init[tid] = (sp.init && cs) ? to_f32(cs[tid]) : 0.0f;
+        hist[tid] = (a.has_initial_state && cs) ? to_f32(cs[tid]) : 0.0f;
 
-    // The row is walked in tiles aligned to 128-bit vectors: column j of the
-    // walk is sequence step j - m, where m places the sequence's first sample
-    // inside its vector.  Samples outside the sequence are replaced by the
-    // history (before it) or by zeros (after it) and never stored.
-    const int64_t first = (sp.block * a.channels + c) * a.seqlen + sp.begin;
-    const int m = VEC ? (int)(first % E) : 0;
-    const T *xr = static_cast<const T *>(a.x) + (first - m);
-    T *orow = static_cast<T *>(a.out) + (first - m);
-    const int64_t room = a.x_elems - (first - m);  // elements of x from xr on
+    const T *xr = static_cast<const T *>(a.x) + row * a.seqlen;
+    T *orow = static_cast<T *>(a.out) + row * a.seqlen;
 
-    __syncthreads();  // init visible
-    if (tid < H) {
-        // columns -H..-1 of the first tile are steps -m-H..-m-1
-        const int tau = tid - H - m;
-        hist[tid] = tau >= -H ? init[H + tau] : 0.0f;
-    }
-    for (int t0 = 0; t0 < m + len; t0 += TILE) {
+    for (int t0 = 0; t0 < a.seqlen; t0 += TILE) {
         const int t = t0 + tid * E;
+        const int len = min(TILE, a.seqlen - t0);
         float v[E];
-        if (VEC && t < m + len && t + E <= room) {
+        if (VEC && t + E <= a.seqlen) {
             load_vec<T, E>(xr + t, v);
         } else {
 #pragma unroll
-            for (int i = 0; i < E; ++i) {
-                const int j = t + i;
-                v[i] = (j >= m && j < m + len) ? to_f32(xr[j]) : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const int tau = t + i - m;
-            if (tau < 0)
-                v[i] = tau >= -H ? init[H + tau] : 0.0f;
-            else if (tau >= len)
-                v[i] = 0.0f;
+            for (int i = 0; i < E; ++i)
+                v[i] = (t + i < a.seqlen) ? to_f32(xr[t + i]) : 0.0f;
         }
         __syncthreads();  // hist written / previous tile's readers finished
 #pragma unroll
@@ -110,23 +86,275 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
                 acc = fmaf(w[k], xs[OFF + tid * E + i - H + k], acc);
             o[i] = a.apply_silu ? silu_f32(acc) : acc;
         }
-        if (VEC && t >= m && t + E <= m + len) {
+        if (VEC && t + E <= a.seqlen) {
             store_vec<T, E>(orow + t, o);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i)
-                if (t + i >= m && t + i < m + len)
+                if (t + i < a.seqlen)
                     orow[t + i] = from_f32<T>(o[i]);
         }
+        // history of the next tile: the last H samples of history||tile
         if (tid < H)
-            hist[tid] = xs[OFF + TILE - H + tid];
+            hist[tid] = xs[OFF + len - H + tid];
     }
-    __syncthreads();  // every lane has read init and the cache row
-    if (cs && tid < H) {
-        // the new tail: the last H samples of history || sequence, copied
-        const int tau = len - H + tid;
-        cs[tid] = tau >= 0 ? xr[m + tau] : from_f32<T>(init[H + tau]);
+    __syncthreads();
+    if (cs && tid < H)
+        cs[tid] = from_f32<T>(hist[tid]);  // exact: the values came from T
+}
+
+// Packed variable-length batch: x [channels, T] holds the sequences side by
+// side.  One workgroup per (tile of a packed row, channel): every tile is the
+// same amount of work whatever the mix of lengths.
+//
+// Away from sequence starts an output is the dense conv of the packed row.
+// The taps of the first W-1 columns of a sequence reach in front of it and
+// read its history instead (the slot's cache when the sequence continues from
+// it, else zeros).  The workgroup therefore stages in LDS, besides the tile, a
+// bitmask of the columns where a sequence starts, the sequence table and the
+// history of each sequence starting in the tile.  A lane whose taps meet no
+// start (two 32-bit LDS reads tell) computes the dense conv; the few others
+// find the sequence and its history in LDS.  Tiles that hold columns of a
+// padded sequence (which must be left untouched) or columns outside every
+// sequence, and tables of more than kSeqCap sequences, take a
+// column-by-column path that reads the table from global memory.
+//
+// The caches are not written here: conv_varlen_tail_kernel runs afterwards,
+// so no workgroup can overwrite a history that another one still has to read.
+constexpr int kSeqCap = 255;
+
+__device__ __forceinline__ int cu_at(const int32_t *__restrict__ cu, int i, int T)
+{
+    return min(max(cu[i], 0), T);
+}
+
+template <typename T, int W, bool VEC>
+__global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
+{
+    constexpr int E = 16 / StorageSize<T>::value;
+    constexpr int TILE = 256 * E;
+    constexpr int H = W - 1;
+    constexpr int HS = H > 0 ? H : 1;
+    constexpr int OFF = 4;
+    constexpr int NW = TILE / 32 + 1;   // start bits: bit o is column j0 - 32 + o
+    __shared__ float xs[OFF + TILE];
+    __shared__ uint32_t sbits[NW];
+    __shared__ unsigned char sseq[TILE + 32];  // at a start column: the sequence starting there
+    __shared__ float lhist[kSeqCap][HS];       // history of each sequence starting in the tile
+
+    const int k = blockIdx.x, c = blockIdx.y;  // tile, channel
+    const int Tn = a.seqlen, tid = threadIdx.x, nseq = a.batch;
+    const int64_t first = (int64_t)c * Tn;     // column 0 of row c
+    const int m = VEC ? (int)(first % E) : 0;  // vector alignment of the row
+    const T *xr = static_cast<const T *>(a.x) + first;
+    T *orow = static_cast<T *>(a.out) + first;
+    const int j0 = k * TILE - m;               // first packed column of the tile
+    const int jend = min(j0 + TILE, Tn);       // end of the tile's columns in the row
+    const bool staged = nseq <= kSeqCap;
+
+    int need_slow = staged ? 0 : 1;
+    // stage columns [j0 - H, j0 + TILE) of the row (zeros outside [0, T));
+    // all loads from clamped addresses, issued together
+    {
+        const int j = j0 + tid * E;
+        float v[E];
+        if (VEC && j >= 0 && j + E <= Tn) {
+            load_vec<T, E>(xr + j, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const bool ok = j + i >= 0 && j + i < Tn;
+                const float xv = to_f32(xr[ok ? j + i : 0]);
+                v[i] = ok ? xv : 0.0f;
+            }
+        }
+        const int q = j0 - H + (tid < H ? tid : 0);
+        const bool qok = tid < H && q >= 0 && q < Tn;
+        const float hv = to_f32(xr[qok ? q : 0]);
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            xs[OFF + tid * E + i] = v[i];
+        if (tid < H)
+            xs[OFF - H + tid] = qok ? hv : 0.0f;
+        if (tid < NW)
+            sbits[tid] = 0u;
     }
+    // one lane per sequence: its start, its history, whether it pads this tile
+    int my_start = -1;
+    if (staged && tid <= nseq) {
+        const int ts = min(tid, nseq - 1);
+        const int tb = cu_at(a.cu_seqlens, tid, Tn);
+        const int te = tid < nseq ? max(cu_at(a.cu_seqlens, tid + 1, Tn), tb) : tb;
+        const int slot = a.slot_idx ? a.slot_idx[ts] : ts;
+        const bool init = a.has_init_seq && a.has_init_seq[ts] != 0;
+        const bool touches = te > tb && tb < jend && te > max(j0, 0);
+        if (touches && slot < 0)
+            need_slow = 1;  // a padded sequence's columns must stay untouched
+        if (te > tb && slot >= 0 && tb > j0 - H && tb < jend) {
+            my_start = tb;
+            const T *cs = (init && a.conv_state)
+                              ? static_cast<const T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H
+                              : nullptr;
+#pragma unroll
+            for (int h = 0; h < H; ++h)
+                lhist[tid][h] = cs ? to_f32(cs[h]) : 0.0f;
+        }
+        if (tid == 0 || tid == nseq) {
+            // columns in front of the first sequence or after the last one
+            const int lo0 = max(j0, 0);
+            if ((tid == 0 && tb > lo0 && lo0 < jend) || (tid == nseq && tb < jend))
+                need_slow = 1;
+        }
+    }
+    float w[W];
+#pragma unroll
+    for (int kk = 0; kk < W; ++kk)
+        w[kk] = a.weight[(int64_t)c * W + kk];
+    const float bias = a.bias ? a.bias[c] : 0.0f;
+    const bool slow = __syncthreads_or(need_slow) != 0;  // tile, table, histories, cleared bits
+    if (my_start >= 0) {
+        const int o = my_start - j0 + 32;
+        atomicOr(&sbits[o >> 5], 1u << (o & 31));
+        sseq[o] = (unsigned char)tid;  // read only where the bit is set
+    }
+    __syncthreads();
+
+    const int jl = j0 + tid * E;  // the lane's first column
+    if (!slow) {
+        // starts among columns jl-H+1 .. jl+E-1 (the ones that can cut a tap)
+        const int olo = tid * E + 32 - H + 1, ohi = tid * E + 32 + E - 1;
+        const uint64_t win = (uint64_t)sbits[olo >> 5] | ((uint64_t)sbits[ohi >> 5] << 32);
+        const int base = olo & ~31;  // bit 0 of win is bit `base`
+        const uint64_t lanebits = (win >> (olo - base)) & ((1ull << (ohi - olo + 1)) - 1);
+        float o_[E];
+        if (lanebits == 0) {
+            // no sequence starts among the lane's taps: the dense conv
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                float acc = bias;
+#pragma unroll
+                for (int kk = 0; kk < W; ++kk)
+                    acc = fmaf(w[kk], xs[OFF + tid * E + i - H + kk], acc);
+                o_[i] = a.apply_silu ? silu_f32(acc) : acc;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                // latest start b in (j-H, j]: bit (i + H - 1 - d) of lanebits is column j - d
+                int b = INT32_MIN / 2;
+#pragma unroll
+                for (int d = H - 1; d >= 0; --d)
+                    if ((lanebits >> (i + H - 1 - d)) & 1ull)
+                        b = jl + i - d;
+                const bool has_b = b != INT32_MIN / 2;
+                const int sq = sseq[has_b ? b - j0 + 32 : 32];  // meaningful when has_b
+                float acc = bias;
+#pragma unroll
+                for (int kk = 0; kk < W; ++kk) {
+                    const int q = jl + i - H + kk;  // tap column
+                    const bool use_h = has_b && q < b;
+                    const float xv = xs[OFF + tid * E + i - H + kk];
+                    const float hv = lhist[use_h ? sq : 0][use_h ? H + q - b : 0];
+                    acc = fmaf(w[kk], use_h ? hv : xv, acc);
+                }
+                o_[i] = a.apply_silu ? silu_f32(acc) : acc;
+            }
+        }
+        bool all = true;
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            all = all && (jl + i >= 0 && jl + i < Tn);
+        if (VEC && all) {
+            store_vec<T, E>(orow + jl, o_);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                if (jl + i >= 0 && jl + i < Tn)
+                    orow[jl + i] = from_f32<T>(o_[i]);
+        }
+        return;
+    }
+
+    // column by column, the table read from global memory
+    int s = 0;
+    {
+        const int jc = max(min(jl, Tn - 1), 0);
+        int lo = 0, hi = nseq;  // the last s with cu[s] <= jc
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu_at(a.cu_seqlens, mid, Tn) <= jc)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        s = lo;
+    }
+    int cur = -1, tb = 0, te = 0, slot = -1;
+    const T *hist = nullptr;  // the sequence's cached history, or null (zeros)
+    for (int i = 0; i < E; ++i) {
+        const int j = jl + i;
+        if (j < 0 || j >= Tn)
+            continue;
+        // advance to the sequence holding column j (skipping empty ones)
+        while (s + 1 < nseq && cu_at(a.cu_seqlens, s + 1, Tn) <= j)
+            ++s;
+        if (s != cur) {
+            cur = s;
+            tb = cu_at(a.cu_seqlens, s, Tn);
+            te = max(cu_at(a.cu_seqlens, s + 1, Tn), tb);
+            slot = a.slot_idx ? a.slot_idx[s] : s;
+            const bool init = a.has_init_seq && a.has_init_seq[s] != 0;
+            hist = (init && a.conv_state && slot >= 0)
+                       ? static_cast<const T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H
+                       : nullptr;
+        }
+        if (slot < 0 || j < tb || j >= te)
+            continue;
+        float acc = bias;
+#pragma unroll
+        for (int kk = 0; kk < W; ++kk) {
+            const int q = j - H + kk;  // tap column
+            float xv;
+            if (q >= tb)
+                xv = xs[OFF + tid * E + i - H + kk];
+            else
+                xv = hist ? to_f32(hist[H + q - tb]) : 0.0f;
+            acc = fmaf(w[kk], xv, acc);
+        }
+        orow[j] = from_f32<T>(a.apply_silu ? silu_f32(acc) : acc);
+    }
+}
+
+// Conv caches of a packed batch, after conv_varlen_kernel: one lane per
+// (sequence, channel) copies the last W-1 samples of history || sequence
+// into the slot.  Each lane reads only the cache row it writes.
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_varlen_tail_kernel(ConvArgs a)
+{
+    constexpr int H = W - 1;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)a.batch * a.channels)
+        return;
+    const int s = (int)(i / a.channels), c = (int)(i % a.channels);
+    const int Tn = a.seqlen;
+    const int tb = min(max(a.cu_seqlens[s], 0), Tn);
+    const int te = min(max(a.cu_seqlens[s + 1], tb), Tn);
+    const int slot = a.slot_idx ? a.slot_idx[s] : s;
+    if (slot < 0 || te == tb)
+        return;
+    const bool init = a.has_init_seq && a.has_init_seq[s] != 0;
+    T *cs = static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H;
+    const T *xr = static_cast<const T *>(a.x) + (int64_t)c * Tn + tb;
+    const int len = te - tb;
+    T v[H > 0 ? H : 1];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        const int tau = len - H + k;  // step of the k-th kept sample
+        v[k] = tau >= 0 ? xr[tau] : (init ? cs[H + tau] : from_f32<T>(0.0f));
+    }
+#pragma unroll
+    for (int k = 0; k < H; ++k)
+        cs[k] = v[k];
 }
 
 template <typename T, int W>
@@ -236,6 +464,21 @@ static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
         const int64_t n = (int64_t)a.batch * a.channels;
         hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            stream, a);
+    } else if (a.cu_seqlens) {
+        constexpr int E = 16 / StorageSize<T>::value;
+        // rows start inside a vector only when the packed length is not a
+        // multiple of E; then one more tile covers the shifted walk
+        const int ntiles = (a.seqlen + (a.seqlen % E ? E - 1 : 0) + 256 * E - 1) / (256 * E);
+        const dim3 grid((unsigned)ntiles, (unsigned)a.channels);
+        if (a.vec)
+            hipLaunchKernelGGL((conv_varlen_kernel<T, W, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((conv_varlen_kernel<T, W, false>), grid, dim3(256), 0, stream, a);
+        if (a.conv_state && W > 1) {  // the caches, once every tile has read them
+            const int64_t n = (int64_t)a.batch * a.channels;
+            hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                               0, stream, a);
+        }
     } else {
         const dim3 grid((unsigned)((int64_t)a.batch * a.channels));
         if (a.vec)

@@ -178,7 +178,11 @@ void scan_kernel(ScanArgs a)
     const int L = a.seqlen, N = a.dstate, P = a.headdim;  // L: row length
     const int cpg = a.heads_per_group * P;  // channels per group (contiguous)
     const int nblk_g = (cpg + CPB - 1) / CPB;
-    const uint32_t lb = xcd_block_order(blockIdx.x, gridDim.x);
+    // Dense batches: consecutive blocks (one request's channels, sharing its
+    // B/C) stay on one XCD.  Packed batches keep the hardware order, which
+    // spreads every sequence over all XCDs: there the longest sequence is the
+    // critical path and must not be confined to an eighth of the chip.
+    const uint32_t lb = a.cu_seqlens ? blockIdx.x : xcd_block_order(blockIdx.x, gridDim.x);
     const int cb = (int)(lb % nblk_g);
     const int bg = (int)(lb / nblk_g);
     const int g = bg % a.ngroups, b = bg / a.ngroups;

@@ -51,6 +51,8 @@ int conv_call(const void *x, const float *weight, const float *bias, void *conv_
         return SSM_ERR_ALIGN;
     if ((int64_t)batch * channels > INT32_MAX)
         return SSM_ERR_UNSUPPORTED;
+    if (cu_seqlens && channels > 65535)  // packed rows index the grid's y dimension
+        return SSM_ERR_UNSUPPORTED;
     if (batch == 0 || seqlen == 0)
         return SSM_OK;
     ssm::ConvArgs a;
@@ -62,7 +64,6 @@ int conv_call(const void *x, const float *weight, const float *bias, void *conv_
     a.out = out;
     a.cu_seqlens = cu_seqlens;
     a.has_init_seq = has_init_seq;
-    a.x_elems = (int64_t)(cu_seqlens ? 1 : batch) * channels * seqlen;
     a.batch = batch;
     a.channels = channels;
     a.seqlen = seqlen;
@@ -71,7 +72,9 @@ int conv_call(const void *x, const float *weight, const float *bias, void *conv_
     a.dtype = dtype;
     a.has_initial_state = has_initial_state ? 1 : 0;
     a.apply_silu = apply_silu ? 1 : 0;
-    a.vec = aligned(x, 16) && aligned(out, 16);
+    // dense rows need a length that keeps every row 16-byte aligned; the
+    // packed kernel aligns its tiles to each row itself
+    a.vec = aligned(x, 16) && aligned(out, 16) && (cu_seqlens || seqlen % 8 == 0);
     a.vec_decode = (seqlen == 1) && (channels % 8 == 0) && aligned(x, 16) && aligned(out, 16) &&
                    aligned(conv_state, 16) && aligned(weight, 16) && aligned(bias, 16);
     return status_of(ssm::launch_conv(a, static_cast<hipStream_t>(stream)));

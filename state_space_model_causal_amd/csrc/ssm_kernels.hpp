@@ -23,8 +23,7 @@ struct ConvArgs {
     int batch, channels, seqlen, width, nslots;
     int dtype;                // 0 f32, 1 f16, 2 bf16
     int has_initial_state, apply_silu;
-    int64_t x_elems;          // elements of x (bounds the last vector load)
-    int vec;                  // x and out 16-byte aligned
+    int vec;                  // x and out 16-byte aligned (dense: and seqlen % 8 == 0)
     int vec_decode;           // seqlen 1, channels % 8 == 0, 16-byte aligned tensors
 };
 

@@ -54,6 +54,12 @@ VARLEN_CASES = [
                           a_per_state=False, nslots=4, seed=17), [261, 0, 6, 3], None),  # 270
     ("m2_f16_N16_G4", dict(io="f16", state="bf16", nheads=8, headdim=4, dstate=16, ngroups=4,
                            a_per_state=False, nslots=6, seed=18), [1, 1, 510, 8], 0),   # 520
+    # more sequences than the conv kernel stages in LDS (its global-table path)
+    ("m1_f16_300_seqs", dict(io="f16", state="f32", nheads=8, nslots=320, seed=19),
+     [0, 3] + W.varlen_lengths(19, 298, 2395), None),                    # total 2398
+    # many sequences, none padded: every tile takes the staged path
+    ("m1_bf16_200_seqs", dict(io="bf16", state="f32", nheads=8, nslots=210, seed=20),
+     W.varlen_lengths(20, 200, 3000), None),                             # total 3000 (vec)
 ]
 
 
