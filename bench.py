@@ -36,11 +36,13 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 # x 2 flop x 2.4 GHz (the published 157.3 TFLOP/s counts packed FP32)
 VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp"],
-                  "state_update": ["ssu.hip", "ssm_device.hpp"],
-                  "decode_step": ["ssu.hip", "ssm_device.hpp"],
-                  "conv1d_prefill": ["conv1d.hip", "ssm_device.hpp"],
-                  "conv1d_decode": ["conv1d.hip", "ssm_device.hpp"]}
+KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "state_update": ["ssu.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "decode_step": ["ssu.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "conv1d_prefill": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "conv1d_decode": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "conv1d_varlen": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "selective_scan_varlen": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"]}
 # rocprofv3 kernel names of each kernel in the benchmarked configuration
 KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "decode_step": "ssu_kernel",
                   "conv1d_prefill": "conv_prefill_kernel"}
@@ -56,7 +58,12 @@ def parse():
                    help="target duration of the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (for counter calibration)")
-    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+    p.add_argument("--ssu-sweep", action="store_true",
+                   help="time the Mamba-2 state update over batch, groups and cache dtype "
+                        "and print one JSON line per point")
+    p.add_argument("--no-varlen", action="store_true",
+                   help="skip the packed variable-length prefill measurement")
+    p.add_argument("--only", choices=["prefill", "decode", "varlen"], default=None,
                    help="run only one half of the step (for profiling)")
     p.add_argument("--unfused-decode", action="store_true",
                    help="decode with the separate conv-update and state-update calls instead "
@@ -77,7 +84,7 @@ def profile_commands(out):
     stats, then one counter per pass (FETCH_SIZE, WRITE_SIZE) on the step and
     on a plain 1 GiB device copy (the calibration), and the SQ counters of the
     prefill half."""
-    b = "python -u bench.py --no-cpu-baseline"
+    b = "python -u bench.py --no-cpu-baseline --no-varlen"
     pmc = "timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d {o}/{n} -o run -- {cmd}"
     return [
         ("trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d {out}/trace "
@@ -90,6 +97,9 @@ def profile_commands(out):
                                   cmd="python -u bench.py --copy-calibration")),
         ("sq", pmc.format(c=SQ_COUNTERS, o=out, n="sq",
                           cmd=f"{b} --steps 3 --warmup 1 --only prefill")),
+        ("varlen_trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d "
+                         f"{out}/varlen_trace -o run -- python -u bench.py --only varlen "
+                         f"--steps 20 --warmup 5"),
     ]
 
 
@@ -193,6 +203,37 @@ def summarize_profile(out):
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
+    # packed variable-length prefill: its own traced run
+    vstats = list(csv.DictReader(open(glob.glob(f"{out}/varlen_trace/*kernel_stats.csv")[0])))
+    vline = {}
+    with open(f"{out}/varlen_trace.log") as f:
+        for ln in f:
+            if ln.startswith("{") and "varlen_prefill" in ln:
+                vline = json.loads(ln)["varlen_prefill"]
+    vl = ["# Kernel trace: packed variable-length prefill (Mamba-1 2.8B layer)", "",
+          f"Workload: {vline.get('workload')}; lengths {vline.get('lengths')}.", "",
+          "Command (run from the repository root on the MI355X):", "",
+          f"    {cmds['varlen_trace']}", "",
+          "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for sym in ("conv_varlen_kernel", "conv_varlen_tail_kernel", "scan_kernel"):
+        rows = [r for r in vstats if sym in r["Name"] and
+                (sym != "conv_varlen_kernel" or "tail" not in r["Name"])]
+        calls = sum(int(r["Calls"]) for r in rows)
+        tot = sum(float(r["TotalDurationNs"]) for r in rows)
+        if calls:
+            vl.append(f"| {sym} | {calls} | {tot / calls / 1e3:.1f} | "
+                      f"{min(float(r['MinNs']) for r in rows) / 1e3:.1f} | "
+                      f"{max(float(r['MaxNs']) for r in rows) / 1e3:.1f} |")
+    if vline:
+        vl += ["", f"Event-timed in the same run: conv1d (with the cache-tail pass) "
+                   f"{vline['conv1d_varlen']['us']:.1f} us for {vline['conv1d_varlen']['bytes'] / 1e6:.1f} MB, "
+                   f"scan {vline['selective_scan_varlen']['us']:.1f} us for "
+                   f"{vline['selective_scan_varlen']['bytes'] / 1e6:.1f} MB; "
+                   f"{vline['tokens_per_s'] / 1e6:.1f} M tokens/s."]
+    with open(os.path.join(PROFILES, "mamba1_varlen_prefill_kernels.md"), "w") as f:
+        f.write("\n".join(vl) + "\n")
+    print("\n".join(vl))
+
 
 def kernel_source_sha(names):
     h = hashlib.sha256()
@@ -265,6 +306,15 @@ def main():
     pbytes = W.algorithmic_bytes(pspec)
     dbytes = W.algorithmic_bytes(dspec)
 
+    stream = torch.cuda.current_stream()
+    if args.ssu_sweep:
+        ssu_sweep(ssm, W, dev, stream)
+        return
+    if args.only == "varlen":
+        print(json.dumps({"varlen_prefill": measure_varlen(ssm, W, dev, stream, args.steps,
+                                                           args.warmup)}), flush=True)
+        return
+
     # buffer sets: 2 prefill sets (~0.5 GB each) and 3 decode sets (~0.19 GB)
     NP, ND = 2, 3
     psets, dsets = [], []
@@ -280,8 +330,6 @@ def main():
         t["out"] = torch.empty_like(t["x"])
         dsets.append(t)
     torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
 
     fused = not args.unfused_decode
 
@@ -397,6 +445,10 @@ def main():
     roofline["avg_launch_us"] = dk["us"]
     roofline["kernel_source_sha"] = sha
 
+    varlen = None
+    if not args.no_varlen and args.only is None:
+        varlen = measure_varlen(ssm, W, dev, stream, max(args.steps // 2, 5), 3)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds, pspec, dspec)
@@ -432,12 +484,135 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "varlen_prefill": varlen,
         "step_ms_median": float(np.median(step_ms)),
         "wall_s_timed": t_wall,
         "device": props.name,
         "arch": getattr(props, "gcnArchName", None),
     }
     print(json.dumps(line), flush=True)
+
+
+def ssu_sweep(ssm, W, dev, stream, iters=20):
+    """Mamba-2 decode state update at the two head shapes (headdim 64 /
+    dstate 128 with 80 heads; headdim 128 / dstate 256 with 64 heads) over
+    batch, ngroups and cache dtype.  Each point rotates through disjoint slot
+    sets covering at least 1 GB of cache, so no launch finds its state in the
+    on-chip caches."""
+    import math
+
+    import torch
+
+    points = []
+    shapes = [("hd64_N128", W.m2_ssu_64, (1, 8), ("f16", "f32"), (1, 16, 256, 1024)),
+              ("hd128_N256", W.m2_ssu_128, (1,), ("bf16", "f32"), (1, 8, 64, 512))]
+    for name, factory, groups, caches, batches in shapes:
+        for G in groups:
+            for cache in caches:
+                for Bt in batches:
+                    probe = factory(batch=Bt, state=cache, ngroups=G)
+                    ssz = 4 if cache == "f32" else 2
+                    per_req = 2 * probe.nheads * probe.headdim * probe.dstate * ssz
+                    R = max(1, math.ceil(1e9 / (Bt * per_req)))
+                    spec = factory(batch=Bt, state=cache, ngroups=G, nslots=Bt * R,
+                                   random_slots=False)
+                    t = W.make(spec, dev)
+                    out = torch.empty_like(t["x"])
+                    sets = [(torch.arange(Bt, dtype=torch.int32, device=dev) + r * Bt).contiguous()
+                            for r in range(R)]
+
+                    def run(i):
+                        ssm.state_update(t["ssm_state"], t["x"], t["dt"], t["A"], t["B"], t["C"],
+                                         D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                                         slot_idx=sets[i % R], out=out, stream=stream)
+
+                    for i in range(5):
+                        run(i)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for i in range(iters):
+                        run(i)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / iters
+                    b = W.algorithmic_bytes(spec)["ssu"]
+                    pt = {"shape": name, "ngroups": G, "cache": cache, "batch": Bt,
+                          "effective_batch": Bt * spec.nheads, "us": us, "bytes": b,
+                          "GBps": b / (us * 1e-6) / 1e9,
+                          "pct_hbm": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS * 100,
+                          "rotation_sets": R}
+                    print(json.dumps({"ssu_sweep": pt}), flush=True)
+                    points.append(pt)
+                    del t, out, sets
+                    torch.cuda.empty_cache()
+    return points
+
+
+VARLEN_NSEQ, VARLEN_TOKENS, VARLEN_SEED = 16, 8192, 5
+
+
+def measure_varlen(ssm, W, dev, stream, steps, warmup):
+    """Packed variable-length prefill (continuous batching): 16 sequences of
+    mixed lengths, 8192 tokens in all (the token count of the dense prefill),
+    every other one continuing from its slot of a 512-slot cache; conv1d
+    (with its cache-tail pass) then the scan, each timed with events on the
+    launch stream over two rotating buffer sets."""
+    import numpy as np
+    import torch
+
+    lengths = W.varlen_lengths(VARLEN_SEED, VARLEN_NSEQ, VARLEN_TOKENS)
+    spec = W.prefill(nslots=512)
+    sets = []
+    for k in range(2):
+        t = W.make_varlen(W.prefill(nslots=512, seed=40 + k), lengths, dev)
+        t["u"] = torch.empty_like(t["x"])
+        t["out"] = torch.empty_like(t["x"])
+        sets.append(t)
+    n_init = int(sets[0]["has_init"].sum().item())
+    vb = W.varlen_bytes(spec, lengths, n_init)
+
+    def run(i, ev=None):
+        t = sets[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        ssm.causal_conv1d_varlen(t["x"], t["conv_w"], t["cu_seqlens"], bias=t["conv_b"],
+                                 conv_state=t["conv_state"], slot_idx=t["slot_idx"],
+                                 has_initial_state=t["has_init"], out=t["u"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ssm.selective_scan_varlen(t["u"], t["dt"], t["A"], t["B"], t["C"], t["cu_seqlens"],
+                                  D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                                  ssm_state=t["ssm_state"], slot_idx=t["slot_idx"],
+                                  has_initial_state=t["has_init"], out=t["out"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        run(i, ev[i])
+    torch.cuda.synchronize()
+    per = np.array([[ev[i][0].elapsed_time(ev[i][1]), ev[i][1].elapsed_time(ev[i][2])]
+                    for i in range(steps)]).mean(axis=0) * 1e3  # us
+    tot_us = per.sum()
+    return {
+        "workload": f"{VARLEN_NSEQ} packed sequences, {VARLEN_TOKENS} tokens, mixed lengths "
+                    "(log-uniform), every other one continuing from its slot; Mamba-1 2.8B "
+                    "layer (d_inner 5120, d_state 16, conv 4, f16 io / f32 state)",
+        "lengths": lengths,
+        "conv1d_varlen": {"bytes": vb["conv"], "us": per[0],
+                          "GBps": vb["conv"] / (per[0] * 1e-6) / 1e9,
+                          "kernel_source_sha": kernel_source_sha(KERNEL_SOURCES["conv1d_varlen"])},
+        "selective_scan_varlen": {"bytes": vb["scan"], "us": per[1],
+                                  "GBps": vb["scan"] / (per[1] * 1e-6) / 1e9,
+                                  "kernel_source_sha": kernel_source_sha(
+                                      KERNEL_SOURCES["selective_scan_varlen"])},
+        "GBps": (vb["conv"] + vb["scan"]) / (tot_us * 1e-6) / 1e9,
+        "tokens_per_s": VARLEN_TOKENS / (tot_us * 1e-6),
+        "steps": steps,
+    }
 
 
 def cpu_baseline(target_s, pspec, dspec):
