@@ -498,7 +498,7 @@ def ssu_sweep(ssm, W, dev, stream, iters=20):
     dstate 128 with 80 heads; headdim 128 / dstate 256 with 64 heads) over
     batch, ngroups and cache dtype.  Each point rotates through disjoint slot
     sets covering at least 1 GB of cache, so no launch finds its state in the
-    on-chip caches."""
+    on-chip caches, and is timed as replays of a HIP graph of the launches."""
     import math
 
     import torch
@@ -524,17 +524,27 @@ def ssu_sweep(ssm, W, dev, stream, iters=20):
                     def run(i):
                         ssm.state_update(t["ssm_state"], t["x"], t["dt"], t["A"], t["B"], t["C"],
                                          D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
-                                         slot_idx=sets[i % R], out=out, stream=stream)
+                                         slot_idx=sets[i % R], out=out)
 
-                    for i in range(5):
+                    # a graph of `launches` launches, replayed: device time
+                    # per launch, without the host's launch rate
+                    for i in range(3):
                         run(i)
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    for i in range(iters):
-                        run(i)
-                    e1.record(stream)
                     torch.cuda.synchronize()
-                    us = e0.elapsed_time(e1) * 1e3 / iters
+                    launches = max(iters, R)
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(graph):
+                        for i in range(launches):
+                            run(i)
+                    graph.replay()
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(3):
+                        graph.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / (3 * launches)
                     b = W.algorithmic_bytes(spec)["ssu"]
                     pt = {"shape": name, "ngroups": G, "cache": cache, "batch": Bt,
                           "effective_batch": Bt * spec.nheads, "us": us, "bytes": b,
@@ -543,7 +553,7 @@ def ssu_sweep(ssm, W, dev, stream, iters=20):
                           "rotation_sets": R}
                     print(json.dumps({"ssu_sweep": pt}), flush=True)
                     points.append(pt)
-                    del t, out, sets
+                    del t, out, sets, graph
                     torch.cuda.empty_cache()
     return points
 

@@ -148,6 +148,48 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x,
                      int dt_softplus, void *stream);
 
 /*
+ * Launch geometry of the state update.  "[XPU] Add tuned Mamba SSU configs for
+ * Intel Arc Pro B70" (vLLM PR #50534 report, section "实现拆解", steps 2-3)
+ * tunes the update's launch configuration per device over a grid of
+ * effective batches (batch x nheads) for each (headdim, dstate, dtype) key and
+ * keeps a tuned entry only where it beats the heuristic.  Here the
+ * geometry is the number of consecutive states each lane owns (8 or 16) and
+ * the workgroup size (64, 128, 256 or 512 lanes); the library carries a table
+ * tuned on gfx950 and falls back to a heuristic for other shapes: 32 bytes of
+ * state per lane (16 states of a 2-byte cache for rows of >= 32 states that
+ * are a multiple of 16, else 8) in 256-lane workgroups.
+ */
+typedef struct ssm_launch_config {
+    int states_per_lane; /* 8 or 16                */
+    int block_threads;   /* 64, 128, 256 or 512    */
+} ssm_launch_config;
+
+/*
+ * ssm_state_update_config -- the geometry ssm_state_update would use for a
+ * shape (no device call).  *from_table (may be NULL) is set to 1 when the
+ * tuned table supplied it, 0 for the heuristic.
+ */
+int ssm_state_update_config(int batch, int nheads, int headdim, int dstate,
+                            int io_dtype, int state_dtype,
+                            ssm_launch_config *config, int *from_table);
+
+/*
+ * ssm_state_update_ex -- ssm_state_update with the caller's geometry (the
+ * override hook of the tuning method); config NULL = the library's choice.
+ * Every geometry computes the same values: the cache bytes are identical, the
+ * outputs differ only in the summation order of the readout.  An invalid
+ * config returns SSM_ERR_SHAPE.
+ */
+int ssm_state_update_ex(void *state, const int32_t *slot_idx, const void *x,
+                        const void *dt, const float *dt_bias, const float *A,
+                        const void *B, const void *C, const float *D,
+                        const void *z, void *out, int batch, int nheads,
+                        int headdim, int dstate, int ngroups, int nslots,
+                        int io_dtype, int state_dtype, int a_per_state,
+                        int dt_softplus, const ssm_launch_config *config,
+                        void *stream);
+
+/*
  * ssm_decode_step -- one decode token per request: the conv update followed by
  * the state update, in one kernel (the causal-conv1d and silu operators of
  * InfiniLM-Rust PR #48 section 2.1 at seqlen 1, feeding the

@@ -34,8 +34,14 @@ SSM_F32, SSM_F16, SSM_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: SSM_BF16}
 
 EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_state_update",
+            "ssm_state_update_ex", "ssm_state_update_config",
             "ssm_decode_step", "ssm_causal_conv1d_varlen", "ssm_selective_scan_varlen",
             "ssm_status_string", "ssm_abi_version")
+
+
+class LaunchConfig(ctypes.Structure):
+    """ssm_launch_config: the state update's geometry."""
+    _fields_ = [("states_per_lane", ctypes.c_int), ("block_threads", ctypes.c_int)]
 
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE",
           4: "SSM_ERR_ALIGN", 5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_HIP"}
@@ -69,6 +75,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
                                      I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_state_update.restype = I
+    lib.ssm_state_update_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
+                                        I, I, I, I, I, I, I, I, I, I, P, P]
+    lib.ssm_state_update_ex.restype = I
+    lib.ssm_state_update_config.argtypes = [I, I, I, I, I, I, P, P]
+    lib.ssm_state_update_config.restype = I
     lib.ssm_decode_step.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P,
                                     I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_decode_step.restype = I
@@ -168,8 +179,10 @@ def selective_scan(u, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=Tru
 
 
 def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
-                 slot_idx=None, out=None, stream=None):
-    """ssm_state_update: one token per request, state cache updated in place."""
+                 slot_idx=None, out=None, stream=None, config=None):
+    """ssm_state_update: one token per request, state cache updated in place.
+    config: (states_per_lane, block_threads) to override the library's launch
+    geometry (ssm_state_update_ex), or None."""
     nslots, nheads, headdim, dstate = state.shape
     batch = x.shape[0]
     ngroups = B.shape[1]
@@ -177,14 +190,31 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplu
     if out is None:
         out = torch.empty_like(x)
     _same_io(x.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
-    st = load_library().ssm_state_update(
-        _ptr(state, "state"), _ptr(slot_idx, "slot_idx", torch.int32), _ptr(x, "x"),
-        _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32),
-        _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32), _ptr(z, "z"), _ptr(out, "out"),
-        batch, nheads, headdim, dstate, ngroups, nslots, _code(x, "x"), _code(state, "state"),
-        a_per_state, int(bool(dt_softplus)), _stream(stream))
-    _check("ssm_state_update", st)
+    args = (_ptr(state, "state"), _ptr(slot_idx, "slot_idx", torch.int32), _ptr(x, "x"),
+            _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32),
+            _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32), _ptr(z, "z"),
+            _ptr(out, "out"), batch, nheads, headdim, dstate, ngroups, nslots, _code(x, "x"),
+            _code(state, "state"), a_per_state, int(bool(dt_softplus)))
+    if config is None:
+        st = load_library().ssm_state_update(*args, _stream(stream))
+        _check("ssm_state_update", st)
+    else:
+        cfg = LaunchConfig(*config)
+        st = load_library().ssm_state_update_ex(*args, ctypes.byref(cfg), _stream(stream))
+        _check("ssm_state_update_ex", st)
     return out
+
+
+def state_update_config(batch, nheads, headdim, dstate, io_dtype, state_dtype):
+    """ssm_state_update_config: the geometry the library picks for a shape,
+    as (states_per_lane, block_threads, from_table).  Dtypes are torch dtypes."""
+    cfg = LaunchConfig()
+    ft = ctypes.c_int(0)
+    st = load_library().ssm_state_update_config(batch, nheads, headdim, dstate,
+                                                _DTYPE_CODE[io_dtype], _DTYPE_CODE[state_dtype],
+                                                ctypes.byref(cfg), ctypes.byref(ft))
+    _check("ssm_state_update_config", st)
+    return cfg.states_per_lane, cfg.block_threads, bool(ft.value)
 
 
 def decode_step(state, conv_state, x, conv_weight, dt, A, B, C, conv_bias=None, D=None, z=None,
@@ -261,7 +291,8 @@ def selective_scan_varlen(u, dt, A, B, C, cu_seqlens, D=None, z=None, dt_bias=No
     return out
 
 
-__all__ = ["causal_conv1d", "selective_scan", "state_update", "decode_step",
+__all__ = ["causal_conv1d", "selective_scan", "state_update", "state_update_config",
+           "LaunchConfig", "decode_step",
            "causal_conv1d_varlen", "selective_scan_varlen", "load_library",
            "SsmError",
            "SSM_F32", "SSM_F16", "SSM_BF16", "EXPORTED", "LIB_PATH"]

@@ -216,13 +216,58 @@ int ssm_selective_scan_varlen(const void *u, const void *dt, const float *dt_bia
 
 namespace {
 
-// Validation and launch geometry shared by ssm_state_update and
+// ----------------------------------------------------------- SSU geometry
+// One tuned entry: for the key (headdim, dstate, io dtype, cache dtype) and
+// effective batches (batch x nheads) in (eff_lo, eff_hi], use this geometry.
+struct SsuTableEntry {
+    int headdim, dstate, io_dtype, state_dtype;
+    int64_t eff_lo, eff_hi;
+    int states_per_lane, block_threads;
+};
+
+// The gfx950 table, written by state_space_model_causal_amd/tune_ssu.py from
+// measurements on an MI355X; only entries that beat the heuristic are kept.
+const SsuTableEntry kSsuTable[] = {
+#include "ssu_table_gfx950.inc"
+    {0, 0, 0, 0, 0, 0, 0, 0}  // end marker
+};
+
+bool valid_ssu_config(int V, int block)
+{
+    return (V == 8 || V == 16) && (block == 64 || block == 128 || block == 256 || block == 512);
+}
+
+// The library's choice: the table entry covering the shape, else the
+// heuristic: 32 bytes of state per lane (16 states of a 2-byte cache, for rows
+// of >= 32 states that are a multiple of 16; else 8 states) in 256-lane
+// workgroups.
+void choose_ssu(int batch, int nheads, int headdim, int dstate, int io_dtype, int state_dtype,
+                int &V, int &block, int &from_table)
+{
+    const int64_t eff = (int64_t)batch * nheads;
+    for (const SsuTableEntry *e = kSsuTable; e->headdim != 0; ++e) {
+        if (e->headdim == headdim && e->dstate == dstate && e->io_dtype == io_dtype &&
+            e->state_dtype == state_dtype && eff > e->eff_lo && eff <= e->eff_hi &&
+            valid_ssu_config(e->states_per_lane, e->block_threads)) {
+            V = e->states_per_lane;
+            block = e->block_threads;
+            from_table = 1;
+            return;
+        }
+    }
+    V = (dtype_size(state_dtype) == 2 && dstate % 16 == 0 && dstate >= 32) ? 16 : 8;
+    block = 256;
+    from_table = 0;
+}
+
+// Validation and launch geometry shared by ssm_state_update(_ex) and
 // ssm_decode_step; fills `a` and returns SSM_OK, or an error status.
+// cfg: the caller's geometry, or null for the library's choice.
 int prepare_ssu(ssm::SsuArgs &a, void *state, const int32_t *slot_idx, const void *x,
                 const void *dt, const float *dt_bias, const float *A, const void *B,
                 const void *C, const float *D, const void *z, void *out, int batch, int nheads,
                 int headdim, int dstate, int ngroups, int nslots, int io_dtype, int state_dtype,
-                int a_per_state, int dt_softplus)
+                int a_per_state, int dt_softplus, const ssm_launch_config *cfg = nullptr)
 {
     if (!state || !x || !dt || !A || !B || !C || !out)
         return SSM_ERR_NULL_ARG;
@@ -240,10 +285,16 @@ int prepare_ssu(ssm::SsuArgs &a, void *state, const int32_t *slot_idx, const voi
         !aligned(C, es) || !aligned(z, es) || !aligned(out, es) || !aligned(A, 4) ||
         !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(slot_idx, 4))
         return SSM_ERR_ALIGN;
-    // states per lane: 16 for rows of >= 32 states that are a multiple of 16
-    // (more bytes in flight per lane), else 8; lanes per (b,h,p) row:
-    // ceil(dstate/V) rounded up to a power of two (<= 64)
-    const int V = (dstate % 16 == 0 && dstate >= 32) ? 16 : 8;
+    int V, block, from_table;
+    if (cfg) {
+        if (!valid_ssu_config(cfg->states_per_lane, cfg->block_threads))
+            return SSM_ERR_SHAPE;
+        V = cfg->states_per_lane;
+        block = cfg->block_threads;
+    } else {
+        choose_ssu(batch, nheads, headdim, dstate, io_dtype, state_dtype, V, block, from_table);
+    }
+    // lanes per (b,h,p) row: ceil(dstate/V) rounded up to a power of two (<= 64)
     int lanes = (dstate + V - 1) / V, lg = 0;
     while ((1 << lg) < lanes)
         ++lg;
@@ -272,11 +323,12 @@ int prepare_ssu(ssm::SsuArgs &a, void *state, const int32_t *slot_idx, const voi
     a.heads_per_group = nheads / ngroups;
     a.lanes_per_row_log2 = lg;
     a.states_per_lane = V;
+    a.block_threads = block;
     a.io_dtype = io_dtype;
     a.state_dtype = state_dtype;
     a.a_per_state = a_per_state ? 1 : 0;
     a.dt_softplus = dt_softplus ? 1 : 0;
-    a.vec = (dstate % 8 == 0) && aligned(state, 16) && aligned(B, 16) && aligned(C, 16) &&
+    a.vec = (dstate % V == 0) && aligned(state, 16) && aligned(B, 16) && aligned(C, 16) &&
             aligned(A, 16);
     // a request's lanes fill whole waves: the slot index is then wave-uniform
     a.wave_per_request = ((((int64_t)nheads * headdim) << lg) % 64) == 0;
@@ -303,6 +355,44 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x, const 
     if (batch == 0)
         return SSM_OK;
     return status_of(ssm::launch_ssu(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_state_update_ex(void *state, const int32_t *slot_idx, const void *x, const void *dt,
+                        const float *dt_bias, const float *A, const void *B, const void *C,
+                        const float *D, const void *z, void *out, int batch, int nheads,
+                        int headdim, int dstate, int ngroups, int nslots, int io_dtype,
+                        int state_dtype, int a_per_state, int dt_softplus,
+                        const ssm_launch_config *config, void *stream)
+{
+    ssm::SsuArgs a;
+    const int st = prepare_ssu(a, state, slot_idx, x, dt, dt_bias, A, B, C, D, z, out, batch,
+                               nheads, headdim, dstate, ngroups, nslots, io_dtype, state_dtype,
+                               a_per_state, dt_softplus, config);
+    if (st != SSM_OK)
+        return st;
+    if (batch == 0)
+        return SSM_OK;
+    return status_of(ssm::launch_ssu(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_state_update_config(int batch, int nheads, int headdim, int dstate, int io_dtype,
+                            int state_dtype, ssm_launch_config *config, int *from_table)
+{
+    if (!config)
+        return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
+        return SSM_ERR_DTYPE;
+    if (batch < 0 || nheads < 1 || headdim < 1 || dstate < 1)
+        return SSM_ERR_SHAPE;
+    if (dstate > ssm::kMaxSsuDstate)
+        return SSM_ERR_UNSUPPORTED;
+    int V, block, ft;
+    choose_ssu(batch, nheads, headdim, dstate, io_dtype, state_dtype, V, block, ft);
+    config->states_per_lane = V;
+    config->block_threads = block;
+    if (from_table)
+        *from_table = ft;
+    return SSM_OK;
 }
 
 int ssm_decode_step(void *state, void *conv_state, const int32_t *slot_idx, const void *x,

@@ -85,6 +85,7 @@ struct SsuArgs {
     int heads_per_group;
     int lanes_per_row_log2;          // lanes per (b,h,p) row = 2^this
     int states_per_lane;             // 8 or 16
+    int block_threads;               // 64, 128, 256 or 512 lanes per workgroup
     int io_dtype, state_dtype;
     int a_per_state, dt_softplus;
     int vec;                         // dstate % 8 == 0 and 16-byte aligned bases

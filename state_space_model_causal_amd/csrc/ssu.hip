@@ -14,7 +14,9 @@
 // a row of dstate states is dstate/V lanes (rounded up to a power of two that
 // divides 64) and a wave covers 64*V consecutive states of the cache, read and
 // written with 128-bit accesses.  The readout sum over states is a butterfly
-// across the row's lanes.  No LDS, no barriers.
+// across the row's lanes.  No LDS, no barriers.  V and the workgroup size
+// (64 to 512 lanes) are chosen per shape on the host, from a table tuned on
+// gfx950 or a heuristic, or given by the caller.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -161,10 +163,10 @@ __device__ __forceinline__ float ssu_compute(const SsuArgs &a, int j, SsuRow<TS,
 // One (b,h,p) row per group of 2^lanes_per_row_log2 lanes, each lane owning V
 // consecutive states; all of a lane's loads are issued before any arithmetic.
 template <typename TS, typename TI, bool A_PER_STATE, bool VEC, int V, bool WAVE_REQ, int CW>
-__global__ __launch_bounds__(256) void ssu_kernel(SsuArgs a)
+__global__ __launch_bounds__(512) void ssu_kernel(SsuArgs a)
 {
     const int lpr_log2 = a.lanes_per_row_log2;
-    const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t row = gtid >> lpr_log2;                // (b*H + h)*P + p
     const int j = (int)(gtid & ((1 << lpr_log2) - 1));   // lane within the row
     SsuRow<TS, TI, V, CW> r;
@@ -186,9 +188,10 @@ template <typename TS, typename TI, bool APS, bool VEC, int V, bool WREQ>
 static void launch_ssu_cw(const SsuArgs &a, dim3 grid, hipStream_t stream)
 {
     if (a.conv_width == kFusedConvWidth)
-        hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V, WREQ, kFusedConvWidth>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V, WREQ, kFusedConvWidth>), grid, dim3(a.block_threads), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V, WREQ, 0>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((ssu_kernel<TS, TI, APS, VEC, V, WREQ, 0>), grid, dim3(a.block_threads), 0, stream, a);
 }
 
 template <typename TS, typename TI, bool APS, bool VEC, int V>
@@ -204,7 +207,7 @@ template <typename TS, typename TI>
 static hipError_t launch_ssu_t(const SsuArgs &a, hipStream_t stream)
 {
     const int64_t threads = a.nrows << a.lanes_per_row_log2;
-    const dim3 grid((unsigned)((threads + 255) / 256));
+    const dim3 grid((unsigned)((threads + a.block_threads - 1) / a.block_threads));
     if (a.states_per_lane == 16) {
         if (a.a_per_state) {
             if (a.vec) launch_ssu_v<TS, TI, true, true, 16>(a, grid, stream);

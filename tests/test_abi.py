@@ -147,3 +147,64 @@ def dstep(lib, **kw):
 ])
 def test_decode_step_validation(lib, kw, code):
     assert dstep(lib, **kw) == code
+
+
+def ssu_ex(lib, cfg, **kw):
+    import ctypes
+    import state_space_model_causal_amd as ssm
+
+    a = dict(st=FAKE, idx=None, x=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None,
+             z=None, out=FAKE, batch=2, H=8, P=4, N=16, G=1, S=2, io=1, sd=0, aps=0, sp=1)
+    a.update(kw)
+    c = None if cfg is None else ctypes.byref(ssm.LaunchConfig(*cfg))
+    return lib.ssm_state_update_ex(a["st"], a["idx"], a["x"], a["dt"], a["bias"], a["A"], a["B"],
+                                   a["C"], a["D"], a["z"], a["out"], a["batch"], a["H"], a["P"],
+                                   a["N"], a["G"], a["S"], a["io"], a["sd"], a["aps"], a["sp"],
+                                   c, None)
+
+
+@pytest.mark.parametrize("cfg", [(4, 256), (32, 256), (8, 32), (16, 1024), (8, 96), (0, 0)])
+def test_state_update_ex_rejects_bad_geometry(lib, cfg):
+    assert ssu_ex(lib, cfg) == SHAPE
+
+
+def test_state_update_ex_validates_like_the_plain_call(lib):
+    # the override does not bypass the argument checks (none of these launch)
+    assert ssu_ex(lib, (8, 256), st=None) == NULL
+    assert ssu_ex(lib, (8, 256), N=513) == UNSUP
+    assert ssu_ex(lib, (16, 64), batch=0) == 0
+
+
+def test_state_update_config_choices(lib):
+    import torch
+    import state_space_model_causal_amd as ssm
+
+    for batch, H, P, N, io, st in [(245, 5120, 1, 16, torch.float16, torch.float32),
+                                   (1, 80, 64, 128, torch.float16, torch.float16),
+                                   (1024, 80, 64, 128, torch.float16, torch.float32),
+                                   (8, 64, 128, 256, torch.bfloat16, torch.bfloat16),
+                                   (3, 7, 3, 24, torch.float32, torch.float32)]:
+        v, b, from_table = ssm.state_update_config(batch, H, P, N, io, st)
+        assert v in (8, 16) and b in (64, 128, 256, 512)
+        if not from_table:  # the documented heuristic: 32 bytes of state per lane
+            two = st in (torch.float16, torch.bfloat16)
+            assert (v, b) == ((16 if two and N % 16 == 0 and N >= 32 else 8), 256)
+    with pytest.raises(ssm.SsmError):
+        ssm.state_update_config(1, 8, 4, 513, torch.float16, torch.float16)
+
+
+def test_tuned_table_entries_are_valid():
+    # every line of the compiled-in table names a legal geometry and a
+    # non-empty effective-batch range
+    import re
+
+    path = os.path.join(ROOT, "state_space_model_causal_amd", "csrc", "ssu_table_gfx950.inc")
+    for line in open(path):
+        line = line.split("//")[0].strip()
+        if not line:
+            continue
+        vals = [int(v) for v in re.findall(r"-?\d+", line)]
+        assert len(vals) == 8, line
+        P, N, io, st, lo, hi, v, b = vals
+        assert P >= 1 and 1 <= N <= 512 and io in (0, 1, 2) and st in (0, 1, 2)
+        assert 0 <= lo < hi and v in (8, 16) and b in (64, 128, 256, 512)

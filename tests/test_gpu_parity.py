@@ -456,3 +456,51 @@ def test_decode_step_chain_matches_prefill(dev, ssm, oracle):
     o, sc, _, _ = oracle.selective_scan(uo, f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
                                         D=f(t["D"]), z=f(t["z"]), dt_bias=f(t["dt_bias"]))
     check(torch.cat(ys, dim=2), o, sc, 1e-5, "f32", "prefill + fused decode")
+
+
+# ------------------------------------------------- state-update geometries
+GEOMETRY_SHAPES = [
+    # (label, spec kwargs): row widths that exercise 1 to 64 lanes per row,
+    # partial lanes (dstate 24) and the scalar path (dstate 20 with 16 per lane)
+    ("m1_N16", dict(seqlen=1, nheads=96, dstate=16, io="f16", state="f32", batch=5, nslots=9,
+                    random_slots=True, index_sensitive=True)),
+    ("hd3_N24", dict(seqlen=1, nheads=6, headdim=3, dstate=24, io="f32", state="f16",
+                     a_per_state=True, batch=3, index_sensitive=True)),
+    ("hd4_N20", dict(seqlen=1, nheads=4, headdim=4, dstate=20, io="f32", state="f32",
+                     a_per_state=False, batch=2, index_sensitive=True)),
+    ("hd64_N128", dict(seqlen=1, nheads=16, headdim=64, dstate=128, io="f16", state="f16",
+                       a_per_state=False, ngroups=4, batch=3, index_sensitive=True)),
+    ("hd8_N512", dict(seqlen=1, nheads=2, headdim=8, dstate=512, io="bf16", state="f32",
+                      a_per_state=False, batch=2, index_sensitive=True)),
+]
+
+
+@pytest.mark.parametrize("label,kw", GEOMETRY_SHAPES, ids=[g[0] for g in GEOMETRY_SHAPES])
+def test_state_update_every_geometry(dev, ssm, oracle, label, kw):
+    # every geometry the override accepts meets the parity bar, and all of
+    # them leave the same cache bytes (the update of a state does not depend
+    # on how states are spread over lanes)
+    spec = W.tiny(**kw)
+    t = W.make(spec, dev)
+    st0 = t["ssm_state"].clone()
+    idx = t["slot_idx"]
+    idx_np = idx.cpu().numpy()
+    o, s, st, sts = oracle.state_update(f(st0), f(t["x"]), f(t["dt"]), f(t["A"]), f(t["B"]),
+                                        f(t["C"]), D=f(t["D"]), z=f(t["z"]),
+                                        dt_bias=f(t["dt_bias"]), slot_idx=idx_np)
+    first = None
+    for v in (8, 16):
+        for b in (64, 128, 256, 512):
+            state = st0.clone()
+            out = ssm.state_update(state, t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"],
+                                   z=t["z"], dt_bias=t["dt_bias"], slot_idx=idx, config=(v, b))
+            torch.cuda.synchronize()
+            check(out, o, s, RTOL[spec.io], spec.io, f"ssu {label} {v}x{b} out")
+            if first is None:
+                first = state
+                gst = f(state)
+                named = _named(idx_np)
+                check(gst[named], st[named], sts[named], RTOL[spec.io], spec.state,
+                      f"ssu {label} state")
+            else:
+                assert torch.equal(state, first), f"{label} {v}x{b}: cache bytes differ"
