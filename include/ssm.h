@@ -123,6 +123,35 @@ int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias,
                        void *stream);
 
 /*
+ * ssm_selective_scan_ex -- ssm_selective_scan with a choice of algorithm.
+ *   algo  SSM_SCAN_AUTO: the library's choice;
+ *         SSM_SCAN_RECURRENT: the step-by-step recurrence (any shape);
+ *         SSM_SCAN_CHUNKED: the chunked matrix form on the matrix cores.
+ * The chunked form needs one decay per head (a_per_state == 0), bf16 I/O,
+ * dstate 64, 128 or 256, headdim a multiple of 64, seqlen a multiple of 8 and
+ * 16-byte aligned tensors; otherwise SSM_SCAN_CHUNKED returns
+ * SSM_ERR_UNSUPPORTED.  SSM_SCAN_AUTO takes it whenever it applies.  The
+ * chunked form computes the same recurrence: over a chunk of steps with one
+ * scalar decay per step, the state recursion unrolls into products of small
+ * matrices (decay-weighted C.B^T within the chunk, C times the carried state,
+ * and the decay-weighted B times u for the next state), which run on MFMA
+ * with float32 accumulation; operands that are not exact in bf16 are split
+ * into two bf16 parts (about 16 significant bits per product).  Other
+ * arguments as in ssm_selective_scan.
+ */
+#define SSM_SCAN_AUTO 0
+#define SSM_SCAN_RECURRENT 1
+#define SSM_SCAN_CHUNKED 2
+int ssm_selective_scan_ex(const void *u, const void *dt, const float *dt_bias,
+                          const float *A, const void *B, const void *C,
+                          const float *D, const void *z, void *ssm_state,
+                          const int32_t *slot_idx, void *out, int batch,
+                          int seqlen, int nheads, int headdim, int dstate,
+                          int ngroups, int nslots, int io_dtype,
+                          int state_dtype, int a_per_state, int dt_softplus,
+                          int has_initial_state, int algo, void *stream);
+
+/*
  * ssm_state_update -- one-token selective state update (decode) in place on a
  * slot-indexed state cache: the selective_state_update call of the vLLM PR
  * #50534 report ("关键源码片段"), same argument set.

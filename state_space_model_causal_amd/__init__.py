@@ -31,9 +31,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm_hip.so")
 
 SSM_F32, SSM_F16, SSM_BF16 = 0, 1, 2
+SCAN_AUTO, SCAN_RECURRENT, SCAN_CHUNKED = 0, 1, 2
 _DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: SSM_BF16}
 
-EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_state_update",
+EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_selective_scan_ex", "ssm_state_update",
             "ssm_state_update_ex", "ssm_state_update_config",
             "ssm_decode_step", "ssm_causal_conv1d_varlen", "ssm_selective_scan_varlen",
             "ssm_status_string", "ssm_abi_version")
@@ -72,6 +73,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_selective_scan.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
                                        I, I, I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_selective_scan.restype = I
+    lib.ssm_selective_scan_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
+                                          I, I, I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_selective_scan_ex.restype = I
     lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
                                      I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_state_update.restype = I
@@ -155,8 +159,10 @@ def causal_conv1d(x, weight, bias=None, conv_state=None, slot_idx=None, out=None
 
 def selective_scan(u, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
                    ssm_state=None, slot_idx=None, has_initial_state=False, out=None,
-                   stream=None):
-    """ssm_selective_scan: u [batch, nheads*headdim, seqlen] -> out."""
+                   stream=None, algo=None):
+    """ssm_selective_scan: u [batch, nheads*headdim, seqlen] -> out.
+    algo: None (the library's choice), SCAN_RECURRENT or SCAN_CHUNKED
+    (ssm_selective_scan_ex)."""
     batch, channels, seqlen = u.shape
     nheads = dt.shape[1]
     headdim = channels // nheads
@@ -167,14 +173,17 @@ def selective_scan(u, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=Tru
     _same_io(u.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
     nslots = ssm_state.shape[0] if ssm_state is not None else 0
     sd = _code(ssm_state, "ssm_state") if ssm_state is not None else SSM_F32
-    st = load_library().ssm_selective_scan(
-        _ptr(u, "u"), _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32),
-        _ptr(A, "A", torch.float32), _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32),
-        _ptr(z, "z"), _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
-        _ptr(out, "out"), batch, seqlen, nheads, headdim, dstate, ngroups, nslots,
-        _code(u, "u"), sd, a_per_state, int(bool(dt_softplus)), int(bool(has_initial_state)),
-        _stream(stream))
-    _check("ssm_selective_scan", st)
+    args = (_ptr(u, "u"), _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32),
+            _ptr(A, "A", torch.float32), _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32),
+            _ptr(z, "z"), _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+            _ptr(out, "out"), batch, seqlen, nheads, headdim, dstate, ngroups, nslots,
+            _code(u, "u"), sd, a_per_state, int(bool(dt_softplus)), int(bool(has_initial_state)))
+    if algo is None:
+        st = load_library().ssm_selective_scan(*args, _stream(stream))
+        _check("ssm_selective_scan", st)
+    else:
+        st = load_library().ssm_selective_scan_ex(*args, int(algo), _stream(stream))
+        _check("ssm_selective_scan_ex", st)
     return out
 
 
@@ -292,7 +301,7 @@ def selective_scan_varlen(u, dt, A, B, C, cu_seqlens, D=None, z=None, dt_bias=No
 
 
 __all__ = ["causal_conv1d", "selective_scan", "state_update", "state_update_config",
-           "LaunchConfig", "decode_step",
+           "LaunchConfig", "decode_step", "SCAN_AUTO", "SCAN_RECURRENT", "SCAN_CHUNKED",
            "causal_conv1d_varlen", "selective_scan_varlen", "load_library",
            "SsmError",
            "SSM_F32", "SSM_F16", "SSM_BF16", "EXPORTED", "LIB_PATH"]

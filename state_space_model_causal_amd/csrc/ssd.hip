@@ -1,0 +1,424 @@
+// ssd.hip -- Mamba-2 prefill (one decay per head) in chunked matrix form on
+// the gfx950 matrix cores.
+//
+// Operation: the same selective scan as scan.hip (the selective-scan operator
+// of "feat(llama.cu): 适配 mamba 模型", InfiniLM-Rust PR #48, section 2.1, with
+// its silu(z) gate and the final state to the request's slot, section 3.1),
+// for the case where the decay exp(delta_t * A_h) is one scalar per head and
+// step.  The result is the recurrence's, up to rounding; only the order of
+// the arithmetic changes.
+//
+// With a scalar decay the recurrence over a chunk of Q steps is a product of
+// small dense matrices.  For head h, rows p (headdim) and states n, with the
+// chunk's cumulative log-decay L_s = sum_{i<=s} delta_i A_h:
+//     Y[s,p]  = sum_{r<=s} C_s.B_r exp(L_s - L_r) delta_r X[r,p]     (within)
+//             + exp(L_s) sum_n C_s[n] H[p,n]                           (carried)
+//     H'[p,n] = exp(L_Q-1) H[p,n] + sum_r exp(L_Q-1 - L_r) delta_r B_r[n] X[r,p]
+// where H is the state entering the chunk.  All four contractions (C^T B over
+// states, the masked decay matrix times X, C times H^T, and B times the
+// weighted X) run on v_mfma_f32_16x16x32_bf16.  Each product has one operand
+// that is exact in bfloat16 (B or C, stored in bf16, or X) and one float32
+// operand (the masked decay matrix, the carried state, the weighted X), which
+// is split into a bf16 high part and a bf16 remainder, so every product keeps
+// about 16 significant bits; the accumulation is float32.
+//
+// Work decomposition: one 512-lane workgroup per (request, head, 64 rows of
+// headdim).  Each wave owns 16 rows and half of the states: its part of the
+// state (dstate/2 x 16, float32) stays in MFMA accumulators for the whole
+// sequence, which is walked in chunks of 64 steps.  Per chunk the workgroup
+// stages B (as is and transposed) and C (transposed) in LDS, builds the
+// masked decay matrix once for all waves, then every wave computes its share
+// of the outputs and updates its part of the state.  Two waves per SIMD let
+// one wave's vector work overlap the other's matrix work.  HBM traffic: u,
+// dt, z, B, C read once (B and C from L2 for every head of a group), out
+// written once, the state read and written once.
+#include "ssm_device.hpp"
+#include "ssm_kernels.hpp"
+
+namespace ssm {
+
+namespace {
+constexpr int SQ = 64;   // chunk length (steps)
+constexpr int SPB = 64;  // headdim rows per workgroup (4 row tiles of 16)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+} // namespace
+
+__device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x = hi + lo with hi, lo in bfloat16 (relative error of the pair ~2^-16)
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8_t &hi, bf16x8_t &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)x[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(x[i] - (float)h);
+    }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8_t, w); }
+
+constexpr int SNW = 8;           // waves per workgroup
+constexpr int STHREADS = 64 * SNW;
+
+// Global data of one chunk, loaded a chunk ahead (registers) so that the
+// loads of chunk c+1 are in flight while chunk c is computed.
+template <int N>
+struct ChunkLoads {
+    static constexpr int NUNITS = (N / 2) * (SQ / 8);  // (pair of states, 8 steps)
+    static constexpr int UNITS = (NUNITS + STHREADS - 1) / STHREADS;
+    u32x4 b0[UNITS], b1[UNITS], c0[UNITS], c1[UNITS];
+    u32x4 x[2];          // X[p][t0 + 32 kk + 8 lq .. +8)
+    uint2 xo[2], zo[2];  // u and z at steps t0 + 16 st + 4 lq .. +4, this wave's 2 row tiles
+    float dt;            // wave 0: dt of step t0 + lane
+};
+
+template <int N>
+__device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, const bf16 *Bg, const bf16 *Cg,
+                                           const bf16 *urow, const bf16 *zrow, const bf16 *dtrow, int tid,
+                                           int w, int l, int lq, int nh)
+{
+#pragma unroll
+    for (int k = 0; k < ChunkLoads<N>::UNITS; ++k) {
+        const int u = min(tid + STHREADS * k, ChunkLoads<N>::NUNITS - 1);
+        const int n = 2 * (u >> 3), tv = u & 7;
+        const int t = t0 + 8 * tv;
+        const int64_t off = (int64_t)n * L + (t < L ? t : 0);  // clamped; zeroed when staged
+        c.b0[k] = *reinterpret_cast<const u32x4 *>(Bg + off);
+        c.b1[k] = *reinterpret_cast<const u32x4 *>(Bg + off + L);
+        c.c0[k] = *reinterpret_cast<const u32x4 *>(Cg + off);
+        c.c1[k] = *reinterpret_cast<const u32x4 *>(Cg + off + L);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int t = t0 + 32 * kk + 8 * lq;
+        c.x[kk] = *reinterpret_cast<const u32x4 *>(urow + (t < L ? t : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = t0 + 16 * (2 * nh + i) + 4 * lq;
+        const int tc = t < L ? t : 0;
+        c.xo[i] = *reinterpret_cast<const uint2 *>(urow + tc);
+        c.zo[i] = zrow ? *reinterpret_cast<const uint2 *>(zrow + tc) : uint2{0u, 0u};
+    }
+    if (w == 0) {
+        const int t = t0 + l;
+        c.dt = to_f32(dtrow[t < L ? t : t0]);
+    }
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Eight waves: wave w owns headdim rows 16 (w%4) .. +16 of the workgroup's 64
+// and half of the states, n-tiles [NT/2 (w/4), NT/2 (w/4 + 1)); the two
+// waves of a row block exchange their halves of C.H through LDS and each
+// writes half of the chunk's output rows (row tiles 2 (w/4) and 2 (w/4) + 1).
+template <typename TS, int N>
+__global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
+{
+    constexpr int LDN = N + 8;   // row stride (elements) of the transposed tiles
+    constexpr int LDQ = SQ + 8;  // row stride of the natural B tile and of M
+    constexpr int NT = N / 16;   // 16-state tiles of the state
+    constexpr int NTH = NT / 2;  // tiles per wave
+    __shared__ __align__(16) __bf16 s_bt[SQ * LDN];  // B^T  [r][n]
+    __shared__ __align__(16) __bf16 s_ct[SQ * LDN];  // C^T  [s][n]
+    __shared__ __align__(16) __bf16 s_bn[N * LDQ];   // B    [n][r]
+    __shared__ __align__(16) __bf16 s_mh[SQ * LDQ];  // masked decay matrix M[s][r], high part
+    __shared__ __align__(16) __bf16 s_ml[SQ * LDQ];  // and remainder
+    __shared__ __align__(16) float s_x[SNW][2][64][4];  // C.H halves for the partner wave
+    __shared__ float s_d[SQ], s_L[SQ], s_eL[SQ], s_w[SQ], s_etot[1];
+
+    const int L = a.seqlen, P = a.headdim, H = a.nheads;
+    const int npb = P / SPB;
+    const int pb = blockIdx.x % npb;
+    const int bh = blockIdx.x / npb;
+    const int h = bh % H, b = bh / H;
+    const int g = h / a.heads_per_group;
+    const int slot = a.slot_idx ? a.slot_idx[b] : b;
+    if (slot < 0)
+        return;  // padded request (uniform over the workgroup)
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int l16 = l & 15, lq = l >> 4;
+    const int pw = w & 3, nh = w >> 2;        // row tile, state half
+    const int partner = pw + 4 * (1 - nh);
+    const int p = pb * SPB + 16 * pw + l16;   // this lane's row of headdim
+    const int Cn = H * P;
+    const int64_t crow = ((int64_t)b * Cn + (int64_t)h * P + p) * L;
+    const bf16 *urow = static_cast<const bf16 *>(a.u) + crow;
+    const bf16 *zrow = a.z ? static_cast<const bf16 *>(a.z) + crow : nullptr;
+    bf16 *orow = static_cast<bf16 *>(a.out) + crow;
+    const bf16 *dtrow = static_cast<const bf16 *>(a.dt) + ((int64_t)b * H + h) * L;
+    const bf16 *Bg = static_cast<const bf16 *>(a.B) + ((int64_t)b * a.ngroups + g) * N * L;
+    const bf16 *Cg = static_cast<const bf16 *>(a.C) + ((int64_t)b * a.ngroups + g) * N * L;
+    TS *srow = a.state ? static_cast<TS *>(a.state) + (((int64_t)slot * H + h) * P + p) * N : nullptr;
+
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    const float A2 = a.A[h] * kLog2e;
+
+    // this wave's state^T tiles: hacc[q][j] = H[p][16 (NTH nh + q) + 4 lq + j]
+    f32x4_t hacc[NTH];
+#pragma unroll
+    for (int q = 0; q < NTH; ++q) {
+        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (srow && a.has_initial_state) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = to_f32(srow[16 * (NTH * nh + q) + 4 * lq + j]);
+        }
+        hacc[q] = v;
+    }
+
+    ChunkLoads<N> cur;
+    load_chunk<N>(cur, 0, L, Bg, Cg, urow, zrow, dtrow, tid, w, l, lq, nh);
+
+    for (int t0 = 0; t0 < L; t0 += SQ) {
+        // ---- stage the chunk (its loads were issued one chunk earlier)
+        if (w == 0) {
+            const bool ok = t0 + l < L;
+            const float v = cur.dt + bias;
+            const float sp = softplus_f32(v);
+            const float d = ok ? (a.dt_softplus ? sp : v) : 0.0f;  // identity step past the end
+            float cum = d * A2;  // log2 of this step's decay, summed over the chunk
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float up = __shfl_up(cum, o, 64);
+                cum += (l >= o) ? up : 0.0f;
+            }
+            const float tot = __shfl(cum, 63, 64);
+            s_d[l] = d;
+            s_L[l] = cum;
+            s_eL[l] = exp2_hw(cum);
+            s_w[l] = exp2_hw(tot - cum) * d;
+            if (l == 0)
+                s_etot[0] = exp2_hw(tot);
+        }
+#pragma unroll
+        for (int k = 0; k < ChunkLoads<N>::UNITS; ++k) {
+            const int u = tid + STHREADS * k;
+            if (u < ChunkLoads<N>::NUNITS) {
+                const int n = 2 * (u >> 3), tv = u & 7;
+                const bool ok = t0 + 8 * tv < L;  // L % 8 == 0: a vector is all in or all out
+                const u32x4 z4 = {0u, 0u, 0u, 0u};
+                const u32x4 b0 = ok ? cur.b0[k] : z4, b1 = ok ? cur.b1[k] : z4;
+                const u32x4 c0 = ok ? cur.c0[k] : z4, c1 = ok ? cur.c1[k] : z4;
+                *reinterpret_cast<u32x4 *>(&s_bn[n * LDQ + 8 * tv]) = b0;
+                *reinterpret_cast<u32x4 *>(&s_bn[(n + 1) * LDQ + 8 * tv]) = b1;
+                const uint32_t bw[4] = {b0.x, b0.y, b0.z, b0.w}, bv[4] = {b1.x, b1.y, b1.z, b1.w};
+                const uint32_t cw[4] = {c0.x, c0.y, c0.z, c0.w}, cv[4] = {c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    // element i of a row is the low (even i) or high half of
+                    // word i/2; pair it with the same element of the next row
+                    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t bp = __builtin_amdgcn_perm(bv[i >> 1], bw[i >> 1], sel);
+                    const uint32_t cp = __builtin_amdgcn_perm(cv[i >> 1], cw[i >> 1], sel);
+                    *reinterpret_cast<uint32_t *>(&s_bt[(8 * tv + i) * LDN + n]) = bp;
+                    *reinterpret_cast<uint32_t *>(&s_ct[(8 * tv + i) * LDN + n]) = cp;
+                }
+            }
+        }
+        bf16x8_t xk[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            xk[kk] = as_bf16x8(t0 + 32 * kk + 8 * lq < L ? cur.x[kk] : u32x4{0u, 0u, 0u, 0u});
+        const uint2 xo[2] = {cur.xo[0], cur.xo[1]}, zo[2] = {cur.zo[0], cur.zo[1]};
+        __syncthreads();
+
+        // ---- the next chunk's loads, in flight during this chunk's work
+        if (t0 + SQ < L)
+            load_chunk<N>(cur, t0 + SQ, L, Bg, Cg, urow, zrow, dtrow, tid, w, l, lq, nh);
+
+        // ---- carried state over this wave's half of the states:
+        // yc[st] = sum_{n in half} C_s[n] H[p][n]; the state as MFMA operands
+        // (high and low parts) in the order the accumulators hold it
+        f32x4_t yc[4];
+        {
+            bf16x8_t hh[NTH / 2], hl[NTH / 2];
+#pragma unroll
+            for (int q2 = 0; q2 < NTH / 2; ++q2) {
+                float hv[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    hv[i] = hacc[2 * q2][i];
+                    hv[4 + i] = hacc[2 * q2 + 1][i];
+                }
+                split_bf16(hv, hh[q2], hl[q2]);
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int q2 = 0; q2 < NTH / 2; ++q2) {
+                    const int kk = (NTH / 2) * nh + q2;  // 32-state step
+                    const __bf16 *cr = &s_ct[(16 * st + l16) * LDN + 32 * kk + 4 * lq];
+                    const uint2 c_lo = *reinterpret_cast<const uint2 *>(cr);
+                    const uint2 c_hi = *reinterpret_cast<const uint2 *>(cr + 16);
+                    const bf16x8_t cv = as_bf16x8(u32x4{c_lo.x, c_lo.y, c_hi.x, c_hi.y});
+                    acc = mma(cv, hh[q2], acc);
+                    acc = mma(cv, hl[q2], acc);
+                }
+                yc[st] = acc;
+            }
+            // the partner needs this half for its output row tiles (selects,
+            // not a register array indexed at run time)
+            *reinterpret_cast<f32x4_t *>(&s_x[partner][0][l][0]) = nh ? yc[0] : yc[2];
+            *reinterpret_cast<f32x4_t *>(&s_x[partner][1][l][0]) = nh ? yc[1] : yc[3];
+        }
+
+        // ---- masked decay matrix M[s][r] = (C_s.B_r) exp(L_s - L_r) delta_r
+        // for r <= s: rows s in [16 pw, 16 pw + 16), r tiles 2 nh, 2 nh + 1
+        {
+            const int s = 16 * pw + l16;
+            const float Ls = s_L[s];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rt = 2 * nh + i;
+                float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (rt <= pw) {
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < N / 32; ++kk) {
+                        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
+                            &s_bt[(16 * rt + l16) * LDN + 32 * kk + 8 * lq]);
+                        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(
+                            &s_ct[(16 * pw + l16) * LDN + 32 * kk + 8 * lq]);
+                        acc = mma(av, bv, acc);
+                    }
+                    const int r0 = 16 * rt + 4 * lq;
+                    const float4 Lr = *reinterpret_cast<const float4 *>(&s_L[r0]);
+                    const float4 dr = *reinterpret_cast<const float4 *>(&s_d[r0]);
+                    const float lr[4] = {Lr.x, Lr.y, Lr.z, Lr.w}, dv[4] = {dr.x, dr.y, dr.z, dr.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        m[j] = (r0 + j <= s) ? acc[j] * exp2_hw(Ls - lr[j]) * dv[j] : 0.0f;
+                }
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                bf16x4_t mh, ml;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    mh[j] = (__bf16)m[j];
+                    ml[j] = (__bf16)(m[j] - (float)mh[j]);
+                }
+                const int r0 = 16 * rt + 4 * lq;
+                *reinterpret_cast<bf16x4_t *>(&s_mh[s * LDQ + r0]) = mh;
+                *reinterpret_cast<bf16x4_t *>(&s_ml[s * LDQ + r0]) = ml;
+            }
+        }
+
+        // ---- state update of this wave's half: H <- exp(L_last) H +
+        // sum_r B_r (w_r X_r)^T, w_r = exp(L_last - L_r) delta_r on this
+        // lane's X (exact B is the other operand)
+        {
+            const float etot = s_etot[0];
+            bf16x8_t xwh[2], xwl[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float4 w0 = *reinterpret_cast<const float4 *>(&s_w[32 * kk + 8 * lq]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&s_w[32 * kk + 8 * lq + 4]);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                float xw[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    xw[i] = (float)xk[kk][i] * wv[i];
+                split_bf16(xw, xwh[kk], xwl[kk]);
+            }
+#pragma unroll
+            for (int q = 0; q < NTH; ++q) {
+                const int nt = NTH * nh + q;
+                f32x4_t acc = hacc[q] * etot;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8_t braw = *reinterpret_cast<const bf16x8_t *>(
+                        &s_bn[(16 * nt + l16) * LDQ + 32 * kk + 8 * lq]);
+                    acc = mma(braw, xwh[kk], acc);
+                    acc = mma(braw, xwl[kk], acc);
+                }
+                hacc[q] = acc;
+            }
+        }
+        __syncthreads();  // M and the C.H halves visible
+
+        // ---- outputs: row tiles st = 2 nh + i, rows s = 16 st + 4 lq + j
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int st = 2 * nh + i;
+            f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk <= nh; ++kk) {  // r < 16 st + 16 <= 32 (nh + 1)
+                const bf16x8_t mh = *reinterpret_cast<const bf16x8_t *>(
+                    &s_mh[(16 * st + l16) * LDQ + 32 * kk + 8 * lq]);
+                const bf16x8_t ml = *reinterpret_cast<const bf16x8_t *>(
+                    &s_ml[(16 * st + l16) * LDQ + 32 * kk + 8 * lq]);
+                y = mma(mh, xk[kk], y);
+                y = mma(ml, xk[kk], y);
+            }
+            const f32x4_t other = *reinterpret_cast<const f32x4_t *>(&s_x[w][i][l][0]);
+            const int s0 = 16 * st + 4 * lq;
+            const int t = t0 + s0;
+            if (t < L) {  // L % 4 == 0: the 4 steps are all in or all out
+                const float4 eL = *reinterpret_cast<const float4 *>(&s_eL[s0]);
+                const float el[4] = {eL.x, eL.y, eL.z, eL.w};
+                const float xv[4] = {bf_lo(xo[i].x), bf_hi(xo[i].x), bf_lo(xo[i].y), bf_hi(xo[i].y)};
+                const float zv[4] = {bf_lo(zo[i].x), bf_hi(zo[i].x), bf_lo(zo[i].y), bf_hi(zo[i].y)};
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4_t mine = i ? (nh ? yc[3] : yc[1]) : (nh ? yc[2] : yc[0]);
+                    float v = y[j] + el[j] * (mine[j] + other[j]) + Dh * xv[j];
+                    if (zrow)
+                        v *= silu_f32(zv[j]);
+                    o[j] = v;
+                }
+                uint2 ov;
+                ov.x = (uint32_t)from_f32<bf16>(o[0]).bits | ((uint32_t)from_f32<bf16>(o[1]).bits << 16);
+                ov.y = (uint32_t)from_f32<bf16>(o[2]).bits | ((uint32_t)from_f32<bf16>(o[3]).bits << 16);
+                *reinterpret_cast<uint2 *>(orow + t) = ov;
+            }
+        }
+        __syncthreads();  // the next chunk overwrites the staged tiles
+    }
+
+    if (srow) {
+#pragma unroll
+        for (int q = 0; q < NTH; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                srow[16 * (NTH * nh + q) + 4 * lq + j] = from_f32<TS>(hacc[q][j]);
+    }
+}
+
+template <typename TS>
+static hipError_t launch_ssd_ts(const ScanArgs &a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((int64_t)a.batch * a.nheads * (a.headdim / SPB)));
+    switch (a.dstate) {
+    case 64: hipLaunchKernelGGL((ssd_kernel<TS, 64>), grid, dim3(STHREADS), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((ssd_kernel<TS, 128>), grid, dim3(STHREADS), 0, stream, a); break;
+    default: hipLaunchKernelGGL((ssd_kernel<TS, 256>), grid, dim3(STHREADS), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+bool ssd_supported(const ScanArgs &a)
+{
+    return !a.cu_seqlens && !a.a_per_state && a.io_dtype == 2 && a.vec &&
+           (a.dstate == 64 || a.dstate == 128 || a.dstate == 256) && a.headdim % SPB == 0;
+}
+
+hipError_t launch_ssd(const ScanArgs &a, hipStream_t stream)
+{
+    switch (a.state_dtype) {
+    case 0: return launch_ssd_ts<float>(a, stream);
+    case 1: return launch_ssd_ts<f16>(a, stream);
+    default: return launch_ssd_ts<bf16>(a, stream);
+    }
+}
+
+} // namespace ssm

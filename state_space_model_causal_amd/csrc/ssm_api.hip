@@ -86,8 +86,10 @@ int scan_call(const void *u, const void *dt, const float *dt_bias, const float *
               const int32_t *slot_idx, const int32_t *cu_seqlens, const int32_t *has_init_seq,
               void *out, int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
               int nslots, int io_dtype, int state_dtype, int a_per_state, int dt_softplus,
-              int has_initial_state, void *stream)
+              int has_initial_state, void *stream, int algo = SSM_SCAN_AUTO)
 {
+    if (algo != SSM_SCAN_AUTO && algo != SSM_SCAN_RECURRENT && algo != SSM_SCAN_CHUNKED)
+        return SSM_ERR_SHAPE;
     if (!u || !dt || !A || !B || !C || !out)
         return SSM_ERR_NULL_ARG;
     if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
@@ -141,6 +143,11 @@ int scan_call(const void *u, const void *dt, const float *dt_bias, const float *
     a.has_initial_state = has_initial_state ? 1 : 0;
     a.vec = (seqlen % 8 == 0) && aligned(u, 16) && aligned(dt, 16) && aligned(B, 16) &&
             aligned(C, 16) && aligned(z, 16) && aligned(out, 16);
+    const bool chunked = ssm::ssd_supported(a);
+    if (algo == SSM_SCAN_CHUNKED && !chunked)
+        return SSM_ERR_UNSUPPORTED;
+    if (chunked && algo != SSM_SCAN_RECURRENT)
+        return status_of(ssm::launch_ssd(a, static_cast<hipStream_t>(stream)));
     return status_of(ssm::launch_scan(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -195,6 +202,18 @@ int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias, cons
     return scan_call(u, dt, dt_bias, A, B, C, D, z, ssm_state, slot_idx, nullptr, nullptr, out,
                      batch, seqlen, nheads, headdim, dstate, ngroups, nslots, io_dtype,
                      state_dtype, a_per_state, dt_softplus, has_initial_state, stream);
+}
+
+int ssm_selective_scan_ex(const void *u, const void *dt, const float *dt_bias, const float *A,
+                          const void *B, const void *C, const float *D, const void *z,
+                          void *ssm_state, const int32_t *slot_idx, void *out, int batch,
+                          int seqlen, int nheads, int headdim, int dstate, int ngroups, int nslots,
+                          int io_dtype, int state_dtype, int a_per_state, int dt_softplus,
+                          int has_initial_state, int algo, void *stream)
+{
+    return scan_call(u, dt, dt_bias, A, B, C, D, z, ssm_state, slot_idx, nullptr, nullptr, out,
+                     batch, seqlen, nheads, headdim, dstate, ngroups, nslots, io_dtype,
+                     state_dtype, a_per_state, dt_softplus, has_initial_state, stream, algo);
 }
 
 int ssm_selective_scan_varlen(const void *u, const void *dt, const float *dt_bias,

@@ -100,6 +100,10 @@ struct SsuArgs {
 
 hipError_t launch_conv(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream);
+// Mamba-2 prefill in chunked matrix form on the matrix cores (dense batches,
+// bf16 I/O, one decay per head, dstate 64/128/256, headdim a multiple of 64)
+bool ssd_supported(const ScanArgs &a);
+hipError_t launch_ssd(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
 
 // Limits the kernels are built for.

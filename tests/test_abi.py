@@ -208,3 +208,27 @@ def test_tuned_table_entries_are_valid():
         P, N, io, st, lo, hi, v, b = vals
         assert P >= 1 and 1 <= N <= 512 and io in (0, 1, 2) and st in (0, 1, 2)
         assert 0 <= lo < hi and v in (8, 16) and b in (64, 128, 256, 512)
+
+
+def scan_ex(lib, algo, **kw):
+    a = dict(u=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, st=None,
+             idx=None, out=FAKE, batch=2, L=64, H=4, P=64, N=128, G=1, S=0, io=2, sd=0, aps=0,
+             sp=1, init=0)
+    a.update(kw)
+    return lib.ssm_selective_scan_ex(a["u"], a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"],
+                                     a["z"], a["st"], a["idx"], a["out"], a["batch"], a["L"],
+                                     a["H"], a["P"], a["N"], a["G"], a["S"], a["io"], a["sd"],
+                                     a["aps"], a["sp"], a["init"], algo, None)
+
+
+@pytest.mark.parametrize("kw", [dict(aps=1, N=16), dict(io=1), dict(io=0), dict(N=96),
+                                dict(P=32), dict(L=60), dict(u=FAKE + 2)])
+def test_scan_chunked_refuses_unsupported_shapes(lib, kw):
+    # the chunked form is asked for explicitly where it does not apply: the
+    # call fails before anything is launched (fake pointers are never touched)
+    assert scan_ex(lib, 2, **kw) == UNSUP
+
+
+def test_scan_ex_rejects_unknown_algorithm(lib):
+    assert scan_ex(lib, 7) == SHAPE
+    assert scan_ex(lib, 2, batch=0) == 0
