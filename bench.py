@@ -63,7 +63,9 @@ def parse():
                         "and print one JSON line per point")
     p.add_argument("--no-varlen", action="store_true",
                    help="skip the packed variable-length prefill measurement")
-    p.add_argument("--only", choices=["prefill", "decode", "varlen"], default=None,
+    p.add_argument("--no-layer", action="store_true",
+                   help="skip the whole decode-layer measurement")
+    p.add_argument("--only", choices=["prefill", "decode", "varlen", "layer"], default=None,
                    help="run only one half of the step (for profiling)")
     p.add_argument("--unfused-decode", action="store_true",
                    help="decode with the separate conv-update and state-update calls instead "
@@ -84,7 +86,7 @@ def profile_commands(out):
     stats, then one counter per pass (FETCH_SIZE, WRITE_SIZE) on the step and
     on a plain 1 GiB device copy (the calibration), and the SQ counters of the
     prefill half."""
-    b = "python -u bench.py --no-cpu-baseline --no-varlen"
+    b = "python -u bench.py --no-cpu-baseline --no-varlen --no-layer"
     pmc = "timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d {o}/{n} -o run -- {cmd}"
     return [
         ("trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d {out}/trace "
@@ -310,6 +312,10 @@ def main():
     if args.ssu_sweep:
         ssu_sweep(ssm, W, dev, stream)
         return
+    if args.only == "layer":
+        print(json.dumps({"layer_decode": measure_layer(ssm, W, dev, stream, args.steps,
+                                                        args.warmup)}), flush=True)
+        return
     if args.only == "varlen":
         print(json.dumps({"varlen_prefill": measure_varlen(ssm, W, dev, stream, args.steps,
                                                            args.warmup)}), flush=True)
@@ -449,6 +455,10 @@ def main():
     if not args.no_varlen and args.only is None:
         varlen = measure_varlen(ssm, W, dev, stream, max(args.steps // 2, 5), 3)
 
+    layer = None
+    if not args.no_layer and args.only is None:
+        layer = measure_layer(ssm, W, dev, stream, max(args.steps // 2, 5), 3)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds, pspec, dspec)
@@ -485,6 +495,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "varlen_prefill": varlen,
+        "layer_decode": layer,
         "step_ms_median": float(np.median(step_ms)),
         "wall_s_timed": t_wall,
         "device": props.name,
@@ -556,6 +567,46 @@ def ssu_sweep(ssm, W, dev, stream, iters=20):
                     del t, out, sets, graph
                     torch.cuda.empty_cache()
     return points
+
+
+def measure_layer(ssm, W, dev, stream, steps, warmup):
+    """One whole Mamba-1 2.8B decode layer (RMSNorm, in_proj, conv update,
+    x_proj, dt_proj, state update, out_proj + residual; random weights) for
+    245 requests from a 512-slot cache, f16 I/O and f32 state; two rotating
+    sets of caches.  Timed with events on the launch stream."""
+    import numpy as np
+    import torch
+
+    sets = [W.mamba1_layer(seed=30 + k, device=dev) for k in range(2)]
+    descs = [ssm.mamba1_layer(t["w"]) for t in sets]
+    lib = ssm.load_library()
+    import ctypes
+    need = lib.ssm_mamba1_decode_layer_workspace(ctypes.byref(descs[0]), 245)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def run(i):
+        t = sets[i % 2]
+        ssm.mamba1_decode_layer(descs[i % 2], t["hidden"], t["conv_state"], t["ssm_state"],
+                                slot_idx=t["slot_idx"], workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e3
+    b = W.layer_bytes(2560, 5120, 16, 160, 4, 245)
+    mean = float(us.mean())
+    return {"workload": "Mamba-1 2.8B decode layer (d_model 2560, d_inner 5120, d_state 16, "
+                        "dt_rank 160, conv 4), 245 requests, f16 I/O and weights, f32 state, "
+                        "random weights",
+            "us": mean, "us_median": float(np.median(us)), "tokens_per_s": 245 / (mean * 1e-6),
+            "bytes": b["total"], "GBps": b["total"] / (mean * 1e-6) / 1e9,
+            "model_tokens_per_s_64_layers": 245 / (64 * mean * 1e-6), "steps": steps}
 
 
 VARLEN_NSEQ, VARLEN_TOKENS, VARLEN_SEED = 16, 8192, 5

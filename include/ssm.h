@@ -40,6 +40,7 @@
 #ifndef SSM_H
 #define SSM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -302,6 +303,75 @@ int ssm_selective_scan_varlen(const void *u, const void *dt, const float *dt_bia
                               int ngroups, int nslots, int io_dtype,
                               int state_dtype, int a_per_state, int dt_softplus,
                               void *stream);
+
+/*
+ * One whole Mamba-1 decode layer around the path, and its two building
+ * blocks.  The Mamba-2.8B model of InfiniLM-Rust PR #48 (sections 2.1-2.2)
+ * runs its conv and scan operators inside residual layers whose other steps
+ * are linear projections and a normalisation; the pages do not spell the
+ * layer out, so it is taken as the standard Mamba-1 block (the reading is
+ * documented with the tests):
+ *   hn        = RMSNorm(hidden) * norm_weight
+ *   x | z     = hn . in_proj^T                 in_proj  [2 d_inner, d_model]
+ *   u         = silu(conv1d update of x)       (ssm_causal_conv1d, seqlen 1)
+ *   dt_low | B | C = u . x_proj^T              x_proj   [dt_rank + 2 d_state, d_inner]
+ *   dt        = dt_low . dt_proj^T             dt_proj  [d_inner, dt_rank]
+ *   y         = ssm_state_update(u, dt + dt_bias through softplus, A, B, C, D, z)
+ *   hidden   += y . out_proj^T                 out_proj [d_model, d_inner]
+ * Weights are row-major in the io dtype (f16 or bf16; the products run on
+ * the matrix cores with float32 accumulation); norm weight, conv weight and
+ * bias, dt_bias, A and D are float32.  Intermediates between steps are
+ * stored in the io dtype in a caller-provided workspace.
+ */
+
+/*
+ * ssm_linear -- out[M, N] = x[M, K] . weight[N, K]^T (+ residual[M, N]).
+ * f16 or bf16 (f32 returns SSM_ERR_UNSUPPORTED); K a multiple of 8; x and
+ * weight 16-byte aligned.  workspace: ssm_linear_workspace(M, N, K) bytes
+ * (may be 0 and NULL) of device memory for split-K partial sums.
+ */
+size_t ssm_linear_workspace(int M, int N, int K);
+int ssm_linear(const void *x, const void *weight, const void *residual,
+               void *out, int M, int N, int K, int dtype, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* ssm_rmsnorm -- out[m, :] = x[m, :] / sqrt(mean(x[m, :]^2) + eps) * weight
+ * (weight float32 [D]; x, out f16 or bf16 [M, D]). */
+int ssm_rmsnorm(const void *x, const float *weight, void *out, int M, int D,
+                float eps, int dtype, void *stream);
+
+typedef struct ssm_mamba1_layer {
+    int d_model, d_inner, d_state, dt_rank, conv_width;
+    float norm_eps;
+    const float *norm_weight;  /* [d_model]                          */
+    const void *in_proj;       /* [2 d_inner, d_model], io dtype     */
+    const float *conv_weight;  /* [d_inner, conv_width]              */
+    const float *conv_bias;    /* [d_inner] or NULL                  */
+    const void *x_proj;        /* [dt_rank + 2 d_state, d_inner]     */
+    const void *dt_proj;       /* [d_inner, dt_rank]                 */
+    const float *dt_bias;      /* [d_inner] or NULL                  */
+    const float *A;            /* [d_inner, d_state]                 */
+    const float *D;            /* [d_inner] or NULL                  */
+    const void *out_proj;      /* [d_model, d_inner]                 */
+} ssm_mamba1_layer;
+
+/* Bytes of workspace ssm_mamba1_decode_layer needs for `batch` requests. */
+size_t ssm_mamba1_decode_layer_workspace(const ssm_mamba1_layer *layer,
+                                         int batch);
+
+/*
+ * ssm_mamba1_decode_layer -- one decode token per request through the whole
+ * layer.  hidden [batch, d_model] io dtype, updated in place (rows of padded
+ * requests, slot < 0, are left as they are); conv_state [nslots, d_inner,
+ * conv_width-1] io dtype and ssm_state [nslots, d_inner, 1, d_state] state
+ * dtype, read and updated for the named slots.  d_model, d_inner, dt_rank,
+ * d_state multiples of 8; conv_width <= 4; d_state <= 512.
+ */
+int ssm_mamba1_decode_layer(const ssm_mamba1_layer *layer, void *hidden,
+                            void *conv_state, void *ssm_state,
+                            const int32_t *slot_idx, int batch, int nslots,
+                            int io_dtype, int state_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *ssm_status_string(int status);

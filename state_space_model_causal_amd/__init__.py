@@ -37,7 +37,19 @@ _DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: S
 EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_selective_scan_ex", "ssm_state_update",
             "ssm_state_update_ex", "ssm_state_update_config",
             "ssm_decode_step", "ssm_causal_conv1d_varlen", "ssm_selective_scan_varlen",
-            "ssm_status_string", "ssm_abi_version")
+            "ssm_linear", "ssm_linear_workspace", "ssm_rmsnorm", "ssm_mamba1_decode_layer",
+            "ssm_mamba1_decode_layer_workspace", "ssm_status_string", "ssm_abi_version")
+
+
+class Mamba1Layer(ctypes.Structure):
+    """ssm_mamba1_layer: dimensions and device pointers of one layer's weights."""
+    _fields_ = [("d_model", ctypes.c_int), ("d_inner", ctypes.c_int), ("d_state", ctypes.c_int),
+                ("dt_rank", ctypes.c_int), ("conv_width", ctypes.c_int),
+                ("norm_eps", ctypes.c_float), ("norm_weight", ctypes.c_void_p),
+                ("in_proj", ctypes.c_void_p), ("conv_weight", ctypes.c_void_p),
+                ("conv_bias", ctypes.c_void_p), ("x_proj", ctypes.c_void_p),
+                ("dt_proj", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("A", ctypes.c_void_p),
+                ("D", ctypes.c_void_p), ("out_proj", ctypes.c_void_p)]
 
 
 class LaunchConfig(ctypes.Structure):
@@ -92,6 +104,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_selective_scan_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P,
                                               I, I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_selective_scan_varlen.restype = I
+    Z = ctypes.c_size_t
+    lib.ssm_linear_workspace.argtypes = [I, I, I]
+    lib.ssm_linear_workspace.restype = Z
+    lib.ssm_linear.argtypes = [P, P, P, P, I, I, I, I, P, Z, P]
+    lib.ssm_linear.restype = I
+    lib.ssm_rmsnorm.argtypes = [P, P, P, I, I, ctypes.c_float, I, P]
+    lib.ssm_rmsnorm.restype = I
+    lib.ssm_mamba1_decode_layer_workspace.argtypes = [P, I]
+    lib.ssm_mamba1_decode_layer_workspace.restype = Z
+    lib.ssm_mamba1_decode_layer.argtypes = [P, P, P, P, P, I, I, I, I, P, Z, P]
+    lib.ssm_mamba1_decode_layer.restype = I
     lib.ssm_status_string.argtypes = [I]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -300,7 +323,82 @@ def selective_scan_varlen(u, dt, A, B, C, cu_seqlens, D=None, z=None, dt_bias=No
     return out
 
 
-__all__ = ["causal_conv1d", "selective_scan", "state_update", "state_update_config",
+def _workspace(nbytes, device):
+    # caller-side allocation of a library workspace (the library allocates nothing)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def linear(x, weight, residual=None, out=None, workspace=None, stream=None):
+    """ssm_linear: out[M, N] = x[M, K] . weight[N, K]^T (+ residual)."""
+    M, K = x.shape
+    N = weight.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=x.dtype, device=x.device)
+    _same_io(x.dtype, (weight, "weight"), (residual, "residual"), (out, "out"))
+    need = load_library().ssm_linear_workspace(M, N, K)
+    if workspace is None:
+        workspace = _workspace(need, x.device)
+    st = load_library().ssm_linear(
+        _ptr(x, "x"), _ptr(weight, "weight"), _ptr(residual, "residual"), _ptr(out, "out"), M, N, K,
+        _code(x, "x"), _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ssm_linear", st)
+    return out
+
+
+def rmsnorm(x, weight, eps=1e-5, out=None, stream=None):
+    """ssm_rmsnorm over the last dimension of x [M, D]."""
+    M, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    st = load_library().ssm_rmsnorm(_ptr(x, "x"), _ptr(weight, "weight", torch.float32),
+                                    _ptr(out, "out"), M, D, float(eps), _code(x, "x"),
+                                    _stream(stream))
+    _check("ssm_rmsnorm", st)
+    return out
+
+
+def mamba1_layer(weights: dict, eps=1e-5):
+    """Build the ssm_mamba1_layer descriptor from a dict of GPU tensors (keys:
+    norm_weight, in_proj, conv_weight, conv_bias, x_proj, dt_proj, dt_bias, A,
+    D, out_proj).  The tensors must outlive the descriptor."""
+    w = weights
+    d_inner, d_model = w["in_proj"].shape[0] // 2, w["in_proj"].shape[1]
+    d_state = w["A"].shape[1]
+    dt_rank = w["dt_proj"].shape[1]
+    f32 = torch.float32
+    return Mamba1Layer(d_model, d_inner, d_state, dt_rank, w["conv_weight"].shape[1], float(eps),
+                       _ptr(w["norm_weight"], "norm_weight", f32), _ptr(w["in_proj"], "in_proj"),
+                       _ptr(w["conv_weight"], "conv_weight", f32),
+                       _ptr(w.get("conv_bias"), "conv_bias", f32), _ptr(w["x_proj"], "x_proj"),
+                       _ptr(w["dt_proj"], "dt_proj"), _ptr(w.get("dt_bias"), "dt_bias", f32),
+                       _ptr(w["A"], "A", f32), _ptr(w.get("D"), "D", f32),
+                       _ptr(w["out_proj"], "out_proj"))
+
+
+def mamba1_decode_layer(layer, hidden, conv_state, ssm_state, slot_idx=None, workspace=None,
+                        stream=None):
+    """ssm_mamba1_decode_layer: hidden [batch, d_model] updated in place."""
+    batch = hidden.shape[0]
+    lib = load_library()
+    need = lib.ssm_mamba1_decode_layer_workspace(ctypes.byref(layer), batch)
+    if workspace is None:
+        workspace = _workspace(need, hidden.device)
+    _same_io(hidden.dtype, (conv_state, "conv_state"))
+    st = lib.ssm_mamba1_decode_layer(
+        ctypes.byref(layer), _ptr(hidden, "hidden"), _ptr(conv_state, "conv_state"),
+        _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32), batch,
+        conv_state.shape[0], _code(hidden, "hidden"), _code(ssm_state, "ssm_state"),
+        _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ssm_mamba1_decode_layer", st)
+    return hidden
+
+
+__all__ = ["linear", "rmsnorm", "mamba1_layer", "mamba1_decode_layer", "Mamba1Layer",
+           "causal_conv1d", "selective_scan", "state_update", "state_update_config",
            "LaunchConfig", "decode_step", "SCAN_AUTO", "SCAN_RECURRENT", "SCAN_CHUNKED",
            "causal_conv1d_varlen", "selective_scan_varlen", "load_library",
            "SsmError",

@@ -98,6 +98,29 @@ struct SsuArgs {
     int conv_width;
 };
 
+// out[M, N] = A[M, K] . W[N, K]^T (f16 or bf16, float32 accumulation)
+struct GemmSeg {
+    void *ptr;   // destination of output columns [col0, col0 + ncols)
+    int ld;      // its row stride (elements)
+    int col0, ncols;
+};
+struct GemmArgs {
+    const void *A;           // [M, lda]
+    const void *W;           // [N, K], row-major
+    int lda, M, N, K;
+    int dtype;               // 1 f16, 2 bf16
+    int splits;              // K split over this many workgroups
+    float *partial;          // [splits, M, N] float32 when splits > 1
+    GemmSeg seg[3];
+    int nseg;
+    const void *residual;    // optional: added to the output, [M, ld_residual]
+    int ld_residual;
+    const int32_t *row_slot; // optional: rows with a negative entry are not written
+};
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_rmsnorm(const void *x, const float *w, void *out, int M, int D, float eps, int dtype,
+                          hipStream_t stream);
+
 hipError_t launch_conv(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream);
 // Mamba-2 prefill in chunked matrix form on the matrix cores (dense batches,

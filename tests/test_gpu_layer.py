@@ -1,0 +1,119 @@
+"""GPU parity of the decode layer around the path: the projection kernel
+(ssm_linear), the RMSNorm (ssm_rmsnorm) and one whole Mamba-1 decode layer
+(ssm_mamba1_decode_layer) against the float64 oracle (oracle/layer.py).
+
+Projections: f16 and bf16, shapes from one row to more rows than a
+workgroup covers, narrow outputs (split over K), K not a multiple of the MFMA
+step, a residual.  Layer: the oracle rounds each intermediate to the io dtype
+as the library stores it; tolerance the f16/bf16 bar of tests/_parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests._parity import check, to_f64 as f
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import state_space_model_causal_amd as ssm
+
+    ssm.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    import state_space_model_causal_amd as m
+
+    return m
+
+
+LINEAR_CASES = [
+    # (M, N, K, dtype, residual)
+    (1, 64, 32, torch.float16, False),
+    (7, 100, 40, torch.bfloat16, True),
+    (245, 192, 5120, torch.float16, False),   # split over K
+    (245, 5120, 160, torch.bfloat16, False),
+    (300, 130, 264, torch.float16, True),     # two row blocks, ragged N
+    (245, 2560, 5120, torch.bfloat16, True),  # out_proj shape, split over K
+]
+
+
+@pytest.mark.parametrize("M,N,K,dt,res", LINEAR_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}_{str(c[3])[6:]}{'_res' if c[4] else ''}"
+                              for c in LINEAR_CASES])
+def test_linear_parity(dev, ssm, M, N, K, dt, res):
+    from oracle import layer
+
+    g = torch.Generator(device=dev).manual_seed(M * 7 + N)
+    x = torch.randn(M, K, generator=g, device=dev).to(dt)
+    w = (torch.randn(N, K, generator=g, device=dev) / K ** 0.5).to(dt)
+    r = torch.randn(M, N, generator=g, device=dev).to(dt) if res else None
+    out = ssm.linear(x, w, residual=r)
+    torch.cuda.synchronize()
+    o, s = layer.linear(f(x), f(w), residual=None if r is None else f(r))
+    check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", f"linear {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_rmsnorm_parity(dev, ssm, dt):
+    from oracle import layer
+
+    g = torch.Generator(device=dev).manual_seed(3)
+    x = (torch.randn(37, 2560, generator=g, device=dev) * 3).to(dt)
+    w = torch.rand(2560, generator=g, device=dev) + 0.5
+    out = ssm.rmsnorm(x, w, eps=1e-5)
+    torch.cuda.synchronize()
+    o, s = layer.rmsnorm(f(x), f(w), 1e-5)
+    check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", "rmsnorm")
+
+
+LAYER_CASES = [
+    # (label, mamba1_layer kwargs, pad every)
+    ("small_f16", dict(d_model=256, d_inner=512, d_state=16, dt_rank=32, batch=5, nslots=9,
+                       io="f16", state="f32"), 0),
+    ("small_bf16_pad", dict(d_model=128, d_inner=256, d_state=16, dt_rank=16, batch=6, nslots=8,
+                            io="bf16", state="bf16"), 3),
+    ("mamba1_2.8b_b16", dict(batch=16, nslots=20, io="f16", state="f32"), 5),
+]
+
+
+@pytest.mark.parametrize("label,kw,pad", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_decode_layer_parity(dev, ssm, oracle, label, kw, pad):
+    from oracle import layer
+
+    t = W.mamba1_layer(seed=11, device=dev, **kw)
+    idx = t["slot_idx"].clone()
+    if pad:
+        idx[::pad] = -1
+    h0, cs0, ss0 = t["hidden"].clone(), t["conv_state"].clone(), t["ssm_state"].clone()
+    desc = ssm.mamba1_layer(t["w"], eps=1e-5)
+    ssm.mamba1_decode_layer(desc, t["hidden"], t["conv_state"], t["ssm_state"], slot_idx=idx)
+    torch.cuda.synchronize()
+    kind = oracle.F16 if kw["io"] == "f16" else oracle.BF16
+    wf = {k: f(v) for k, v in t["w"].items()}
+    idx_np = idx.cpu().numpy()
+    stages = {}
+    o, s, cs, ss, sss = layer.mamba1_decode_layer(wf, f(h0), f(cs0), f(ss0), idx_np, eps=1e-5,
+                                                  round_kind=kind, stages=stages)
+    check(t["hidden"], o, s, 3e-3, kw["io"], f"layer {label} hidden")
+    named = idx_np[idx_np >= 0]
+    check(f(t["ssm_state"])[named], ss[named], sss[named], 3e-3, kw["state"], f"layer {label} state")
+    others = np.setdiff1d(np.arange(cs0.shape[0]), named)
+    np.testing.assert_array_equal(f(t["conv_state"])[others], f(cs0)[others])
+    np.testing.assert_array_equal(f(t["ssm_state"])[others], f(ss0)[others])
+    # conv windows: the old samples shift by one exactly; the newest is this
+    # step's x (a projection output, compared at the projection's tolerance)
+    gcs = f(t["conv_state"])[named]
+    np.testing.assert_array_equal(gcs[:, :, :-1], f(cs0)[named][:, :, 1:])
+    live = idx_np >= 0
+    _, xs = layer.linear(stages["hn"], wf["in_proj"])
+    d_inner = wf["in_proj"].shape[0] // 2
+    check(gcs[:, :, -1], stages["x"][live], xs[live][:, :d_inner], 3e-3, kw["io"],
+          f"layer {label} conv window")

@@ -492,3 +492,87 @@ def test_varlen_padded_and_empty_sequences(oracle):
     np.testing.assert_array_equal(cs_new[1], cs[1])
     np.testing.assert_array_equal(cs_new[2], cs[2])
     assert not np.array_equal(cs_new[0], cs[0])
+
+
+# ----------------------------------------------------- decode layer around it
+def test_linear_matches_explicit_loops():
+    # brute force: out[m, n] = sum_k x[m, k] w[n, k] (catches a transposed weight)
+    from oracle import layer
+
+    r = rng(70)
+    x, w, res = r.standard_normal((3, 5)), r.standard_normal((4, 5)), r.standard_normal((3, 4))
+    out, scale = layer.linear(x, w, residual=res)
+    for m in range(3):
+        for n in range(4):
+            s = sum(x[m, k] * w[n, k] for k in range(5))
+            assert abs(out[m, n] - (s + res[m, n])) < 1e-12
+            assert scale[m, n] >= abs(out[m, n]) - 1e-12
+
+
+def test_rmsnorm_closed_forms():
+    from oracle import layer
+
+    # a constant row c maps to sign(c) * w * |c| / sqrt(c^2 + eps)
+    w = np.array([1.0, 2.0, -0.5])
+    out, _ = layer.rmsnorm(np.full((1, 3), -3.0), w, 1e-5)
+    np.testing.assert_allclose(out[0], -w * 3.0 / math.sqrt(9.0 + 1e-5), rtol=1e-14)
+    # without eps the result does not depend on the row's scale, and the
+    # normalised row has mean square 1 (weight 1)
+    x = rng(71).standard_normal((2, 7))
+    a, _ = layer.rmsnorm(x, np.ones(7), 0.0)
+    b, _ = layer.rmsnorm(x * 37.5, np.ones(7), 0.0)
+    np.testing.assert_allclose(a, b, rtol=1e-13)
+    np.testing.assert_allclose(np.mean(a * a, axis=1), 1.0, rtol=1e-13)
+
+
+def test_decode_layer_matches_explicit_loops(oracle):
+    # the layer's wiring (split of x|z and of dt_low|B|C, conv window, softplus
+    # of dt + bias, D skip, z gate, residual, slots) against a per-request,
+    # per-channel loop written out here without the oracle's functions
+    from oracle import layer
+
+    r = rng(72)
+    Dm, Di, N, R, W, S, batch = 8, 6, 4, 3, 4, 5, 2
+    w = {"norm_weight": r.uniform(0.5, 1.5, Dm), "in_proj": r.standard_normal((2 * Di, Dm)) * 0.3,
+         "conv_weight": r.uniform(-0.5, 0.5, (Di, W)), "conv_bias": r.uniform(-0.5, 0.5, Di),
+         "x_proj": r.standard_normal((R + 2 * N, Di)) * 0.3,
+         "dt_proj": r.standard_normal((Di, R)) * 0.3, "dt_bias": r.uniform(-3, -1, Di),
+         "A": -r.uniform(0.5, 4.0, (Di, N)), "D": r.uniform(0.5, 1.5, Di),
+         "out_proj": r.standard_normal((Dm, Di)) * 0.3}
+    hidden = r.standard_normal((batch, Dm))
+    cs = r.standard_normal((S, Di, W - 1))
+    ss = r.standard_normal((S, Di, 1, N))
+    idx = np.array([3, 1], dtype=np.int32)
+    out, _, cs_o, ss_o, _ = layer.mamba1_decode_layer(w, hidden, cs, ss, idx, eps=1e-5)
+
+    sig = lambda v: 1.0 / (1.0 + math.exp(-v))
+    want = hidden.copy()
+    cs_w, ss_w = cs.copy(), ss.copy()
+    for b in range(batch):
+        s = idx[b]
+        ms = sum(v * v for v in hidden[b]) / Dm
+        hn = [hidden[b, i] / math.sqrt(ms + 1e-5) * w["norm_weight"][i] for i in range(Dm)]
+        xz = [sum(w["in_proj"][j, i] * hn[i] for i in range(Dm)) for j in range(2 * Di)]
+        u = []
+        for c in range(Di):
+            win = list(cs[s, c]) + [xz[c]]
+            a = w["conv_bias"][c] + sum(w["conv_weight"][c, k] * win[k] for k in range(W))
+            u.append(a * sig(a))
+            cs_w[s, c] = win[1:]
+        dbc = [sum(w["x_proj"][j, c] * u[c] for c in range(Di)) for j in range(R + 2 * N)]
+        y = []
+        for c in range(Di):
+            v = sum(w["dt_proj"][c, k] * dbc[k] for k in range(R)) + w["dt_bias"][c]
+            d = math.log1p(math.exp(v))
+            acc = 0.0
+            for n in range(N):
+                h = math.exp(d * w["A"][c, n]) * ss[s, c, 0, n] + d * dbc[R + n] * u[c]
+                ss_w[s, c, 0, n] = h
+                acc += dbc[R + N + n] * h
+            zc = xz[Di + c]
+            y.append((acc + w["D"][c] * u[c]) * zc * sig(zc))
+        for i in range(Dm):
+            want[b, i] += sum(w["out_proj"][i, c] * y[c] for c in range(Di))
+    np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(cs_o, cs_w, rtol=1e-13, atol=1e-14)  # x is a computed sum
+    np.testing.assert_allclose(ss_o, ss_w, rtol=1e-11, atol=1e-12)

@@ -253,6 +253,56 @@ def varlen_bytes(spec: Spec, lengths, n_init: int) -> dict:
     return {"conv": conv, "scan": scan}
 
 
+def mamba1_layer(d_model=2560, d_inner=5120, d_state=16, dt_rank=160, width=4, batch=245,
+                 nslots=512, io="f16", state="f32", seed=7, device="cpu") -> dict:
+    """Random weights and decode inputs of one Mamba-1 layer (Mamba-2.8B
+    sizes by default): projections ~ N(0, 1/fan_in) in the io dtype, RMSNorm
+    weight ~ U(0.5, 1.5), conv taps and bias ~ U(-1/2, 1/2), dt bias such
+    that softplus(bias) is log-uniform in [1e-3, 1e-1], A[c, n] = -(n+1),
+    D = 1; hidden ~ N(0, 1), caches ~ N(0, 1); slots = the first `batch`
+    entries of a permutation of the cache."""
+    io_t, st_t = DTYPES[io], DTYPES[state]
+    d = _Draw(seed, device)
+
+    def proj(n_out, n_in):
+        return (d.normal((n_out, n_in), torch.float32) / math.sqrt(n_in)).to(io_t)
+
+    w = {
+        "norm_weight": d.uniform((d_model,), 0.5, 1.5),
+        "in_proj": proj(2 * d_inner, d_model),
+        "conv_weight": d.uniform((d_inner, width), -0.5, 0.5),
+        "conv_bias": d.uniform((d_inner,), -0.5, 0.5),
+        "x_proj": proj(dt_rank + 2 * d_state, d_inner),
+        "dt_proj": proj(d_inner, dt_rank),
+    }
+    dtv = torch.exp(d.uniform((d_inner,), math.log(1e-3), math.log(1e-1)))
+    w["dt_bias"] = dtv + torch.log(-torch.expm1(-dtv))  # softplus^-1
+    w["A"] = -torch.arange(1, d_state + 1, dtype=torch.float32, device=d.device).repeat(d_inner, 1)
+    w["D"] = torch.ones(d_inner, dtype=torch.float32, device=d.device)
+    w["out_proj"] = proj(d_model, d_inner)
+    t = {"w": w,
+         "hidden": d.normal((batch, d_model), io_t),
+         "conv_state": d.normal((nslots, d_inner, width - 1), io_t),
+         "ssm_state": d.normal((nslots, d_inner, 1, d_state), st_t),
+         "slot_idx": d.perm(nslots)[:batch].to(torch.int32).contiguous()}
+    return t
+
+
+def layer_bytes(d_model, d_inner, d_state, dt_rank, width, batch, io="f16", state="f32") -> dict:
+    """Bytes one decode layer must move: every weight once, the state and
+    conv window of each request read and written, the hidden rows read and
+    written, and each intermediate written and read once."""
+    isz = {"f32": 4, "f16": 2, "bf16": 2}
+    io_b, st_b = isz[io], isz[state]
+    weights = (2 * d_inner * d_model + (dt_rank + 2 * d_state) * d_inner + d_inner * dt_rank
+               + d_model * d_inner) * io_b + (d_model + d_inner * (width + 3 + d_state)) * 4
+    caches = batch * d_inner * (2 * (width - 1) * io_b + 2 * d_state * st_b)
+    acts = batch * io_b * (2 * d_model + 2 * (d_model + 5 * d_inner + dt_rank + 2 * d_state
+                                              + d_inner))
+    return {"weights": weights, "caches": caches, "activations": acts,
+            "total": weights + caches + acts}
+
+
 def to_f64(a) -> np.ndarray:
     """Exact float64 widening of a stored tensor (any of f32/f16/bf16/ints)."""
     if a is None:
