@@ -10,14 +10,16 @@
 // Kernel: one 256-lane workgroup per (64 output columns, slice of K, 256
 // rows).  Wave w owns rows [64 w, 64 w + 64) of the block and all 64
 // columns: 4 x 4 tiles of v_mfma_f32_16x16x32_{f16,bf16}, float32
-// accumulation.  Both operands are read straight from global memory with
-// 128-bit loads: a lane's A operand is 8 consecutive k of one activation row
-// and its B operand 8 consecutive k of one weight row, which is how both
-// tensors are stored (row-major, k innermost), so no LDS staging is needed;
-// the next k step's loads are issued before the current step's MFMAs.  The
-// weights, the dominant traffic, stream from HBM once per row block (the
-// activations, 2.6 MB at most, stay in L2).  Narrow outputs split K over
-// several workgroups, whose float32 partial sums a second kernel adds.
+// accumulation.  K is walked in batches of 64: each batch's activation tile
+// (256 rows x 64 k) and weight tile (64 rows x 64 k) are loaded once per
+// workgroup with coalesced 128-bit loads (consecutive lanes, consecutive 16
+// bytes of a row) and staged in LDS, from where each wave reads its MFMA
+// operands (8 consecutive k of one row: row-major, k innermost is the operand
+// order).  The next batch's loads are in flight during the current batch's
+// MFMAs.  The weights, the dominant traffic, stream from
+// HBM once per row block (the activations, 2.6 MB at most, stay in L2).
+// Narrow outputs split K over several workgroups, whose float32 partial sums
+// a second kernel adds.
 //
 // Epilogue: output columns go to up to three destinations (column segments,
 // e.g. the x and z halves of in_proj), optionally added to a residual, rows
@@ -74,24 +76,44 @@ __device__ __forceinline__ void gemm_store(const GemmArgs &a, int row, int col, 
 template <typename T>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
+    // one k batch of both operands in LDS: the activation tile (GM rows) and
+    // the weight tile (GN rows), KBK k each, row stride padded by 16 B
+    constexpr int KB = 2;            // MFMA k-steps per batch
+    constexpr int KBK = KB * GK;     // k per batch
+    constexpr int LDK = KBK + 8;     // elements per LDS row
+    constexpr int CPR = KBK / 8;     // 16-byte chunks per row
+    constexpr int ACH = GM * CPR / 256, WCH = GN * CPR / 256;  // chunks per thread
+    __shared__ __align__(16) T s_a[GM * LDK];
+    __shared__ __align__(16) T s_w[GN * LDK];
+
     const int nb = blockIdx.x, ks = blockIdx.y, mb = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int l16 = l & 15, lq = l >> 4;
     const int K = a.K;
-    const int nsteps = (K + GK - 1) / GK;
-    const int s0 = (int)((int64_t)nsteps * ks / a.splits), s1 = (int)((int64_t)nsteps * (ks + 1) / a.splits);
+    const int nbatch = (K + KBK - 1) / KBK;
+    const int b0 = (int)((int64_t)nbatch * ks / a.splits), b1 = (int)((int64_t)nbatch * (ks + 1) / a.splits);
 
-    // operand rows: activations (clamped to the last row; never stored) and
-    // weights (clamped to the last column)
-    const T *arow[4];
-    const T *wrow[4];
+    // chunk c = tid + 256 q of a tile: row c / CPR, k offset 8 (c % CPR);
+    // consecutive threads read consecutive 16 B of a row
+    const T *asrc[ACH];
+    const T *wsrc[WCH];
+    int adst[ACH], wdst[WCH];
+    const int kofs = 8 * (tid % CPR);  // the same for every chunk of this thread
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = min(mb * GM + 64 * w + 16 * i + l16, a.M - 1);
-        const int n = min(nb * GN + 16 * i + l16, a.N - 1);
-        arow[i] = static_cast<const T *>(a.A) + (int64_t)m * a.lda;
-        wrow[i] = static_cast<const T *>(a.W) + (int64_t)n * K;
+    for (int q = 0; q < ACH; ++q) {
+        const int c = tid + 256 * q, r = c / CPR;
+        const int m = min(mb * GM + r, a.M - 1);  // clamped rows are never stored
+        asrc[q] = static_cast<const T *>(a.A) + (int64_t)m * a.lda + kofs;
+        adst[q] = r * LDK + kofs;
     }
+#pragma unroll
+    for (int q = 0; q < WCH; ++q) {
+        const int c = tid + 256 * q, r = c / CPR;
+        const int n = min(nb * GN + r, a.N - 1);
+        wsrc[q] = static_cast<const T *>(a.W) + (int64_t)n * K + kofs;
+        wdst[q] = r * LDK + kofs;
+    }
+
     f32x4_g acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -99,47 +121,56 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_g{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Loads go out in batches of GB k-steps, one batch ahead of the MFMAs
-    // that use them (the L2 latency is several times one step's MFMA time).
-    // K % 8 == 0: a lane's 8 k are all in or all out.
-    constexpr int GB = 2;
-    auto load = [&](int step, u32x4 (&av)[GB][4], u32x4 (&wv)[GB][4]) {
+    // K % 8 == 0: an 8-element chunk is all in or all out; out of range it
+    // is loaded from the row's first chunk (in bounds) and zeroed
+    u32x4 ar[ACH], wr[WCH];
+    auto load = [&](int batch) {
+        const int k = batch * KBK + kofs;
+        const bool ok = k < K;
+        const int off = ok ? batch * KBK : -kofs;
 #pragma unroll
-        for (int q = 0; q < GB; ++q) {
-            const int k = (step + q) * GK + 8 * lq;
-            const bool ok = step + q < s1 && k < K;
-            const int kc = ok ? k : 0;
+        for (int q = 0; q < ACH; ++q) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(asrc[q] + off);
+            ar[q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                av[q][i] = *reinterpret_cast<const u32x4 *>(arow[i] + kc);
-                wv[q][i] = *reinterpret_cast<const u32x4 *>(wrow[i] + kc);
-                if (!ok) {
-                    av[q][i] = u32x4{0u, 0u, 0u, 0u};
-                    wv[q][i] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
+        for (int q = 0; q < WCH; ++q) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(wsrc[q] + off);
+            wr[q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    u32x4 av[GB][4], wv[GB][4], an[GB][4], wn[GB][4];
-    if (s0 < s1)
-        load(s0, av, wv);
-    for (int st = s0; st < s1; st += GB) {
-        if (st + GB < s1)
-            load(st + GB, an, wn);
+    auto stage = [&]() {
 #pragma unroll
-        for (int q = 0; q < GB; ++q)
+        for (int q = 0; q < ACH; ++q)
+            *reinterpret_cast<u32x4 *>(&s_a[adst[q]]) = ar[q];
+#pragma unroll
+        for (int q = 0; q < WCH; ++q)
+            *reinterpret_cast<u32x4 *>(&s_w[wdst[q]]) = wr[q];
+    };
+
+    if (b0 < b1)
+        load(b0);
+    for (int bt = b0; bt < b1; ++bt) {
+        stage();
+        __syncthreads();
+        if (bt + 1 < b1)
+            load(bt + 1);  // in flight during this batch's MFMAs
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+            u32x4 av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                av[i] = *reinterpret_cast<const u32x4 *>(&s_a[(64 * w + 16 * i + l16) * LDK + q * GK + 8 * lq]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bv[j] = *reinterpret_cast<const u32x4 *>(&s_w[(16 * j + l16) * LDK + q * GK + 8 * lq]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = Mfma<T>::run(av[q][i], wv[q][j], acc[i][j]);
-#pragma unroll
-        for (int q = 0; q < GB; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                av[q][i] = an[q][i];
-                wv[q][i] = wn[q][i];
-            }
+                    acc[i][j] = Mfma<T>::run(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();  // the tiles are restaged next batch
     }
 
     // acc[i][j][e]: row mb*GM + 64 w + 16 i + 4 lq + e, column nb*GN + 16 j + l16

@@ -16,17 +16,16 @@ size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 int status_of(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
 
 // K split so that a narrow output still spreads over the chip: up to 32
-// slices of at least 2 k-steps (4 for long K), aiming at ~512 workgroups.
+// slices of at least 2 k batches, aiming at ~512 workgroups.
 int choose_splits(int M, int N, int K)
 {
-    const int nsteps = (K + 31) / 32;
+    const int nsteps = (K + 63) / 64;  // 64-k batches of the projection kernel
     const int64_t blocks = (int64_t)((N + 63) / 64) * ((M + 255) / 256);
     int s = (int)(512 / (blocks > 0 ? blocks : 1));
     if (s > 32)
         s = 32;
-    const int min_steps = nsteps > 16 ? 4 : 2;
-    if (s > nsteps / min_steps)
-        s = nsteps / min_steps;
+    if (s > nsteps / 2)
+        s = nsteps / 2;
     return s < 1 ? 1 : s;
 }
 
