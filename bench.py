@@ -35,6 +35,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 # fp32 vector FMA rate without packed-FP32 forms: 256 CUs x 4 SIMDs x 16 lanes
 # x 2 flop x 2.4 GHz (the published 157.3 TFLOP/s counts packed FP32)
 VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix rate, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "state_update": ["ssu.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
@@ -42,7 +43,10 @@ KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp", "ssm_kernels.
                   "conv1d_prefill": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "conv1d_decode": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "conv1d_varlen": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
-                  "selective_scan_varlen": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"]}
+                  "selective_scan_varlen": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "chunked_scan": ["ssd.hip", "ssm_kernels.hpp"],
+                  "layer_decode": ["gemm.hip", "layer.hip", "conv1d.hip", "ssu.hip", "ssm_device.hpp",
+                                   "ssm_kernels.hpp"]}
 # rocprofv3 kernel names of each kernel in the benchmarked configuration
 KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "decode_step": "ssu_kernel",
                   "conv1d_prefill": "conv_prefill_kernel"}
@@ -65,7 +69,10 @@ def parse():
                    help="skip the packed variable-length prefill measurement")
     p.add_argument("--no-layer", action="store_true",
                    help="skip the whole decode-layer measurement")
-    p.add_argument("--only", choices=["prefill", "decode", "varlen", "layer"], default=None,
+    p.add_argument("--no-chunked", action="store_true",
+                   help="skip the chunked Mamba-2 prefill measurement")
+    p.add_argument("--only", choices=["prefill", "decode", "varlen", "layer", "chunked"],
+                   default=None,
                    help="run only one half of the step (for profiling)")
     p.add_argument("--unfused-decode", action="store_true",
                    help="decode with the separate conv-update and state-update calls instead "
@@ -86,7 +93,7 @@ def profile_commands(out):
     stats, then one counter per pass (FETCH_SIZE, WRITE_SIZE) on the step and
     on a plain 1 GiB device copy (the calibration), and the SQ counters of the
     prefill half."""
-    b = "python -u bench.py --no-cpu-baseline --no-varlen --no-layer"
+    b = "python -u bench.py --no-cpu-baseline --no-varlen --no-layer --no-chunked"
     pmc = "timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d {o}/{n} -o run -- {cmd}"
     return [
         ("trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d {out}/trace "
@@ -102,7 +109,36 @@ def profile_commands(out):
         ("varlen_trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d "
                          f"{out}/varlen_trace -o run -- python -u bench.py --only varlen "
                          f"--steps 20 --warmup 5"),
+        ("layer_trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d "
+                        f"{out}/layer_trace -o run -- python -u bench.py --only layer "
+                        f"--steps 20 --warmup 5"),
+        ("chunked_trace", f"timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d "
+                          f"{out}/chunked_trace -o run -- python -u bench.py --only chunked "
+                          f"--steps 20 --warmup 5"),
     ]
+
+
+def _trace_table(stats, symbols):
+    """Rows (symbol, calls, avg, min, max us) of a kernel_stats.csv, pooled
+    over the instantiations whose name contains each symbol."""
+    rows = []
+    for sym, excl in symbols:
+        rs = [r for r in stats if sym in r["Name"] and not (excl and excl in r["Name"])]
+        calls = sum(int(r["Calls"]) for r in rs)
+        if calls:
+            tot = sum(float(r["TotalDurationNs"]) for r in rs)
+            rows.append(f"| {sym} | {calls} | {tot / calls / 1e3:.1f} | "
+                        f"{min(float(r['MinNs']) for r in rs) / 1e3:.1f} | "
+                        f"{max(float(r['MaxNs']) for r in rs) / 1e3:.1f} |")
+    return rows
+
+
+def _json_field(log, key):
+    with open(log) as f:
+        for ln in f:
+            if ln.startswith("{") and key in ln:
+                return json.loads(ln)[key]
+    return {}
 
 
 def _read_counters(path):
@@ -236,6 +272,35 @@ def summarize_profile(out):
         f.write("\n".join(vl) + "\n")
     print("\n".join(vl))
 
+    # whole decode layer and chunked Mamba-2 prefill: their own traced runs
+    for name, key, title, fname, syms in (
+            ("layer_trace", "layer_decode", "whole Mamba-1 2.8B decode layer", "mamba1_decode_layer_kernels.md",
+             [("rmsnorm_kernel", None), ("gemm_kernel", None), ("gemm_reduce_kernel", None),
+              ("conv_decode", None), ("ssu_kernel", None)]),
+            ("chunked_trace", "chunked_prefill", "chunked Mamba-2 prefill on MFMA",
+             "mamba2_chunked_prefill_kernels.md", [("ssd_kernel", None)])):
+        st = list(csv.DictReader(open(glob.glob(f"{out}/{name}/*kernel_stats.csv")[0])))
+        rec = _json_field(f"{out}/{name}.log", key)
+        ml = [f"# Kernel trace: {title}", "", f"Workload: {rec.get('workload')}.", "",
+              "Command (run from the repository root on the MI355X):", "", f"    {cmds[name]}", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        ml += _trace_table(st, syms)
+        # every library kernel in the run, by name (the rest set up inputs)
+        ml += ["", "All library kernels of the run (name, calls, avg us):", ""]
+        for r in sorted(st, key=lambda r: -float(r["TotalDurationNs"])):
+            if "ssm" not in r["Name"]:
+                continue
+            ml.append(f"- `{r['Name'][:120]}`: {r['Calls']}, {float(r['AverageNs']) / 1e3:.1f}")
+        if rec:
+            ml += ["", f"Event-timed in the same run: {rec['us']:.1f} us per call"
+                       + (f", {rec['tokens_per_s'] / 1e6:.2f} M tokens/s" if "tokens_per_s" in rec else "")
+                       + (f", {rec['GBps']:.0f} GB/s of algorithmic traffic" if "GBps" in rec else "")
+                       + (f", {rec['mfma_TFLOPs']:.0f} TFLOP/s of algorithmic MFMA work"
+                          if "mfma_TFLOPs" in rec else "") + "."]
+        with open(os.path.join(PROFILES, fname), "w") as f:
+            f.write("\n".join(ml) + "\n")
+        print("\n".join(ml))
+
 
 def kernel_source_sha(names):
     h = hashlib.sha256()
@@ -315,6 +380,10 @@ def main():
     if args.only == "layer":
         print(json.dumps({"layer_decode": measure_layer(ssm, W, dev, stream, args.steps,
                                                         args.warmup)}), flush=True)
+        return
+    if args.only == "chunked":
+        print(json.dumps({"chunked_prefill": measure_chunked(ssm, W, dev, stream, args.steps,
+                                                             args.warmup)}), flush=True)
         return
     if args.only == "varlen":
         print(json.dumps({"varlen_prefill": measure_varlen(ssm, W, dev, stream, args.steps,
@@ -459,6 +528,10 @@ def main():
     if not args.no_layer and args.only is None:
         layer = measure_layer(ssm, W, dev, stream, max(args.steps // 2, 5), 3)
 
+    chunked = None
+    if not args.no_chunked and args.only is None:
+        chunked = measure_chunked(ssm, W, dev, stream, max(args.steps // 2, 5), 3)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds, pspec, dspec)
@@ -496,6 +569,7 @@ def main():
         "cpu_baseline": cpu,
         "varlen_prefill": varlen,
         "layer_decode": layer,
+        "chunked_prefill": chunked,
         "step_ms_median": float(np.median(step_ms)),
         "wall_s_timed": t_wall,
         "device": props.name,
@@ -607,6 +681,50 @@ def measure_layer(ssm, W, dev, stream, steps, warmup):
             "us": mean, "us_median": float(np.median(us)), "tokens_per_s": 245 / (mean * 1e-6),
             "bytes": b["total"], "GBps": b["total"] / (mean * 1e-6) / 1e9,
             "model_tokens_per_s_64_layers": 245 / (64 * mean * 1e-6), "steps": steps}
+
+
+def measure_chunked(ssm, W, dev, stream, steps, warmup):
+    """Mamba-2 prefill in the chunked matrix form (the library's choice for
+    bf16 I/O): 2 requests x L 4096, 64 heads of headdim 128, dstate 256,
+    bf16 I/O, f32 state written to a 1024-slot cache; two rotating buffer
+    sets, timed with events on the launch stream."""
+    import numpy as np
+    import torch
+
+    spec = W.m2_prefill(state="f32")
+    sets = []
+    for k in range(2):
+        t = W.make(W.m2_prefill(state="f32", seed=spec.seed + 100 * k), dev)
+        t["out"] = torch.empty_like(t["x"])
+        sets.append(t)
+
+    def run(i):
+        t = sets[i % 2]
+        ssm.selective_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           dt_bias=t["dt_bias"], ssm_state=t["ssm_state"], slot_idx=t["slot_idx"],
+                           out=t["out"], stream=stream)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e3
+    mean = float(us.mean())
+    b = W.algorithmic_bytes(spec)["scan"]
+    fl = W.chunked_mfma_flops(spec)
+    return {"workload": "Mamba-2 prefill, 2 requests x L 4096, 64 heads, headdim 128, dstate 256, "
+                        "1 group, bf16 I/O, f32 state to a 1024-slot cache, chunks of 64",
+            "us": mean, "us_median": float(np.median(us)),
+            "tokens_per_s": spec.batch * spec.seqlen / (mean * 1e-6),
+            "bytes": b, "GBps": b / (mean * 1e-6) / 1e9,
+            "mfma_flops": fl, "mfma_TFLOPs": fl / (mean * 1e-6) / 1e12,
+            "mfma_frac_bf16_peak": fl / (mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "kernel_source_sha": kernel_source_sha(KERNEL_SOURCES["chunked_scan"]), "steps": steps}
 
 
 VARLEN_NSEQ, VARLEN_TOKENS, VARLEN_SEED = 16, 8192, 5

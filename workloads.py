@@ -361,3 +361,17 @@ def algorithmic_flops(spec: Spec) -> float:
     if not spec.a_per_state:
         flops += Bt * H * L * 2
     return float(flops)
+
+
+def chunked_mfma_flops(spec: Spec, chunk: int = 64) -> float:
+    """Dense matrix work of the chunked (SSD) form of a Mamba-2 prefill, per
+    (request, head, chunk of Q steps): C B^T (Q x Q x N), its masked product
+    with X (Q x Q x P), the readout of the carried state C h (Q x N x P) and
+    the state update B^T X (N x Q x P), two flops per multiply-add.  Counts
+    full Q x Q products (no saving from the causal mask) and operands at
+    their own precision (no split-operand passes)."""
+    Bt, L, H, P, N = spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate
+    Q = chunk
+    nchunks = (L + Q - 1) // Q
+    per = 2 * Q * (Q * N + Q * P + 2 * N * P)
+    return float(Bt * H * nchunks * per)
