@@ -54,14 +54,12 @@ template <> struct Mfma<bf16> {
 };
 } // namespace
 
-// value of output (row, col) to its destination
+// value of output (row, col) to its destination (the general path)
 template <typename T>
 __device__ __forceinline__ void gemm_store(const GemmArgs &a, int row, int col, float v)
 {
-    if (row >= a.M || col >= a.N)
+    if (col >= a.N)
         return;
-    if (a.row_slot && a.row_slot[row] < 0)
-        return;  // padded request
 #pragma unroll
     for (int sgi = 0; sgi < 3; ++sgi) {
         if (sgi < a.nseg && col >= a.seg[sgi].col0 && col < a.seg[sgi].col0 + a.seg[sgi].ncols) {
@@ -71,6 +69,45 @@ __device__ __forceinline__ void gemm_store(const GemmArgs &a, int row, int col, 
             *dst = from_f32<T>(v);
         }
     }
+}
+
+// outputs (row, col .. col + 3) to their destination: one 8-byte store (and
+// one 8-byte residual load) when the four columns share a segment and the
+// addresses are aligned, else element by element.  Rows of padded requests
+// are left untouched.
+template <typename T>
+__device__ __forceinline__ void gemm_store4(const GemmArgs &a, int row, int col, f32x4_g v)
+{
+    if (row >= a.M || col >= a.N)
+        return;
+    if (a.row_slot && a.row_slot[row] < 0)
+        return;
+#pragma unroll
+    for (int sgi = 0; sgi < 3; ++sgi) {
+        const GemmSeg &sg = a.seg[sgi];
+        if (sgi < a.nseg && col >= sg.col0 && col + 3 < sg.col0 + sg.ncols) {
+            T *dst = static_cast<T *>(sg.ptr) + (int64_t)row * sg.ld + (col - sg.col0);
+            const T *res = a.residual ? static_cast<const T *>(a.residual) + (int64_t)row * a.ld_residual + col
+                                      : nullptr;
+            if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(res)) & 7) == 0) {
+                float x[4] = {v[0], v[1], v[2], v[3]};
+                if (res) {
+                    const uint2 r = *reinterpret_cast<const uint2 *>(res);
+                    float rf[4];
+                    unpack_word(r.x, rf, T{});
+                    unpack_word(r.y, rf + 2, T{});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x[e] += rf[e];
+                }
+                *reinterpret_cast<uint2 *>(dst) = uint2{pack_word(x, T{}), pack_word(x + 2, T{})};
+                return;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        gemm_store<T>(a, row, col + e, v[e]);
 }
 
 template <typename T>
@@ -122,30 +159,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             acc[i][j] = f32x4_g{0.0f, 0.0f, 0.0f, 0.0f};
 
     // K % 8 == 0: an 8-element chunk is all in or all out; out of range it
-    // is loaded from the row's first chunk (in bounds) and zeroed
+    // is loaded from the row's first chunk (in bounds) and zeroed when it is
+    // staged.  Zeroing at staging time, not right after the load, keeps the
+    // loads in flight during the MFMAs of the batch before.
     u32x4 ar[ACH], wr[WCH];
+    bool in_range = true;
     auto load = [&](int batch) {
-        const int k = batch * KBK + kofs;
-        const bool ok = k < K;
-        const int off = ok ? batch * KBK : -kofs;
-#pragma unroll
-        for (int q = 0; q < ACH; ++q) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(asrc[q] + off);
-            ar[q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int q = 0; q < WCH; ++q) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(wsrc[q] + off);
-            wr[q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto stage = [&]() {
+        in_range = batch * KBK + kofs < K;
+        const int off = in_range ? batch * KBK : -kofs;
 #pragma unroll
         for (int q = 0; q < ACH; ++q)
-            *reinterpret_cast<u32x4 *>(&s_a[adst[q]]) = ar[q];
+            ar[q] = *reinterpret_cast<const u32x4 *>(asrc[q] + off);
 #pragma unroll
         for (int q = 0; q < WCH; ++q)
-            *reinterpret_cast<u32x4 *>(&s_w[wdst[q]]) = wr[q];
+            wr[q] = *reinterpret_cast<const u32x4 *>(wsrc[q] + off);
+    };
+    auto stage = [&]() {
+        const u32x4 zero{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < ACH; ++q)
+            *reinterpret_cast<u32x4 *>(&s_a[adst[q]]) = in_range ? ar[q] : zero;
+#pragma unroll
+        for (int q = 0; q < WCH; ++q)
+            *reinterpret_cast<u32x4 *>(&s_w[wdst[q]]) = in_range ? wr[q] : zero;
     };
 
     if (b0 < b1)
@@ -168,52 +204,78 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = Mfma<T>::run(av[i], bv[j], acc[i][j]);
+                    acc[i][j] = Mfma<T>::run(bv[j], av[i], acc[i][j]);
         }
         __syncthreads();  // the tiles are restaged next batch
     }
 
-    // acc[i][j][e]: row mb*GM + 64 w + 16 i + 4 lq + e, column nb*GN + 16 j + l16
+    // The products are taken as W . act^T, so acc[i][j][e] is output row
+    // mb*GM + 64 w + 16 i + l16, column nb*GN + 16 j + 4 lq + e: each lane
+    // holds four consecutive columns of one row.
+    const int col0 = nb * GN + 4 * lq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int row = mb * GM + 64 * w + 16 * i + l16;
+        if (a.splits == 1) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
+                gemm_store4<T>(a, row, col0 + 16 * j, acc[i][j]);
+        } else if (row < a.M) {
+            // float32 partials, row-major per split: 16-byte stores when N
+            // keeps them aligned
+            float *prow = a.partial + ((int64_t)ks * a.M + row) * a.N;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = mb * GM + 64 * w + 16 * i + 4 * lq + e;
-                const int col = nb * GN + 16 * j + l16;
-                if (a.splits == 1) {
-                    gemm_store<T>(a, row, col, acc[i][j][e]);
-                } else if (row < a.M && col < a.N) {
-                    a.partial[((int64_t)ks * a.M + row) * a.N + col] = acc[i][j][e];
+            for (int j = 0; j < 4; ++j) {
+                const int col = col0 + 16 * j;
+                if ((a.N & 3) == 0 && col < a.N) {
+                    *reinterpret_cast<f32x4_g *>(prow + col) = acc[i][j];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < a.N)
+                            prow[col + e] = acc[i][j][e];
                 }
             }
+        }
+    }
 }
 
-// sum of the split-K partials, then the epilogue
+// sum of the split-K partials, then the epilogue: each thread takes four
+// consecutive columns of one row (N is padded to a multiple of 4 in the
+// indexing; columns past N are not read)
 template <typename T>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)a.M * a.N)
+    const int nq = (a.N + 3) >> 2;  // column quads per row
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)a.M * nq)
         return;
-    const int row = (int)(i / a.N), col = (int)(i % a.N);
+    const int row = (int)(q / nq), col = 4 * (int)(q % nq);
     const int64_t stride = (int64_t)a.M * a.N;
-    // the partials' loads are independent: issue them in groups of 8
-    float v = 0.0f;
-    int s = 0;
-    for (; s + 8 <= a.splits; s += 8) {
-        float p[8];
+    const float *p = a.partial + (int64_t)row * a.N + col;
+    f32x4_g v{0.0f, 0.0f, 0.0f, 0.0f};
+    if ((a.N & 3) == 0) {
+        // the partials' loads are independent: issue them in groups of 4
+        int s = 0;
+        for (; s + 4 <= a.splits; s += 4) {
+            f32x4_g t[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            p[q] = a.partial[(s + q) * stride + i];
+            for (int u = 0; u < 4; ++u)
+                t[u] = *reinterpret_cast<const f32x4_g *>(p + (s + u) * stride);
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            v += p[q];
+            for (int u = 0; u < 4; ++u)
+                v += t[u];
+        }
+        for (; s < a.splits; ++s)
+            v += *reinterpret_cast<const f32x4_g *>(p + s * stride);
+    } else {
+        for (int s = 0; s < a.splits; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (col + e < a.N)
+                    v[e] += p[s * stride + e];
     }
-    for (; s < a.splits; ++s)
-        v += a.partial[s * stride + i];
-    gemm_store<T>(a, row, col, v);
+    gemm_store4<T>(a, row, col, v);
 }
 
 template <typename T>
@@ -222,7 +284,7 @@ static hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t stream)
     const dim3 grid((unsigned)((a.N + GN - 1) / GN), (unsigned)a.splits, (unsigned)((a.M + GM - 1) / GM));
     hipLaunchKernelGGL((gemm_kernel<T>), grid, dim3(256), 0, stream, a);
     if (a.splits > 1) {
-        const int64_t n = (int64_t)a.M * a.N;
+        const int64_t n = (int64_t)a.M * ((a.N + 3) / 4);
         hipLaunchKernelGGL((gemm_reduce_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
     }
     return hipGetLastError();

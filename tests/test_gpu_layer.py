@@ -42,6 +42,8 @@ LINEAR_CASES = [
     (245, 5120, 160, torch.bfloat16, False),
     (300, 130, 264, torch.float16, True),     # two row blocks, ragged N
     (245, 2560, 5120, torch.bfloat16, True),  # out_proj shape, split over K
+    (33, 70, 24, torch.float16, True),        # N % 4 != 0, K not split: stores in the reduce pass
+    (300, 128, 64, torch.bfloat16, True),     # two row blocks, outputs stored by the main kernel
 ]
 
 
@@ -59,6 +61,27 @@ def test_linear_parity(dev, ssm, M, N, K, dt, res):
     torch.cuda.synchronize()
     o, s = layer.linear(f(x), f(w), residual=None if r is None else f(r))
     check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", f"linear {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_linear_unaligned_output(dev, ssm, dt):
+    """An output (and residual) only 2-byte aligned: the main kernel's stores
+    fall back from 8-byte to element stores."""
+    from oracle import layer
+
+    M, N, K = 40, 96, 136
+    g = torch.Generator(device=dev).manual_seed(11)
+    x = torch.randn(M, K, generator=g, device=dev).to(dt)
+    w = (torch.randn(N, K, generator=g, device=dev) / K ** 0.5).to(dt)
+    rbuf = torch.randn(M * N + 1, generator=g, device=dev).to(dt)
+    r = rbuf[1:].view(M, N)
+    obuf = torch.zeros(M * N + 1, device=dev, dtype=dt)
+    out = obuf[1:].view(M, N)
+    ssm.linear(x, w, residual=r, out=out)
+    torch.cuda.synchronize()
+    assert obuf[0].item() == 0.0
+    o, s = layer.linear(f(x), f(w), residual=f(r))
+    check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", "linear unaligned")
 
 
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
