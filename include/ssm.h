@@ -183,14 +183,18 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x,
  * tunes the update's launch configuration per device over a grid of
  * effective batches (batch x nheads) for each (headdim, dstate, dtype) key and
  * keeps a tuned entry only where it beats the heuristic.  Here the
- * geometry is the number of consecutive states each lane owns (8 or 16) and
- * the workgroup size (64, 128, 256 or 512 lanes); the library carries a table
- * tuned on gfx950 and falls back to a heuristic for other shapes: 32 bytes of
- * state per lane (16 states of a 2-byte cache for rows of >= 32 states that
- * are a multiple of 16, else 8) in 256-lane workgroups.
+ * geometry is the number of consecutive states each lane owns (4, 8 or 16;
+ * 4 only for a 4-byte cache, and a row of dstate states must span at most 64
+ * lanes) and the workgroup size (64, 128, 256 or 512 lanes); the library
+ * carries a table tuned on gfx950 and falls back to a heuristic for other
+ * shapes: 32 bytes of state per lane (16 states of a 2-byte cache for rows of
+ * >= 32 states that are a multiple of 16, else 8) in 256-lane workgroups.
+ * Independently of the geometry, with one channel per head (headdim 1) and
+ * at least 8 requests each lane updates its states for two requests in
+ * turn.
  */
 typedef struct ssm_launch_config {
-    int states_per_lane; /* 8 or 16                */
+    int states_per_lane; /* 4, 8 or 16             */
     int block_threads;   /* 64, 128, 256 or 512    */
 } ssm_launch_config;
 

@@ -89,7 +89,7 @@ struct SsuArgs {
     int io_dtype, state_dtype;
     int a_per_state, dt_softplus;
     int vec;                         // dstate % 8 == 0 and 16-byte aligned bases
-    int wave_per_request;            // every wave's rows belong to one request
+    int requests_per_lane;           // 1, 2 or 4 requests taken in turn by each lane
     // fused decode step (conv update in front of the state update); width 0 = none
     void *conv_state;                // [nslots, nheads*headdim, width-1], io dtype
     const float *conv_weight;        // [nheads*headdim, width]

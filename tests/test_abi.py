@@ -163,9 +163,13 @@ def ssu_ex(lib, cfg, **kw):
                                    c, None)
 
 
-@pytest.mark.parametrize("cfg", [(4, 256), (32, 256), (8, 32), (16, 1024), (8, 96), (0, 0)])
-def test_state_update_ex_rejects_bad_geometry(lib, cfg):
-    assert ssu_ex(lib, cfg) == SHAPE
+@pytest.mark.parametrize("cfg,kw", [
+    ((4, 256), dict(sd=1)),    # 4 states per lane only for a 4-byte cache
+    ((4, 256), dict(N=512)),   # a row of 128 lanes would not fit in a wave
+    ((32, 256), {}), ((8, 32), {}), ((16, 1024), {}), ((8, 96), {}), ((0, 0), {}),
+])
+def test_state_update_ex_rejects_bad_geometry(lib, cfg, kw):
+    assert ssu_ex(lib, cfg, **kw) == SHAPE
 
 
 def test_state_update_ex_validates_like_the_plain_call(lib):

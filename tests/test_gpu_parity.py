@@ -195,6 +195,14 @@ SSU_CASES = [
                         nslots=20, random_slots=True, index_sensitive=True), dict(pad=3)),
     ("m1_N16_f16", dict(seqlen=1, nheads=64, dstate=16, io="f16", state="f16", batch=5,
                         nslots=6, random_slots=True, index_sensitive=True), {}),
+    # batch >= 8 with one channel per head: two requests per lane, an odd
+    # batch leaving the last lane's second request empty, padded requests
+    ("m1_N16_f32_two_per_lane", dict(seqlen=1, nheads=96, dstate=16, io="f16", state="f32",
+                                     batch=9, nslots=24, random_slots=True,
+                                     index_sensitive=True), dict(pad=4)),
+    ("m1_N16_bf16_two_per_lane", dict(seqlen=1, nheads=64, dstate=16, io="bf16", state="bf16",
+                                      batch=8, nslots=8, random_slots=True,
+                                      index_sensitive=True), {}),
     ("m2_hd64_N128_f16", dict(seqlen=1, nheads=80, headdim=64, dstate=128, io="f16", state="f16",
                               a_per_state=False, batch=3, index_sensitive=True), {}),
     ("m2_hd64_N128_G8_f32", dict(seqlen=1, nheads=80, headdim=64, dstate=128, ngroups=8, io="f16",
@@ -379,6 +387,9 @@ DECODE_CASES = [
                              nslots=20, random_slots=True, index_sensitive=True), dict(pad=3)),
     ("m1_bf16_bf16state", dict(seqlen=1, nheads=64, dstate=16, io="bf16", state="bf16", batch=5,
                                nslots=6, random_slots=True, index_sensitive=True), {}),
+    # two requests per lane (batch >= 8), odd batch, padded requests
+    ("m1_f16_two_per_lane", dict(seqlen=1, nheads=160, dstate=16, io="f16", state="f32", batch=11,
+                                 nslots=30, random_slots=True, index_sensitive=True), dict(pad=3)),
     ("m1_f32_noz_noD", dict(seqlen=1, nheads=40, dstate=16, io="f32", state="f32", batch=3,
                             index_sensitive=True), dict(z=False, D=False, bias=False)),
     ("m2_hd64_N128_G8", dict(seqlen=1, nheads=16, headdim=64, dstate=128, ngroups=8, io="f16",
@@ -489,7 +500,7 @@ def test_state_update_every_geometry(dev, ssm, oracle, label, kw):
                                         f(t["C"]), D=f(t["D"]), z=f(t["z"]),
                                         dt_bias=f(t["dt_bias"]), slot_idx=idx_np)
     first = None
-    for v in (8, 16):
+    for v in ((4, 8, 16) if spec.state == "f32" and spec.dstate <= 256 else (8, 16)):
         for b in (64, 128, 256, 512):
             state = st0.clone()
             out = ssm.state_update(state, t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"],
