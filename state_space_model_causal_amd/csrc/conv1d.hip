@@ -8,12 +8,13 @@
 //     out[b,c,t] = silu(bias[c] + sum_{k<W} w[c,k] * xh[b,c,t-W+1+k])
 // where xh is x preceded by the cached history (or zeros).
 //
-// Dense prefill kernel: one 256-lane workgroup per (b, c) row walks the row
-// in tiles of 256*E samples (E = one 128-bit load per lane).  The tile plus
-// its W-1 history is staged in LDS so each lane reads its neighbours' samples
-// without re-fetching them from memory; the history of the next tile is kept
-// in LDS, and the row's final W-1 samples go to the cache at the end.  HBM
-// traffic: x read once, out written once.
+// Dense prefill, 16-byte aligned rows (the common case): two rows per
+// 256-lane workgroup, each lane one 128-bit chunk of each row per tile plus
+// the few samples in front of it, no LDS and no barriers (conv_rows_kernel).
+// Other dense rows: one workgroup per (b, c) row walks the row in tiles of
+// 256*E samples staged in LDS with their W-1 history (conv_prefill_kernel).
+// Either way HBM traffic is x read once, out written once, and the row's
+// final W-1 samples go to the cache at the end.
 //
 // Packed variable-length batches (sequences of different lengths side by side
 // along time, each with its own slot and initial-state flag) use a row-tiled
@@ -22,10 +23,13 @@
 //
 // Decode kernels (seqlen == 1): gather the window from the slot, one output,
 // shift the window by one in place.  The vector kernel gives each lane 8
-// channels with 128-bit accesses; the scalar kernel (any channel count or
-// alignment) gives each lane one channel.
+// channels of two requests with 128-bit accesses (the taps loaded once for
+// both); the scalar kernel (any channel count or alignment) gives each lane
+// one channel.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
+
+#include <type_traits>
 
 namespace ssm {
 
@@ -101,6 +105,115 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
     __syncthreads();
     if (cs && tid < H)
         cs[tid] = from_f32<T>(hist[tid]);  // exact: the values came from T
+}
+
+// Dense prefill with 16-byte aligned rows (seqlen % 8 == 0): no LDS and no
+// barriers.  A workgroup takes RPW rows; per tile, each lane takes E samples
+// of each of its rows (one 128-bit load per row, all issued before any
+// arithmetic, so RPW loads are in flight per lane) and, for the taps that
+// reach in front of them, the 4 samples before (an 8- or 16-byte load of its
+// neighbour's samples, already in cache).  The first chunk of a row takes
+// the row's history instead (the slot's cache or zeros).  Lane 0 reads the
+// histories before its first chunk and writes the rows' new tails after the
+// walk, so the two accesses to a cache slot are ordered within one lane.
+template <typename T, int W, int RPW>
+__global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
+{
+    constexpr int E = 16 / StorageSize<T>::value;  // samples per 128-bit access
+    constexpr int H = W - 1;
+    constexpr int PW = 4;                           // samples loaded in front of a chunk (>= H)
+    constexpr int PB = PW * StorageSize<T>::value;  // their bytes: 8 or 16
+    using Prev = typename std::conditional<PB == 16, u32x4, uint2>::type;
+    const int64_t nrows = (int64_t)a.batch * a.channels;
+    const int64_t row0 = (int64_t)xcd_block_order(blockIdx.x, gridDim.x) * RPW;
+    const int tid = threadIdx.x, L = a.seqlen;
+
+    float w[RPW][W], bias[RPW], hist[RPW][PW];
+    bool live[RPW];
+    const T *xr[RPW];
+    T *orow[RPW];
+    T *cs[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int64_t row = row0 + r;  // b*channels + c, uniform over the workgroup
+        const int64_t rr = row < nrows ? row : 0;
+        const int b = (int)(rr / a.channels), c = (int)(rr % a.channels);
+        const int slot = a.slot_idx ? a.slot_idx[b] : b;
+        live[r] = row < nrows && slot >= 0;  // padded request: untouched
+#pragma unroll
+        for (int k = 0; k < W; ++k)
+            w[r][k] = a.weight[(int64_t)c * W + k];
+        bias[r] = a.bias ? a.bias[c] : 0.0f;
+        xr[r] = static_cast<const T *>(a.x) + rr * L;
+        orow[r] = static_cast<T *>(a.out) + rr * L;
+        cs[r] = (a.conv_state && slot >= 0) ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H
+                                            : nullptr;
+        // history in front of sample 0 (only lane 0 uses it)
+#pragma unroll
+        for (int k = 0; k < PW; ++k)
+            hist[r][k] = 0.0f;
+        if (tid == 0 && live[r] && a.has_initial_state && cs[r]) {
+#pragma unroll
+            for (int k = 0; k < H; ++k)
+                hist[r][PW - H + k] = to_f32(cs[r][k]);
+        }
+    }
+
+    for (int t0 = 0; t0 < L; t0 += 256 * E) {
+        const int t = t0 + tid * E;
+        const bool tin = t < L;  // L % E == 0: a chunk is all in or all out
+        const int tc = tin ? t : 0;
+        const int tp = tc > 0 ? tc - PW : 0;  // clamped; sample 0 takes the history
+        u32x4 raw[RPW];
+        Prev praw[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            raw[r] = *reinterpret_cast<const u32x4 *>(xr[r] + tc);
+            praw[r] = *reinterpret_cast<const Prev *>(xr[r] + tp);
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            if (!(live[r] && tin))
+                continue;
+            float xw[PW + E];
+            const uint32_t *pw = reinterpret_cast<const uint32_t *>(&praw[r]);
+#pragma unroll
+            for (int q = 0; q < PB / 4; ++q)
+                unpack_word(pw[q], &xw[q * PerWord<T>::value], T{});
+            if (tc == 0) {
+#pragma unroll
+                for (int k = 0; k < PW; ++k)
+                    xw[k] = hist[r][k];
+            }
+            unpack_word(raw[r].x, &xw[PW + 0 * PerWord<T>::value], T{});
+            unpack_word(raw[r].y, &xw[PW + 1 * PerWord<T>::value], T{});
+            unpack_word(raw[r].z, &xw[PW + 2 * PerWord<T>::value], T{});
+            unpack_word(raw[r].w, &xw[PW + 3 * PerWord<T>::value], T{});
+            float o[E];
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                float acc = bias[r];
+#pragma unroll
+                for (int k = 0; k < W; ++k)
+                    acc = fmaf(w[r][k], xw[PW - H + i + k], acc);
+                o[i] = a.apply_silu ? silu_f32(acc) : acc;
+            }
+            store_vec<T, E>(orow[r] + tc, o);
+        }
+    }
+    // the new cache tail: the last H samples of history || x
+    if (tid == 0) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            if (!live[r] || !cs[r])
+                continue;
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
+                const int s = L - H + k;  // position in x (negative: in the history)
+                cs[r][k] = s >= 0 ? xr[r][s] : from_f32<T>(hist[r][PW + s]);
+            }
+        }
+    }
 }
 
 // Packed variable-length batch: x [channels, T] holds the sequences side by
@@ -395,21 +508,18 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(ConvArgs a)
 // request (channels % 8 == 0, 16-byte aligned tensors).  The 8 windows of
 // width-1 samples are contiguous in the cache row, so a lane reads and writes
 // them as whole vectors; the window values pass through float32 unchanged.
-template <typename T, int W>
+template <typename T, int W, int RB>
 __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
 {
+    // blockIdx.x: groups of G channels; blockIdx.y: RB consecutive requests,
+    // which each lane takes in turn with the same taps and bias (loaded once)
     constexpr int H = W - 1, G = 8;
     const int groups = a.channels / G;
-    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gi >= (int64_t)a.batch * groups)
+    const int gi = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (gi >= groups)
         return;
-    const int b = (int)(gi / groups), c0 = (int)(gi % groups) * G;
-    const int slot = a.slot_idx ? a.slot_idx[b] : b;
-    if (slot < 0)
-        return;
-    const int64_t xo = (int64_t)b * a.channels + c0;
-    float xv[G], w[G * W], bias[G];
-    load_vec_cached<T, G>(static_cast<const T *>(a.x) + xo, xv);
+    const int c0 = gi * G;
+    float w[G * W], bias[G];
     load_vec_cached<float, G * W>(a.weight + (int64_t)c0 * W, w);
     if (a.bias)
         load_vec_cached<float, G>(a.bias + c0, bias);
@@ -417,38 +527,56 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
 #pragma unroll
         for (int g = 0; g < G; ++g)
             bias[g] = 0.0f;
-    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c0) * H : nullptr;
-    float win[G * H > 0 ? G * H : 1];
-    if constexpr (H > 0) {
-        if (cs && a.has_initial_state)
-            load_vec_cached<T, G * H>(cs, win);
-        else
+    // every request's loads are issued before any arithmetic
+    float xv[RB][G], win[RB][G * H > 0 ? G * H : 1];
+    T *cs[RB];
+    bool live[RB];
 #pragma unroll
-            for (int k = 0; k < G * H; ++k)
-                win[k] = 0.0f;
+    for (int k = 0; k < RB; ++k) {
+        const int b = (int)blockIdx.y * RB + k;  // uniform over the workgroup
+        const int bb = b < a.batch ? b : 0;
+        const int slot = a.slot_idx ? a.slot_idx[bb] : bb;
+        live[k] = b < a.batch && slot >= 0;  // padded request: untouched
+        const int s = slot >= 0 ? slot : 0;
+        load_vec_cached<T, G>(static_cast<const T *>(a.x) + (int64_t)bb * a.channels + c0, xv[k]);
+        cs[k] = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)s * a.channels + c0) * H : nullptr;
+        if constexpr (H > 0) {
+            if (cs[k] && a.has_initial_state)
+                load_vec_cached<T, G * H>(cs[k], win[k]);
+            else
+#pragma unroll
+                for (int q = 0; q < G * H; ++q)
+                    win[k][q] = 0.0f;
+        }
     }
-    float o[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float acc = bias[g];
+    for (int k = 0; k < RB; ++k) {
+        if (!live[k])
+            continue;
+        const int b = (int)blockIdx.y * RB + k;
+        float o[G];
 #pragma unroll
-        for (int k = 0; k < H; ++k)
-            acc = fmaf(w[g * W + k], win[g * H + k], acc);
-        acc = fmaf(w[g * W + H], xv[g], acc);
-        o[g] = a.apply_silu ? silu_f32(acc) : acc;
-    }
-    store_vec_cached<T, G>(static_cast<T *>(a.out) + xo, o);
-    if constexpr (H > 0) {
-        if (cs) {
-            float nw[G * H];
+        for (int g = 0; g < G; ++g) {
+            float acc = bias[g];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int q = 0; q < H; ++q)
+                acc = fmaf(w[g * W + q], win[k][g * H + q], acc);
+            acc = fmaf(w[g * W + H], xv[k][g], acc);
+            o[g] = a.apply_silu ? silu_f32(acc) : acc;
+        }
+        store_vec_cached<T, G>(static_cast<T *>(a.out) + (int64_t)b * a.channels + c0, o);
+        if constexpr (H > 0) {
+            if (cs[k]) {
+                float nw[G * H];
 #pragma unroll
-                for (int k = 0; k + 1 < H; ++k)
-                    nw[g * H + k] = win[g * H + k + 1];
-                nw[g * H + H - 1] = xv[g];
+                for (int g = 0; g < G; ++g) {
+#pragma unroll
+                    for (int q = 0; q + 1 < H; ++q)
+                        nw[g * H + q] = win[k][g * H + q + 1];
+                    nw[g * H + H - 1] = xv[k][g];
+                }
+                store_vec_cached<T, G * H>(cs[k], nw);
             }
-            store_vec_cached<T, G * H>(cs, nw);
         }
     }
 }
@@ -456,10 +584,14 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
 template <typename T, int W>
 static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
 {
-    if (!a.cu_seqlens && a.seqlen == 1 && a.vec_decode) {
-        const int64_t n = (int64_t)a.batch * (a.channels / 8);
-        hipLaunchKernelGGL((conv_decode_vec_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                           stream, a);
+    // decode: two requests per lane in 64-lane workgroups (8.3 -> 7.0 us on
+    // the 245-request Mamba-1 2.8B step; four per lane, or wider workgroups,
+    // leave too few workgroups to fill the chip)
+    if (!a.cu_seqlens && a.seqlen == 1 && a.vec_decode && (a.batch + 1) / 2 <= 65535) {
+        constexpr int RB = 2;   // requests per lane (grid y = request groups)
+        constexpr int BT = 64;  // lanes per workgroup
+        const dim3 grid((unsigned)((a.channels / 8 + BT - 1) / BT), (unsigned)((a.batch + RB - 1) / RB));
+        hipLaunchKernelGGL((conv_decode_vec_kernel<T, W, RB>), grid, dim3(BT), 0, stream, a);
     } else if (!a.cu_seqlens && a.seqlen == 1) {
         const int64_t n = (int64_t)a.batch * a.channels;
         hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
@@ -479,12 +611,13 @@ static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
             hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256),
                                0, stream, a);
         }
+    } else if (a.vec) {
+        constexpr int RPW = 2;  // rows per workgroup
+        const dim3 grid((unsigned)(((int64_t)a.batch * a.channels + RPW - 1) / RPW));
+        hipLaunchKernelGGL((conv_rows_kernel<T, W, RPW>), grid, dim3(256), 0, stream, a);
     } else {
         const dim3 grid((unsigned)((int64_t)a.batch * a.channels));
-        if (a.vec)
-            hipLaunchKernelGGL((conv_prefill_kernel<T, W, true>), grid, dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((conv_prefill_kernel<T, W, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((conv_prefill_kernel<T, W, false>), grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -60,6 +60,14 @@ CONV_CASES = [
     ("f16_L2048", dict(seqlen=2048, io="f16", nheads=24, batch=2), False, 0),
     ("bf16_L2049_w1", dict(seqlen=2049, io="bf16", nheads=5, width=1, batch=2), True, 0),
     ("f16_L4104", dict(seqlen=4104, io="f16", nheads=6, batch=1), True, 0),
+    # 16-byte rows (seqlen % 8 == 0): two rows per workgroup, an odd row count,
+    # padded requests, history through every width, several tiles
+    ("f16_L1024_odd_rows_pad", dict(seqlen=1024, io="f16", nheads=7, batch=3, nslots=6,
+                                    random_slots=True), True, 2),
+    ("bf16_L256_w2", dict(seqlen=256, io="bf16", nheads=10, width=2, batch=2), True, 0),
+    ("f32_L4096_init", dict(seqlen=4096, io="f32", nheads=3, batch=2, nslots=3,
+                            random_slots=True), True, 0),
+    ("bf16_L16_w1", dict(seqlen=16, io="bf16", nheads=9, width=1, batch=2), True, 0),
     # decode through the 8-channels-per-lane vector kernel (channels % 8 == 0)
     ("f16_L1_vec", dict(seqlen=1, io="f16", nheads=512, batch=7, nslots=11, random_slots=True),
      True, 3),
