@@ -49,7 +49,7 @@ KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp", "ssm_kernels.
                                    "ssm_kernels.hpp"]}
 # rocprofv3 kernel names of each kernel in the benchmarked configuration
 KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "decode_step": "ssu_kernel",
-                  "conv1d_prefill": "conv_prefill_kernel"}
+                  "conv1d_prefill": "conv_rows_kernel"}
 
 
 def parse():

@@ -74,7 +74,8 @@ struct ChunkLoads {
     u32x4 b0[UNITS], b1[UNITS], c0[UNITS], c1[UNITS];
     u32x4 x[2];          // X[p][t0 + 32 kk + 8 lq .. +8)
     uint2 xo[2], zo[2];  // u and z at steps t0 + 16 st + 4 lq .. +4, this wave's 2 row tiles
-    float dt;            // wave 0: dt of step t0 + lane
+    bf16 dt;             // wave 0: dt of step t0 + lane, as stored (widened when staged, so
+                         // that this wave does not wait for the chunk's loads when issuing them)
 };
 
 template <int N>
@@ -107,7 +108,7 @@ __device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, cons
     }
     if (w == 0) {
         const int t = t0 + l;
-        c.dt = to_f32(dtrow[t < L ? t : t0]);
+        c.dt = dtrow[t < L ? t : t0];
     }
 }
 
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         // ---- stage the chunk (its loads were issued one chunk earlier)
         if (w == 0) {
             const bool ok = t0 + l < L;
-            const float v = cur.dt + bias;
+            const float v = to_f32(cur.dt) + bias;
             const float sp = softplus_f32(v);
             const float d = ok ? (a.dt_softplus ? sp : v) : 0.0f;  // identity step past the end
             float cum = d * A2;  // log2 of this step's decay, summed over the chunk
