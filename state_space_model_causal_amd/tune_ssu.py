@@ -8,7 +8,8 @@ effective batches (batch x nheads), and keep a tuned entry only
 where the best candidate beats the heuristic by more than 10%; elsewhere the
 heuristic stays.  The grid runs to 2M (the Mamba-1 2.8B decode of 245
 requests is 1.25M), skipping points whose cache would exceed --max-state-bytes.  The candidates are the geometries ssm_state_update_ex
-accepts: 8 or 16 states per lane, workgroups of 64, 128, 256 or 512 lanes.
+accepts: 8 or 16 states per lane (also 4 for a float32 cache of at most
+256 states per row), workgroups of 64, 128, 256 or 512 lanes.
 
 Each timing captures a HIP graph of launches that rotate through disjoint
 slot sets (so repeated launches do not find their state in the on-chip
@@ -50,7 +51,13 @@ SHAPES = [
     ("mamba2 hd128 n256 f32 cache", 64, 128, 256, torch.bfloat16, torch.float32, False),
 ]
 GRID = [8 << i for i in range(19)]  # effective batch 8 .. 2097152
-CANDIDATES = [(v, b) for v in (8, 16) for b in (64, 128, 256, 512)]
+BLOCKS = (64, 128, 256, 512)
+
+
+def candidates(dstate, cache):
+    """The geometries ssm_state_update_ex accepts for a shape."""
+    vs = ((4,) if cache == torch.float32 and dstate <= 256 else ()) + (8, 16)
+    return [(v, b) for v in vs for b in BLOCKS]
 ADOPT = 0.9  # a tuned geometry must take at most 90% of the heuristic's time
 
 
@@ -122,7 +129,8 @@ def tune(shapes, grid, ngroups, min_bytes, max_state_bytes):
             eff = batch * H
             t = make_inputs(H, P, N, io, cache, aps, batch, ngroups, dev, min_bytes)
             launches = max(16, len(t["sets"]))
-            times = {c: time_config(t, c, launches) for c in CANDIDATES}
+            cands = candidates(N, cache)
+            times = {c: time_config(t, c, launches) for c in cands}
             best = min(times, key=times.get)
             adopted = best != hv and times[best] <= ADOPT * times[hv]
             state_bytes = 2 * batch * H * P * N * t["state"].element_size()
@@ -130,7 +138,7 @@ def tune(shapes, grid, ngroups, min_bytes, max_state_bytes):
                    "heuristic": list(hv), "heuristic_us": times[hv], "best": list(best),
                    "best_us": times[best], "adopted": adopted,
                    "state_GBps_best": state_bytes / (times[best] * 1e-6) / 1e9,
-                   "all_us": {f"{v}x{b}": times[(v, b)] for v, b in CANDIDATES}}
+                   "all_us": {f"{v}x{b}": times[(v, b)] for v, b in cands}}
             print(json.dumps(rec), flush=True)
             report.append(rec)
             if adopted:

@@ -189,7 +189,7 @@ def test_state_update_config_choices(lib):
                                    (8, 64, 128, 256, torch.bfloat16, torch.bfloat16),
                                    (3, 7, 3, 24, torch.float32, torch.float32)]:
         v, b, from_table = ssm.state_update_config(batch, H, P, N, io, st)
-        assert v in (8, 16) and b in (64, 128, 256, 512)
+        assert v in (4, 8, 16) and b in (64, 128, 256, 512)
         if not from_table:  # the documented heuristic: 32 bytes of state per lane
             two = st in (torch.float16, torch.bfloat16)
             assert (v, b) == ((16 if two and N % 16 == 0 and N >= 32 else 8), 256)
@@ -211,7 +211,10 @@ def test_tuned_table_entries_are_valid():
         assert len(vals) == 8, line
         P, N, io, st, lo, hi, v, b = vals
         assert P >= 1 and 1 <= N <= 512 and io in (0, 1, 2) and st in (0, 1, 2)
-        assert 0 <= lo < hi and v in (8, 16) and b in (64, 128, 256, 512)
+        assert 0 <= lo < hi and b in (64, 128, 256, 512)
+        # 4 states per lane only for a float32 cache, with the row within a wave
+        assert v in (8, 16) or (v == 4 and st == 0), line
+        assert (N + v - 1) // v <= 64, line
 
 
 def scan_ex(lib, algo, **kw):
