@@ -126,8 +126,13 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     constexpr int LDQ = SQ + 8;  // row stride of the natural B tile and of M
     constexpr int NT = N / 16;   // 16-state tiles of the state
     constexpr int NTH = NT / 2;  // tiles per wave
-    __shared__ __align__(16) __bf16 s_bt[SQ * LDN];  // B^T  [r][n]
-    __shared__ __align__(16) __bf16 s_ct[SQ * LDN];  // C^T  [s][n]
+    // B^T [r][n] and C^T [s][n]: rows padded by 16 B, and the 16-byte
+    // groups of each row permuted by the row's 8-row block (XOR), so that the
+    // staging writes of 8 rows 8 apart fall in different banks while every
+    // MFMA operand read stays one aligned 16-byte (or 8-byte) access
+    __shared__ __align__(16) __bf16 s_bt[SQ * LDN];
+    __shared__ __align__(16) __bf16 s_ct[SQ * LDN];
+    auto tpos = [](int r, int c) { return r * LDN + ((((c >> 3) ^ (r >> 3)) & (N / 8 - 1)) << 3) + (c & 7); };
     __shared__ __align__(16) __bf16 s_bn[N * LDQ];   // B    [n][r]
     __shared__ __align__(16) __bf16 s_mh[SQ * LDQ];  // masked decay matrix M[s][r], high part
     __shared__ __align__(16) __bf16 s_ml[SQ * LDQ];  // and remainder
@@ -220,8 +225,8 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                     const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
                     const uint32_t bp = __builtin_amdgcn_perm(bv[i >> 1], bw[i >> 1], sel);
                     const uint32_t cp = __builtin_amdgcn_perm(cv[i >> 1], cw[i >> 1], sel);
-                    *reinterpret_cast<uint32_t *>(&s_bt[(8 * tv + i) * LDN + n]) = bp;
-                    *reinterpret_cast<uint32_t *>(&s_ct[(8 * tv + i) * LDN + n]) = cp;
+                    *reinterpret_cast<uint32_t *>(&s_bt[tpos(8 * tv + i, n)]) = bp;
+                    *reinterpret_cast<uint32_t *>(&s_ct[tpos(8 * tv + i, n)]) = cp;
                 }
             }
         }
@@ -258,9 +263,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 #pragma unroll
                 for (int q2 = 0; q2 < NTH / 2; ++q2) {
                     const int kk = (NTH / 2) * nh + q2;  // 32-state step
-                    const __bf16 *cr = &s_ct[(16 * st + l16) * LDN + 32 * kk + 4 * lq];
-                    const uint2 c_lo = *reinterpret_cast<const uint2 *>(cr);
-                    const uint2 c_hi = *reinterpret_cast<const uint2 *>(cr + 16);
+                    const int cr = 16 * st + l16, cc = 32 * kk + 4 * lq;
+                    const uint2 c_lo = *reinterpret_cast<const uint2 *>(&s_ct[tpos(cr, cc)]);
+                    const uint2 c_hi = *reinterpret_cast<const uint2 *>(&s_ct[tpos(cr, cc + 16)]);
                     const bf16x8_t cv = as_bf16x8(u32x4{c_lo.x, c_lo.y, c_hi.x, c_hi.y});
                     acc = mma(cv, hh[q2], acc);
                     acc = mma(cv, hl[q2], acc);
@@ -287,9 +292,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 #pragma unroll
                     for (int kk = 0; kk < N / 32; ++kk) {
                         const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
-                            &s_bt[(16 * rt + l16) * LDN + 32 * kk + 8 * lq]);
+                            &s_bt[tpos(16 * rt + l16, 32 * kk + 8 * lq)]);
                         const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(
-                            &s_ct[(16 * pw + l16) * LDN + 32 * kk + 8 * lq]);
+                            &s_ct[tpos(16 * pw + l16, 32 * kk + 8 * lq)]);
                         acc = mma(av, bv, acc);
                     }
                     const int r0 = 16 * rt + 4 * lq;
