@@ -48,7 +48,7 @@ KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp", "ssm_kernels.
                   "layer_decode": ["gemm.hip", "layer.hip", "conv1d.hip", "ssu.hip", "ssm_device.hpp",
                                    "ssm_kernels.hpp"]}
 # rocprofv3 kernel names of each kernel in the benchmarked configuration
-KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "decode_step": "ssu_kernel",
+KERNEL_SYMBOLS = {"selective_scan": "scan_kernel", "decode_step": "ssu_ilv_kernel",
                   "conv1d_prefill": "conv_rows_kernel"}
 
 
@@ -276,7 +276,7 @@ def summarize_profile(out):
     for name, key, title, fname, syms in (
             ("layer_trace", "layer_decode", "whole Mamba-1 2.8B decode layer", "mamba1_decode_layer_kernels.md",
              [("rmsnorm_kernel", None), ("gemm_kernel", None), ("gemm_reduce_kernel", None),
-              ("conv_decode", None), ("ssu_kernel", None)]),
+              ("conv_decode", None), ("ssu_ilv_kernel", None)]),
             ("chunked_trace", "chunked_prefill", "chunked Mamba-2 prefill on MFMA",
              "mamba2_chunked_prefill_kernels.md", [("ssd_kernel", None)])):
         st = list(csv.DictReader(open(glob.glob(f"{out}/{name}/*kernel_stats.csv")[0])))

@@ -195,8 +195,6 @@ enum : int {
     DPP_ROW_SHR4 = 0x114,
     DPP_ROW_SHR8 = 0x118,
     DPP_ROW_ROR1 = 0x121,
-    DPP_QUAD_BCAST2 = 0xA0,  // quad_perm [0,0,2,2]: lane 0 of each pair to both
-    DPP_QUAD_BCAST4 = 0x00,  // quad_perm [0,0,0,0]: lane 0 of each quad to all four
 };
 
 // Read `src` from another lane of the same 16-lane row; lanes whose source

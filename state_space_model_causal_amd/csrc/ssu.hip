@@ -10,13 +10,20 @@
 // with h' written back to state[s,h,p,n] in the cache dtype.
 //
 // Design: the kernel is bound by streaming the state cache once (read +
-// write).  One lane owns V (8 or 16) consecutive states of one (b,h,p) row, so
-// a row of dstate states is dstate/V lanes (rounded up to a power of two that
-// divides 64) and a wave covers 64*V consecutive states of the cache, read and
-// written with 128-bit accesses.  The readout sum over states is a butterfly
-// across the row's lanes.  No LDS, no barriers.  V and the workgroup size
-// (64 to 512 lanes) are chosen per shape on the host, from a table tuned on
-// gfx950 or a heuristic, or given by the caller.
+// write).  Each lane holds V states (V*sizeof(state) = 16, 32 or 64 bytes) of
+// every request it takes, and a wave covers 64*V consecutive states of the
+// cache, read and written with 128-bit accesses.  Two lane maps:
+//  - blocked (ssu_kernel): a lane owns V consecutive states of one (b,h,p)
+//    row, a row is dstate/V lanes (rounded up to a power of two dividing 64);
+//  - interleaved (ssu_ilv_kernel, 32 bytes per lane, power-of-two rows of at
+//    most 1 KB, large batches): the k-th access of a wave reads the k-th
+//    contiguous kilobyte of its block, lane L the 16 bytes at 16L.  Every
+//    access instruction then fills whole cache lines, where the blocked map
+//    touches twice the lines per instruction, half of each.
+// The readout sum over states is a butterfly across a row's lanes.  No LDS,
+// no barriers.  V and the workgroup size (64 to 512 lanes) are chosen per
+// shape on the host, from a table tuned on gfx950 or a heuristic, or given by
+// the caller.
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -40,8 +47,8 @@ struct SsuParams {
 template <typename TS, typename TI, int V, int CW>
 struct SsuReq {
     float hs[V], bv[V], cv[V];
-    // the row's values as stored (loaded by its first lane; widened when used,
-    // so that no load waits inside the branch that issues it)
+    // the row's values as stored (widened when used, after every load of the
+    // lane has been issued)
     TI dt_raw, x_raw, z_raw;
     TI win_raw[CW > 1 ? CW - 1 : 1];
     float delta, xv, zv;
@@ -80,21 +87,18 @@ __device__ __forceinline__ void ssu_params(const SsuArgs &a, int64_t hp, int j, 
     } else {
         q.a2 = a.A[q.h] * kLog2e;
     }
-    // the row's first lane takes the step size, the conv and the readout's
-    // D term: only it needs dt_bias, D and the conv taps
-    q.dtb = q.Dh = q.cbias = 0.0f;
+    // every lane of the row takes the step size, the conv and the readout's
+    // D term itself (same addresses within a wave: one access per row)
+    q.dtb = a.dt_bias ? a.dt_bias[q.h] : 0.0f;
+    q.Dh = a.D ? a.D[q.h] : 0.0f;
+    q.cbias = 0.0f;
+    if constexpr (CW > 0) {
 #pragma unroll
-    for (int k = 0; k < (CW > 0 ? CW : 1); ++k)
-        q.tap[k] = 0.0f;
-    if (j == 0) {
-        q.dtb = a.dt_bias ? a.dt_bias[q.h] : 0.0f;
-        q.Dh = a.D ? a.D[q.h] : 0.0f;
-        if constexpr (CW > 0) {
-#pragma unroll
-            for (int k = 0; k < CW; ++k)
-                q.tap[k] = a.conv_weight[q.hp * CW + k];
-            q.cbias = a.conv_bias ? a.conv_bias[q.hp] : 0.0f;
-        }
+        for (int k = 0; k < CW; ++k)
+            q.tap[k] = a.conv_weight[q.hp * CW + k];
+        q.cbias = a.conv_bias ? a.conv_bias[q.hp] : 0.0f;
+    } else {
+        q.tap[0] = 0.0f;
     }
 }
 
@@ -148,16 +152,17 @@ __device__ __forceinline__ void ssu_load(const SsuArgs &a, int b, int j, const S
     }
 }
 
-// Phase 1b: the row's values (dt, x, z, the conv window), loaded by the row's
-// first lane only, after every lane's state loads have been issued (a wait
-// for these then covers all of them at once).
+// Phase 1b: the row's values (dt, x, z, the conv window), loaded by every lane
+// of the row after all state loads have been issued, with no branch around
+// them: a conversion inside a branch would be placed right after its load, and
+// the wait for it would also cover every load issued before.
 template <typename TS, typename TI, int V, int CW>
 __device__ __forceinline__ void ssu_load_row(const SsuArgs &a, SsuReq<TS, TI, V, CW> &r)
 {
     r.dt_raw = static_cast<const TI *>(a.dt)[r.bh];
     r.x_raw = static_cast<const TI *>(a.x)[r.row];
-    if (a.z)
-        r.z_raw = static_cast<const TI *>(a.z)[r.row];
+    // without a gate this reads x, and the value goes unused
+    r.z_raw = static_cast<const TI *>(a.z ? a.z : a.x)[r.row];
     if constexpr (CW > 0) {
 #pragma unroll
         for (int k = 0; k < CW - 1; ++k)
@@ -170,14 +175,12 @@ template <typename TS, typename TI, bool A_PER_STATE, bool VEC, int V, int CW>
 __device__ __forceinline__ float ssu_compute(const SsuArgs &a, int j, const SsuParams<V, CW> &q,
                                              SsuReq<TS, TI, V, CW> &r)
 {
-    // the row's first lane holds dt, x, z and the window: it takes the step
-    // size and the conv, then shares both with the row's other lanes
     float xv = to_f32(r.x_raw);
     r.zv = to_f32(r.z_raw);
     if constexpr (CW > 0) {
-        // fused conv update of channel hp; the first lane also shifts the
-        // cached window (its stored values depend on the window loads, so
-        // the read has returned first)
+        // fused conv update of channel hp; the row's first lane also shifts
+        // the cached window (its stored values depend on the window loads,
+        // so the read has returned first)
         constexpr int HW = CW - 1;
         float acc = q.cbias;
 #pragma unroll
@@ -197,21 +200,7 @@ __device__ __forceinline__ float ssu_compute(const SsuArgs &a, int j, const SsuP
         xv = u;  // the update reads the float32 conv output
     }
     const float v = to_f32(r.dt_raw) + q.dtb;
-    float delta = a.dt_softplus ? softplus_f32(v) : v;
-    // rows of 2 or 4 lanes: a quad permutation (a VALU move); wider rows: the
-    // LDS crossbar
-    if (a.lanes_per_row_log2 == 1) {
-        delta = dpp_move_zero<DPP_QUAD_BCAST2>(delta);
-        xv = dpp_move_zero<DPP_QUAD_BCAST2>(xv);
-    } else if (a.lanes_per_row_log2 == 2) {
-        delta = dpp_move_zero<DPP_QUAD_BCAST4>(delta);
-        xv = dpp_move_zero<DPP_QUAD_BCAST4>(xv);
-    } else if (a.lanes_per_row_log2 > 2) {
-        const int lead = (int)(threadIdx.x & 63) & ~((1 << a.lanes_per_row_log2) - 1);
-        delta = __shfl(delta, lead, 64);
-        xv = __shfl(xv, lead, 64);
-    }
-    r.delta = delta;
+    r.delta = a.dt_softplus ? softplus_f32(v) : v;
     r.xv = xv;
     const float dx = r.delta * xv;
     float y = 0.0f;
@@ -261,11 +250,12 @@ __global__ __launch_bounds__(512) void ssu_kernel(SsuArgs a)
 #pragma unroll
     for (int k = 0; k < RB; ++k)
         ssu_load<TS, TI, VEC, V, CW>(a, (int)blockIdx.y * RB + k, j, q, r[k]);
-    if (j == 0) {
 #pragma unroll
-        for (int k = 0; k < RB; ++k)
-            ssu_load_row<TS, TI, V, CW>(a, r[k]);
-    }
+    for (int k = 0; k < RB; ++k)
+        ssu_load_row<TS, TI, V, CW>(a, r[k]);
+    // keep the scheduler from moving arithmetic (and the waits it needs) in
+    // between the loads above
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
         float y = ssu_compute<TS, TI, A_PER_STATE, VEC, V, CW>(a, j, q, r[k]);
@@ -280,6 +270,221 @@ __global__ __launch_bounds__(512) void ssu_kernel(SsuArgs a)
             static_cast<TI *>(a.out)[r[k].row] = from_f32<TI>(y);
         }
     }
+}
+
+// E elements of B or C at p (E * sizeof(T) is 8 bytes or a multiple of 16;
+// p aligned to 16 bytes, or to 8 for an 8-byte read).
+template <typename T, int E>
+__device__ __forceinline__ void load_bc(const T *p, float (&dst)[E])
+{
+    if constexpr (E * StorageSize<T>::value >= 16) {
+        load_vec_cached<T, E>(p, dst);
+    } else {
+        static_assert(E * StorageSize<T>::value == 8, "8-byte access");
+        const uint2 w = *reinterpret_cast<const uint2 *>(p);
+        unpack_word(w.x, &dst[0], T{});
+        unpack_word(w.y, &dst[PerWord<T>::value], T{});
+    }
+}
+
+// Interleaved lane map (same operation as ssu_kernel).  A wave's block is
+// NCH kilobytes of one request's slot: NCH * RPC consecutive (h,p) rows of
+// rowbytes = dstate * sizeof(state) each, RPC = 1024 / rowbytes.  Access k
+// reads kilobyte k, lane L its 16 bytes at 16L: row k*RPC + L/LPR of the
+// block, states (L % LPR)*E .. +E-1, with LPR = rowbytes / 16 lanes per row
+// and E = 16 / sizeof(state).  Every lane holds all values of each of its NCH
+// rows (step size, x, z, conv window) itself, so no lane waits on another.
+// The host takes this map only when every wave's block lies in one group of
+// heads (its B and C are shared by the block).
+template <typename TS, typename TI, bool A_PER_STATE, int CW, int RB, int NCH>
+__global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
+{
+    constexpr int E = 16 / StorageSize<TS>::value;
+    constexpr int HW = CW > 1 ? CW - 1 : 1;  // cached window length
+    const int lg = a.lanes_per_row_log2;       // log2(LPR)
+    const int lpr = 1 << lg, rpc = 64 >> lg;
+    const int lane = (int)(threadIdx.x & 63);
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t HP = (int64_t)a.nheads * a.headdim;
+    const int N = a.dstate;
+    const int jl = lane & (lpr - 1);  // lane within its row
+    const int n0 = jl * E;
+
+    // request-independent values of the lane's NCH rows
+    int64_t hp[NCH];
+    int hh[NCH];
+    bool in[NCH];
+    float an[NCH][A_PER_STATE ? E : 1], a2[NCH], dtb[NCH], Dh[NCH], cbias[NCH], tap[NCH][CW > 0 ? CW : 1];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int64_t row = (wave * NCH + k) * rpc + (lane >> lg);
+        in[k] = row < HP;
+        hp[k] = in[k] ? row : 0;  // a wave past the last row reads row 0 and stores nothing
+        hh[k] = (int)(hp[k] / a.headdim);
+        if constexpr (A_PER_STATE) {
+            load_vec_cached<float, E>(a.A + (int64_t)hh[k] * N + n0, an[k]);
+#pragma unroll
+            for (int i = 0; i < E; ++i)
+                an[k][i] *= kLog2e;
+            a2[k] = 0.0f;
+        } else {
+            a2[k] = a.A[hh[k]] * kLog2e;
+        }
+        dtb[k] = a.dt_bias ? a.dt_bias[hh[k]] : 0.0f;
+        Dh[k] = a.D ? a.D[hh[k]] : 0.0f;
+        cbias[k] = 0.0f;
+        tap[k][0] = 0.0f;
+        if constexpr (CW > 0) {
+#pragma unroll
+            for (int c = 0; c < CW; ++c)
+                tap[k][c] = a.conv_weight[hp[k] * CW + c];
+            cbias[k] = a.conv_bias ? a.conv_bias[hp[k]] : 0.0f;
+        }
+    }
+    const int g = hh[0] / a.heads_per_group;
+
+    // phase 1: every load of the RB requests (state and B/C first, then the
+    // rows' values), before any arithmetic
+    float hs[RB][NCH][E], bv[RB][E], cv[RB][E];
+    TI dt_raw[RB][NCH], x_raw[RB][NCH], z_raw[RB][NCH], win[RB][NCH][HW];
+    bool live[RB];
+    TS *sp[RB];
+    TI *cwp[RB];
+    int64_t brow[RB], bhead[RB];
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+        const int b = (int)blockIdx.y * RB + q;
+        const bool bin = b < a.batch;
+        const int bb = bin ? b : 0;
+        const int slot = a.slot_idx ? a.slot_idx[bb] : bb;  // uniform over the workgroup
+        live[q] = bin && slot >= 0;                         // padded: loads from slot 0, discarded
+        const int s = slot >= 0 ? slot : 0;
+        sp[q] = static_cast<TS *>(a.state) + (int64_t)s * HP * N + n0;
+        cwp[q] = CW > 0 ? static_cast<TI *>(a.conv_state) + (int64_t)s * HP * HW : nullptr;
+        brow[q] = (int64_t)bb * HP;
+        bhead[q] = (int64_t)bb * a.nheads;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            load_vec_cached<TS, E>(sp[q] + hp[k] * N, hs[q][k]);
+        const int64_t bc = ((int64_t)bb * a.ngroups + g) * N + n0;
+        load_bc<TI, E>(static_cast<const TI *>(a.B) + bc, bv[q]);
+        load_bc<TI, E>(static_cast<const TI *>(a.C) + bc, cv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            dt_raw[q][k] = static_cast<const TI *>(a.dt)[bhead[q] + hh[k]];
+            x_raw[q][k] = static_cast<const TI *>(a.x)[brow[q] + hp[k]];
+            // without a gate this reads x, and the value goes unused
+            z_raw[q][k] = static_cast<const TI *>(a.z ? a.z : a.x)[brow[q] + hp[k]];
+            if constexpr (CW > 1) {
+#pragma unroll
+                for (int c = 0; c < HW; ++c)
+                    win[q][k][c] = cwp[q][hp[k] * HW + c];
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // phase 2: (fused conv), update, store, readout
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const bool ok = live[q] && in[k];
+            float xv = to_f32(x_raw[q][k]);
+            if constexpr (CW > 0) {
+                float acc = cbias[k];
+#pragma unroll
+                for (int c = 0; c < CW - 1; ++c)
+                    acc = fmaf(tap[k][c], to_f32(win[q][k][c]), acc);
+                acc = fmaf(tap[k][CW - 1], xv, acc);
+                const float u = silu_f32(acc);
+                if (ok && jl == 0) {  // the row's first lane shifts the window
+                    TI *w = cwp[q] + hp[k] * HW;
+#pragma unroll
+                    for (int c = 0; c + 1 < CW - 1; ++c)
+                        w[c] = win[q][k][c + 1];
+                    if (CW > 1)
+                        w[CW - 2] = x_raw[q][k];
+                    if (a.u_out)
+                        static_cast<TI *>(a.u_out)[brow[q] + hp[k]] = from_f32<TI>(u);
+                }
+                xv = u;  // the update reads the float32 conv output
+            }
+            const float v = to_f32(dt_raw[q][k]) + dtb[k];
+            const float delta = a.dt_softplus ? softplus_f32(v) : v;
+            const float dx = delta * xv;
+            float hn[E];
+            float y = 0.0f;
+            if constexpr (A_PER_STATE) {
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    hn[i] = fmaf(exp2_hw(delta * an[k][i]), hs[q][k][i], dx * bv[q][i]);
+                    y = fmaf(cv[q][i], hn[i], y);
+                }
+            } else {
+                const float dA = exp2_hw(delta * a2[k]);
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    hn[i] = fmaf(dA, hs[q][k][i], dx * bv[q][i]);
+                    y = fmaf(cv[q][i], hn[i], y);
+                }
+            }
+            if (ok)
+                store_vec_cached<TS, E>(sp[q] + hp[k] * N, hn);
+            for (int o = lpr >> 1; o > 0; o >>= 1)
+                y += __shfl_xor(y, o, 64);
+            if (ok && jl == 0) {
+                if (a.D)
+                    y = fmaf(Dh[k], xv, y);
+                if (a.z)
+                    y *= silu_f32(to_f32(z_raw[q][k]));
+                static_cast<TI *>(a.out)[brow[q] + hp[k]] = from_f32<TI>(y);
+            }
+        }
+    }
+}
+
+// The interleaved map for a launch, if it applies: 32 bytes of state per lane
+// (two kilobyte accesses per wave), aligned 128-bit vectors, rows of
+// power-of-two size from 32 bytes to 1 KB, every wave's block inside one
+// group, and at least kIlvMinRows (request, row) pairs.  Below that the launch
+// is latency-bound and the blocked map, with half the rows per lane, was 4-5%
+// faster (Mamba-2 shapes at batch 8-16).  Returns log2(lanes per row), or -1.
+constexpr int64_t kIlvMinRows = int64_t(1) << 18;
+template <typename TS>
+static int ilv_lanes_log2(const SsuArgs &a)
+{
+    const int rowbytes = a.dstate * StorageSize<TS>::value;
+    if (!a.vec || a.states_per_lane * StorageSize<TS>::value != 32 || (rowbytes & (rowbytes - 1)) != 0 ||
+        rowbytes < 32 || rowbytes > 1024)
+        return -1;
+    int lg = 0;
+    while ((16 << lg) < rowbytes)
+        ++lg;
+    const int64_t rows_per_wave = 2 * (64 >> lg);
+    if (((int64_t)a.heads_per_group * a.headdim) % rows_per_wave != 0 ||
+        (int64_t)a.batch * a.nheads * a.headdim < kIlvMinRows)
+        return -1;
+    return lg;
+}
+
+template <typename TS, typename TI, bool APS, int CW>
+static void launch_ssu_ilv(const SsuArgs &a0, int lg, hipStream_t stream)
+{
+    constexpr int NCH = 2;
+    SsuArgs a = a0;
+    a.lanes_per_row_log2 = lg;
+    const int64_t rows_per_wave = NCH * (64 >> lg);
+    const int64_t lanes = ((int64_t)a.nheads * a.headdim + rows_per_wave - 1) / rows_per_wave * 64;
+    const int rb = a.requests_per_lane;
+    const dim3 grid((unsigned)((lanes + a.block_threads - 1) / a.block_threads), (unsigned)((a.batch + rb - 1) / rb));
+    if (rb == 2)
+        hipLaunchKernelGGL((ssu_ilv_kernel<TS, TI, APS, CW, 2, NCH>), grid, dim3(a.block_threads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((ssu_ilv_kernel<TS, TI, APS, CW, 1, NCH>), grid, dim3(a.block_threads), 0, stream, a);
 }
 
 template <typename TS, typename TI, bool APS, bool VEC, int V, int CW>
@@ -299,6 +504,16 @@ static void launch_ssu_rb(const SsuArgs &a, hipStream_t stream)
 template <typename TS, typename TI, bool APS, bool VEC, int V>
 static void launch_ssu_v(const SsuArgs &a, hipStream_t stream)
 {
+    if constexpr (VEC && V * StorageSize<TS>::value == 32) {
+        const int lg = ilv_lanes_log2<TS>(a);
+        if (lg >= 0) {
+            if (a.conv_width == kFusedConvWidth)
+                launch_ssu_ilv<TS, TI, APS, kFusedConvWidth>(a, lg, stream);
+            else
+                launch_ssu_ilv<TS, TI, APS, 0>(a, lg, stream);
+            return;
+        }
+    }
     if (a.conv_width == kFusedConvWidth)
         launch_ssu_rb<TS, TI, APS, VEC, V, kFusedConvWidth>(a, stream);
     else

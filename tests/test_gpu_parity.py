@@ -230,6 +230,27 @@ SSU_CASES = [
                   a_per_state=False, batch=2, index_sensitive=True), {}),
     ("hd1_noz_noD", dict(seqlen=1, nheads=50, dstate=16, io="f32", state="f32", batch=3,
                          index_sensitive=True), dict(z=False, D=False, bias=False)),
+    # interleaved lane map (32 bytes of state per lane, power-of-two rows,
+    # >= 2^18 (request, row) pairs): 2, 16, 32 and 64 lanes per row, groups,
+    # two requests per lane with an odd batch, padded requests, a workgroup
+    # whose last wave lies past the last row
+    ("ilv_m1_N16_f32", dict(seqlen=1, nheads=2048, dstate=16, io="f16", state="f32", batch=129,
+                            nslots=140, random_slots=True, index_sensitive=True), dict(pad=5)),
+    ("ilv_m1_N16_past_last_row", dict(seqlen=1, nheads=96, dstate=16, io="f16", state="f32",
+                                      batch=2731, index_sensitive=True), dict(pad=2)),
+    ("ilv_m1_N16_f32io_noz_noD", dict(seqlen=1, nheads=2048, dstate=16, io="f32", state="f32",
+                                      batch=128, index_sensitive=True),
+     dict(z=False, D=False, bias=False)),
+    ("ilv_m2_hd64_N128_G8_f16", dict(seqlen=1, nheads=80, headdim=64, dstate=128, ngroups=8,
+                                     io="f16", state="f16", a_per_state=False, batch=52,
+                                     nslots=60, random_slots=True, index_sensitive=True),
+     dict(pad=3)),
+    ("ilv_m2_hd128_N256_bf16", dict(seqlen=1, nheads=64, headdim=128, dstate=256, io="bf16",
+                                    state="bf16", a_per_state=False, batch=33, nslots=36,
+                                    random_slots=True, index_sensitive=True), {}),
+    ("ilv_N256_f32_1KB_rows", dict(seqlen=1, nheads=16, headdim=64, dstate=256, io="f16",
+                                   state="f32", a_per_state=False, batch=257,
+                                   index_sensitive=True), {}),
 ]
 
 
@@ -405,6 +426,12 @@ DECODE_CASES = [
     ("m2_hd128_N256_bf16", dict(seqlen=1, nheads=4, headdim=128, dstate=256, io="bf16",
                                 state="f32", a_per_state=False, batch=2, nslots=5,
                                 random_slots=True, index_sensitive=True), dict(pad=2)),
+    # interleaved lane map (>= 2^18 (request, channel) pairs)
+    ("ilv_m1_f16_f32state", dict(seqlen=1, nheads=2048, dstate=16, io="f16", state="f32",
+                                 batch=129, nslots=140, random_slots=True, index_sensitive=True),
+     dict(pad=5)),
+    ("ilv_m1_f32_noz_noD", dict(seqlen=1, nheads=2048, dstate=16, io="f32", state="f32", batch=128,
+                                index_sensitive=True), dict(z=False, D=False, bias=False)),
 ]
 
 
@@ -429,6 +456,13 @@ def run_decode_step(ssm, oracle, spec, t, opts, label):
     # the fused step hands the float32 conv output to the update (no rounding)
     o, so, st, sts = oracle.state_update(
         f(st0), uo.reshape(shp), f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
+        D=None if D is None else f(D), z=None if z is None else f(z),
+        dt_bias=None if bias is None else f(bias), slot_idx=idx_np, out=f(out0))
+    # That conv output carries the rounding of the conv's own terms (scale
+    # uso >= |u|), which a near-cancelling conv leaves large next to |u|: the
+    # update's scales are taken with uso in place of |u|.
+    _, so, _, sts = oracle.state_update(
+        f(st0), uso.reshape(shp), f(t["dt"]), f(t["A"]), f(t["B"]), f(t["C"]),
         D=None if D is None else f(D), z=None if z is None else f(z),
         dt_bias=None if bias is None else f(bias), slot_idx=idx_np, out=f(out0))
     check(out, o, so, RTOL[spec.io], spec.io, f"decode_step {label} out")
