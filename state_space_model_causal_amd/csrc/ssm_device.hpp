@@ -160,16 +160,17 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log1p(e) for e in [0, 1], accurate to a few ulp.  w = 1 + e is rounded; the
-// factor e / (w - 1) corrects the rounding of w exactly to first order
-// (Goldberg, "What every computer scientist should know about floating-point
-// arithmetic", 1991, Theorem 4).  Branch-free.
+// log1p(e) for e in [0, 1], accurate to a few ulp.  w = 1 + e is rounded and
+// c = e - (w - 1) is its rounding error, exactly (Dekker's Fast2Sum, 1971:
+// 1 >= e).  Then log1p(e) = log(w) + log(1 + c/w), and since |c| <= 2^-24
+// and w is in [1, 2], log(1 + c/w) = c up to 2^-24 * e, about an ulp of the
+// result at most.  When w rounds to 1 the result is c = e.  One
+// transcendental, no division.
 __device__ __forceinline__ float log1p_unit(float e)
 {
     const float w = 1.0f + e;
-    const float d = w - 1.0f;
-    const float l = log2_hw(w) * kLn2 * (e * rcp_hw(d));
-    return d == 0.0f ? e : l;
+    const float c = e - (w - 1.0f);
+    return fmaf(log2_hw(w), kLn2, c);
 }
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^{-|v|}); for v > 20 the
