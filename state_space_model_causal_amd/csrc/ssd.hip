@@ -26,9 +26,10 @@
 // headdim).  Each wave owns 16 rows and half of the states: its part of the
 // state (dstate/2 x 16, float32) stays in MFMA accumulators for the whole
 // sequence, which is walked in chunks of 64 steps.  Per chunk the workgroup
-// stages B (as is and transposed) and C (transposed) in LDS, builds the
-// masked decay matrix once for all waves, then every wave computes its share
-// of the outputs and updates its part of the state.  Two waves per SIMD let
+// stages B and C in LDS as stored ([state][step]; the operands that need them
+// transposed use gfx950's transpose reads), builds the masked decay matrix
+// once for all waves, then every wave computes its share of the outputs and
+// updates its part of the state.  Two waves per SIMD let
 // one wave's vector work overlap the other's matrix work.  HBM traffic: u,
 // dt, z, B, C read once (B and C from L2 for every head of a group), out
 // written once, the state read and written once.
@@ -61,6 +62,33 @@ __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8_t &hi, bf
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8_t, w); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// gfx950 transpose read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane 4i + a supplies the address of 4 consecutive 16-bit elements; lane
+// 4a + b receives element b of lanes a, 4 + a, 8 + a, 12 + a.  So if lane
+// 4i + a points at row n0 + i, columns c0 + 4a .. +3 of a row-major tile, lane
+// d = 4a + b receives column c0 + d of rows n0 .. n0 + 3: a column of the
+// tile, as an MFMA operand holds it.
+__device__ __forceinline__ uint2 ds_read_tr(const __bf16 *p)
+{
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// 8 consecutive rows n0 .. n0 + 7 (read as rows n0 + i and n0 + 4 + i) of
+// column c0 + (lane % 16) of a row-major LDS tile with row stride ld: the
+// k-operand of one lane of v_mfma_f32_16x16x32_bf16 from the natural layout.
+// n0 and c0 may differ between the lane's 16-lane groups.
+__device__ __forceinline__ bf16x8_t col8_tr(const __bf16 *tile, int ld, int n0, int n0b, int c0, int l16)
+{
+    const int i = l16 >> 2, a = l16 & 3;
+    const uint2 lo = ds_read_tr(tile + (n0 + i) * ld + c0 + 4 * a);
+    const uint2 hi = ds_read_tr(tile + (n0b + i) * ld + c0 + 4 * a);
+    return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
 
 constexpr int SNW = 8;           // waves per workgroup
 constexpr int STHREADS = 64 * SNW;
@@ -122,18 +150,13 @@ __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 
 template <typename TS, int N>
 __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 {
-    constexpr int LDN = N + 8;   // row stride (elements) of the transposed tiles
-    constexpr int LDQ = SQ + 8;  // row stride of the natural B tile and of M
+    constexpr int LDQ = SQ + 8;  // row stride of the natural B and C tiles and of M
     constexpr int NT = N / 16;   // 16-state tiles of the state
     constexpr int NTH = NT / 2;  // tiles per wave
-    // B^T [r][n] and C^T [s][n]: rows padded by 16 B, and the 16-byte
-    // groups of each row permuted by the row's 8-row block (XOR), so that the
-    // staging writes of 8 rows 8 apart fall in different banks while every
-    // MFMA operand read stays one aligned 16-byte (or 8-byte) access
-    __shared__ __align__(16) __bf16 s_bt[SQ * LDN];
-    __shared__ __align__(16) __bf16 s_ct[SQ * LDN];
-    auto tpos = [](int r, int c) { return r * LDN + ((((c >> 3) ^ (r >> 3)) & (N / 8 - 1)) << 3) + (c & 7); };
-    __shared__ __align__(16) __bf16 s_bn[N * LDQ];   // B    [n][r]
+    // B and C of the chunk as stored, [n][r] and [n][s]; the operands that
+    // need them transposed read them with transpose reads
+    __shared__ __align__(16) __bf16 s_bn[N * LDQ];
+    __shared__ __align__(16) __bf16 s_cn[N * LDQ];
     __shared__ __align__(16) __bf16 s_mh[SQ * LDQ];  // masked decay matrix M[s][r], high part
     __shared__ __align__(16) __bf16 s_ml[SQ * LDQ];  // and remainder
     __shared__ __align__(16) float s_x[SNW][2][64][4];  // C.H halves for the partner wave
@@ -216,18 +239,8 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 const u32x4 c0 = ok ? cur.c0[k] : z4, c1 = ok ? cur.c1[k] : z4;
                 *reinterpret_cast<u32x4 *>(&s_bn[n * LDQ + 8 * tv]) = b0;
                 *reinterpret_cast<u32x4 *>(&s_bn[(n + 1) * LDQ + 8 * tv]) = b1;
-                const uint32_t bw[4] = {b0.x, b0.y, b0.z, b0.w}, bv[4] = {b1.x, b1.y, b1.z, b1.w};
-                const uint32_t cw[4] = {c0.x, c0.y, c0.z, c0.w}, cv[4] = {c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    // element i of a row is the low (even i) or high half of
-                    // word i/2; pair it with the same element of the next row
-                    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-                    const uint32_t bp = __builtin_amdgcn_perm(bv[i >> 1], bw[i >> 1], sel);
-                    const uint32_t cp = __builtin_amdgcn_perm(cv[i >> 1], cw[i >> 1], sel);
-                    *reinterpret_cast<uint32_t *>(&s_bt[tpos(8 * tv + i, n)]) = bp;
-                    *reinterpret_cast<uint32_t *>(&s_ct[tpos(8 * tv + i, n)]) = cp;
-                }
+                *reinterpret_cast<u32x4 *>(&s_cn[n * LDQ + 8 * tv]) = c0;
+                *reinterpret_cast<u32x4 *>(&s_cn[(n + 1) * LDQ + 8 * tv]) = c1;
             }
         }
         bf16x8_t xk[2];
@@ -263,10 +276,10 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 #pragma unroll
                 for (int q2 = 0; q2 < NTH / 2; ++q2) {
                     const int kk = (NTH / 2) * nh + q2;  // 32-state step
-                    const int cr = 16 * st + l16, cc = 32 * kk + 4 * lq;
-                    const uint2 c_lo = *reinterpret_cast<const uint2 *>(&s_ct[tpos(cr, cc)]);
-                    const uint2 c_hi = *reinterpret_cast<const uint2 *>(&s_ct[tpos(cr, cc + 16)]);
-                    const bf16x8_t cv = as_bf16x8(u32x4{c_lo.x, c_lo.y, c_hi.x, c_hi.y});
+                    // C_s[n] for s = 16 st + l16 and the states of hh's order:
+                    // n = 32 kk + 4 lq + i and 32 kk + 16 + 4 lq + i
+                    const int nc = 32 * kk + 4 * lq;
+                    const bf16x8_t cv = col8_tr(s_cn, LDQ, nc, nc + 16, 16 * st, l16);
                     acc = mma(cv, hh[q2], acc);
                     acc = mma(cv, hl[q2], acc);
                 }
@@ -291,10 +304,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int kk = 0; kk < N / 32; ++kk) {
-                        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
-                            &s_bt[tpos(16 * rt + l16, 32 * kk + 8 * lq)]);
-                        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(
-                            &s_ct[tpos(16 * pw + l16, 32 * kk + 8 * lq)]);
+                        const int nb = 32 * kk + 8 * lq;
+                        const bf16x8_t av = col8_tr(s_bn, LDQ, nb, nb + 4, 16 * rt, l16);
+                        const bf16x8_t bv = col8_tr(s_cn, LDQ, nb, nb + 4, 16 * pw, l16);
                         acc = mma(av, bv, acc);
                     }
                     const int r0 = 16 * rt + 4 * lq;
