@@ -251,6 +251,16 @@ SSU_CASES = [
     ("ilv_N256_f32_1KB_rows", dict(seqlen=1, nheads=16, headdim=64, dstate=256, io="f16",
                                    state="f32", a_per_state=False, batch=257,
                                    index_sensitive=True), {}),
+    ("ilv_N8_f32_2_lanes_per_row", dict(seqlen=1, nheads=64, headdim=64, dstate=8, io="f16",
+                                        state="f32", a_per_state=False, batch=65,
+                                        index_sensitive=True), {}),
+    ("ilv_N64_f16_8_lanes_per_row", dict(seqlen=1, nheads=32, headdim=64, dstate=64, io="bf16",
+                                         state="f16", a_per_state=True, batch=129,
+                                         index_sensitive=True), dict(pad=1)),
+    # as many (request, row) pairs, but groups of 10 rows do not hold whole
+    # 32-row wave blocks: the blocked map
+    ("blocked_groups_not_wave_aligned", dict(seqlen=1, nheads=80, dstate=16, ngroups=8, io="f16",
+                                             state="f32", batch=3300, index_sensitive=True), {}),
 ]
 
 
