@@ -191,7 +191,11 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x,
  * >= 32 states that are a multiple of 16, else 8) in 256-lane workgroups.
  * Independently of the geometry, with one channel per head (headdim 1) and
  * at least 8 requests each lane updates its states for two requests in
- * turn.
+ * turn.  With 32 bytes of state per lane, rows of a power-of-two size up to
+ * 1 KB and at least 2^18 (request, row) pairs, the lanes take the same number
+ * of states in an interleaved order instead (each 128-bit access of a wave
+ * covers a contiguous kilobyte of the cache); the cache bytes written are the
+ * same.
  */
 typedef struct ssm_launch_config {
     int states_per_lane; /* 4, 8 or 16             */
