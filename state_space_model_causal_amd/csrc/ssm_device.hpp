@@ -196,6 +196,9 @@ enum : int {
     DPP_ROW_SHR4 = 0x114,
     DPP_ROW_SHR8 = 0x118,
     DPP_ROW_ROR1 = 0x121,
+    DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
+    DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
+    DPP_QUAD_NEXT = 0xF9,  // quad_perm [1,2,3,3]: lane i of a quad reads lane min(i+1, 3)
 };
 
 // Read `src` from another lane of the same 16-lane row; lanes whose source
@@ -214,6 +217,13 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move_zero(float src)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(src), CTRL, 0xf, 0xf, true));
+}
+
+// Same, on raw 32-bit values.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move_bits(uint32_t src)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)src, CTRL, 0xf, 0xf, true);
 }
 
 // ---------------------------------------------------------------- block order

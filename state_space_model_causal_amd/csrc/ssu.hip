@@ -272,6 +272,15 @@ __global__ __launch_bounds__(512) void ssu_kernel(SsuArgs a)
     }
 }
 
+// A stored element's bits in a 32-bit register and back (for lane moves).
+__device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t raw_bits(f16 v) { return __builtin_bit_cast(uint16_t, v); }
+__device__ __forceinline__ uint32_t raw_bits(bf16 v) { return v.bits; }
+template <typename T> __device__ __forceinline__ T from_bits(uint32_t b);
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t b) { return __uint_as_float(b); }
+template <> __device__ __forceinline__ f16 from_bits<f16>(uint32_t b) { return __builtin_bit_cast(f16, (uint16_t)b); }
+template <> __device__ __forceinline__ bf16 from_bits<bf16>(uint32_t b) { bf16 r; r.bits = (uint16_t)b; return r; }
+
 // E elements of B or C at p (E * sizeof(T) is 8 bytes or a multiple of 16;
 // p aligned to 16 bytes, or to 8 for an 8-byte read).
 template <typename T, int E>
@@ -296,9 +305,18 @@ __device__ __forceinline__ void load_bc(const T *p, float (&dst)[E])
 // rows (step size, x, z, conv window) itself, so no lane waits on another.
 // The host takes this map only when every wave's block lies in one group of
 // heads (its B and C are shared by the block).
-template <typename TS, typename TI, bool A_PER_STATE, int CW, int RB, int NCH>
+//
+// Fused conv with rows of at least 4 lanes (COOP): the first 4 lanes of a row
+// (and every further quad of it, redundantly) share the conv.  Lane v of the
+// quad loads one value (window sample v for v < 3, x for v = 3) and its tap,
+// the 4 products are summed across the quad, and lane v < 3 writes the
+// shifted window's sample v (the quad neighbour's value), so each value is
+// loaded and stored by one lane.  Without it every lane loads the whole
+// window and x, and the row's first lane shifts the window.
+template <typename TS, typename TI, bool A_PER_STATE, int CW, int RB, int NCH, bool COOP>
 __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
 {
+    static_assert(!COOP || CW == 4, "the quad conv takes 4 taps");
     constexpr int E = 16 / StorageSize<TS>::value;
     constexpr int HW = CW > 1 ? CW - 1 : 1;  // cached window length
     const int lg = a.lanes_per_row_log2;       // log2(LPR)
@@ -334,7 +352,10 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
         Dh[k] = a.D ? a.D[hh[k]] : 0.0f;
         cbias[k] = 0.0f;
         tap[k][0] = 0.0f;
-        if constexpr (CW > 0) {
+        if constexpr (COOP) {
+            tap[k][0] = a.conv_weight[hp[k] * CW + (jl & 3)];  // this lane's tap
+            cbias[k] = a.conv_bias ? a.conv_bias[hp[k]] : 0.0f;
+        } else if constexpr (CW > 0) {
 #pragma unroll
             for (int c = 0; c < CW; ++c)
                 tap[k][c] = a.conv_weight[hp[k] * CW + c];
@@ -375,13 +396,20 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             dt_raw[q][k] = static_cast<const TI *>(a.dt)[bhead[q] + hh[k]];
-            x_raw[q][k] = static_cast<const TI *>(a.x)[brow[q] + hp[k]];
             // without a gate this reads x, and the value goes unused
             z_raw[q][k] = static_cast<const TI *>(a.z ? a.z : a.x)[brow[q] + hp[k]];
-            if constexpr (CW > 1) {
+            if constexpr (COOP) {
+                // window sample v of the row, or x for v = 3
+                const int v = jl & 3;
+                const TI *src = v < 3 ? cwp[q] + hp[k] * HW + v : static_cast<const TI *>(a.x) + brow[q] + hp[k];
+                x_raw[q][k] = *src;
+            } else {
+                x_raw[q][k] = static_cast<const TI *>(a.x)[brow[q] + hp[k]];
+                if constexpr (CW > 1) {
 #pragma unroll
-                for (int c = 0; c < HW; ++c)
-                    win[q][k][c] = cwp[q][hp[k] * HW + c];
+                    for (int c = 0; c < HW; ++c)
+                        win[q][k][c] = cwp[q][hp[k] * HW + c];
+                }
             }
         }
     }
@@ -394,7 +422,21 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
         for (int k = 0; k < NCH; ++k) {
             const bool ok = live[q] && in[k];
             float xv = to_f32(x_raw[q][k]);
-            if constexpr (CW > 0) {
+            if constexpr (COOP) {
+                const int v = jl & 3;
+                float acc = tap[k][0] * xv + (v == 3 ? cbias[k] : 0.0f);
+                acc += dpp_move_zero<DPP_QUAD_XOR1>(acc);
+                acc += dpp_move_zero<DPP_QUAD_XOR2>(acc);
+                const float u = silu_f32(acc);
+                // lane v < 3 of the row's first quad writes the shifted
+                // window's sample v: the value lane v + 1 loaded
+                const uint32_t nb = dpp_move_bits<DPP_QUAD_NEXT>(raw_bits(x_raw[q][k]));
+                if (ok && jl < 3)
+                    cwp[q][hp[k] * HW + jl] = from_bits<TI>(nb);
+                if (ok && jl == 0 && a.u_out)
+                    static_cast<TI *>(a.u_out)[brow[q] + hp[k]] = from_f32<TI>(u);
+                xv = u;
+            } else if constexpr (CW > 0) {
                 float acc = cbias[k];
 #pragma unroll
                 for (int c = 0; c < CW - 1; ++c)
@@ -471,20 +513,32 @@ static int ilv_lanes_log2(const SsuArgs &a)
     return lg;
 }
 
-template <typename TS, typename TI, bool APS, int CW>
-static void launch_ssu_ilv(const SsuArgs &a0, int lg, hipStream_t stream)
+template <typename TS, typename TI, bool APS, int CW, bool COOP>
+static void launch_ssu_ilv_c(const SsuArgs &a, hipStream_t stream)
 {
     constexpr int NCH = 2;
-    SsuArgs a = a0;
-    a.lanes_per_row_log2 = lg;
-    const int64_t rows_per_wave = NCH * (64 >> lg);
+    const int64_t rows_per_wave = NCH * (64 >> a.lanes_per_row_log2);
     const int64_t lanes = ((int64_t)a.nheads * a.headdim + rows_per_wave - 1) / rows_per_wave * 64;
     const int rb = a.requests_per_lane;
     const dim3 grid((unsigned)((lanes + a.block_threads - 1) / a.block_threads), (unsigned)((a.batch + rb - 1) / rb));
     if (rb == 2)
-        hipLaunchKernelGGL((ssu_ilv_kernel<TS, TI, APS, CW, 2, NCH>), grid, dim3(a.block_threads), 0, stream, a);
+        hipLaunchKernelGGL((ssu_ilv_kernel<TS, TI, APS, CW, 2, NCH, COOP>), grid, dim3(a.block_threads), 0, stream, a);
     else
-        hipLaunchKernelGGL((ssu_ilv_kernel<TS, TI, APS, CW, 1, NCH>), grid, dim3(a.block_threads), 0, stream, a);
+        hipLaunchKernelGGL((ssu_ilv_kernel<TS, TI, APS, CW, 1, NCH, COOP>), grid, dim3(a.block_threads), 0, stream, a);
+}
+
+template <typename TS, typename TI, bool APS, int CW>
+static void launch_ssu_ilv(const SsuArgs &a0, int lg, hipStream_t stream)
+{
+    SsuArgs a = a0;
+    a.lanes_per_row_log2 = lg;
+    if constexpr (CW == 4) {
+        if (lg >= 2) {  // rows of at least 4 lanes share the conv
+            launch_ssu_ilv_c<TS, TI, APS, CW, true>(a, stream);
+            return;
+        }
+    }
+    launch_ssu_ilv_c<TS, TI, APS, CW, false>(a, stream);
 }
 
 template <typename TS, typename TI, bool APS, bool VEC, int V, int CW>
