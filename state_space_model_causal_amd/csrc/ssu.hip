@@ -423,10 +423,10 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
             const bool ok = live[q] && in[k];
             float xv = to_f32(x_raw[q][k]);
             if constexpr (COOP) {
-                const int v = jl & 3;
-                float acc = tap[k][0] * xv + (v == 3 ? cbias[k] : 0.0f);
+                float acc = tap[k][0] * xv;
                 acc += dpp_move_zero<DPP_QUAD_XOR1>(acc);
                 acc += dpp_move_zero<DPP_QUAD_XOR2>(acc);
+                acc += cbias[k];
                 const float u = silu_f32(acc);
                 // lane v < 3 of the row's first quad writes the shifted
                 // window's sample v: the value lane v + 1 loaded
