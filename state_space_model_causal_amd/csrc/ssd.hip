@@ -102,8 +102,7 @@ struct ChunkLoads {
     u32x4 b0[UNITS], b1[UNITS], c0[UNITS], c1[UNITS];
     u32x4 x[2];          // X[p][t0 + 32 kk + 8 lq .. +8)
     uint2 xo[2], zo[2];  // u and z at steps t0 + 16 st + 4 lq .. +4, this wave's 2 row tiles
-    bf16 dt;             // wave 0: dt of step t0 + lane, as stored (widened when staged, so
-                         // that this wave does not wait for the chunk's loads when issuing them)
+    bf16 dt;             // dt of step t0 + lane, as stored (wave 0 widens it when staging)
 };
 
 template <int N>
@@ -127,14 +126,20 @@ __device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, cons
         const int t = t0 + 32 * kk + 8 * lq;
         c.x[kk] = *reinterpret_cast<const u32x4 *>(urow + (t < L ? t : 0));
     }
+    // No load below sits under a branch or next to a select on its value:
+    // the compiler would wait for it there, and that wait would also cover
+    // every load issued before it (the whole chunk).  Without a gate the z
+    // load reads u, and the value goes unused; every wave loads dt (wave 0
+    // uses it).
+    const bf16 *zsrc = zrow ? zrow : urow;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int t = t0 + 16 * (2 * nh + i) + 4 * lq;
         const int tc = t < L ? t : 0;
         c.xo[i] = *reinterpret_cast<const uint2 *>(urow + tc);
-        c.zo[i] = zrow ? *reinterpret_cast<const uint2 *>(zrow + tc) : uint2{0u, 0u};
+        c.zo[i] = *reinterpret_cast<const uint2 *>(zsrc + tc);
     }
-    if (w == 0) {
+    {
         const int t = t0 + l;
         c.dt = dtrow[t < L ? t : t0];
     }
