@@ -168,7 +168,10 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
         Prev praw[RPW];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            raw[r] = *reinterpret_cast<const u32x4 *>(xr[r] + tc);
+            // x is streamed once: non-temporal (41.9 -> 35.7 us per call on
+            // the 4 x 5120 x 2048 f16 prefill); the few samples in front come
+            // from the neighbour's chunk, through the cache
+            raw[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr[r] + tc));
             praw[r] = *reinterpret_cast<const Prev *>(xr[r] + tp);
         }
 #pragma unroll
