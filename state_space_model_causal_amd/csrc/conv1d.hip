@@ -530,10 +530,17 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
 #pragma unroll
         for (int g = 0; g < G; ++g)
             bias[g] = 0.0f;
-    // every request's loads are issued before any arithmetic
-    float xv[RB][G], win[RB][G * H > 0 ? G * H : 1];
+    // every request's loads are issued before any arithmetic, with no
+    // branch or select around them: widening a value inside a branch makes
+    // the compiler wait for it there, and that wait covers every load issued
+    // before (the next request's loads would start a second round trip)
+    constexpr int NWV = H > 0 ? G * H * (int)sizeof(T) / 16 : 1;  // window vectors
+    static_assert(H == 0 || NWV * 16 == G * H * (int)sizeof(T), "G*H samples fill whole vectors");
+    float xv[RB][G];
+    u32x4 wraw[RB][NWV];
     T *cs[RB];
     bool live[RB];
+    const bool init = a.conv_state && a.has_initial_state;
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
         const int b = (int)blockIdx.y * RB + k;  // uniform over the workgroup
@@ -544,12 +551,13 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
         load_vec_cached<T, G>(static_cast<const T *>(a.x) + (int64_t)bb * a.channels + c0, xv[k]);
         cs[k] = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)s * a.channels + c0) * H : nullptr;
         if constexpr (H > 0) {
-            if (cs[k] && a.has_initial_state)
-                load_vec_cached<T, G * H>(cs[k], win[k]);
-            else
+            // without a cache (or its history) the weights are read instead
+            // and the values replaced by zeros below
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                init ? static_cast<const void *>(cs[k]) : static_cast<const void *>(a.weight));
 #pragma unroll
-                for (int q = 0; q < G * H; ++q)
-                    win[k][q] = 0.0f;
+            for (int v = 0; v < NWV; ++v)
+                wraw[k][v] = src[v];
         }
     }
 #pragma unroll
@@ -557,13 +565,27 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
         if (!live[k])
             continue;
         const int b = (int)blockIdx.y * RB + k;
+        float win[G * H > 0 ? G * H : 1];
+        if constexpr (H > 0) {
+            constexpr int PW = PerWord<T>::value;
+#pragma unroll
+            for (int v = 0; v < NWV; ++v) {
+                unpack_word(wraw[k][v].x, &win[(4 * v + 0) * PW], T{});
+                unpack_word(wraw[k][v].y, &win[(4 * v + 1) * PW], T{});
+                unpack_word(wraw[k][v].z, &win[(4 * v + 2) * PW], T{});
+                unpack_word(wraw[k][v].w, &win[(4 * v + 3) * PW], T{});
+            }
+#pragma unroll
+            for (int q = 0; q < G * H; ++q)
+                win[q] = init ? win[q] : 0.0f;
+        }
         float o[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float acc = bias[g];
 #pragma unroll
             for (int q = 0; q < H; ++q)
-                acc = fmaf(w[g * W + q], win[k][g * H + q], acc);
+                acc = fmaf(w[g * W + q], win[g * H + q], acc);
             acc = fmaf(w[g * W + H], xv[k][g], acc);
             o[g] = a.apply_silu ? silu_f32(acc) : acc;
         }
@@ -575,7 +597,7 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
                 for (int g = 0; g < G; ++g) {
 #pragma unroll
                     for (int q = 0; q + 1 < H; ++q)
-                        nw[g * H + q] = win[k][g * H + q + 1];
+                        nw[g * H + q] = win[g * H + q + 1];
                     nw[g * H + H - 1] = xv[k][g];
                 }
                 store_vec_cached<T, G * H>(cs[k], nw);
