@@ -34,8 +34,8 @@ namespace ssm {
 
 namespace {
 constexpr int R = 16;        // lanes per channel
-constexpr int K = 16;        // timesteps per lane per tile
-constexpr int T = R * K;     // timesteps per tile
+constexpr int KD = 16;       // timesteps per lane per tile: dense batches
+constexpr int KP = 8;        // packed batches (half the padding at each sequence's last tile)
 constexpr int CPB = 256 / R; // channels per workgroup
 constexpr int NC = 16;       // states per LDS chunk of B/C
 } // namespace
@@ -48,7 +48,7 @@ constexpr int NC = 16;       // states per LDS chunk of B/C
 // issued unconditionally from a clamped, in-bounds address and the
 // out-of-range values are replaced afterwards, so all loads of a lane are in
 // flight together instead of each waiting behind its own branch.
-template <typename TI, bool VEC>
+template <typename TI, bool VEC, int K>
 __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, int lo, int hi, float (&dst)[K])
 {
     constexpr int E = 16 / StorageSize<TI>::value;
@@ -76,7 +76,7 @@ __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, i
 
 // Raw 128-bit loads of timesteps [tl, tl+K) of one row (VEC rows only),
 // issued back to back; widen() converts them once they are needed.
-template <typename TI>
+template <typename TI, int K>
 struct RawSteps {
     static constexpr int E = 16 / StorageSize<TI>::value;
     static constexpr int NV = K / E;
@@ -84,12 +84,12 @@ struct RawSteps {
     bool ok[NV];
 };
 
-template <typename TI>
-__device__ __forceinline__ void load_raw(RawSteps<TI> &r, const TI *__restrict__ row, int tl, int hi)
+template <typename TI, int K>
+__device__ __forceinline__ void load_raw(RawSteps<TI, K> &r, const TI *__restrict__ row, int tl, int hi)
 {
 #pragma unroll
-    for (int v = 0; v < RawSteps<TI>::NV; ++v) {
-        const int off = tl + v * RawSteps<TI>::E;
+    for (int v = 0; v < RawSteps<TI, K>::NV; ++v) {
+        const int off = tl + v * RawSteps<TI, K>::E;
         r.ok[v] = off < hi;
         r.w[v] = *reinterpret_cast<const u32x4 *>(row + (r.ok[v] ? off : 0));
     }
@@ -99,12 +99,12 @@ __device__ __forceinline__ void load_raw(RawSteps<TI> &r, const TI *__restrict__
 // in-bounds addresses, and the caller zeroes the step size and the input of
 // those columns, which makes them identity steps (decay 1, input 0) whose
 // outputs are never stored.
-template <typename TI>
-__device__ __forceinline__ void widen(const RawSteps<TI> &r, float (&dst)[K])
+template <typename TI, int K>
+__device__ __forceinline__ void widen(const RawSteps<TI, K> &r, float (&dst)[K])
 {
-    constexpr int E = RawSteps<TI>::E, PW = PerWord<TI>::value;
+    constexpr int E = RawSteps<TI, K>::E, PW = PerWord<TI>::value;
 #pragma unroll
-    for (int v = 0; v < RawSteps<TI>::NV; ++v) {
+    for (int v = 0; v < RawSteps<TI, K>::NV; ++v) {
         float part[E];
         unpack_word(r.w[v].x, &part[0 * PW], TI{});
         unpack_word(r.w[v].y, &part[1 * PW], TI{});
@@ -119,7 +119,7 @@ __device__ __forceinline__ void widen(const RawSteps<TI> &r, float (&dst)[K])
 // Store columns [tl, tl+K) that lie in [lo, hi): whole vectors where the
 // sequence covers them, single elements at its two ends (the neighbouring
 // columns belong to other sequences).
-template <typename TI, bool VEC>
+template <typename TI, bool VEC, int K>
 __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int lo, int hi, const float (&src)[K])
 {
     constexpr int E = 16 / StorageSize<TI>::value;
@@ -148,20 +148,23 @@ __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int lo
     }
 }
 
-// Register budget: the float16 vector paths (except per-state decays over
-// several state chunks) fit three waves per SIMD (at most 168 VGPRs) without
-// spilling; the other variants are allowed two.
-template <typename TI, bool VEC, bool A_PER_STATE, bool ONE_CHUNK>
+// Register budget: with 16 steps per lane the float16 vector paths (except
+// per-state decays over several state chunks) fit three waves per SIMD (at
+// most 168 VGPRs) without spilling, and the other variants are allowed two;
+// 8 steps per lane take about half the registers of the per-step arrays.
+template <typename TI, bool VEC, bool A_PER_STATE, bool ONE_CHUNK, int K>
 constexpr int scan_waves_per_simd()
 {
-    return (std::is_same<TI, f16>::value && VEC && (ONE_CHUNK || !A_PER_STATE)) ? 3 : 2;
+    return (std::is_same<TI, f16>::value && VEC && (ONE_CHUNK || !A_PER_STATE)) ? (K == KP ? 5 : 3)
+                                                                                    : (K == KP ? 3 : 2);
 }
 
-template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK>
+template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK, int K>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, VEC, A_PER_STATE, ONE_CHUNK>())))
+__attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, VEC, A_PER_STATE, ONE_CHUNK, K>())))
 void scan_kernel(ScanArgs a)
 {
+    constexpr int T = R * K;  // timesteps per tile
     constexpr int E = 16 / StorageSize<TI>::value;
     // B/C chunk in a lane-interleaved layout: the float4 holding timesteps
     // [16r + 4q, 16r + 4q + 4) of local state nl sits at (nl*(K/4) + q)*R + r,
@@ -225,11 +228,11 @@ void scan_kernel(ScanArgs a)
     for (int t0 = 0; t0 < hi; t0 += T) {
         const int tl = t0 + r * K;
         float dl[K], du[K], y[K];
-        RawSteps<TI> rz;  // the gate's loads are issued with the others
+        RawSteps<TI, K> rz;  // the gate's loads are issued with the others
         {
             float uu[K], dd[K];
             if constexpr (VEC) {
-                RawSteps<TI> ru, rd;
+                RawSteps<TI, K> ru, rd;
                 load_raw(ru, urow, tl, hi);
                 load_raw(rd, dtrow, tl, hi);
                 // 2-byte gates are fetched early (8 VGPRs); 4-byte ones at the end
@@ -238,8 +241,8 @@ void scan_kernel(ScanArgs a)
                 widen(ru, uu);
                 widen(rd, dd);
             } else {
-                load_steps<TI, VEC>(urow, tl, lo, hi, uu);
-                load_steps<TI, VEC>(dtrow, tl, lo, hi, dd);
+                load_steps<TI, VEC, K>(urow, tl, lo, hi, uu);
+                load_steps<TI, VEC, K>(dtrow, tl, lo, hi, dd);
             }
 #pragma unroll
             for (int i = 0; i < K; ++i) {
@@ -385,13 +388,13 @@ void scan_kernel(ScanArgs a)
             if constexpr (VEC && StorageSize<TI>::value == 2)
                 widen(rz, zz);
             else
-                load_steps<TI, VEC>(zrow, tl, lo, hi, zz);
+                load_steps<TI, VEC, K>(zrow, tl, lo, hi, zz);
 #pragma unroll
             for (int i = 0; i < K; ++i)
                 y[i] *= silu_f32(zz[i]);
         }
         if (active)
-            store_steps<TI, VEC>(orow, tl, lo, hi, y);
+            store_steps<TI, VEC, K>(orow, tl, lo, hi, y);
     }
     __syncthreads();
     if (srow && active)
@@ -402,10 +405,21 @@ void scan_kernel(ScanArgs a)
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC>
 static void launch_scan_v(const ScanArgs &a, dim3 grid, hipStream_t stream)
 {
-    if (a.dstate <= NC)
-        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false>), grid, dim3(256), 0, stream, a);
+    // Packed batches take 8 steps per lane: each sequence pads its last tile
+    // to a tile boundary, and halving the tile halves that waste (packed
+    // 16-sequence Mamba-1 prefill 281 -> 261 us).  Dense batches keep 16,
+    // whose lane scan costs less per step (227 vs 238 us).
+    if (a.cu_seqlens) {
+        if (a.dstate <= NC)
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, KP>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, KP>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (a.dstate <= NC)
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, KD>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, KD>), grid, dim3(256), 0, stream, a);
+    }
 }
 
 template <typename TI, typename TS>

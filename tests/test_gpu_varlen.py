@@ -112,8 +112,11 @@ def test_varlen_prefill_parity(dev, ssm, oracle, label, kw, lengths, pad):
 
 @pytest.mark.parametrize("io", ["f16", "f32"])
 def test_varlen_equal_lengths_match_dense_kernels(dev, ssm, io):
-    # sequences of one length packed side by side give the dense call's bits
-    # (same kernels, same arithmetic order)
+    # sequences of one length packed side by side give the dense call's
+    # results: the conv's bits, and the scan's up to the order of its sums
+    # (the packed scan walks 8 steps per lane, the dense one 16), within the
+    # parity tolerance of the io dtype; both are checked against the oracle
+    # elsewhere
     spec = W.tiny(io=io, state="f32", nheads=48, nslots=6, seed=21)
     L, nseq = 264, 3
     t = W.make_varlen(spec, [L] * nseq, dev, init_every=1)
@@ -136,9 +139,14 @@ def test_varlen_equal_lengths_match_dense_kernels(dev, ssm, io):
                              has_initial_state=True)
     torch.cuda.synchronize()
     assert torch.equal(dense(u_v), u_d)
-    assert torch.equal(dense(o_v), o_d)
     assert torch.equal(cs_v, cs_d)
-    assert torch.equal(st_v, st_d)
+    rtol = RTOL[io]
+    ov, od = dense(o_v).double(), o_d.double()
+    # |difference| <= rtol * max|o| + half an ulp of the io dtype at |o|
+    tol = rtol * od.abs().max() + 0.5 * od.abs() * (2.0 ** -10 if io == "f16" else 2.0 ** -23)
+    assert bool(((ov - od).abs() <= tol).all())
+    sv, sd = st_v.double(), st_d.double()
+    assert bool(((sv - sd).abs() <= 1e-5 * sd.abs().max()).all())
 
 
 def test_varlen_all_empty_is_noop(dev, ssm):
