@@ -11,13 +11,13 @@
 //   * Workgroup = 256 lanes = 16 channels x 16 lanes ("a row": one DPP row).
 //     All 16 channels belong to one (request, group), so they share one B/C
 //     stream, which is staged once per tile in LDS and read by all of them.
-//   * The sequence is walked in tiles of 256 timesteps; lane r of a channel
-//     owns timesteps [16r, 16r+16) of the tile (two or four 128-bit loads of
-//     u, dt and z).
-//   * For each state n, every lane reduces its 16 steps to one affine map
+//   * The sequence is walked in tiles of 16 K timesteps; lane r of a channel
+//     owns timesteps [K r, K r + K) of the tile (K = 16 for dense batches,
+//     8 for packed ones; one to four 128-bit loads of u, dt and z).
+//   * For each state n, every lane reduces its K steps to one affine map
 //     h -> a*h + b (a = product of decays, b = local state from zero), the 16
 //     maps of a row are combined by an inclusive Hillis-Steele scan with DPP
-//     row shifts (4 steps), and each lane then re-runs its 16 steps from the
+//     row shifts (4 steps), and each lane then re-runs its K steps from the
 //     exact incoming state, accumulating C_t[n] h_t[n] into its outputs.  The
 //     tile-end state of each channel (lane 15's scan result, rotated into lane
 //     0) carries to the next tile in registers (through LDS when dstate > 16).
