@@ -442,6 +442,14 @@ DECODE_CASES = [
      dict(pad=5)),
     ("ilv_m1_f32_noz_noD", dict(seqlen=1, nheads=2048, dstate=16, io="f32", state="f32", batch=128,
                                 index_sensitive=True), dict(z=False, D=False, bias=False)),
+    # the quad-shared conv with 16 lanes per row (every quad of a row computes
+    # it, the first one writes the window), and the per-lane conv at 2 lanes
+    # per row
+    ("ilv_m2_hd64_N128_f16_conv_16_lanes", dict(seqlen=1, nheads=64, headdim=64, dstate=128, io="f16",
+                                                state="f16", a_per_state=False, batch=65, nslots=70,
+                                                random_slots=True, index_sensitive=True), dict(pad=2)),
+    ("ilv_N8_f32_conv_2_lanes", dict(seqlen=1, nheads=2048, headdim=2, dstate=8, io="bf16", state="f32",
+                                     batch=65, index_sensitive=True), {}),
 ]
 
 
