@@ -253,7 +253,9 @@ def summarize_profile(out):
           "Command (run from the repository root on the MI355X):", "",
           f"    {cmds['varlen_trace']}", "",
           "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    for sym in ("conv_varlen_kernel", "conv_varlen_tail_kernel", "scan_kernel"):
+    # a plain sequence table runs the dense row kernel over the packed rows
+    # (its tail pass fixes the starts); other tables the tiled kernel
+    for sym in ("conv_rows_kernel", "conv_varlen_kernel", "conv_varlen_tail_kernel", "scan_kernel"):
         rows = [r for r in vstats if sym in r["Name"] and
                 (sym != "conv_varlen_kernel" or "tail" not in r["Name"])]
         calls = sum(int(r["Calls"]) for r in rows)

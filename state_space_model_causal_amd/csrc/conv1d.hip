@@ -17,9 +17,13 @@
 // final W-1 samples go to the cache at the end.
 //
 // Packed variable-length batches (sequences of different lengths side by side
-// along time, each with its own slot and initial-state flag) use a row-tiled
-// kernel whose workgroups each take one tile of a packed channel row, plus a
-// tail kernel that updates the caches afterwards.
+// along time, each with its own slot and initial-state flag), when the packed
+// rows suit the dense row kernel and the sequence table is plain (no padded
+// sequence, columns covered exactly): the dense conv of each packed row, then
+// a tail kernel that redoes the first W-1 outputs of every sequence from its
+// own history and updates the caches.  Other tables take a start-aware
+// row-tiled path (each workgroup one tile of a packed channel row) before the
+// same tail kernel's cache update.
 //
 // Decode kernels (seqlen == 1): gather the window from the slot, one output,
 // shift the window by one in place.  The vector kernel gives each lane 8
@@ -116,7 +120,11 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
 // the row's history instead (the slot's cache or zeros).  Lane 0 reads the
 // histories before its first chunk and writes the rows' new tails after the
 // walk, so the two accesses to a cache slot are ordered within one lane.
-template <typename T, int W, int RPW>
+template <typename T, int W, bool VEC>
+__device__ __forceinline__ void conv_varlen_tile(const ConvArgs &a, const int k, const int c);
+__device__ __forceinline__ bool varlen_table_plain(const ConvArgs &a);
+
+template <typename T, int W, int RPW, bool VARLEN>
 __global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
 {
     constexpr int E = 16 / StorageSize<T>::value;  // samples per 128-bit access
@@ -124,8 +132,32 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
     constexpr int PW = 4;                           // samples loaded in front of a chunk (>= H)
     constexpr int PB = PW * StorageSize<T>::value;  // their bytes: 8 or 16
     using Prev = typename std::conditional<PB == 16, u32x4, uint2>::type;
-    const int64_t nrows = (int64_t)a.batch * a.channels;
     const int64_t row0 = (int64_t)xcd_block_order(blockIdx.x, gridDim.x) * RPW;
+    if constexpr (VARLEN) {
+        // A packed batch: with a plain sequence table, the dense conv of each
+        // packed channel row (one request, no history); the tail pass then
+        // redoes the first W-1 outputs of every sequence.  Otherwise the
+        // workgroup walks its rows tile by tile with the start-aware code.
+        if (!varlen_table_plain(a)) {
+            constexpr int TILE = 256 * E;
+            const int ntiles = (a.seqlen + TILE - 1) / TILE;
+            for (int r = 0; r < RPW; ++r) {
+                const int64_t c = row0 + r;
+                if (c >= a.channels)
+                    break;
+                for (int k = 0; k < ntiles; ++k) {
+                    __syncthreads();  // the previous tile's LDS is free
+                    conv_varlen_tile<T, W, true>(a, k, (int)c);
+                }
+            }
+            return;
+        }
+        a.batch = 1;
+        a.slot_idx = nullptr;
+        a.conv_state = nullptr;
+        a.has_initial_state = 0;
+    }
+    const int64_t nrows = (int64_t)a.batch * a.channels;
     const int tid = threadIdx.x, L = a.seqlen;
 
     float w[RPW][W], bias[RPW], hist[RPW][PW];
@@ -245,7 +277,7 @@ __device__ __forceinline__ int cu_at(const int32_t *__restrict__ cu, int i, int 
 }
 
 template <typename T, int W, bool VEC>
-__global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
+__device__ __forceinline__ void conv_varlen_tile(const ConvArgs &a, const int k, const int c)
 {
     constexpr int E = 16 / StorageSize<T>::value;
     constexpr int TILE = 256 * E;
@@ -258,7 +290,6 @@ __global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
     __shared__ unsigned char sseq[TILE + 32];  // at a start column: the sequence starting there
     __shared__ float lhist[kSeqCap][HS];       // history of each sequence starting in the tile
 
-    const int k = blockIdx.x, c = blockIdx.y;  // tile, channel
     const int Tn = a.seqlen, tid = threadIdx.x, nseq = a.batch;
     const int64_t first = (int64_t)c * Tn;     // column 0 of row c
     const int m = VEC ? (int)(first % E) : 0;  // vector alignment of the row
@@ -441,14 +472,47 @@ __global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
     }
 }
 
-// Conv caches of a packed batch, after conv_varlen_kernel: one lane per
+template <typename T, int W, bool VEC>
+__global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
+{
+    conv_varlen_tile<T, W, VEC>(a, blockIdx.x, blockIdx.y);  // tile, channel
+}
+
+// True (in every lane of the workgroup) when the sequence table of a packed
+// batch of at most 255 sequences covers the packed row exactly and holds no
+// padded sequence: cu_seqlens rises from 0 to the packed length and every
+// slot is valid.  Then every column belongs to exactly one sequence and
+// every output is written.
+__device__ __forceinline__ bool varlen_table_plain(const ConvArgs &a)
+{
+    const int tid = threadIdx.x, nseq = a.batch;
+    int bad = 0;
+    if (tid <= nseq) {
+        const int cb = a.cu_seqlens[tid];
+        const int ce = a.cu_seqlens[tid < nseq ? tid + 1 : tid];
+        const int slot = (tid < nseq && a.slot_idx) ? a.slot_idx[tid] : 0;
+        bad = ce < cb || (tid == 0 && cb != 0) || (tid == nseq && cb != a.seqlen) || slot < 0;
+    }
+    return __syncthreads_or(bad) == 0;
+}
+
+// Conv caches of a packed batch, after the conv pass: one lane per
 // (sequence, channel) copies the last W-1 samples of history || sequence
 // into the slot.  Each lane reads only the cache row it writes.
-template <typename T, int W>
+//
+// FIX: the conv pass ran the dense conv over the whole packed row (a plain
+// table), so the first W-1 outputs of every sequence took their taps in front
+// of the start from the previous sequence; the lane recomputes them from the
+// sequence's own history (its slot's cache, or zeros) before replacing that
+// cache.  The lane sums the taps in the same order as the conv pass.
+template <typename T, int W, bool FIX>
 __global__ __launch_bounds__(256) void conv_varlen_tail_kernel(ConvArgs a)
 {
     constexpr int H = W - 1;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // with a table that is not plain the conv pass took the tiled path,
+    // which handles the starts itself
+    const bool fix = FIX && varlen_table_plain(a);
     if (i >= (int64_t)a.batch * a.channels)
         return;
     const int s = (int)(i / a.channels), c = (int)(i % a.channels);
@@ -459,9 +523,35 @@ __global__ __launch_bounds__(256) void conv_varlen_tail_kernel(ConvArgs a)
     if (slot < 0 || te == tb)
         return;
     const bool init = a.has_init_seq && a.has_init_seq[s] != 0;
-    T *cs = static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H;
+    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
     const T *xr = static_cast<const T *>(a.x) + (int64_t)c * Tn + tb;
     const int len = te - tb;
+    if (fix) {
+        float hx[2 * (H > 0 ? H : 1)];  // history || the first H samples (zeros past the end)
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            hx[k] = (init && cs) ? to_f32(cs[k]) : 0.0f;
+            hx[H + k] = k < len ? to_f32(xr[k]) : 0.0f;
+        }
+        const float bias = a.bias ? a.bias[c] : 0.0f;
+        float w[W];
+#pragma unroll
+        for (int kk = 0; kk < W; ++kk)
+            w[kk] = a.weight[(int64_t)c * W + kk];
+        T *orow = static_cast<T *>(a.out) + (int64_t)c * Tn + tb;
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            if (j >= len)
+                break;
+            float acc = bias;
+#pragma unroll
+            for (int kk = 0; kk < W; ++kk)
+                acc = fmaf(w[kk], hx[j + kk], acc);
+            orow[j] = from_f32<T>(a.apply_silu ? silu_f32(acc) : acc);
+        }
+    }
+    if (!cs)
+        return;
     T v[H > 0 ? H : 1];
 #pragma unroll
     for (int k = 0; k < H; ++k) {
@@ -621,6 +711,18 @@ static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
         const int64_t n = (int64_t)a.batch * a.channels;
         hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            stream, a);
+    } else if (a.cu_seqlens && a.vec && a.seqlen % 8 == 0 && a.batch <= 255) {
+        // packed batch whose rows the dense kernel can walk: the dense conv
+        // (or, for a table with padded sequences, the tiled code) and the
+        // tail pass that fixes the starts and writes the caches
+        constexpr int RPW = 2;
+        const dim3 grid((unsigned)((a.channels + RPW - 1) / RPW));
+        hipLaunchKernelGGL((conv_rows_kernel<T, W, RPW, true>), grid, dim3(256), 0, stream, a);
+        if (W > 1) {
+            const int64_t n = (int64_t)a.batch * a.channels;
+            hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W, true>), dim3((unsigned)((n + 255) / 256)),
+                               dim3(256), 0, stream, a);
+        }
     } else if (a.cu_seqlens) {
         constexpr int E = 16 / StorageSize<T>::value;
         // rows start inside a vector only when the packed length is not a
@@ -633,13 +735,13 @@ static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
             hipLaunchKernelGGL((conv_varlen_kernel<T, W, false>), grid, dim3(256), 0, stream, a);
         if (a.conv_state && W > 1) {  // the caches, once every tile has read them
             const int64_t n = (int64_t)a.batch * a.channels;
-            hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256),
-                               0, stream, a);
+            hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W, false>), dim3((unsigned)((n + 255) / 256)),
+                               dim3(256), 0, stream, a);
         }
     } else if (a.vec) {
         constexpr int RPW = 2;  // rows per workgroup
         const dim3 grid((unsigned)(((int64_t)a.batch * a.channels + RPW - 1) / RPW));
-        hipLaunchKernelGGL((conv_rows_kernel<T, W, RPW>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((conv_rows_kernel<T, W, RPW, false>), grid, dim3(256), 0, stream, a);
     } else {
         const dim3 grid((unsigned)((int64_t)a.batch * a.channels));
         hipLaunchKernelGGL((conv_prefill_kernel<T, W, false>), grid, dim3(256), 0, stream, a);

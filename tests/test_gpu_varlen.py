@@ -54,6 +54,14 @@ VARLEN_CASES = [
                           a_per_state=False, nslots=4, seed=17), [261, 0, 6, 3], None),  # 270
     ("m2_f16_N16_G4", dict(io="f16", state="bf16", nheads=8, headdim=4, dstate=16, ngroups=4,
                            a_per_state=False, nslots=6, seed=18), [1, 1, 510, 8], 0),   # 520
+    # plain tables (no padded sequence, vector totals): the conv runs the dense
+    # kernel over the packed rows, and the tail pass redoes each sequence's
+    # first width-1 outputs from its history, here for sequences shorter
+    # than the window too
+    ("m1_f16_vec_mix_plain", dict(io="f16", state="f32", nheads=64, nslots=16, seed=21),
+     [0, 1, 2, 3, 5, 17, 255, 256, 257, 700], None),                  # total 1496 (vec)
+    ("m1_f32_w3_plain", dict(io="f32", state="f32", nheads=20, dstate=20, width=3, nslots=8,
+                             seed=22), [9, 600, 31, 0, 2, 6], None),  # total 648 (vec)
     # more sequences than the conv kernel stages in LDS (its global-table path)
     ("m1_f16_300_seqs", dict(io="f16", state="f32", nheads=8, nslots=320, seed=19),
      [0, 3] + W.varlen_lengths(19, 298, 2395), None),                    # total 2398
