@@ -159,6 +159,35 @@ constexpr int scan_waves_per_simd()
                                                                                     : (K == KP ? 3 : 2);
 }
 
+// Packed batches of at most 256 sequences: the sequence of rank r when the
+// sequences are sorted by length, longest first (ties by index).  Every
+// workgroup derives the same order from the table, so the ranks form a
+// permutation whatever the table holds.  Call from every lane.
+__device__ __forceinline__ int packed_seq_of_rank(const int32_t *__restrict__ cu, int nseq, int L, int r)
+{
+    __shared__ int s_len[256];
+    __shared__ int s_pick;
+    const int tid = threadIdx.x;
+    int len = 0;
+    if (tid < nseq) {
+        const int lo = min(max(cu[tid], 0), L);
+        len = min(max(cu[tid + 1], lo), L) - lo;
+        s_len[tid] = len;
+    }
+    __syncthreads();
+    if (tid < nseq) {
+        int rank = 0;
+        for (int j = 0; j < nseq; ++j) {
+            const int lj = s_len[j];
+            rank += (lj > len || (lj == len && j < tid)) ? 1 : 0;
+        }
+        if (rank == r)
+            s_pick = tid;
+    }
+    __syncthreads();
+    return s_pick;
+}
+
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK, int K>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, VEC, A_PER_STATE, ONE_CHUNK, K>())))
@@ -188,7 +217,15 @@ void scan_kernel(ScanArgs a)
     const uint32_t lb = a.cu_seqlens ? blockIdx.x : xcd_block_order(blockIdx.x, gridDim.x);
     const int cb = (int)(lb % nblk_g);
     const int bg = (int)(lb / nblk_g);
-    const int g = bg % a.ngroups, b = bg / a.ngroups;
+    const int g = bg % a.ngroups;
+    int b = bg / a.ngroups;
+    if constexpr (K == KP) {
+        // packed batches (the only ones with 8 steps per lane): the longest
+        // sequences' workgroups start first, so the longest walks do not
+        // begin late and leave the chip idle at the end
+        if (a.batch <= 256)
+            b = packed_seq_of_rank(a.cu_seqlens, a.batch, L, b);
+    }
     const SeqSpan sp = seq_span(a.cu_seqlens, a.has_init_seq, b, L, a.has_initial_state);
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0 || sp.len == 0)
