@@ -253,8 +253,9 @@ def summarize_profile(out):
           "Command (run from the repository root on the MI355X):", "",
           f"    {cmds['varlen_trace']}", "",
           "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    # a plain sequence table runs the dense row kernel over the packed rows
-    # (its tail pass fixes the starts); other tables the tiled kernel
+    # aligned packed rows of at most 255 sequences: the row kernel, which
+    # also fixes the starts and writes the caches; other packed rows: the
+    # tiled kernel and its cache pass
     for sym in ("conv_rows_kernel", "conv_varlen_kernel", "conv_varlen_tail_kernel", "scan_kernel"):
         rows = [r for r in vstats if sym in r["Name"] and
                 (sym != "conv_varlen_kernel" or "tail" not in r["Name"])]
@@ -265,7 +266,7 @@ def summarize_profile(out):
                       f"{min(float(r['MinNs']) for r in rows) / 1e3:.1f} | "
                       f"{max(float(r['MaxNs']) for r in rows) / 1e3:.1f} |")
     if vline:
-        vl += ["", f"Event-timed in the same run: conv1d (with the cache-tail pass) "
+        vl += ["", f"Event-timed in the same run: conv1d (the whole call) "
                    f"{vline['conv1d_varlen']['us']:.1f} us for {vline['conv1d_varlen']['bytes'] / 1e6:.1f} MB, "
                    f"scan {vline['selective_scan_varlen']['us']:.1f} us for "
                    f"{vline['selective_scan_varlen']['bytes'] / 1e6:.1f} MB; "

@@ -18,12 +18,14 @@
 //
 // Packed variable-length batches (sequences of different lengths side by side
 // along time, each with its own slot and initial-state flag), when the packed
-// rows suit the dense row kernel and the sequence table is plain (no padded
-// sequence, columns covered exactly): the dense conv of each packed row, then
-// a tail kernel that redoes the first W-1 outputs of every sequence from its
-// own history and updates the caches.  Other tables take a start-aware
-// row-tiled path (each workgroup one tile of a packed channel row) before the
-// same tail kernel's cache update.
+// rows suit the dense row kernel: each workgroup owns whole channel rows.
+// With a plain sequence table (no padded sequence, columns covered exactly)
+// it runs the dense conv of each packed row and then redoes the first W-1
+// outputs of every sequence from the sequence's own history; with any other
+// table it walks the rows tile by tile with start-aware code.  Either way it
+// writes the rows' new cache tails last.  Other packed rows (unaligned, or
+// more than 255 sequences) take the tiled code with one workgroup per tile
+// and a separate pass for the caches.
 //
 // Decode kernels (seqlen == 1): gather the window from the slot, one output,
 // shift the window by one in place.  The vector kernel gives each lane 8
@@ -120,43 +122,14 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
 // the row's history instead (the slot's cache or zeros).  Lane 0 reads the
 // histories before its first chunk and writes the rows' new tails after the
 // walk, so the two accesses to a cache slot are ordered within one lane.
-template <typename T, int W, bool VEC>
-__device__ __forceinline__ void conv_varlen_tile(const ConvArgs &a, const int k, const int c);
-__device__ __forceinline__ bool varlen_table_plain(const ConvArgs &a);
-
-template <typename T, int W, int RPW, bool VARLEN>
-__global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
+template <typename T, int W, int RPW>
+__device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t row0)
 {
     constexpr int E = 16 / StorageSize<T>::value;  // samples per 128-bit access
     constexpr int H = W - 1;
     constexpr int PW = 4;                           // samples loaded in front of a chunk (>= H)
     constexpr int PB = PW * StorageSize<T>::value;  // their bytes: 8 or 16
     using Prev = typename std::conditional<PB == 16, u32x4, uint2>::type;
-    const int64_t row0 = (int64_t)xcd_block_order(blockIdx.x, gridDim.x) * RPW;
-    if constexpr (VARLEN) {
-        // A packed batch: with a plain sequence table, the dense conv of each
-        // packed channel row (one request, no history); the tail pass then
-        // redoes the first W-1 outputs of every sequence.  Otherwise the
-        // workgroup walks its rows tile by tile with the start-aware code.
-        if (!varlen_table_plain(a)) {
-            constexpr int TILE = 256 * E;
-            const int ntiles = (a.seqlen + TILE - 1) / TILE;
-            for (int r = 0; r < RPW; ++r) {
-                const int64_t c = row0 + r;
-                if (c >= a.channels)
-                    break;
-                for (int k = 0; k < ntiles; ++k) {
-                    __syncthreads();  // the previous tile's LDS is free
-                    conv_varlen_tile<T, W, true>(a, k, (int)c);
-                }
-            }
-            return;
-        }
-        a.batch = 1;
-        a.slot_idx = nullptr;
-        a.conv_state = nullptr;
-        a.has_initial_state = 0;
-    }
     const int64_t nrows = (int64_t)a.batch * a.channels;
     const int tid = threadIdx.x, L = a.seqlen;
 
@@ -267,8 +240,10 @@ __global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
 // sequence, and tables of more than kSeqCap sequences, take a
 // column-by-column path that reads the table from global memory.
 //
-// The caches are not written here: conv_varlen_tail_kernel runs afterwards,
-// so no workgroup can overwrite a history that another one still has to read.
+// The caches are not written here: they are written after every tile of a
+// channel has read its histories (by conv_varlen_tail_kernel when each tile
+// is its own workgroup, at the end of the row kernel when one workgroup
+// walks all tiles of its channels).
 constexpr int kSeqCap = 255;
 
 __device__ __forceinline__ int cu_at(const int32_t *__restrict__ cu, int i, int T)
@@ -478,41 +453,150 @@ __global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
     conv_varlen_tile<T, W, VEC>(a, blockIdx.x, blockIdx.y);  // tile, channel
 }
 
-// True (in every lane of the workgroup) when the sequence table of a packed
-// batch of at most 255 sequences covers the packed row exactly and holds no
-// padded sequence: cu_seqlens rises from 0 to the packed length and every
-// slot is valid.  Then every column belongs to exactly one sequence and
-// every output is written.
-__device__ __forceinline__ bool varlen_table_plain(const ConvArgs &a)
+// A packed batch over the dense row kernel's grid: the workgroup owns its
+// channel rows for every sequence, so it alone reads and rewrites those rows'
+// caches and no separate cache pass is needed.
+//
+// Plain sequence table (every slot valid, cu_seqlens rising from 0 to the
+// packed length): the dense conv of each packed channel row as one request
+// with no history; then one lane per (sequence, row) redoes the sequence's
+// first W-1 outputs, whose taps in front of the start read the previous
+// sequence's samples, from the sequence's own history (its slot's cache, or
+// zeros), summing the taps in the dense order.  Any other table: the
+// start-aware tiled code over the rows (it leaves padded sequences' columns
+// untouched).  Either way the same lanes then write each sequence's new cache
+// tail, the last W-1 samples of history || sequence.
+template <typename T, int W, int RPW>
+__device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
 {
-    const int tid = threadIdx.x, nseq = a.batch;
-    int bad = 0;
+    constexpr int E = 16 / StorageSize<T>::value;
+    constexpr int H = W - 1;
+    constexpr int HS = H > 0 ? H : 1;
+    const int tid = threadIdx.x, nseq = a.batch, Tn = a.seqlen;
+    const ConvArgs pa = a;  // the packed-batch arguments
+    // lane t <= nseq: entry t of the table (lane t < nseq: sequence t)
+    int cb = 0, ce = 0, slot = -1, bad = 0;
+    bool init = false;
     if (tid <= nseq) {
-        const int cb = a.cu_seqlens[tid];
-        const int ce = a.cu_seqlens[tid < nseq ? tid + 1 : tid];
-        const int slot = (tid < nseq && a.slot_idx) ? a.slot_idx[tid] : 0;
-        bad = ce < cb || (tid == 0 && cb != 0) || (tid == nseq && cb != a.seqlen) || slot < 0;
+        cb = a.cu_seqlens[tid];
+        ce = a.cu_seqlens[tid < nseq ? tid + 1 : tid];
+        slot = tid < nseq ? (a.slot_idx ? a.slot_idx[tid] : tid) : -1;
+        init = tid < nseq && a.has_init_seq && a.has_init_seq[tid] != 0;
+        bad = ce < cb || (tid == 0 && cb != 0) || (tid == nseq && cb != Tn) || (tid < nseq && slot < 0);
     }
-    return __syncthreads_or(bad) == 0;
+    const bool plain = __syncthreads_or(bad) == 0;
+    if (plain) {
+        a.batch = 1;
+        a.slot_idx = nullptr;
+        a.conv_state = nullptr;
+        a.has_initial_state = 0;
+        conv_rows_walk<T, W, RPW>(a, row0);
+    } else {
+        constexpr int TILE = 256 * E;
+        const int ntiles = (Tn + TILE - 1) / TILE;
+        for (int r = 0; r < RPW; ++r) {
+            const int64_t c = row0 + r;
+            if (c >= pa.channels)
+                break;
+            for (int k = 0; k < ntiles; ++k) {
+                __syncthreads();  // the previous tile's LDS is free
+                conv_varlen_tile<T, W, true>(pa, k, (int)c);
+            }
+        }
+    }
+    if (H == 0)
+        return;
+    // every wave's stores of the rows' outputs have completed (reached the
+    // L2, which all waves of the workgroup write through) before any lane
+    // rewrites a start: vmcnt(0), expcnt and lgkmcnt left free
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (tid >= nseq || slot < 0)
+        return;
+    const int tb = min(max(cb, 0), Tn);
+    const int te = min(max(ce, tb), Tn);
+    const int len = te - tb;
+    if (len == 0)
+        return;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int64_t c = row0 + r;
+        if (c >= pa.channels)
+            break;
+        T *cs = pa.conv_state ? static_cast<T *>(pa.conv_state) + ((int64_t)slot * pa.channels + c) * H
+                              : nullptr;
+        const T *xr = static_cast<const T *>(pa.x) + c * Tn + tb;
+        // every sample the lane needs, from in-bounds addresses, issued
+        // together: the cached history, the first and the last H samples
+        T hraw[HS], xb[HS], xe[HS];
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            hraw[k] = cs ? cs[k] : from_f32<T>(0.0f);
+            xb[k] = xr[min(k, len - 1)];
+            xe[k] = xr[max(len - H + k, 0)];
+        }
+        if (plain) {
+            float hx[2 * HS];  // history || the first H samples (zeros past the end)
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
+                hx[k] = init ? to_f32(hraw[k]) : 0.0f;
+                hx[H + k] = k < len ? to_f32(xb[k]) : 0.0f;
+            }
+            float w[W];
+#pragma unroll
+            for (int kk = 0; kk < W; ++kk)
+                w[kk] = pa.weight[c * W + kk];
+            const float bias = pa.bias ? pa.bias[c] : 0.0f;
+            T *orow = static_cast<T *>(pa.out) + c * Tn + tb;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                if (j >= len)
+                    break;
+                float acc = bias;
+#pragma unroll
+                for (int kk = 0; kk < W; ++kk)
+                    acc = fmaf(w[kk], hx[j + kk], acc);
+                orow[j] = from_f32<T>(pa.apply_silu ? silu_f32(acc) : acc);
+            }
+        }
+        if (cs) {
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
+                const int tau = len - H + k;  // step of the k-th kept sample
+                T v = from_f32<T>(0.0f);      // before the sequence, with no history
+                if (tau >= 0) {
+                    v = xe[k];
+                } else if (init) {
+#pragma unroll
+                    for (int m = 0; m < H; ++m)
+                        if (m == H + tau)
+                            v = hraw[m];
+                }
+                cs[k] = v;
+            }
+        }
+    }
 }
 
-// Conv caches of a packed batch, after the conv pass: one lane per
+template <typename T, int W, int RPW, bool VARLEN>
+__global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
+{
+    const int64_t row0 = (int64_t)xcd_block_order(blockIdx.x, gridDim.x) * RPW;
+    if constexpr (VARLEN)
+        conv_rows_packed<T, W, RPW>(a, row0);
+    else
+        conv_rows_walk<T, W, RPW>(a, row0);
+}
+
+
+// Conv caches of a packed batch, after conv_varlen_kernel: one lane per
 // (sequence, channel) copies the last W-1 samples of history || sequence
 // into the slot.  Each lane reads only the cache row it writes.
-//
-// FIX: the conv pass ran the dense conv over the whole packed row (a plain
-// table), so the first W-1 outputs of every sequence took their taps in front
-// of the start from the previous sequence; the lane recomputes them from the
-// sequence's own history (its slot's cache, or zeros) before replacing that
-// cache.  The lane sums the taps in the same order as the conv pass.
-template <typename T, int W, bool FIX>
+template <typename T, int W>
 __global__ __launch_bounds__(256) void conv_varlen_tail_kernel(ConvArgs a)
 {
     constexpr int H = W - 1;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    // with a table that is not plain the conv pass took the tiled path,
-    // which handles the starts itself
-    const bool fix = FIX && varlen_table_plain(a);
     if (i >= (int64_t)a.batch * a.channels)
         return;
     const int s = (int)(i / a.channels), c = (int)(i % a.channels);
@@ -523,35 +607,9 @@ __global__ __launch_bounds__(256) void conv_varlen_tail_kernel(ConvArgs a)
     if (slot < 0 || te == tb)
         return;
     const bool init = a.has_init_seq && a.has_init_seq[s] != 0;
-    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
+    T *cs = static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H;
     const T *xr = static_cast<const T *>(a.x) + (int64_t)c * Tn + tb;
     const int len = te - tb;
-    if (fix) {
-        float hx[2 * (H > 0 ? H : 1)];  // history || the first H samples (zeros past the end)
-#pragma unroll
-        for (int k = 0; k < H; ++k) {
-            hx[k] = (init && cs) ? to_f32(cs[k]) : 0.0f;
-            hx[H + k] = k < len ? to_f32(xr[k]) : 0.0f;
-        }
-        const float bias = a.bias ? a.bias[c] : 0.0f;
-        float w[W];
-#pragma unroll
-        for (int kk = 0; kk < W; ++kk)
-            w[kk] = a.weight[(int64_t)c * W + kk];
-        T *orow = static_cast<T *>(a.out) + (int64_t)c * Tn + tb;
-#pragma unroll
-        for (int j = 0; j < H; ++j) {
-            if (j >= len)
-                break;
-            float acc = bias;
-#pragma unroll
-            for (int kk = 0; kk < W; ++kk)
-                acc = fmaf(w[kk], hx[j + kk], acc);
-            orow[j] = from_f32<T>(a.apply_silu ? silu_f32(acc) : acc);
-        }
-    }
-    if (!cs)
-        return;
     T v[H > 0 ? H : 1];
 #pragma unroll
     for (int k = 0; k < H; ++k) {
@@ -713,16 +771,11 @@ static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
                            stream, a);
     } else if (a.cu_seqlens && a.vec && a.seqlen % 8 == 0 && a.batch <= 255) {
         // packed batch whose rows the dense kernel can walk: the dense conv
-        // (or, for a table with padded sequences, the tiled code) and the
-        // tail pass that fixes the starts and writes the caches
+        // (or, for a table with padded sequences, the tiled code), then the
+        // starts and the caches, in one launch
         constexpr int RPW = 2;
         const dim3 grid((unsigned)((a.channels + RPW - 1) / RPW));
         hipLaunchKernelGGL((conv_rows_kernel<T, W, RPW, true>), grid, dim3(256), 0, stream, a);
-        if (W > 1) {
-            const int64_t n = (int64_t)a.batch * a.channels;
-            hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W, true>), dim3((unsigned)((n + 255) / 256)),
-                               dim3(256), 0, stream, a);
-        }
     } else if (a.cu_seqlens) {
         constexpr int E = 16 / StorageSize<T>::value;
         // rows start inside a vector only when the packed length is not a
@@ -735,8 +788,8 @@ static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
             hipLaunchKernelGGL((conv_varlen_kernel<T, W, false>), grid, dim3(256), 0, stream, a);
         if (a.conv_state && W > 1) {  // the caches, once every tile has read them
             const int64_t n = (int64_t)a.batch * a.channels;
-            hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W, false>), dim3((unsigned)((n + 255) / 256)),
-                               dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((conv_varlen_tail_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                               0, stream, a);
         }
     } else if (a.vec) {
         constexpr int RPW = 2;  // rows per workgroup
