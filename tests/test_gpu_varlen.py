@@ -219,3 +219,19 @@ def test_varlen_then_decode_continues(dev, ssm, oracle):
         # the last step of the long prefill is the decode token; the GPU's
         # decode reads u in float32, as does this float64 chain
         check(yd[s].reshape(H), o[0, :, -1], sc[0, :, -1], 1e-5, "f32", f"decode after varlen {s}")
+
+
+@pytest.mark.parametrize("io,silu", [("f16", True), ("f32", False)])
+def test_varlen_conv_without_cache(dev, ssm, oracle, io, silu):
+    """No conv cache, no slot table, no bias: every sequence starts from zeros
+    (the row kernel's start fix-up with an empty history), with and without
+    the SiLU."""
+    spec = W.tiny(io=io, state="f32", nheads=16, nslots=8, seed=25)
+    lengths = [3, 1, 700, 0, 2, 90, 4]  # total 800 (vector rows)
+    t = W.make_varlen(spec, lengths, dev)
+    cu = t["cu_seqlens"]
+    u = ssm.causal_conv1d_varlen(t["x"], t["conv_w"], cu, apply_silu=silu)
+    torch.cuda.synchronize()
+    uo, us, _ = oracle.causal_conv1d_varlen(f(t["x"]), f(t["conv_w"]), cu.cpu().numpy(),
+                                            apply_silu=silu)
+    check(u, uo, us, RTOL[io], io, f"varlen conv without cache {io}")
