@@ -737,8 +737,8 @@ def measure_varlen(ssm, W, dev, stream, steps, warmup):
     """Packed variable-length prefill (continuous batching): 16 sequences of
     mixed lengths, 8192 tokens in all (the token count of the dense prefill),
     every other one continuing from its slot of a 512-slot cache; conv1d
-    (with its cache-tail pass) then the scan, each timed with events on the
-    launch stream over two rotating buffer sets."""
+    (the whole call, caches included) then the scan, each timed with events
+    on the launch stream over two rotating buffer sets."""
     import numpy as np
     import torch
 
