@@ -19,10 +19,11 @@
 // Packed variable-length batches (sequences of different lengths side by side
 // along time, each with its own slot and initial-state flag), when the packed
 // rows suit the dense row kernel: each workgroup owns whole channel rows.
-// With a plain sequence table (no padded sequence, columns covered exactly)
-// it runs the dense conv of each packed row and then redoes the first W-1
-// outputs of every sequence from the sequence's own history; with any other
-// table it walks the rows tile by tile with start-aware code.  Either way it
+// With a sequence table that covers the columns exactly (and at most 8 padded
+// sequences, whose columns it stores around) it runs the dense conv of each
+// packed row and then redoes the first W-1 outputs of every sequence from the
+// sequence's own history; with any other table it walks the rows tile by
+// tile with start-aware code.  Either way it
 // writes the rows' new cache tails last.  Other packed rows (unaligned, or
 // more than 255 sequences) take the tiled code with one workgroup per tile
 // and a separate pass for the caches.
@@ -122,8 +123,9 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
 // the row's history instead (the slot's cache or zeros).  Lane 0 reads the
 // histories before its first chunk and writes the rows' new tails after the
 // walk, so the two accesses to a cache slot are ordered within one lane.
-template <typename T, int W, int RPW>
-__device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t row0)
+template <typename T, int W, int RPW, bool MASKED = false>
+__device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t row0,
+                                               const int *pads = nullptr, int npad = 0)
 {
     constexpr int E = 16 / StorageSize<T>::value;  // samples per 128-bit access
     constexpr int H = W - 1;
@@ -205,6 +207,24 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
                 for (int k = 0; k < W; ++k)
                     acc = fmaf(w[r][k], xw[PW - H + i + k], acc);
                 o[i] = a.apply_silu ? silu_f32(acc) : acc;
+            }
+            if constexpr (MASKED) {
+                // column ranges [pads[2j], pads[2j+1]) of padded sequences
+                // stay untouched: a chunk meeting one stores around it
+                bool hit = false;
+                for (int j = 0; j < npad; ++j)
+                    hit = hit || (tc < pads[2 * j + 1] && tc + E > pads[2 * j]);
+                if (hit) {
+#pragma unroll
+                    for (int i = 0; i < E; ++i) {
+                        bool pad = false;
+                        for (int j = 0; j < npad; ++j)
+                            pad = pad || (tc + i >= pads[2 * j] && tc + i < pads[2 * j + 1]);
+                        if (!pad)
+                            orow[r][tc + i] = from_f32<T>(o[i]);
+                    }
+                    continue;
+                }
             }
             store_vec<T, E>(orow[r] + tc, o);
         }
@@ -457,15 +477,16 @@ __global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
 // channel rows for every sequence, so it alone reads and rewrites those rows'
 // caches and no separate cache pass is needed.
 //
-// Plain sequence table (every slot valid, cu_seqlens rising from 0 to the
-// packed length): the dense conv of each packed channel row as one request
-// with no history; then one lane per (sequence, row) redoes the sequence's
-// first W-1 outputs, whose taps in front of the start read the previous
-// sequence's samples, from the sequence's own history (its slot's cache, or
-// zeros), summing the taps in the dense order.  Any other table: the
-// start-aware tiled code over the rows (it leaves padded sequences' columns
-// untouched).  Either way the same lanes then write each sequence's new cache
-// tail, the last W-1 samples of history || sequence.
+// Table covering the packed row (cu_seqlens rising from 0 to the packed
+// length) with at most 8 padded sequences: the dense conv of each packed
+// channel row as one request with no history, storing around the padded
+// sequences' columns; then one lane per (sequence, row) redoes the
+// sequence's first W-1 outputs, whose taps in front of the start read the
+// previous sequence's samples, from the sequence's own history (its slot's
+// cache, or zeros), summing the taps in the dense order.  Any other table:
+// the start-aware tiled code over the rows.  Either way the same lanes then
+// write each sequence's new cache tail, the last W-1 samples of history ||
+// sequence.
 template <typename T, int W, int RPW>
 __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
 {
@@ -475,22 +496,44 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
     const int tid = threadIdx.x, nseq = a.batch, Tn = a.seqlen;
     const ConvArgs pa = a;  // the packed-batch arguments
     // lane t <= nseq: entry t of the table (lane t < nseq: sequence t)
-    int cb = 0, ce = 0, slot = -1, bad = 0;
+    constexpr int kPadCap = 8;  // padded sequences the dense walk stores around
+    __shared__ int s_pads[2 * kPadCap];
+    __shared__ int s_npad;
+    int cb = 0, ce = 0, slot = -1, bad = 0, padded = 0;
     bool init = false;
+    if (tid == 0)
+        s_npad = 0;
     if (tid <= nseq) {
         cb = a.cu_seqlens[tid];
         ce = a.cu_seqlens[tid < nseq ? tid + 1 : tid];
         slot = tid < nseq ? (a.slot_idx ? a.slot_idx[tid] : tid) : -1;
         init = tid < nseq && a.has_init_seq && a.has_init_seq[tid] != 0;
-        bad = ce < cb || (tid == 0 && cb != 0) || (tid == nseq && cb != Tn) || (tid < nseq && slot < 0);
+        bad = ce < cb || (tid == 0 && cb != 0) || (tid == nseq && cb != Tn);
+        padded = tid < nseq && slot < 0 && ce > cb;
     }
-    const bool plain = __syncthreads_or(bad) == 0;
-    if (plain) {
+    // the table covers the packed row exactly; with no padded sequence the
+    // dense walk stores every column, with a few it stores around them
+    const bool covered = __syncthreads_or(bad) == 0;
+    const int npad = __syncthreads_count(padded);
+    const bool plain = covered && npad == 0;
+    const bool masked = covered && npad > 0 && npad <= kPadCap;
+    if (masked) {
+        if (padded) {
+            const int j = atomicAdd(&s_npad, 1);
+            s_pads[2 * j] = cb;
+            s_pads[2 * j + 1] = ce;
+        }
+        __syncthreads();
+    }
+    if (plain || masked) {
         a.batch = 1;
         a.slot_idx = nullptr;
         a.conv_state = nullptr;
         a.has_initial_state = 0;
-        conv_rows_walk<T, W, RPW>(a, row0);
+        if (plain)
+            conv_rows_walk<T, W, RPW>(a, row0);
+        else
+            conv_rows_walk<T, W, RPW, true>(a, row0, s_pads, npad);
     } else {
         constexpr int TILE = 256 * E;
         const int ntiles = (Tn + TILE - 1) / TILE;
@@ -535,7 +578,7 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
             xb[k] = xr[min(k, len - 1)];
             xe[k] = xr[max(len - H + k, 0)];
         }
-        if (plain) {
+        if (plain || masked) {
             float hx[2 * HS];  // history || the first H samples (zeros past the end)
 #pragma unroll
             for (int k = 0; k < H; ++k) {
