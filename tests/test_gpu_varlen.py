@@ -37,7 +37,7 @@ def ssm():
 
 
 VARLEN_CASES = [
-    # (label, spec kwargs, lengths, padded sequence index or None)
+    # (label, spec kwargs, lengths, padded sequence index (or list) or None)
     ("m1_f16_vec_mix", dict(io="f16", state="f32", nheads=64, nslots=16, seed=11),
      [0, 1, 2, 3, 5, 17, 255, 256, 257, 700], 4),                     # total 1496 (vec)
     ("m1_f16_scalar_mix", dict(io="f16", state="f16", nheads=40, nslots=8, seed=12),
@@ -63,12 +63,16 @@ VARLEN_CASES = [
     ("m1_f32_w3_plain", dict(io="f32", state="f32", nheads=20, dstate=20, width=3, nslots=8,
                              seed=22), [9, 600, 31, 0, 2, 6], None),  # total 648 (vec)
     # a padded sequence in packed rows of several conv tiles (2048 f16 or 1024
-    # f32 columns): the row kernel walks each row tile by tile with the
-    # start-aware code, a barrier between tiles, then writes the caches
+    # f32 columns): the dense walk stores around the padded columns
+    # (a padded first sequence: m2_f16_N16_G4)
     ("m1_f16_padded_3_tiles", dict(io="f16", state="f32", nheads=8, nslots=8, seed=23),
      [1500, 3, 2000, 1497], 1),                                      # total 5000 (vec)
     ("m1_f32_w2_padded_3_tiles", dict(io="f32", state="f32", nheads=6, width=2, nslots=8,
                                       seed=24), [700, 900, 5, 795], 3),  # total 2400 (vec)
+    # more than 8 padded sequences: the row kernel walks each row tile by
+    # tile with the start-aware code, a barrier between tiles
+    ("m1_f16_10_padded_3_tiles", dict(io="f16", state="f32", nheads=8, nslots=24, seed=26),
+     W.varlen_lengths(26, 20, 5000), [0, 2, 3, 4, 6, 8, 10, 12, 16, 18]),  # total 5000 (vec)
     # more sequences than the conv kernel stages in LDS (its global-table path)
     ("m1_f16_300_seqs", dict(io="f16", state="f32", nheads=8, nslots=320, seed=19),
      [0, 3] + W.varlen_lengths(19, 298, 2395), None),                    # total 2398
