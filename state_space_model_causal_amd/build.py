@@ -1,6 +1,11 @@
-"""Build libssm_hip.so (the gfx950 kernels + C ABI) in-tree with hipcc."""
+"""Build libssm_hip.so (the gfx950 kernels + C ABI) in-tree with hipcc.
+
+Each source is compiled to its own object in parallel (every kernel is
+launched from the file that defines it, so no device code crosses files),
+then the objects are linked into one shared library."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -11,12 +16,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm_hip.so")
+OBJDIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are disabled: the kernels are written in plain float
 # arithmetic and compiled without v_pk_{add,mul,fma}_f32.
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
@@ -33,9 +39,31 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def _jobs() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
+
+    def compile_one(src):
+        obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), *inc, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        return obj
+
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(_jobs()) as ex:
+        objs = list(ex.map(compile_one, srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
