@@ -6,32 +6,41 @@
  * causal-conv1d, selective-scan, silu and element-mul; section 3.1 places the
  * per-request mamba-cache reads and writes at the conv and scan operators) and
  * after the decode call of "[XPU] Add tuned Mamba SSU configs for Intel Arc Pro
- * B70" (vLLM PR #50534 report, section "关键源码片段":
- * selective_state_update(state, x, dt, A, B, C, D=D, z=None, dt_bias=dt_bias,
- * dt_softplus=True, out=out)).  The pages name the operators without writing
- * their equations; the equations below are the standard selective SSM that
- * those operator names and arguments describe.
+ * B70" (vLLM PR #50534 report, section "关键源码片段": a selective state
+ * update taking the state cache, x, dt, A, B, C, optional D and z gate, a dt
+ * bias with softplus, and a caller-provided out).  The pages name the
+ * operators without writing their equations; the equations below are the
+ * standard selective SSM that those operator names and arguments describe.
  *
  * Common conventions
  * ------------------
- *  - Every tensor argument is a pointer to DEVICE memory owned by the caller.
- *    The library allocates nothing, frees nothing, keeps no state between
- *    calls and never synchronises: each call validates its arguments on the
- *    host, enqueues its kernels on `stream` (a hipStream_t; NULL = the null
- *    stream) and returns.  Calls can be captured into a HIP graph.
- *  - Tensors are dense row-major with the shapes given per call (element
- *    strides implied by the shape); pointers must be aligned to their element
- *    size.  Outputs must not overlap inputs.
+ *  - Every tensor is an ssm_tensor: a pointer to DEVICE memory owned by the
+ *    caller, its dtype code, and the element strides of its dimensions in the
+ *    order of the shape given per call (outermost first; entries past the
+ *    tensor's rank are ignored).  data == NULL marks an optional tensor as
+ *    absent.  The library allocates nothing, frees nothing, keeps no state
+ *    between calls and never synchronises: each call validates its arguments
+ *    on the host, enqueues its kernels on `stream` (a hipStream_t; NULL = the
+ *    null stream) and returns.  Calls can be captured into a HIP graph.
+ *  - Layout rules: the innermost dimension must have stride 1 (a dimension of
+ *    size 1 may have any stride), every stride must be >= 0, and data must be
+ *    aligned to the element size; otherwise SSM_ERR_LAYOUT / SSM_ERR_ALIGN.
+ *    Outer strides are free, so views such as the x and z halves of a
+ *    [batch, 2*channels, seqlen] projection output are taken as they are.
+ *    The 128-bit vector paths are used when the base pointer and every outer
+ *    stride are 16-byte multiples; other layouts take element-wise paths with
+ *    the same results.  Outputs must not overlap inputs or one another.
  *  - dtype codes (ssm_dtype): SSM_F32, SSM_F16 (IEEE binary16), SSM_BF16.
- *    "io dtype" covers x/u, dt, B, C, z, out and the conv cache; A, D, dt_bias,
- *    conv weight and conv bias are always float32.  All arithmetic is float32;
- *    narrowing to f16/bf16 rounds to nearest, ties to even.
- *  - Slots: slot_idx (int32 [batch], may be NULL) maps request b to cache row
- *    slot_idx[b]; NULL means slot b.  A negative index marks a padded request:
- *    nothing is written for it (its out rows keep their contents) and its
- *    inputs affect no output.
- *    Non-negative indices must be < nslots and distinct within a call
- *    (duplicates race; this is not checked on the device).
+ *    "io dtype" covers x/u, dt, B, C, z, out and the conv cache, which must
+ *    all have the same dtype; A, D, dt_bias, conv weight and conv bias are
+ *    always float32.  The state cache's dtype is its own.  All arithmetic is
+ *    float32; narrowing to f16/bf16 rounds to nearest, ties to even.
+ *  - Slots: slot_idx (int32 [batch], device memory, may be NULL) maps request
+ *    b to cache row slot_idx[b]; NULL means slot b.  A negative index marks a
+ *    padded request: nothing is written for it (its out rows keep their
+ *    contents) and its inputs affect no output.  Non-negative indices must be
+ *    < nslots and distinct within a call (duplicates race; this is not
+ *    checked on the device).
  *  - batch == 0 or seqlen == 0 is a no-op returning SSM_OK.
  *  - Errors are returned synchronously, before anything is enqueued, as
  *    ssm_status codes; asynchronous device faults surface at the caller's
@@ -47,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum ssm_dtype {
     SSM_F32 = 0,
@@ -57,13 +66,23 @@ typedef enum ssm_dtype {
 
 typedef enum ssm_status {
     SSM_OK = 0,
-    SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL                     */
-    SSM_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree       */
-    SSM_ERR_DTYPE = 3,       /* unknown dtype code                             */
-    SSM_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size   */
-    SSM_ERR_UNSUPPORTED = 5, /* a size beyond what the kernels are built for   */
-    SSM_ERR_HIP = 6          /* the HIP runtime refused a launch               */
+    SSM_ERR_NULL_ARG = 1,         /* a required tensor or pointer is NULL              */
+    SSM_ERR_SHAPE = 2,            /* a size is out of range or sizes disagree          */
+    SSM_ERR_DTYPE = 3,            /* unknown dtype code, or dtypes that must agree don't */
+    SSM_ERR_ALIGN = 4,            /* a pointer is not aligned to its element size      */
+    SSM_ERR_UNSUPPORTED = 5,      /* a size or variant the kernels are not built for   */
+    SSM_ERR_HIP = 6,              /* the HIP runtime refused a launch                  */
+    SSM_ERR_LAYOUT = 7,           /* an innermost stride is not 1, or a stride is < 0  */
+    SSM_ERR_OUT_OF_RESOURCES = 8  /* a launch geometry beyond the kernels' register,
+                                     LDS or workgroup-size budget                     */
 } ssm_status;
+
+typedef struct ssm_tensor {
+    void *data;         /* device memory; NULL = absent                              */
+    int32_t dtype;      /* ssm_dtype                                                  */
+    int32_t reserved;   /* 0                                                          */
+    int64_t stride[4];  /* element strides, outermost dimension first                 */
+} ssm_tensor;
 
 /*
  * ssm_causal_conv1d -- causal depthwise conv1d + bias + optional SiLU, with an
@@ -72,8 +91,8 @@ typedef enum ssm_status {
  *
  *   x, out      io dtype [batch, channels, seqlen]   (time innermost)
  *   weight      f32 [channels, width]; tap width-1 multiplies the newest sample
- *   bias        f32 [channels] or NULL
- *   conv_state  io dtype [nslots, channels, width-1] or NULL; oldest sample
+ *   bias        f32 [channels] or absent
+ *   conv_state  io dtype [nslots, channels, width-1] or absent; oldest sample
  *               first.  In: the history before x[...,0] when
  *               has_initial_state (else the history is zeros).  Out: the last
  *               width-1 samples of history||x, copied bit-exactly.
@@ -83,45 +102,42 @@ typedef enum ssm_status {
  *
  * seqlen == 1 with has_initial_state is the decode update (one output, window
  * shifted by one); prefill writes the tail a later decode step starts from.
- * Limits: 1 <= width <= 4.
+ * Limits: 1 <= width <= 4 (else SSM_ERR_UNSUPPORTED).
  */
-int ssm_causal_conv1d(const void *x, const float *weight, const float *bias,
-                      void *conv_state, const int32_t *slot_idx, void *out,
-                      int batch, int channels, int seqlen, int width,
-                      int nslots, int dtype, int has_initial_state,
-                      int apply_silu, void *stream);
+int ssm_causal_conv1d(ssm_tensor x, ssm_tensor weight, ssm_tensor bias, ssm_tensor conv_state,
+                      const int32_t *slot_idx, ssm_tensor out, int batch, int channels,
+                      int seqlen, int width, int nslots, int has_initial_state, int apply_silu,
+                      void *stream);
 
 /*
  * ssm_selective_scan -- selective scan over a whole sequence (prefill): the
  * selective-scan operator with its silu(z) element-mul gate (InfiniLM-Rust PR
  * #48, section 2.1), final state stored to the request's cache slot (3.1).
  *
- *   u, z, out   io dtype [batch, nheads*headdim, seqlen]; z may be NULL
+ *   u, z, out   io dtype [batch, nheads*headdim, seqlen]; z may be absent
  *   dt          io dtype [batch, nheads, seqlen]
- *   dt_bias     f32 [nheads] or NULL;  D  f32 [nheads] or NULL
+ *   dt_bias, D  f32 [nheads] or absent
  *   A           f32 [nheads, dstate] when a_per_state (Mamba-1: one decay per
  *               channel and state, headdim 1), else f32 [nheads] (Mamba-2:
  *               one decay per head)
  *   B, C        io dtype [batch, ngroups, dstate, seqlen]; head h reads group
  *               h / (nheads/ngroups)
- *   ssm_state   state dtype [nslots, nheads, headdim, dstate] or NULL; in: the
- *               initial state when has_initial_state (else zeros); out: the
- *               state after the last token
+ *   ssm_state   state dtype [nslots, nheads, headdim, dstate] or absent; in:
+ *               the initial state when has_initial_state (else zeros); out:
+ *               the state after the last token
  *
  *   delta_t = softplus(dt_t + dt_bias) (or dt_t + dt_bias if !dt_softplus)
  *   h_t[n]  = exp(delta_t*A[n]) * h_{t-1}[n] + delta_t * B_t[n] * u_t
  *   out_t   = (sum_n C_t[n] h_t[n] + D u_t) * silu(z_t)
  *
- * Limits: nheads % ngroups == 0; 1 <= dstate <= 256.
+ * Limits: nheads % ngroups == 0; 1 <= dstate <= 256 (the carried states of
+ * a workgroup's channels are held in LDS; larger: SSM_ERR_OUT_OF_RESOURCES).
  */
-int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias,
-                       const float *A, const void *B, const void *C,
-                       const float *D, const void *z, void *ssm_state,
-                       const int32_t *slot_idx, void *out, int batch,
-                       int seqlen, int nheads, int headdim, int dstate,
-                       int ngroups, int nslots, int io_dtype, int state_dtype,
-                       int a_per_state, int dt_softplus, int has_initial_state,
-                       void *stream);
+int ssm_selective_scan(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, ssm_tensor A,
+                       ssm_tensor B, ssm_tensor C, ssm_tensor D, ssm_tensor z,
+                       ssm_tensor ssm_state, const int32_t *slot_idx, ssm_tensor out, int batch,
+                       int seqlen, int nheads, int headdim, int dstate, int ngroups, int nslots,
+                       int a_per_state, int dt_softplus, int has_initial_state, void *stream);
 
 /*
  * ssm_selective_scan_ex -- ssm_selective_scan with a choice of algorithm.
@@ -129,53 +145,51 @@ int ssm_selective_scan(const void *u, const void *dt, const float *dt_bias,
  *         SSM_SCAN_RECURRENT: the step-by-step recurrence (any shape);
  *         SSM_SCAN_CHUNKED: the chunked matrix form on the matrix cores.
  * The chunked form needs one decay per head (a_per_state == 0), bf16 I/O,
- * dstate 64, 128 or 256, headdim a multiple of 64, seqlen a multiple of 8 and
- * 16-byte aligned tensors; otherwise SSM_SCAN_CHUNKED returns
- * SSM_ERR_UNSUPPORTED.  SSM_SCAN_AUTO takes it whenever it applies.  The
- * chunked form computes the same recurrence: over a chunk of steps with one
- * scalar decay per step, the state recursion unrolls into products of small
- * matrices (decay-weighted C.B^T within the chunk, C times the carried state,
- * and the decay-weighted B times u for the next state), which run on MFMA
- * with float32 accumulation; operands that are not exact in bf16 are split
- * into two bf16 parts (about 16 significant bits per product).  Other
- * arguments as in ssm_selective_scan.
+ * dstate 64, 128 or 256, headdim a multiple of 64, seqlen a multiple of 8,
+ * 16-byte aligned rows and a dense [.., headdim, dstate] state slot;
+ * otherwise SSM_SCAN_CHUNKED returns SSM_ERR_UNSUPPORTED.  SSM_SCAN_AUTO
+ * takes it whenever it applies.  The chunked form computes the same
+ * recurrence: over a chunk of steps with one scalar decay per step, the state
+ * recursion unrolls into products of small matrices (decay-weighted C.B^T
+ * within the chunk, C times the carried state, and the decay-weighted B
+ * times u for the next state), which run on MFMA with float32 accumulation;
+ * operands that are not exact in bf16 are split into two bf16 parts (about
+ * 16 significant bits per product).  Other arguments as in
+ * ssm_selective_scan.
  */
 #define SSM_SCAN_AUTO 0
 #define SSM_SCAN_RECURRENT 1
 #define SSM_SCAN_CHUNKED 2
-int ssm_selective_scan_ex(const void *u, const void *dt, const float *dt_bias,
-                          const float *A, const void *B, const void *C,
-                          const float *D, const void *z, void *ssm_state,
-                          const int32_t *slot_idx, void *out, int batch,
-                          int seqlen, int nheads, int headdim, int dstate,
-                          int ngroups, int nslots, int io_dtype,
-                          int state_dtype, int a_per_state, int dt_softplus,
+int ssm_selective_scan_ex(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, ssm_tensor A,
+                          ssm_tensor B, ssm_tensor C, ssm_tensor D, ssm_tensor z,
+                          ssm_tensor ssm_state, const int32_t *slot_idx, ssm_tensor out,
+                          int batch, int seqlen, int nheads, int headdim, int dstate,
+                          int ngroups, int nslots, int a_per_state, int dt_softplus,
                           int has_initial_state, int algo, void *stream);
 
 /*
  * ssm_state_update -- one-token selective state update (decode) in place on a
- * slot-indexed state cache: the selective_state_update call of the vLLM PR
- * #50534 report ("关键源码片段"), same argument set.
+ * slot-indexed state cache: the selective state update of the vLLM PR #50534
+ * report ("关键源码片段"), same argument set.
  *
  *   state       state dtype [nslots, nheads, headdim, dstate], read-modify-
  *               written in place for the named slots only
- *   x, z, out   io dtype [batch, nheads, headdim]; z may be NULL
+ *   x, z, out   io dtype [batch, nheads, headdim]; z may be absent
  *   dt          io dtype [batch, nheads]
- *   dt_bias, D  f32 [nheads] or NULL
+ *   dt_bias, D  f32 [nheads] or absent
  *   A           f32 [nheads, dstate] (a_per_state) or f32 [nheads]
  *   B, C        io dtype [batch, ngroups, dstate]
  *
  *   h' = exp(delta*A) * h + delta * B * x;  out = (C.h' + D x) * silu(z)
  * The readout uses the float32 h'; the cache receives h' rounded to the state
- * dtype.  Limits: nheads % ngroups == 0; 1 <= dstate <= 512.
+ * dtype.  Limits: nheads % ngroups == 0; 1 <= dstate <= 512 (a row spans at
+ * most one wave; larger: SSM_ERR_OUT_OF_RESOURCES).
  */
-int ssm_state_update(void *state, const int32_t *slot_idx, const void *x,
-                     const void *dt, const float *dt_bias, const float *A,
-                     const void *B, const void *C, const float *D,
-                     const void *z, void *out, int batch, int nheads,
-                     int headdim, int dstate, int ngroups, int nslots,
-                     int io_dtype, int state_dtype, int a_per_state,
-                     int dt_softplus, void *stream);
+int ssm_state_update(ssm_tensor state, const int32_t *slot_idx, ssm_tensor x, ssm_tensor dt,
+                     ssm_tensor dt_bias, ssm_tensor A, ssm_tensor B, ssm_tensor C, ssm_tensor D,
+                     ssm_tensor z, ssm_tensor out, int batch, int nheads, int headdim,
+                     int dstate, int ngroups, int nslots, int a_per_state, int dt_softplus,
+                     void *stream);
 
 /*
  * Launch geometry of the state update.  "[XPU] Add tuned Mamba SSU configs for
@@ -192,10 +206,10 @@ int ssm_state_update(void *state, const int32_t *slot_idx, const void *x,
  * Independently of the geometry, with one channel per head (headdim 1) and
  * at least 8 requests each lane updates its states for two requests in
  * turn.  With 32 bytes of state per lane, rows of a power-of-two size up to
- * 1 KB and at least 2^18 (request, row) pairs, the lanes take the same number
- * of states in an interleaved order instead (each 128-bit access of a wave
- * covers a contiguous kilobyte of the cache); the cache bytes written are the
- * same.
+ * 1 KB, dense state slots and at least 2^18 (request, row) pairs, the lanes
+ * take the same number of states in an interleaved order instead (each
+ * 128-bit access of a wave covers a contiguous kilobyte of the cache); the
+ * cache bytes written are the same.
  */
 typedef struct ssm_launch_config {
     int states_per_lane; /* 4, 8 or 16             */
@@ -215,30 +229,34 @@ int ssm_state_update_config(int batch, int nheads, int headdim, int dstate,
  * ssm_state_update_ex -- ssm_state_update with the caller's geometry (the
  * override hook of the tuning method); config NULL = the library's choice.
  * Every geometry computes the same values: the cache bytes are identical, the
- * outputs differ only in the summation order of the readout.  An invalid
- * config returns SSM_ERR_SHAPE.
+ * outputs differ only in the summation order of the readout.  A geometry
+ * past what the kernels are built for returns SSM_ERR_OUT_OF_RESOURCES
+ * (more than 16 states per lane: the registers of the state arrays; more than
+ * 512 lanes per workgroup: the kernels' launch bound; a row of more than 64
+ * lanes: the readout sums within one wave), the analogue of the skipped
+ * out-of-resources configurations of the vLLM tuning benchmark; any other
+ * invalid geometry (states per lane or workgroup size not one of the listed
+ * values, 4 states per lane with a 2-byte cache) returns SSM_ERR_SHAPE.
  */
-int ssm_state_update_ex(void *state, const int32_t *slot_idx, const void *x,
-                        const void *dt, const float *dt_bias, const float *A,
-                        const void *B, const void *C, const float *D,
-                        const void *z, void *out, int batch, int nheads,
-                        int headdim, int dstate, int ngroups, int nslots,
-                        int io_dtype, int state_dtype, int a_per_state,
-                        int dt_softplus, const ssm_launch_config *config,
+int ssm_state_update_ex(ssm_tensor state, const int32_t *slot_idx, ssm_tensor x,
+                        ssm_tensor dt, ssm_tensor dt_bias, ssm_tensor A, ssm_tensor B,
+                        ssm_tensor C, ssm_tensor D, ssm_tensor z, ssm_tensor out, int batch,
+                        int nheads, int headdim, int dstate, int ngroups, int nslots,
+                        int a_per_state, int dt_softplus, const ssm_launch_config *config,
                         void *stream);
 
 /*
  * ssm_decode_step -- one decode token per request: the conv update followed by
  * the state update, in one kernel (the causal-conv1d and silu operators of
- * InfiniLM-Rust PR #48 section 2.1 at seqlen 1, feeding the
- * selective_state_update call of the vLLM PR #50534 report).
+ * InfiniLM-Rust PR #48 section 2.1 at seqlen 1, feeding the selective state
+ * update of the vLLM PR #50534 report).
  *
  *   x           io dtype [batch, nheads, headdim]: the token's input to the
  *               conv (channel c = h*headdim + p)
  *   conv_state  io dtype [nslots, nheads*headdim, conv_width-1], in/out: the
  *               window before the token, shifted by one on return
- *   conv_weight f32 [nheads*headdim, conv_width]; conv_bias f32 or NULL
- *   u_out       io dtype [batch, nheads, headdim] or NULL: the conv output
+ *   conv_weight f32 [nheads*headdim, conv_width]; conv_bias f32 or absent
+ *   u_out       io dtype [batch, nheads, headdim] or absent: the conv output
  *   every other argument as in ssm_state_update
  *
  *   u = silu(conv_bias + sum_k conv_weight[c,k] * window_k (newest = x))
@@ -248,13 +266,11 @@ int ssm_state_update_ex(void *state, const int32_t *slot_idx, const void *x,
  * of being rounded to the io dtype in between.  Limits: conv_width == 4, plus
  * those of ssm_state_update.
  */
-int ssm_decode_step(void *state, void *conv_state, const int32_t *slot_idx,
-                    const void *x, const float *conv_weight,
-                    const float *conv_bias, int conv_width, const void *dt,
-                    const float *dt_bias, const float *A, const void *B,
-                    const void *C, const float *D, const void *z, void *out,
-                    void *u_out, int batch, int nheads, int headdim, int dstate,
-                    int ngroups, int nslots, int io_dtype, int state_dtype,
+int ssm_decode_step(ssm_tensor state, ssm_tensor conv_state, const int32_t *slot_idx,
+                    ssm_tensor x, ssm_tensor conv_weight, ssm_tensor conv_bias, int conv_width,
+                    ssm_tensor dt, ssm_tensor dt_bias, ssm_tensor A, ssm_tensor B, ssm_tensor C,
+                    ssm_tensor D, ssm_tensor z, ssm_tensor out, ssm_tensor u_out, int batch,
+                    int nheads, int headdim, int dstate, int ngroups, int nslots,
                     int a_per_state, int dt_softplus, void *stream);
 
 /*
@@ -286,12 +302,11 @@ int ssm_decode_step(void *state, void *conv_state, const int32_t *slot_idx,
  *   other arguments as in ssm_causal_conv1d; the conv cache of each sequence
  *   receives the last width-1 samples of its history || its samples.
  */
-int ssm_causal_conv1d_varlen(const void *x, const float *weight, const float *bias,
-                             void *conv_state, const int32_t *slot_idx,
-                             const int32_t *has_initial_state,
-                             const int32_t *cu_seqlens, void *out, int nseq,
-                             int channels, int total_len, int width, int nslots,
-                             int dtype, int apply_silu, void *stream);
+int ssm_causal_conv1d_varlen(ssm_tensor x, ssm_tensor weight, ssm_tensor bias,
+                             ssm_tensor conv_state, const int32_t *slot_idx,
+                             const int32_t *has_initial_state, const int32_t *cu_seqlens,
+                             ssm_tensor out, int nseq, int channels, int total_len, int width,
+                             int nslots, int apply_silu, void *stream);
 
 /*
  * ssm_selective_scan_varlen -- ssm_selective_scan over a packed batch.
@@ -301,16 +316,13 @@ int ssm_causal_conv1d_varlen(const void *x, const float *weight, const float *bi
  *   other arguments as in ssm_selective_scan; each sequence's final state goes
  *   to its slot.
  */
-int ssm_selective_scan_varlen(const void *u, const void *dt, const float *dt_bias,
-                              const float *A, const void *B, const void *C,
-                              const float *D, const void *z, void *ssm_state,
-                              const int32_t *slot_idx,
-                              const int32_t *has_initial_state,
-                              const int32_t *cu_seqlens, void *out, int nseq,
-                              int total_len, int nheads, int headdim, int dstate,
-                              int ngroups, int nslots, int io_dtype,
-                              int state_dtype, int a_per_state, int dt_softplus,
-                              void *stream);
+int ssm_selective_scan_varlen(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, ssm_tensor A,
+                              ssm_tensor B, ssm_tensor C, ssm_tensor D, ssm_tensor z,
+                              ssm_tensor ssm_state, const int32_t *slot_idx,
+                              const int32_t *has_initial_state, const int32_t *cu_seqlens,
+                              ssm_tensor out, int nseq, int total_len, int nheads, int headdim,
+                              int dstate, int ngroups, int nslots, int a_per_state,
+                              int dt_softplus, void *stream);
 
 /*
  * One whole Mamba-1 decode layer around the path, and its two building
@@ -326,27 +338,27 @@ int ssm_selective_scan_varlen(const void *u, const void *dt, const float *dt_bia
  *   dt        = dt_low . dt_proj^T             dt_proj  [d_inner, dt_rank]
  *   y         = ssm_state_update(u, dt + dt_bias through softplus, A, B, C, D, z)
  *   hidden   += y . out_proj^T                 out_proj [d_model, d_inner]
- * Weights are row-major in the io dtype (f16 or bf16; the products run on
- * the matrix cores with float32 accumulation); norm weight, conv weight and
- * bias, dt_bias, A and D are float32.  Intermediates between steps are
- * stored in the io dtype in a caller-provided workspace.
+ * Weights are dense row-major in the io dtype (f16 or bf16; the products run
+ * on the matrix cores with float32 accumulation); norm weight, conv weight
+ * and bias, dt_bias, A and D are dense float32.  Intermediates between steps
+ * are stored in the io dtype in a caller-provided workspace.
  */
 
 /*
  * ssm_linear -- out[M, N] = x[M, K] . weight[N, K]^T (+ residual[M, N]).
  * f16 or bf16 (f32 returns SSM_ERR_UNSUPPORTED); K a multiple of 8; x and
- * weight 16-byte aligned.  workspace: ssm_linear_workspace(M, N, K) bytes
- * (may be 0 and NULL) of device memory for split-K partial sums.
+ * weight rows 16-byte aligned (base and row stride); out and residual may be
+ * strided views with unit inner stride.  workspace: ssm_linear_workspace(M,
+ * N, K) bytes (may be 0 and NULL) of device memory for split-K partial sums.
  */
 size_t ssm_linear_workspace(int M, int N, int K);
-int ssm_linear(const void *x, const void *weight, const void *residual,
-               void *out, int M, int N, int K, int dtype, void *workspace,
-               size_t workspace_bytes, void *stream);
+int ssm_linear(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M,
+               int N, int K, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ssm_rmsnorm -- out[m, :] = x[m, :] / sqrt(mean(x[m, :]^2) + eps) * weight
- * (weight float32 [D]; x, out f16 or bf16 [M, D]). */
-int ssm_rmsnorm(const void *x, const float *weight, void *out, int M, int D,
-                float eps, int dtype, void *stream);
+ * (weight float32 [D], dense; x, out f16 or bf16 [M, D]). */
+int ssm_rmsnorm(ssm_tensor x, ssm_tensor weight, ssm_tensor out, int M, int D, float eps,
+                void *stream);
 
 typedef struct ssm_mamba1_layer {
     int d_model, d_inner, d_state, dt_rank, conv_width;
@@ -369,16 +381,17 @@ size_t ssm_mamba1_decode_layer_workspace(const ssm_mamba1_layer *layer,
 
 /*
  * ssm_mamba1_decode_layer -- one decode token per request through the whole
- * layer.  hidden [batch, d_model] io dtype, updated in place (rows of padded
- * requests, slot < 0, are left as they are); conv_state [nslots, d_inner,
- * conv_width-1] io dtype and ssm_state [nslots, d_inner, 1, d_state] state
- * dtype, read and updated for the named slots.  d_model, d_inner, dt_rank,
- * d_state multiples of 8; conv_width <= 4; d_state <= 512.
+ * layer.  hidden [batch, d_model] io dtype (f16 or bf16), updated in place
+ * (rows of padded requests, slot < 0, are left as they are); conv_state
+ * [nslots, d_inner, conv_width-1] io dtype and ssm_state [nslots, d_inner, 1,
+ * d_state] state dtype, read and updated for the named slots.  d_model,
+ * d_inner, dt_rank, d_state multiples of 8; conv_width <= 4; d_state <= 512.
+ * Every argument of every step is checked before the first launch, so an
+ * error leaves hidden and both caches untouched.
  */
-int ssm_mamba1_decode_layer(const ssm_mamba1_layer *layer, void *hidden,
-                            void *conv_state, void *ssm_state,
-                            const int32_t *slot_idx, int batch, int nslots,
-                            int io_dtype, int state_dtype, void *workspace,
+int ssm_mamba1_decode_layer(const ssm_mamba1_layer *layer, ssm_tensor hidden,
+                            ssm_tensor conv_state, ssm_tensor ssm_state,
+                            const int32_t *slot_idx, int batch, int nslots, void *workspace,
                             size_t workspace_bytes, void *stream);
 
 /* Human-readable text for a status code (static storage; never NULL). */

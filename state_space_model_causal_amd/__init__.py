@@ -6,7 +6,9 @@ kernels behind the C ABI of ``include/ssm.h``.  PyTorch supplies device memory
 fallback: if the library is missing or the tensors are not on the GPU the
 calls raise.
 
-Layouts (dense, row-major, time innermost for prefill):
+Tensors are passed with their strides (views such as the x and z halves of a
+projection output are taken as they are); the innermost dimension must be
+contiguous.  Layouts (time innermost for prefill):
     prefill  u/x/z/out [batch, channels, seqlen], dt [batch, nheads, seqlen],
              B/C [batch, ngroups, dstate, seqlen]
     decode   x/z/out [batch, nheads, headdim], dt [batch, nheads],
@@ -41,6 +43,13 @@ EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_selective_scan_ex", 
             "ssm_mamba1_decode_layer_workspace", "ssm_status_string", "ssm_abi_version")
 
 
+class Tensor(ctypes.Structure):
+    """ssm_tensor: device pointer, dtype code and element strides (outermost
+    first).  data = NULL marks an absent optional tensor."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("stride", ctypes.c_int64 * 4)]
+
+
 class Mamba1Layer(ctypes.Structure):
     """ssm_mamba1_layer: dimensions and device pointers of one layer's weights."""
     _fields_ = [("d_model", ctypes.c_int), ("d_inner", ctypes.c_int), ("d_state", ctypes.c_int),
@@ -57,7 +66,8 @@ class LaunchConfig(ctypes.Structure):
     _fields_ = [("states_per_lane", ctypes.c_int), ("block_threads", ctypes.c_int)]
 
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE",
-          4: "SSM_ERR_ALIGN", 5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_HIP"}
+          4: "SSM_ERR_ALIGN", 5: "SSM_ERR_UNSUPPORTED", 6: "SSM_ERR_HIP", 7: "SSM_ERR_LAYOUT",
+          8: "SSM_ERR_OUT_OF_RESOURCES"}
 
 
 class SsmError(RuntimeError):
@@ -79,41 +89,41 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             f"{path} is missing: the HIP extension has not been built "
             "(run __graft_entry__.build() or python state_space_model_causal_amd/build.py)")
     lib = ctypes.CDLL(path)
-    P, I = ctypes.c_void_p, ctypes.c_int
-    lib.ssm_causal_conv1d.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+    P, I, T = ctypes.c_void_p, ctypes.c_int, Tensor
+    lib.ssm_causal_conv1d.argtypes = [T, T, T, T, P, T, I, I, I, I, I, I, I, P]
     lib.ssm_causal_conv1d.restype = I
-    lib.ssm_selective_scan.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
-                                       I, I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_selective_scan.argtypes = [T, T, T, T, T, T, T, T, T, P, T,
+                                       I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_selective_scan.restype = I
-    lib.ssm_selective_scan_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
-                                          I, I, I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_selective_scan_ex.argtypes = [T, T, T, T, T, T, T, T, T, P, T,
+                                          I, I, I, I, I, I, I, I, I, I, I, P]
     lib.ssm_selective_scan_ex.restype = I
-    lib.ssm_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
-                                     I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_state_update.argtypes = [T, P, T, T, T, T, T, T, T, T, T,
+                                     I, I, I, I, I, I, I, I, P]
     lib.ssm_state_update.restype = I
-    lib.ssm_state_update_ex.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
-                                        I, I, I, I, I, I, I, I, I, I, P, P]
+    lib.ssm_state_update_ex.argtypes = [T, P, T, T, T, T, T, T, T, T, T,
+                                        I, I, I, I, I, I, I, I, P, P]
     lib.ssm_state_update_ex.restype = I
     lib.ssm_state_update_config.argtypes = [I, I, I, I, I, I, P, P]
     lib.ssm_state_update_config.restype = I
-    lib.ssm_decode_step.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P,
-                                    I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_decode_step.argtypes = [T, T, P, T, T, T, I, T, T, T, T, T, T, T, T, T,
+                                    I, I, I, I, I, I, I, I, P]
     lib.ssm_decode_step.restype = I
-    lib.ssm_causal_conv1d_varlen.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.ssm_causal_conv1d_varlen.argtypes = [T, T, T, T, P, P, P, T, I, I, I, I, I, I, P]
     lib.ssm_causal_conv1d_varlen.restype = I
-    lib.ssm_selective_scan_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P,
-                                              I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.ssm_selective_scan_varlen.argtypes = [T, T, T, T, T, T, T, T, T, P, P, P, T,
+                                              I, I, I, I, I, I, I, I, I, P]
     lib.ssm_selective_scan_varlen.restype = I
     Z = ctypes.c_size_t
     lib.ssm_linear_workspace.argtypes = [I, I, I]
     lib.ssm_linear_workspace.restype = Z
-    lib.ssm_linear.argtypes = [P, P, P, P, I, I, I, I, P, Z, P]
+    lib.ssm_linear.argtypes = [T, T, T, T, I, I, I, P, Z, P]
     lib.ssm_linear.restype = I
-    lib.ssm_rmsnorm.argtypes = [P, P, P, I, I, ctypes.c_float, I, P]
+    lib.ssm_rmsnorm.argtypes = [T, T, T, I, I, ctypes.c_float, P]
     lib.ssm_rmsnorm.restype = I
     lib.ssm_mamba1_decode_layer_workspace.argtypes = [P, I]
     lib.ssm_mamba1_decode_layer_workspace.restype = Z
-    lib.ssm_mamba1_decode_layer.argtypes = [P, P, P, P, P, I, I, I, I, P, Z, P]
+    lib.ssm_mamba1_decode_layer.argtypes = [P, T, T, T, P, I, I, P, Z, P]
     lib.ssm_mamba1_decode_layer.restype = I
     lib.ssm_status_string.argtypes = [I]
     lib.ssm_status_string.restype = ctypes.c_char_p
@@ -129,18 +139,35 @@ def _check(fn: str, status: int):
         raise SsmError(fn, status, load_library().ssm_status_string(status).decode())
 
 
-def _ptr(t, name, dtype=None):
-    if t is None:
-        return None
+def _gpu(t, name, dtype=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU (got {t.device})")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _ptr(t, name, dtype=None):
+    """Raw device pointer of a dense tensor (index tables, layer weights)."""
+    if t is None:
+        return None
+    _gpu(t, name, dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _tensor(t, name, dtype=None):
+    """ssm_tensor of a torch tensor: its pointer, dtype code and strides as
+    they are (views included); an empty Tensor for None."""
+    if t is None:
+        return Tensor()
+    _gpu(t, name, dtype)
+    if t.dim() > 4:
+        raise ValueError(f"{name} has more than 4 dimensions")
+    st = (ctypes.c_int64 * 4)(*(list(t.stride()) + [0] * (4 - t.dim())))
+    return Tensor(t.data_ptr(), _code(t, name), 0, st)
 
 
 def _code(t, name):
@@ -156,10 +183,9 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _same_io(name_dtype, *pairs):
-    for t, n in pairs:
-        if t is not None and t.dtype != name_dtype:
-            raise TypeError(f"{n} must have the io dtype {name_dtype} (got {t.dtype})")
+def _new_like(t):
+    # a dense output of t's shape and dtype
+    return torch.empty(t.shape, dtype=t.dtype, device=t.device)
 
 
 def causal_conv1d(x, weight, bias=None, conv_state=None, slot_idx=None, out=None,
@@ -168,13 +194,12 @@ def causal_conv1d(x, weight, bias=None, conv_state=None, slot_idx=None, out=None
     batch, channels, seqlen = x.shape
     width = weight.shape[1]
     if out is None:
-        out = torch.empty_like(x)
-    _same_io(x.dtype, (out, "out"), (conv_state, "conv_state"))
+        out = _new_like(x)
     nslots = conv_state.shape[0] if conv_state is not None else 0
     st = load_library().ssm_causal_conv1d(
-        _ptr(x, "x"), _ptr(weight, "weight", torch.float32), _ptr(bias, "bias", torch.float32),
-        _ptr(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32), _ptr(out, "out"),
-        batch, channels, seqlen, width, nslots, _code(x, "x"), int(bool(has_initial_state)),
+        _tensor(x, "x"), _tensor(weight, "weight"), _tensor(bias, "bias"),
+        _tensor(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+        _tensor(out, "out"), batch, channels, seqlen, width, nslots, int(bool(has_initial_state)),
         int(bool(apply_silu)), _stream(stream))
     _check("ssm_causal_conv1d", st)
     return out
@@ -192,15 +217,13 @@ def selective_scan(u, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=Tru
     ngroups, dstate = B.shape[1], B.shape[2]
     a_per_state = 1 if A.dim() == 2 else 0
     if out is None:
-        out = torch.empty_like(u)
-    _same_io(u.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
+        out = _new_like(u)
     nslots = ssm_state.shape[0] if ssm_state is not None else 0
-    sd = _code(ssm_state, "ssm_state") if ssm_state is not None else SSM_F32
-    args = (_ptr(u, "u"), _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32),
-            _ptr(A, "A", torch.float32), _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32),
-            _ptr(z, "z"), _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
-            _ptr(out, "out"), batch, seqlen, nheads, headdim, dstate, ngroups, nslots,
-            _code(u, "u"), sd, a_per_state, int(bool(dt_softplus)), int(bool(has_initial_state)))
+    args = (_tensor(u, "u"), _tensor(dt, "dt"), _tensor(dt_bias, "dt_bias"), _tensor(A, "A"),
+            _tensor(B, "B"), _tensor(C, "C"), _tensor(D, "D"), _tensor(z, "z"),
+            _tensor(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+            _tensor(out, "out"), batch, seqlen, nheads, headdim, dstate, ngroups, nslots,
+            a_per_state, int(bool(dt_softplus)), int(bool(has_initial_state)))
     if algo is None:
         st = load_library().ssm_selective_scan(*args, _stream(stream))
         _check("ssm_selective_scan", st)
@@ -220,13 +243,11 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplu
     ngroups = B.shape[1]
     a_per_state = 1 if A.dim() == 2 else 0
     if out is None:
-        out = torch.empty_like(x)
-    _same_io(x.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
-    args = (_ptr(state, "state"), _ptr(slot_idx, "slot_idx", torch.int32), _ptr(x, "x"),
-            _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32),
-            _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32), _ptr(z, "z"),
-            _ptr(out, "out"), batch, nheads, headdim, dstate, ngroups, nslots, _code(x, "x"),
-            _code(state, "state"), a_per_state, int(bool(dt_softplus)))
+        out = _new_like(x)
+    args = (_tensor(state, "state"), _ptr(slot_idx, "slot_idx", torch.int32), _tensor(x, "x"),
+            _tensor(dt, "dt"), _tensor(dt_bias, "dt_bias"), _tensor(A, "A"), _tensor(B, "B"),
+            _tensor(C, "C"), _tensor(D, "D"), _tensor(z, "z"), _tensor(out, "out"), batch,
+            nheads, headdim, dstate, ngroups, nslots, a_per_state, int(bool(dt_softplus)))
     if config is None:
         st = load_library().ssm_state_update(*args, _stream(stream))
         _check("ssm_state_update", st)
@@ -259,17 +280,15 @@ def decode_step(state, conv_state, x, conv_weight, dt, A, B, C, conv_bias=None, 
     ngroups = B.shape[1]
     a_per_state = 1 if A.dim() == 2 else 0
     if out is None:
-        out = torch.empty_like(x)
-    _same_io(x.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"),
-             (conv_state, "conv_state"), (u_out, "u_out"))
+        out = _new_like(x)
     st = load_library().ssm_decode_step(
-        _ptr(state, "state"), _ptr(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32),
-        _ptr(x, "x"), _ptr(conv_weight, "conv_weight", torch.float32),
-        _ptr(conv_bias, "conv_bias", torch.float32), conv_weight.shape[1], _ptr(dt, "dt"),
-        _ptr(dt_bias, "dt_bias", torch.float32), _ptr(A, "A", torch.float32), _ptr(B, "B"),
-        _ptr(C, "C"), _ptr(D, "D", torch.float32), _ptr(z, "z"), _ptr(out, "out"),
-        _ptr(u_out, "u_out"), batch, nheads, headdim, dstate, ngroups, nslots, _code(x, "x"),
-        _code(state, "state"), a_per_state, int(bool(dt_softplus)), _stream(stream))
+        _tensor(state, "state"), _tensor(conv_state, "conv_state"),
+        _ptr(slot_idx, "slot_idx", torch.int32), _tensor(x, "x"),
+        _tensor(conv_weight, "conv_weight"), _tensor(conv_bias, "conv_bias"),
+        conv_weight.shape[1], _tensor(dt, "dt"), _tensor(dt_bias, "dt_bias"), _tensor(A, "A"),
+        _tensor(B, "B"), _tensor(C, "C"), _tensor(D, "D"), _tensor(z, "z"), _tensor(out, "out"),
+        _tensor(u_out, "u_out"), batch, nheads, headdim, dstate, ngroups, nslots, a_per_state,
+        int(bool(dt_softplus)), _stream(stream))
     _check("ssm_decode_step", st)
     return out
 
@@ -282,15 +301,14 @@ def causal_conv1d_varlen(x, weight, cu_seqlens, bias=None, conv_state=None, slot
     nseq = cu_seqlens.shape[0] - 1
     width = weight.shape[1]
     if out is None:
-        out = torch.empty_like(x)
-    _same_io(x.dtype, (out, "out"), (conv_state, "conv_state"))
+        out = _new_like(x)
     nslots = conv_state.shape[0] if conv_state is not None else 0
     st = load_library().ssm_causal_conv1d_varlen(
-        _ptr(x, "x"), _ptr(weight, "weight", torch.float32), _ptr(bias, "bias", torch.float32),
-        _ptr(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+        _tensor(x, "x"), _tensor(weight, "weight"), _tensor(bias, "bias"),
+        _tensor(conv_state, "conv_state"), _ptr(slot_idx, "slot_idx", torch.int32),
         _ptr(has_initial_state, "has_initial_state", torch.int32),
-        _ptr(cu_seqlens, "cu_seqlens", torch.int32), _ptr(out, "out"), nseq, channels,
-        total_len, width, nslots, _code(x, "x"), int(bool(apply_silu)), _stream(stream))
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32), _tensor(out, "out"), nseq, channels,
+        total_len, width, nslots, int(bool(apply_silu)), _stream(stream))
     _check("ssm_causal_conv1d_varlen", st)
     return out
 
@@ -307,18 +325,15 @@ def selective_scan_varlen(u, dt, A, B, C, cu_seqlens, D=None, z=None, dt_bias=No
     nseq = cu_seqlens.shape[0] - 1
     a_per_state = 1 if A.dim() == 2 else 0
     if out is None:
-        out = torch.empty_like(u)
-    _same_io(u.dtype, (dt, "dt"), (B, "B"), (C, "C"), (z, "z"), (out, "out"))
+        out = _new_like(u)
     nslots = ssm_state.shape[0] if ssm_state is not None else 0
-    sd = _code(ssm_state, "ssm_state") if ssm_state is not None else SSM_F32
     st = load_library().ssm_selective_scan_varlen(
-        _ptr(u, "u"), _ptr(dt, "dt"), _ptr(dt_bias, "dt_bias", torch.float32),
-        _ptr(A, "A", torch.float32), _ptr(B, "B"), _ptr(C, "C"), _ptr(D, "D", torch.float32),
-        _ptr(z, "z"), _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
+        _tensor(u, "u"), _tensor(dt, "dt"), _tensor(dt_bias, "dt_bias"), _tensor(A, "A"),
+        _tensor(B, "B"), _tensor(C, "C"), _tensor(D, "D"), _tensor(z, "z"),
+        _tensor(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32),
         _ptr(has_initial_state, "has_initial_state", torch.int32),
-        _ptr(cu_seqlens, "cu_seqlens", torch.int32), _ptr(out, "out"), nseq, total_len, nheads,
-        headdim, dstate, ngroups, nslots, _code(u, "u"), sd, a_per_state,
-        int(bool(dt_softplus)), _stream(stream))
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32), _tensor(out, "out"), nseq, total_len, nheads,
+        headdim, dstate, ngroups, nslots, a_per_state, int(bool(dt_softplus)), _stream(stream))
     _check("ssm_selective_scan_varlen", st)
     return out
 
@@ -336,13 +351,12 @@ def linear(x, weight, residual=None, out=None, workspace=None, stream=None):
     N = weight.shape[0]
     if out is None:
         out = torch.empty(M, N, dtype=x.dtype, device=x.device)
-    _same_io(x.dtype, (weight, "weight"), (residual, "residual"), (out, "out"))
     need = load_library().ssm_linear_workspace(M, N, K)
     if workspace is None:
         workspace = _workspace(need, x.device)
     st = load_library().ssm_linear(
-        _ptr(x, "x"), _ptr(weight, "weight"), _ptr(residual, "residual"), _ptr(out, "out"), M, N, K,
-        _code(x, "x"), _ptr(workspace, "workspace"),
+        _tensor(x, "x"), _tensor(weight, "weight"), _tensor(residual, "residual"),
+        _tensor(out, "out"), M, N, K, _ptr(workspace, "workspace"),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ssm_linear", st)
     return out
@@ -352,10 +366,9 @@ def rmsnorm(x, weight, eps=1e-5, out=None, stream=None):
     """ssm_rmsnorm over the last dimension of x [M, D]."""
     M, D = x.shape
     if out is None:
-        out = torch.empty_like(x)
-    st = load_library().ssm_rmsnorm(_ptr(x, "x"), _ptr(weight, "weight", torch.float32),
-                                    _ptr(out, "out"), M, D, float(eps), _code(x, "x"),
-                                    _stream(stream))
+        out = _new_like(x)
+    st = load_library().ssm_rmsnorm(_tensor(x, "x"), _tensor(weight, "weight"), _tensor(out, "out"),
+                                    M, D, float(eps), _stream(stream))
     _check("ssm_rmsnorm", st)
     return out
 
@@ -386,18 +399,16 @@ def mamba1_decode_layer(layer, hidden, conv_state, ssm_state, slot_idx=None, wor
     need = lib.ssm_mamba1_decode_layer_workspace(ctypes.byref(layer), batch)
     if workspace is None:
         workspace = _workspace(need, hidden.device)
-    _same_io(hidden.dtype, (conv_state, "conv_state"))
     st = lib.ssm_mamba1_decode_layer(
-        ctypes.byref(layer), _ptr(hidden, "hidden"), _ptr(conv_state, "conv_state"),
-        _ptr(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32), batch,
-        conv_state.shape[0], _code(hidden, "hidden"), _code(ssm_state, "ssm_state"),
-        _ptr(workspace, "workspace"),
+        ctypes.byref(layer), _tensor(hidden, "hidden"), _tensor(conv_state, "conv_state"),
+        _tensor(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32), batch,
+        conv_state.shape[0], _ptr(workspace, "workspace"),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ssm_mamba1_decode_layer", st)
     return hidden
 
 
-__all__ = ["linear", "rmsnorm", "mamba1_layer", "mamba1_decode_layer", "Mamba1Layer",
+__all__ = ["Tensor", "linear", "rmsnorm", "mamba1_layer", "mamba1_decode_layer", "Mamba1Layer",
            "causal_conv1d", "selective_scan", "state_update", "state_update_config",
            "LaunchConfig", "decode_step", "SCAN_AUTO", "SCAN_RECURRENT", "SCAN_CHUNKED",
            "causal_conv1d_varlen", "selective_scan_varlen", "load_library",

@@ -60,15 +60,15 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
     float w[W];
 #pragma unroll
     for (int k = 0; k < W; ++k)
-        w[k] = a.weight[(int64_t)c * W + k];
+        w[k] = a.weight[c * a.w_sc + k];
     const float bias = a.bias ? a.bias[c] : 0.0f;
 
-    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
+    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + slot * a.cs_ss + c * a.cs_sc : nullptr;
     if (tid < H)
         hist[tid] = (a.has_initial_state && cs) ? to_f32(cs[tid]) : 0.0f;
 
-    const T *xr = static_cast<const T *>(a.x) + row * a.seqlen;
-    T *orow = static_cast<T *>(a.out) + row * a.seqlen;
+    const T *xr = static_cast<const T *>(a.x) + b * a.x_sb + c * a.x_sc;
+    T *orow = static_cast<T *>(a.out) + b * a.o_sb + c * a.o_sc;
 
     for (int t0 = 0; t0 < a.seqlen; t0 += TILE) {
         const int t = t0 + tid * E;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
         cs[tid] = from_f32<T>(hist[tid]);  // exact: the values came from T
 }
 
-// Dense prefill with 16-byte aligned rows (seqlen % 8 == 0): no LDS and no
+// Dense prefill with rows of whole 16-byte vectors: no LDS and no
 // barriers.  A workgroup takes RPW rows; per tile, each lane takes E samples
 // of each of its rows (one 128-bit load per row, all issued before any
 // arithmetic, so RPW loads are in flight per lane) and, for the taps that
@@ -149,11 +149,11 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
         live[r] = row < nrows && slot >= 0;  // padded request: untouched
 #pragma unroll
         for (int k = 0; k < W; ++k)
-            w[r][k] = a.weight[(int64_t)c * W + k];
+            w[r][k] = a.weight[c * a.w_sc + k];
         bias[r] = a.bias ? a.bias[c] : 0.0f;
-        xr[r] = static_cast<const T *>(a.x) + rr * L;
-        orow[r] = static_cast<T *>(a.out) + rr * L;
-        cs[r] = (a.conv_state && slot >= 0) ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H
+        xr[r] = static_cast<const T *>(a.x) + b * a.x_sb + c * a.x_sc;
+        orow[r] = static_cast<T *>(a.out) + b * a.o_sb + c * a.o_sc;
+        cs[r] = (a.conv_state && slot >= 0) ? static_cast<T *>(a.conv_state) + slot * a.cs_ss + c * a.cs_sc
                                             : nullptr;
         // history in front of sample 0 (only lane 0 uses it)
 #pragma unroll
@@ -286,10 +286,11 @@ __device__ __forceinline__ void conv_varlen_tile(const ConvArgs &a, const int k,
     __shared__ float lhist[kSeqCap][HS];       // history of each sequence starting in the tile
 
     const int Tn = a.seqlen, tid = threadIdx.x, nseq = a.batch;
-    const int64_t first = (int64_t)c * Tn;     // column 0 of row c
-    const int m = VEC ? (int)(first % E) : 0;  // vector alignment of the row
-    const T *xr = static_cast<const T *>(a.x) + first;
-    T *orow = static_cast<T *>(a.out) + first;
+    // vector alignment of the row (x and out rows share it: same row stride,
+    // or rows that are whole vectors)
+    const int m = VEC ? (int)((c * a.x_sc) % E) : 0;
+    const T *xr = static_cast<const T *>(a.x) + c * a.x_sc;  // column 0 of row c
+    T *orow = static_cast<T *>(a.out) + c * a.o_sc;
     const int j0 = k * TILE - m;               // first packed column of the tile
     const int jend = min(j0 + TILE, Tn);       // end of the tile's columns in the row
     const bool staged = nseq <= kSeqCap;
@@ -335,7 +336,7 @@ __device__ __forceinline__ void conv_varlen_tile(const ConvArgs &a, const int k,
         if (te > tb && slot >= 0 && tb > j0 - H && tb < jend) {
             my_start = tb;
             const T *cs = (init && a.conv_state)
-                              ? static_cast<const T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H
+                              ? static_cast<const T *>(a.conv_state) + slot * a.cs_ss + c * a.cs_sc
                               : nullptr;
 #pragma unroll
             for (int h = 0; h < H; ++h)
@@ -351,7 +352,7 @@ __device__ __forceinline__ void conv_varlen_tile(const ConvArgs &a, const int k,
     float w[W];
 #pragma unroll
     for (int kk = 0; kk < W; ++kk)
-        w[kk] = a.weight[(int64_t)c * W + kk];
+        w[kk] = a.weight[c * a.w_sc + kk];
     const float bias = a.bias ? a.bias[c] : 0.0f;
     const bool slow = __syncthreads_or(need_slow) != 0;  // tile, table, histories, cleared bits
     if (my_start >= 0) {
@@ -447,7 +448,7 @@ __device__ __forceinline__ void conv_varlen_tile(const ConvArgs &a, const int k,
             slot = a.slot_idx ? a.slot_idx[s] : s;
             const bool init = a.has_init_seq && a.has_init_seq[s] != 0;
             hist = (init && a.conv_state && slot >= 0)
-                       ? static_cast<const T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H
+                       ? static_cast<const T *>(a.conv_state) + slot * a.cs_ss + c * a.cs_sc
                        : nullptr;
         }
         if (slot < 0 || j < tb || j >= te)
@@ -566,9 +567,8 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
         const int64_t c = row0 + r;
         if (c >= pa.channels)
             break;
-        T *cs = pa.conv_state ? static_cast<T *>(pa.conv_state) + ((int64_t)slot * pa.channels + c) * H
-                              : nullptr;
-        const T *xr = static_cast<const T *>(pa.x) + c * Tn + tb;
+        T *cs = pa.conv_state ? static_cast<T *>(pa.conv_state) + slot * pa.cs_ss + c * pa.cs_sc : nullptr;
+        const T *xr = static_cast<const T *>(pa.x) + c * pa.x_sc + tb;
         // every sample the lane needs, from in-bounds addresses, issued
         // together: the cached history, the first and the last H samples
         T hraw[HS], xb[HS], xe[HS];
@@ -588,9 +588,9 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
             float w[W];
 #pragma unroll
             for (int kk = 0; kk < W; ++kk)
-                w[kk] = pa.weight[c * W + kk];
+                w[kk] = pa.weight[c * pa.w_sc + kk];
             const float bias = pa.bias ? pa.bias[c] : 0.0f;
-            T *orow = static_cast<T *>(pa.out) + c * Tn + tb;
+            T *orow = static_cast<T *>(pa.out) + c * pa.o_sc + tb;
 #pragma unroll
             for (int j = 0; j < H; ++j) {
                 if (j >= len)
@@ -650,8 +650,8 @@ __global__ __launch_bounds__(256) void conv_varlen_tail_kernel(ConvArgs a)
     if (slot < 0 || te == tb)
         return;
     const bool init = a.has_init_seq && a.has_init_seq[s] != 0;
-    T *cs = static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H;
-    const T *xr = static_cast<const T *>(a.x) + (int64_t)c * Tn + tb;
+    T *cs = static_cast<T *>(a.conv_state) + slot * a.cs_ss + c * a.cs_sc;
+    const T *xr = static_cast<const T *>(a.x) + c * a.x_sc + tb;
     const int len = te - tb;
     T v[H > 0 ? H : 1];
 #pragma unroll
@@ -675,18 +675,18 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(ConvArgs a)
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0)
         return;
-    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)slot * a.channels + c) * H : nullptr;
-    const T xv_raw = static_cast<const T *>(a.x)[i];
+    T *cs = a.conv_state ? static_cast<T *>(a.conv_state) + slot * a.cs_ss + c * a.cs_sc : nullptr;
+    const T xv_raw = static_cast<const T *>(a.x)[b * a.x_sb + c * a.x_sc];
     T win[H > 0 ? H : 1];
     float acc = a.bias ? a.bias[c] : 0.0f;
 #pragma unroll
     for (int k = 0; k < H; ++k) {
         win[k] = cs ? cs[k] : T{};
         const float hv = (a.has_initial_state && cs) ? to_f32(win[k]) : 0.0f;
-        acc = fmaf(a.weight[(int64_t)c * W + k], hv, acc);
+        acc = fmaf(a.weight[c * a.w_sc + k], hv, acc);
     }
-    acc = fmaf(a.weight[(int64_t)c * W + H], to_f32(xv_raw), acc);
-    static_cast<T *>(a.out)[i] = from_f32<T>(a.apply_silu ? silu_f32(acc) : acc);
+    acc = fmaf(a.weight[c * a.w_sc + H], to_f32(xv_raw), acc);
+    static_cast<T *>(a.out)[b * a.o_sb + c * a.o_sc] = from_f32<T>(a.apply_silu ? silu_f32(acc) : acc);
     if (cs) {
         // shift the window by one; without an initial state the history is
         // zeros, so the new window is (0, ..., 0, x)
@@ -699,9 +699,10 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(ConvArgs a)
 }
 
 // Decode with 128-bit accesses: one lane per 8 consecutive channels of one
-// request (channels % 8 == 0, 16-byte aligned tensors).  The 8 windows of
-// width-1 samples are contiguous in the cache row, so a lane reads and writes
-// them as whole vectors; the window values pass through float32 unchanged.
+// request (channels % 8 == 0; x, out, the cache rows and the taps contiguous
+// over channels and 16-byte aligned).  The 8 windows of width-1 samples are
+// contiguous in the cache row, so a lane reads and writes them as whole
+// vectors; the window values pass through float32 unchanged.
 template <typename T, int W, int RB>
 __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
 {
@@ -739,8 +740,8 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
         const int slot = a.slot_idx ? a.slot_idx[bb] : bb;
         live[k] = b < a.batch && slot >= 0;  // padded request: untouched
         const int s = slot >= 0 ? slot : 0;
-        load_vec_cached<T, G>(static_cast<const T *>(a.x) + (int64_t)bb * a.channels + c0, xv[k]);
-        cs[k] = a.conv_state ? static_cast<T *>(a.conv_state) + ((int64_t)s * a.channels + c0) * H : nullptr;
+        load_vec_cached<T, G>(static_cast<const T *>(a.x) + bb * a.x_sb + c0, xv[k]);
+        cs[k] = a.conv_state ? static_cast<T *>(a.conv_state) + s * a.cs_ss + (int64_t)c0 * H : nullptr;
         if constexpr (H > 0) {
             // without a cache (or its history) the weights are read instead
             // and the values replaced by zeros below
@@ -780,7 +781,7 @@ __global__ __launch_bounds__(256) void conv_decode_vec_kernel(ConvArgs a)
             acc = fmaf(w[g * W + H], xv[k][g], acc);
             o[g] = a.apply_silu ? silu_f32(acc) : acc;
         }
-        store_vec_cached<T, G>(static_cast<T *>(a.out) + (int64_t)b * a.channels + c0, o);
+        store_vec_cached<T, G>(static_cast<T *>(a.out) + b * a.o_sb + c0, o);
         if constexpr (H > 0) {
             if (cs[k]) {
                 float nw[G * H];
@@ -812,18 +813,20 @@ static hipError_t launch_conv_tw(const ConvArgs &a, hipStream_t stream)
         const int64_t n = (int64_t)a.batch * a.channels;
         hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            stream, a);
-    } else if (a.cu_seqlens && a.vec && a.seqlen % 8 == 0 && a.batch <= 255) {
-        // packed batch whose rows the dense kernel can walk: the dense conv
-        // (or, for a table with padded sequences, the tiled code), then the
-        // starts and the caches, in one launch
+    } else if (a.cu_seqlens && a.rows16 && a.batch <= 255) {
+        // packed batch whose rows the dense kernel can walk: the dense walk
+        // (storing around up to 8 padded sequences), else the tiled code;
+        // then the starts and the caches, in one launch
         constexpr int RPW = 2;
         const dim3 grid((unsigned)((a.channels + RPW - 1) / RPW));
         hipLaunchKernelGGL((conv_rows_kernel<T, W, RPW, true>), grid, dim3(256), 0, stream, a);
     } else if (a.cu_seqlens) {
         constexpr int E = 16 / StorageSize<T>::value;
-        // rows start inside a vector only when the packed length is not a
-        // multiple of E; then one more tile covers the shifted walk
-        const int ntiles = (a.seqlen + (a.seqlen % E ? E - 1 : 0) + 256 * E - 1) / (256 * E);
+        // rows start inside a vector only when the row stride or the packed
+        // length is not a multiple of E; then one more tile covers the
+        // shifted walk
+        const bool shifted = (a.x_sc % E) != 0 || (a.seqlen % E) != 0;
+        const int ntiles = (a.seqlen + (shifted ? E - 1 : 0) + 256 * E - 1) / (256 * E);
         const dim3 grid((unsigned)ntiles, (unsigned)a.channels);
         if (a.vec)
             hipLaunchKernelGGL((conv_varlen_kernel<T, W, true>), grid, dim3(256), 0, stream, a);

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     for (int q = 0; q < WCH; ++q) {
         const int c = tid + 256 * q, r = c / CPR;
         const int n = min(nb * GN + r, a.N - 1);
-        wsrc[q] = static_cast<const T *>(a.W) + (int64_t)n * K + kofs;
+        wsrc[q] = static_cast<const T *>(a.W) + (int64_t)n * a.ldw + kofs;
         wdst[q] = r * LDK + kofs;
     }
 
@@ -298,12 +298,13 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 // RMSNorm of each row: out = x / sqrt(mean(x^2) + eps) * weight (weight in
 // float32), one workgroup per row.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ x, const float *__restrict__ wt,
-                                                      T *__restrict__ out, int M, int D, float eps)
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ x, int64_t ldx,
+                                                      const float *__restrict__ wt, T *__restrict__ out,
+                                                      int64_t ldo, int M, int D, float eps)
 {
     __shared__ float red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
-    const T *xr = x + (int64_t)row * D;
+    const T *xr = x + row * ldx;
     float ss = 0.0f;
     for (int i = tid; i < D; i += 256) {
         const float v = to_f32(xr[i]);
@@ -317,18 +318,18 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ x, c
     const float tot = red[0] + red[1] + red[2] + red[3];
     const float inv = 1.0f / sqrtf(tot / (float)D + eps);
     for (int i = tid; i < D; i += 256)
-        out[(int64_t)row * D + i] = from_f32<T>(to_f32(xr[i]) * inv * wt[i]);
+        out[row * ldo + i] = from_f32<T>(to_f32(xr[i]) * inv * wt[i]);
 }
 
-hipError_t launch_rmsnorm(const void *x, const float *w, void *out, int M, int D, float eps, int dtype,
-                          hipStream_t stream)
+hipError_t launch_rmsnorm(const void *x, int64_t ldx, const float *w, void *out, int64_t ldo, int M, int D,
+                          float eps, int dtype, hipStream_t stream)
 {
     if (dtype == 1)
-        hipLaunchKernelGGL((rmsnorm_kernel<f16>), dim3(M), dim3(256), 0, stream, static_cast<const f16 *>(x), w,
-                           static_cast<f16 *>(out), M, D, eps);
+        hipLaunchKernelGGL((rmsnorm_kernel<f16>), dim3(M), dim3(256), 0, stream, static_cast<const f16 *>(x), ldx,
+                           w, static_cast<f16 *>(out), ldo, M, D, eps);
     else
-        hipLaunchKernelGGL((rmsnorm_kernel<bf16>), dim3(M), dim3(256), 0, stream, static_cast<const bf16 *>(x), w,
-                           static_cast<bf16 *>(out), M, D, eps);
+        hipLaunchKernelGGL((rmsnorm_kernel<bf16>), dim3(M), dim3(256), 0, stream, static_cast<const bf16 *>(x),
+                           ldx, w, static_cast<bf16 *>(out), ldo, M, D, eps);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ bool mfma_dtype(int d) { return d == SSM_F16 || d == SSM_BF16; }
 bool valid_dtype_code(int d) { return d == SSM_F32 || d == SSM_F16 || d == SSM_BF16; }
 bool al(const void *p, uintptr_t n) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
-int status_of(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
+using ssm::status_of;
 
 // K split so that a narrow output still spreads over the chip: up to 32
 // slices of at least 2 k batches, aiming at ~512 workgroups.
@@ -35,16 +35,51 @@ size_t linear_partial_bytes(int M, int N, int K)
     return s > 1 ? round_up((size_t)s * M * N * sizeof(float)) : 0;
 }
 
-int check_linear(const void *x, const void *w, const void *out, int M, int N, int K, int dtype)
+ssm_tensor dense(const void *p, int dtype, int64_t s0, int64_t s1 = 1, int64_t s2 = 1)
 {
-    if (!x || !w || !out)
+    ssm_tensor t{};
+    t.data = const_cast<void *>(p);
+    t.dtype = dtype;
+    t.stride[0] = s0;
+    t.stride[1] = s1;
+    t.stride[2] = s2;
+    t.stride[3] = 1;
+    return t;
+}
+
+// A [rows, cols] operand of the projections: f16/bf16 of the given dtype,
+// unit inner stride, non-negative row stride that fits the kernels' int.
+int check_matrix(const ssm_tensor &t, int rows, int cols, int dtype, bool rows16)
+{
+    if (!t.data)
+        return SSM_OK;
+    if (!valid_dtype_code(t.dtype) || t.dtype != dtype)
+        return SSM_ERR_DTYPE;
+    if (t.stride[0] < 0 || t.stride[1] < 0 || (cols > 1 && t.stride[1] != 1))
+        return SSM_ERR_LAYOUT;
+    if (t.stride[0] > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
+    if (!al(t.data, 2))
+        return SSM_ERR_ALIGN;
+    if (rows16 && (!al(t.data, 16) || (rows > 1 && (t.stride[0] * 2) % 16 != 0)))
+        return SSM_ERR_ALIGN;
+    return SSM_OK;
+}
+
+int check_linear(const ssm_tensor &x, const ssm_tensor &w, const ssm_tensor &res, const ssm_tensor &out, int M,
+                 int N, int K)
+{
+    if (!x.data || !w.data || !out.data)
         return SSM_ERR_NULL_ARG;
-    if (!mfma_dtype(dtype))
-        return valid_dtype_code(dtype) ? SSM_ERR_UNSUPPORTED : SSM_ERR_DTYPE;
+    if (!mfma_dtype(x.dtype))
+        return valid_dtype_code(x.dtype) ? SSM_ERR_UNSUPPORTED : SSM_ERR_DTYPE;
     if (M < 0 || N < 1 || K < 8 || K % 8 != 0)
         return SSM_ERR_SHAPE;
-    if (!al(x, 16) || !al(w, 16) || !al(out, 2))
-        return SSM_ERR_ALIGN;
+    int st;
+    if ((st = check_matrix(x, M, K, x.dtype, true)) != SSM_OK || (st = check_matrix(w, N, K, x.dtype, true)) != SSM_OK ||
+        (st = check_matrix(out, M, N, x.dtype, false)) != SSM_OK ||
+        (st = check_matrix(res, M, N, x.dtype, false)) != SSM_OK)
+        return st;
     if ((int64_t)M * N > INT32_MAX || (int64_t)N * K > INT32_MAX)
         return SSM_ERR_UNSUPPORTED;
     return SSM_OK;
@@ -71,13 +106,13 @@ size_t ssm_linear_workspace(int M, int N, int K)
     return linear_partial_bytes(M, N, K);
 }
 
-int ssm_linear(const void *x, const void *weight, const void *residual, void *out, int M, int N, int K,
-               int dtype, void *workspace, size_t workspace_bytes, void *stream)
+int ssm_linear(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M, int N, int K,
+               void *workspace, size_t workspace_bytes, void *stream)
 {
-    const int st = check_linear(x, weight, out, M, N, K, dtype);
+    const int st = check_linear(x, weight, residual, out, M, N, K);
     if (st != SSM_OK)
         return st;
-    if (!al(residual, 2) || !al(workspace, 16))
+    if (!al(workspace, 16))
         return SSM_ERR_ALIGN;
     if (M == 0)
         return SSM_OK;
@@ -85,31 +120,40 @@ int ssm_linear(const void *x, const void *weight, const void *residual, void *ou
     if (need && (!workspace || workspace_bytes < need))
         return SSM_ERR_SHAPE;
     ssm::GemmArgs g{};
-    g.A = x;
-    g.W = weight;
-    g.lda = K;
-    g.dtype = dtype;
-    g.seg[0] = ssm::GemmSeg{out, N, 0, N};
+    g.A = x.data;
+    g.lda = (int)x.stride[0];
+    g.W = weight.data;
+    g.ldw = (int)weight.stride[0];
+    g.dtype = x.dtype;
+    g.seg[0] = ssm::GemmSeg{out.data, (int)out.stride[0], 0, N};
     g.nseg = 1;
-    g.residual = residual;
-    g.ld_residual = N;
+    g.residual = residual.data;
+    g.ld_residual = residual.data ? (int)residual.stride[0] : 0;
     return run_linear(g, M, N, K, workspace, static_cast<hipStream_t>(stream));
 }
 
-int ssm_rmsnorm(const void *x, const float *weight, void *out, int M, int D, float eps, int dtype,
-                void *stream)
+int ssm_rmsnorm(ssm_tensor x, ssm_tensor weight, ssm_tensor out, int M, int D, float eps, void *stream)
 {
-    if (!x || !weight || !out)
+    if (!x.data || !weight.data || !out.data)
         return SSM_ERR_NULL_ARG;
-    if (!mfma_dtype(dtype))
-        return valid_dtype_code(dtype) ? SSM_ERR_UNSUPPORTED : SSM_ERR_DTYPE;
+    if (!mfma_dtype(x.dtype))
+        return valid_dtype_code(x.dtype) ? SSM_ERR_UNSUPPORTED : SSM_ERR_DTYPE;
+    if (weight.dtype != SSM_F32)
+        return SSM_ERR_DTYPE;
     if (M < 0 || D < 1 || !(eps >= 0.0f))
         return SSM_ERR_SHAPE;
-    if (!al(x, 2) || !al(out, 2) || !al(weight, 4))
+    int st;
+    if ((st = check_matrix(x, M, D, x.dtype, false)) != SSM_OK ||
+        (st = check_matrix(out, M, D, x.dtype, false)) != SSM_OK)
+        return st;
+    if (D > 1 && weight.stride[0] != 1)
+        return SSM_ERR_LAYOUT;
+    if (!al(weight.data, 4))
         return SSM_ERR_ALIGN;
     if (M == 0)
         return SSM_OK;
-    return status_of(ssm::launch_rmsnorm(x, weight, out, M, D, eps, dtype, static_cast<hipStream_t>(stream)));
+    return status_of(ssm::launch_rmsnorm(x.data, x.stride[0], static_cast<const float *>(weight.data), out.data,
+                                         out.stride[0], M, D, eps, x.dtype, static_cast<hipStream_t>(stream)));
 }
 
 // Workspace of one decode layer: the intermediates of the batch, each
@@ -167,59 +211,78 @@ size_t ssm_mamba1_decode_layer_workspace(const ssm_mamba1_layer *layer, int batc
     return layer_ws(layer, batch).total;
 }
 
-int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, void *hidden, void *conv_state, void *ssm_state,
-                            const int32_t *slot_idx, int batch, int nslots, int io_dtype, int state_dtype,
-                            void *workspace, size_t workspace_bytes, void *stream)
+int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, ssm_tensor hidden, ssm_tensor conv_state,
+                            ssm_tensor ssm_state, const int32_t *slot_idx, int batch, int nslots, void *workspace,
+                            size_t workspace_bytes, void *stream)
 {
     int st = check_layer(L, batch);
     if (st != SSM_OK)
         return st;
-    if (!hidden || !conv_state || !ssm_state)
+    if (!hidden.data || !conv_state.data || !ssm_state.data)
         return SSM_ERR_NULL_ARG;
-    if (!mfma_dtype(io_dtype))
-        return valid_dtype_code(io_dtype) ? SSM_ERR_UNSUPPORTED : SSM_ERR_DTYPE;
-    if (!valid_dtype_code(state_dtype))
-        return SSM_ERR_DTYPE;
-    if (!al(hidden, 16) || !al(L->in_proj, 16) || !al(L->x_proj, 16) || !al(L->dt_proj, 16) ||
-        !al(L->out_proj, 16) || !al(workspace, 256))
+    const int io = hidden.dtype;
+    if (!mfma_dtype(io))
+        return valid_dtype_code(io) ? SSM_ERR_UNSUPPORTED : SSM_ERR_DTYPE;
+    const int M = batch, Dm = L->d_model, Di = L->d_inner, N = L->d_state, R = L->dt_rank;
+    if ((st = check_matrix(hidden, M, Dm, io, true)) != SSM_OK)
+        return st;
+    if (!al(L->in_proj, 16) || !al(L->x_proj, 16) || !al(L->dt_proj, 16) || !al(L->out_proj, 16) ||
+        !al(workspace, 256))
         return SSM_ERR_ALIGN;
-    if (batch == 0)
-        return SSM_OK;
-    const LayerWs w = layer_ws(L, batch);
-    if (!workspace || workspace_bytes < w.total)
+    const LayerWs w = layer_ws(L, batch > 0 ? batch : 1);
+    if (batch > 0 && (!workspace || workspace_bytes < w.total))
         return SSM_ERR_SHAPE;
     char *ws = static_cast<char *>(workspace);
     void *hn = ws + w.hn, *x = ws + w.x, *z = ws + w.z, *u = ws + w.u, *dtl = ws + w.dtl;
     void *Bm = ws + w.B, *Cm = ws + w.C, *dt = ws + w.dt, *y = ws + w.y, *part = ws + w.partial;
-    const int M = batch, Dm = L->d_model, Di = L->d_inner, N = L->d_state, R = L->dt_rank;
+
+    // every later step's arguments, checked before the first launch so that
+    // an error leaves hidden and both caches untouched
+    ssm::ConvArgs ca;
+    st = ssm::prepare_conv(ca, dense(x, io, Di, 1, 1), dense(L->conv_weight, SSM_F32, L->conv_width),
+                           dense(L->conv_bias, SSM_F32, 1), conv_state, slot_idx, nullptr, nullptr,
+                           dense(u, io, Di, 1, 1), M, Di, 1, L->conv_width, nslots, 1, 1);
+    if (st != SSM_OK)
+        return st;
+    // the state update: one channel per head (headdim 1)
+    ssm::SsuArgs sa;
+    st = ssm::prepare_ssu(sa, ssm_state, slot_idx, dense(u, io, Di, 1, 1), dense(dt, io, Di, 1),
+                          dense(L->dt_bias, SSM_F32, 1), dense(L->A, SSM_F32, N, 1), dense(Bm, io, N, N, 1),
+                          dense(Cm, io, N, N, 1), dense(L->D, SSM_F32, 1), dense(z, io, Di, 1, 1),
+                          dense(y, io, Di, 1, 1), M, Di, 1, N, 1, nslots, 1, 1, nullptr);
+    if (st != SSM_OK)
+        return st;
+    if (batch == 0)
+        return SSM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // 1. normalised hidden state
-    st = status_of(ssm::launch_rmsnorm(hidden, L->norm_weight, hn, M, Dm, L->norm_eps, io_dtype, s));
+    st = status_of(ssm::launch_rmsnorm(hidden.data, hidden.stride[0], L->norm_weight, hn, Dm, M, Dm, L->norm_eps,
+                                       io, s));
     if (st != SSM_OK)
         return st;
     // 2. in_proj -> x | z
     ssm::GemmArgs g{};
-    g.dtype = io_dtype;
+    g.dtype = io;
     g.A = hn;
     g.lda = Dm;
     g.W = L->in_proj;
+    g.ldw = Dm;
     g.seg[0] = ssm::GemmSeg{x, Di, 0, Di};
     g.seg[1] = ssm::GemmSeg{z, Di, Di, Di};
     g.nseg = 2;
     if ((st = run_linear(g, M, 2 * Di, Dm, part, s)) != SSM_OK)
         return st;
     // 3. conv update + SiLU of x (the request's window in its slot)
-    st = ssm_causal_conv1d(x, L->conv_weight, L->conv_bias, conv_state, slot_idx, u, M, Di, 1,
-                           L->conv_width, nslots, io_dtype, 1, 1, stream);
-    if (st != SSM_OK)
+    if ((st = status_of(ssm::launch_conv(ca, s))) != SSM_OK)
         return st;
     // 4. x_proj -> dt_low | B | C
     g = ssm::GemmArgs{};
-    g.dtype = io_dtype;
+    g.dtype = io;
     g.A = u;
     g.lda = Di;
     g.W = L->x_proj;
+    g.ldw = Di;
     g.seg[0] = ssm::GemmSeg{dtl, R, 0, R};
     g.seg[1] = ssm::GemmSeg{Bm, N, R, N};
     g.seg[2] = ssm::GemmSeg{Cm, N, R + N, N};
@@ -228,29 +291,29 @@ int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, void *hidden, void *conv_
         return st;
     // 5. dt_proj -> dt (its bias goes in with the softplus of the update)
     g = ssm::GemmArgs{};
-    g.dtype = io_dtype;
+    g.dtype = io;
     g.A = dtl;
     g.lda = R;
     g.W = L->dt_proj;
+    g.ldw = R;
     g.seg[0] = ssm::GemmSeg{dt, Di, 0, Di};
     g.nseg = 1;
     if ((st = run_linear(g, M, Di, R, part, s)) != SSM_OK)
         return st;
-    // 6. selective state update (one channel per head: headdim 1)
-    st = ssm_state_update(ssm_state, slot_idx, u, dt, L->dt_bias, L->A, Bm, Cm, L->D, z, y, M, Di, 1, N, 1,
-                          nslots, io_dtype, state_dtype, 1, 1, stream);
-    if (st != SSM_OK)
+    // 6. selective state update
+    if ((st = status_of(ssm::launch_ssu(sa, s))) != SSM_OK)
         return st;
     // 7. out_proj + residual, in place on hidden (rows of padded requests kept)
     g = ssm::GemmArgs{};
-    g.dtype = io_dtype;
+    g.dtype = io;
     g.A = y;
     g.lda = Di;
     g.W = L->out_proj;
-    g.seg[0] = ssm::GemmSeg{hidden, Dm, 0, Dm};
+    g.ldw = Di;
+    g.seg[0] = ssm::GemmSeg{hidden.data, (int)hidden.stride[0], 0, Dm};
     g.nseg = 1;
-    g.residual = hidden;
-    g.ld_residual = Dm;
+    g.residual = hidden.data;
+    g.ld_residual = (int)hidden.stride[0];
     g.row_slot = slot_idx;
     return run_linear(g, M, Dm, Di, part, s);
 }

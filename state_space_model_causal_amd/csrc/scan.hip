@@ -240,16 +240,15 @@ void scan_kernel(ScanArgs a)
     const bool active = cig < cpg;
     const int c = g * cpg + (active ? cig : 0);  // inactive lanes shadow a valid channel
     const int h = c / P, p = c % P;
-    const int Cn = a.nheads * P;
 
     const int64_t blk = sp.block;
-    const TI *urow = static_cast<const TI *>(a.u) + (blk * Cn + c) * L + col0;
-    const TI *dtrow = static_cast<const TI *>(a.dt) + (blk * a.nheads + h) * L + col0;
-    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + (blk * Cn + c) * L + col0 : nullptr;
-    TI *orow = static_cast<TI *>(a.out) + (blk * Cn + c) * L + col0;
-    const TI *Bg = static_cast<const TI *>(a.B) + (blk * a.ngroups + g) * N * L + col0;
-    const TI *Cg = static_cast<const TI *>(a.C) + (blk * a.ngroups + g) * N * L + col0;
-    TS *srow = a.state ? static_cast<TS *>(a.state) + (((int64_t)slot * a.nheads + h) * P + p) * N : nullptr;
+    const TI *urow = static_cast<const TI *>(a.u) + blk * a.u_sb + c * a.u_sc + col0;
+    const TI *dtrow = static_cast<const TI *>(a.dt) + blk * a.dt_sb + h * a.dt_sh + col0;
+    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + blk * a.z_sb + c * a.z_sc + col0 : nullptr;
+    TI *orow = static_cast<TI *>(a.out) + blk * a.o_sb + c * a.o_sc + col0;
+    const TI *Bg = static_cast<const TI *>(a.B) + blk * a.B_sb + g * a.B_sg + col0;
+    const TI *Cg = static_cast<const TI *>(a.C) + blk * a.C_sb + g * a.C_sg + col0;
+    TS *srow = a.state ? static_cast<TS *>(a.state) + slot * a.st_ss + h * a.st_sh + p * a.st_sp : nullptr;
     const bool load_init = srow && sp.init;
 
     const float bias_h = a.dt_bias ? a.dt_bias[h] : 0.0f;
@@ -259,7 +258,7 @@ void scan_kernel(ScanArgs a)
     for (int n = r; n < N; n += R) {
         lds_carry[ch][n] = load_init ? to_f32(srow[n]) : 0.0f;
         if constexpr (A_PER_STATE)
-            lds_a2[ch][n] = a.A[(int64_t)h * N + n] * kLog2e;
+            lds_a2[ch][n] = a.A[h * a.A_sh + n] * kLog2e;
     }
 
     for (int t0 = 0; t0 < hi; t0 += T) {
@@ -325,9 +324,8 @@ void scan_kernel(ScanArgs a)
                 if constexpr (VEC) {
                     // clamped address, unconditional load, then select
                     const bool ok = n < N && t < hi;
-                    const int64_t off = ok ? (int64_t)n * L + t : 0;
-                    load_vec_cached<TI, E>(Bg + off, vb);
-                    load_vec_cached<TI, E>(Cg + off, vc);
+                    load_vec_cached<TI, E>(Bg + (ok ? n * a.B_sn + t : 0), vb);
+                    load_vec_cached<TI, E>(Cg + (ok ? n * a.C_sn + t : 0), vc);
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
                         const bool in = ok && t + e >= lo && t + e < hi;
@@ -338,8 +336,8 @@ void scan_kernel(ScanArgs a)
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
                         const bool ok = n < N && t + e >= lo && t + e < hi;
-                        const int64_t off = ok ? (int64_t)n * L + t + e : lo;
-                        const float xb = to_f32(Bg[off]), xc = to_f32(Cg[off]);
+                        const float xb = to_f32(Bg[ok ? n * a.B_sn + t + e : lo]);
+                        const float xc = to_f32(Cg[ok ? n * a.C_sn + t + e : lo]);
                         vb[e] = ok ? xb : 0.0f;
                         vc[e] = ok ? xc : 0.0f;
                     }

@@ -107,19 +107,19 @@ struct ChunkLoads {
 
 template <int N>
 __device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, const bf16 *Bg, const bf16 *Cg,
-                                           const bf16 *urow, const bf16 *zrow, const bf16 *dtrow, int tid,
-                                           int w, int l, int lq, int nh)
+                                           int64_t bsn, int64_t csn, const bf16 *urow, const bf16 *zrow,
+                                           const bf16 *dtrow, int tid, int w, int l, int lq, int nh)
 {
 #pragma unroll
     for (int k = 0; k < ChunkLoads<N>::UNITS; ++k) {
         const int u = min(tid + STHREADS * k, ChunkLoads<N>::NUNITS - 1);
         const int n = 2 * (u >> 3), tv = u & 7;
         const int t = t0 + 8 * tv;
-        const int64_t off = (int64_t)n * L + (t < L ? t : 0);  // clamped; zeroed when staged
-        c.b0[k] = *reinterpret_cast<const u32x4 *>(Bg + off);
-        c.b1[k] = *reinterpret_cast<const u32x4 *>(Bg + off + L);
-        c.c0[k] = *reinterpret_cast<const u32x4 *>(Cg + off);
-        c.c1[k] = *reinterpret_cast<const u32x4 *>(Cg + off + L);
+        const int tc = t < L ? t : 0;  // clamped; zeroed when staged
+        c.b0[k] = *reinterpret_cast<const u32x4 *>(Bg + n * bsn + tc);
+        c.b1[k] = *reinterpret_cast<const u32x4 *>(Bg + (n + 1) * bsn + tc);
+        c.c0[k] = *reinterpret_cast<const u32x4 *>(Cg + n * csn + tc);
+        c.c1[k] = *reinterpret_cast<const u32x4 *>(Cg + (n + 1) * csn + tc);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -182,15 +182,14 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     const int pw = w & 3, nh = w >> 2;        // row tile, state half
     const int partner = pw + 4 * (1 - nh);
     const int p = pb * SPB + 16 * pw + l16;   // this lane's row of headdim
-    const int Cn = H * P;
-    const int64_t crow = ((int64_t)b * Cn + (int64_t)h * P + p) * L;
-    const bf16 *urow = static_cast<const bf16 *>(a.u) + crow;
-    const bf16 *zrow = a.z ? static_cast<const bf16 *>(a.z) + crow : nullptr;
-    bf16 *orow = static_cast<bf16 *>(a.out) + crow;
-    const bf16 *dtrow = static_cast<const bf16 *>(a.dt) + ((int64_t)b * H + h) * L;
-    const bf16 *Bg = static_cast<const bf16 *>(a.B) + ((int64_t)b * a.ngroups + g) * N * L;
-    const bf16 *Cg = static_cast<const bf16 *>(a.C) + ((int64_t)b * a.ngroups + g) * N * L;
-    TS *srow = a.state ? static_cast<TS *>(a.state) + (((int64_t)slot * H + h) * P + p) * N : nullptr;
+    const int64_t c = (int64_t)h * P + p;  // channel
+    const bf16 *urow = static_cast<const bf16 *>(a.u) + b * a.u_sb + c * a.u_sc;
+    const bf16 *zrow = a.z ? static_cast<const bf16 *>(a.z) + b * a.z_sb + c * a.z_sc : nullptr;
+    bf16 *orow = static_cast<bf16 *>(a.out) + b * a.o_sb + c * a.o_sc;
+    const bf16 *dtrow = static_cast<const bf16 *>(a.dt) + b * a.dt_sb + h * a.dt_sh;
+    const bf16 *Bg = static_cast<const bf16 *>(a.B) + b * a.B_sb + g * a.B_sg;
+    const bf16 *Cg = static_cast<const bf16 *>(a.C) + b * a.C_sb + g * a.C_sg;
+    TS *srow = a.state ? static_cast<TS *>(a.state) + slot * a.st_ss + h * a.st_sh + p * a.st_sp : nullptr;
 
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float Dh = a.D ? a.D[h] : 0.0f;
@@ -210,7 +209,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     }
 
     ChunkLoads<N> cur;
-    load_chunk<N>(cur, 0, L, Bg, Cg, urow, zrow, dtrow, tid, w, l, lq, nh);
+    load_chunk<N>(cur, 0, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, w, l, lq, nh);
 
     for (int t0 = 0; t0 < L; t0 += SQ) {
         // ---- stage the chunk (its loads were issued one chunk earlier)
@@ -257,7 +256,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 
         // ---- the next chunk's loads, in flight during this chunk's work
         if (t0 + SQ < L)
-            load_chunk<N>(cur, t0 + SQ, L, Bg, Cg, urow, zrow, dtrow, tid, w, l, lq, nh);
+            load_chunk<N>(cur, t0 + SQ, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, w, l, lq, nh);
 
         // ---- carried state over this wave's half of the states:
         // yc[st] = sum_{n in half} C_s[n] H[p][n]; the state as MFMA operands

@@ -6,15 +6,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssm.h"
+
 namespace ssm {
 
+// Element strides: every tensor's innermost dimension is contiguous (checked
+// on the host); the outer strides below are free.  A packed (varlen) batch
+// has no batch dimension: its batch strides are 0.
 struct ConvArgs {
     const void *x;
     const float *weight;
-    const float *bias;        // may be null
+    const float *bias;        // may be null; dense
     void *conv_state;         // may be null
     const int32_t *slot_idx;  // may be null
     void *out;
+    int64_t x_sb, x_sc;       // x [batch, channels, seqlen]
+    int64_t o_sb, o_sc;       // out, same shape
+    int64_t cs_ss, cs_sc;     // conv_state [nslots, channels, width-1]
+    int64_t w_sc;             // weight [channels, width]
     // Packed variable-length batch: sequence b occupies columns
     // [cu_seqlens[b], cu_seqlens[b+1]) of every channel row of length seqlen
     // (the packed token count); null = dense batch [batch, channels, seqlen].
@@ -23,8 +32,12 @@ struct ConvArgs {
     int batch, channels, seqlen, width, nslots;
     int dtype;                // 0 f32, 1 f16, 2 bf16
     int has_initial_state, apply_silu;
-    int vec;                  // x and out 16-byte aligned (dense: and seqlen % 8 == 0)
-    int vec_decode;           // seqlen 1, channels % 8 == 0, 16-byte aligned tensors
+    int vec;                  // dense: x and out rows 16-byte aligned (base and outer
+                              // strides), seqlen a multiple of a vector; packed: 16-byte
+                              // aligned bases, rows all aligned or sharing one stride
+    int rows16;               // x and out rows 16-byte aligned, seqlen a multiple of a vector
+    int vec_decode;           // seqlen 1, 8 channels per 128-bit access: x, out, cache and
+                              // weight contiguous over channels, 16-byte aligned
 };
 
 struct ScanArgs {
@@ -33,6 +46,12 @@ struct ScanArgs {
     void *state;                     // may be null
     const int32_t *slot_idx;         // may be null
     void *out;
+    int64_t u_sb, u_sc, z_sb, z_sc, o_sb, o_sc;  // [batch, channels, seqlen]
+    int64_t dt_sb, dt_sh;            // dt [batch, nheads, seqlen]
+    int64_t B_sb, B_sg, B_sn;        // B [batch, ngroups, dstate, seqlen]
+    int64_t C_sb, C_sg, C_sn;        // C, same shape
+    int64_t A_sh;                    // A [nheads, dstate] (per-state decays)
+    int64_t st_ss, st_sh, st_sp;     // state [nslots, nheads, headdim, dstate]
     // varlen as in ConvArgs: sequence b is columns [cu_seqlens[b],
     // cu_seqlens[b+1]) of rows of length seqlen; null = dense batch
     const int32_t *cu_seqlens;
@@ -41,7 +60,8 @@ struct ScanArgs {
     int heads_per_group;
     int io_dtype, state_dtype;
     int a_per_state, dt_softplus, has_initial_state;
-    int vec;                         // 16-byte aligned bases and seqlen a multiple of 8
+    int vec;                         // 16-byte aligned rows (bases and outer strides) and
+                                     // seqlen a multiple of a vector
 };
 
 // Where sequence b lies: columns [begin, begin+len) of the rows of row block
@@ -80,6 +100,11 @@ struct SsuArgs {
     const void *x, *dt, *B, *C, *z;  // z may be null
     const float *dt_bias, *A, *D;    // dt_bias, D may be null
     void *out;
+    int64_t x_sb, x_sh, z_sb, z_sh, o_sb, o_sh;  // [batch, nheads, headdim]
+    int64_t dt_sb;                   // dt [batch, nheads]
+    int64_t B_sb, B_sg, C_sb, C_sg;  // B, C [batch, ngroups, dstate]
+    int64_t A_sh;                    // A [nheads, dstate] (per-state decays)
+    int64_t st_ss, st_sh, st_sp;     // state [nslots, nheads, headdim, dstate]
     int64_t nrows;                   // batch * nheads * headdim
     int batch, nheads, headdim, dstate, ngroups, nslots;
     int heads_per_group;
@@ -88,13 +113,14 @@ struct SsuArgs {
     int block_threads;               // 64, 128, 256 or 512 lanes per workgroup
     int io_dtype, state_dtype;
     int a_per_state, dt_softplus;
-    int vec;                         // dstate % 8 == 0 and 16-byte aligned bases
+    int vec;                         // dstate % V == 0, 16-byte aligned state / B / C / A rows
     int requests_per_lane;           // 1, 2 or 4 requests taken in turn by each lane
     // fused decode step (conv update in front of the state update); width 0 = none
     void *conv_state;                // [nslots, nheads*headdim, width-1], io dtype
     const float *conv_weight;        // [nheads*headdim, width]
-    const float *conv_bias;          // [nheads*headdim] or null
-    void *u_out;                     // optional: the conv output, io dtype
+    const float *conv_bias;          // [nheads*headdim] or null; dense
+    void *u_out;                     // optional: the conv output, io dtype [batch, nheads, headdim]
+    int64_t cs_ss, cs_sc, cw_sc, u_sb, u_sh;
     int conv_width;
 };
 
@@ -106,8 +132,8 @@ struct GemmSeg {
 };
 struct GemmArgs {
     const void *A;           // [M, lda]
-    const void *W;           // [N, K], row-major
-    int lda, M, N, K;
+    const void *W;           // [N, ldw], row-major
+    int lda, ldw, M, N, K;
     int dtype;               // 1 f16, 2 bf16
     int splits;              // K split over this many workgroups
     float *partial;          // [splits, M, N] float32 when splits > 1
@@ -118,8 +144,8 @@ struct GemmArgs {
     const int32_t *row_slot; // optional: rows with a negative entry are not written
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
-hipError_t launch_rmsnorm(const void *x, const float *w, void *out, int M, int D, float eps, int dtype,
-                          hipStream_t stream);
+hipError_t launch_rmsnorm(const void *x, int64_t ldx, const float *w, void *out, int64_t ldo, int M, int D,
+                          float eps, int dtype, hipStream_t stream);
 
 hipError_t launch_conv(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t stream);
@@ -128,6 +154,28 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t stream);
 bool ssd_supported(const ScanArgs &a);
 hipError_t launch_ssd(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream);
+
+// Host-side validation of the C entry points (ssm_api.hip): each fills an
+// argument block and returns SSM_OK, or an ssm_status, without any HIP call,
+// so a caller that chains several steps can check all of them first.
+int prepare_conv(ConvArgs &a, const ssm_tensor &x, const ssm_tensor &weight, const ssm_tensor &bias,
+                 const ssm_tensor &conv_state, const int32_t *slot_idx, const int32_t *cu_seqlens,
+                 const int32_t *has_init_seq, const ssm_tensor &out, int batch, int channels, int seqlen,
+                 int width, int nslots, int has_initial_state, int apply_silu);
+int prepare_scan(ScanArgs &a, const ssm_tensor &u, const ssm_tensor &dt, const ssm_tensor &dt_bias,
+                 const ssm_tensor &A, const ssm_tensor &B, const ssm_tensor &C, const ssm_tensor &D,
+                 const ssm_tensor &z, const ssm_tensor &ssm_state, const int32_t *slot_idx,
+                 const int32_t *cu_seqlens, const int32_t *has_init_seq, const ssm_tensor &out, int batch,
+                 int seqlen, int nheads, int headdim, int dstate, int ngroups, int nslots, int a_per_state,
+                 int dt_softplus, int has_initial_state);
+int prepare_ssu(SsuArgs &a, const ssm_tensor &state, const int32_t *slot_idx, const ssm_tensor &x,
+                const ssm_tensor &dt, const ssm_tensor &dt_bias, const ssm_tensor &A, const ssm_tensor &B,
+                const ssm_tensor &C, const ssm_tensor &D, const ssm_tensor &z, const ssm_tensor &out,
+                int batch, int nheads, int headdim, int dstate, int ngroups, int nslots, int a_per_state,
+                int dt_softplus, const ssm_launch_config *cfg);
+int prepare_decode_conv(SsuArgs &a, const ssm_tensor &conv_state, const ssm_tensor &conv_weight,
+                        const ssm_tensor &conv_bias, const ssm_tensor &u_out, int conv_width);
+int status_of(hipError_t e);
 
 // Limits the kernels are built for.
 constexpr int kMaxConvWidth = 4;

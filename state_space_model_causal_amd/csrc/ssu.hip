@@ -38,7 +38,7 @@ struct SsuParams {
     float tap[CW > 0 ? CW : 1];
     float cbias, dtb, Dh;
     int64_t hp;                       // h * headdim + p
-    int h, n0;
+    int h, p, n0;
     bool in;                          // the lane has a row and a state range
 };
 
@@ -52,10 +52,9 @@ struct SsuReq {
     TI dt_raw, x_raw, z_raw;
     TI win_raw[CW > 1 ? CW - 1 : 1];
     float delta, xv, zv;
-    int64_t bh;                       // b * nheads + h
     TS *sp;
     TI *cw;
-    int64_t row;                      // (b * nheads + h) * headdim + p
+    int64_t x_off, z_off, o_off, u_off, dt_off;  // element offsets of the row's values
     bool live;
 };
 
@@ -67,9 +66,10 @@ __device__ __forceinline__ void ssu_params(const SsuArgs &a, int64_t hp, int j, 
     q.in = hp < HP && n0 < a.dstate;
     q.hp = hp < HP ? hp : 0;
     q.h = (int)(q.hp / a.headdim);
+    q.p = (int)(q.hp - (int64_t)q.h * a.headdim);
     q.n0 = n0 < a.dstate ? n0 : 0;
     if constexpr (A_PER_STATE) {
-        const float *Ap = a.A + (int64_t)q.h * a.dstate + q.n0;
+        const float *Ap = a.A + q.h * a.A_sh + q.n0;
         if constexpr (VEC) {
             load_vec_cached<float, V>(Ap, q.an);
         } else {
@@ -95,7 +95,7 @@ __device__ __forceinline__ void ssu_params(const SsuArgs &a, int64_t hp, int j, 
     if constexpr (CW > 0) {
 #pragma unroll
         for (int k = 0; k < CW; ++k)
-            q.tap[k] = a.conv_weight[q.hp * CW + k];
+            q.tap[k] = a.conv_weight[q.hp * a.cw_sc + k];
         q.cbias = a.conv_bias ? a.conv_bias[q.hp] : 0.0f;
     } else {
         q.tap[0] = 0.0f;
@@ -112,17 +112,18 @@ __device__ __forceinline__ void ssu_load(const SsuArgs &a, int b, int j, const S
     const int slot = a.slot_idx ? a.slot_idx[bb] : bb;  // uniform over the workgroup
     r.live = q.in && bin && slot >= 0;  // padded: loads from slot 0, discarded
     const int s = slot >= 0 ? slot : 0;
-    r.row = (int64_t)bb * a.nheads * a.headdim + q.hp;
-    const int64_t bh = (int64_t)bb * a.nheads + q.h;
+    r.x_off = bb * a.x_sb + q.h * a.x_sh + q.p;
+    r.z_off = bb * a.z_sb + q.h * a.z_sh + q.p;
+    r.o_off = bb * a.o_sb + q.h * a.o_sh + q.p;
+    r.u_off = bb * a.u_sb + q.h * a.u_sh + q.p;
+    r.dt_off = bb * a.dt_sb + q.h;
     const int g = q.h / a.heads_per_group;
-    r.sp = static_cast<TS *>(a.state) + (((int64_t)s * a.nheads * a.headdim + q.hp) * a.dstate + q.n0);
-    const int64_t bc_off = ((int64_t)bb * a.ngroups + g) * a.dstate + q.n0;
-    const TI *Bp = static_cast<const TI *>(a.B) + bc_off;
-    const TI *Cp = static_cast<const TI *>(a.C) + bc_off;
+    r.sp = static_cast<TS *>(a.state) + s * a.st_ss + q.h * a.st_sh + q.p * a.st_sp + q.n0;
+    const TI *Bp = static_cast<const TI *>(a.B) + bb * a.B_sb + g * a.B_sg + q.n0;
+    const TI *Cp = static_cast<const TI *>(a.C) + bb * a.C_sb + g * a.C_sg + q.n0;
     r.dt_raw = r.x_raw = r.z_raw = TI{};
-    r.bh = bh;
     if constexpr (CW > 0) {
-        r.cw = static_cast<TI *>(a.conv_state) + ((int64_t)s * a.nheads * a.headdim + q.hp) * (CW - 1);
+        r.cw = static_cast<TI *>(a.conv_state) + s * a.cs_ss + q.hp * a.cs_sc;
 #pragma unroll
         for (int k = 0; k < CW - 1; ++k)
             r.win_raw[k] = TI{};
@@ -159,10 +160,10 @@ __device__ __forceinline__ void ssu_load(const SsuArgs &a, int b, int j, const S
 template <typename TS, typename TI, int V, int CW>
 __device__ __forceinline__ void ssu_load_row(const SsuArgs &a, SsuReq<TS, TI, V, CW> &r)
 {
-    r.dt_raw = static_cast<const TI *>(a.dt)[r.bh];
-    r.x_raw = static_cast<const TI *>(a.x)[r.row];
+    r.dt_raw = static_cast<const TI *>(a.dt)[r.dt_off];
+    r.x_raw = static_cast<const TI *>(a.x)[r.x_off];
     // without a gate this reads x, and the value goes unused
-    r.z_raw = static_cast<const TI *>(a.z ? a.z : a.x)[r.row];
+    r.z_raw = a.z ? static_cast<const TI *>(a.z)[r.z_off] : static_cast<const TI *>(a.x)[r.x_off];
     if constexpr (CW > 0) {
 #pragma unroll
         for (int k = 0; k < CW - 1; ++k)
@@ -195,7 +196,7 @@ __device__ __forceinline__ float ssu_compute(const SsuArgs &a, int j, const SsuP
             if (HW > 0)
                 r.cw[HW - 1] = r.x_raw;
             if (a.u_out)
-                static_cast<TI *>(a.u_out)[r.row] = from_f32<TI>(u);
+                static_cast<TI *>(a.u_out)[r.u_off] = from_f32<TI>(u);
         }
         xv = u;  // the update reads the float32 conv output
     }
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(512) void ssu_kernel(SsuArgs a)
                 y = fmaf(q.Dh, r[k].xv, y);
             if (a.z)
                 y *= silu_f32(r[k].zv);
-            static_cast<TI *>(a.out)[r[k].row] = from_f32<TI>(y);
+            static_cast<TI *>(a.out)[r[k].o_off] = from_f32<TI>(y);
         }
     }
 }
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
 
     // request-independent values of the lane's NCH rows
     int64_t hp[NCH];
-    int hh[NCH];
+    int hh[NCH], pp[NCH];
     bool in[NCH];
     float an[NCH][A_PER_STATE ? E : 1], a2[NCH], dtb[NCH], Dh[NCH], cbias[NCH], tap[NCH][CW > 0 ? CW : 1];
 #pragma unroll
@@ -339,8 +340,9 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
         in[k] = row < HP;
         hp[k] = in[k] ? row : 0;  // a wave past the last row reads row 0 and stores nothing
         hh[k] = (int)(hp[k] / a.headdim);
+        pp[k] = (int)(hp[k] - (int64_t)hh[k] * a.headdim);
         if constexpr (A_PER_STATE) {
-            load_vec_cached<float, E>(a.A + (int64_t)hh[k] * N + n0, an[k]);
+            load_vec_cached<float, E>(a.A + hh[k] * a.A_sh + n0, an[k]);
 #pragma unroll
             for (int i = 0; i < E; ++i)
                 an[k][i] *= kLog2e;
@@ -353,12 +355,12 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
         cbias[k] = 0.0f;
         tap[k][0] = 0.0f;
         if constexpr (COOP) {
-            tap[k][0] = a.conv_weight[hp[k] * CW + (jl & 3)];  // this lane's tap
+            tap[k][0] = a.conv_weight[hp[k] * a.cw_sc + (jl & 3)];  // this lane's tap
             cbias[k] = a.conv_bias ? a.conv_bias[hp[k]] : 0.0f;
         } else if constexpr (CW > 0) {
 #pragma unroll
             for (int c = 0; c < CW; ++c)
-                tap[k][c] = a.conv_weight[hp[k] * CW + c];
+                tap[k][c] = a.conv_weight[hp[k] * a.cw_sc + c];
             cbias[k] = a.conv_bias ? a.conv_bias[hp[k]] : 0.0f;
         }
     }
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
     bool live[RB];
     TS *sp[RB];
     TI *cwp[RB];
-    int64_t brow[RB], bhead[RB];
+    int64_t bb64[RB];
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
         const int b = (int)blockIdx.y * RB + q;
@@ -380,35 +382,36 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
         const int slot = a.slot_idx ? a.slot_idx[bb] : bb;  // uniform over the workgroup
         live[q] = bin && slot >= 0;                         // padded: loads from slot 0, discarded
         const int s = slot >= 0 ? slot : 0;
-        sp[q] = static_cast<TS *>(a.state) + (int64_t)s * HP * N + n0;
-        cwp[q] = CW > 0 ? static_cast<TI *>(a.conv_state) + (int64_t)s * HP * HW : nullptr;
-        brow[q] = (int64_t)bb * HP;
-        bhead[q] = (int64_t)bb * a.nheads;
+        // the slot's (head, row) rows are dense: row hp at hp * N
+        sp[q] = static_cast<TS *>(a.state) + s * a.st_ss + n0;
+        cwp[q] = CW > 0 ? static_cast<TI *>(a.conv_state) + s * a.cs_ss : nullptr;
+        bb64[q] = bb;
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
             load_vec_cached<TS, E>(sp[q] + hp[k] * N, hs[q][k]);
-        const int64_t bc = ((int64_t)bb * a.ngroups + g) * N + n0;
-        load_bc<TI, E>(static_cast<const TI *>(a.B) + bc, bv[q]);
-        load_bc<TI, E>(static_cast<const TI *>(a.C) + bc, cv[q]);
+        load_bc<TI, E>(static_cast<const TI *>(a.B) + bb * a.B_sb + g * a.B_sg + n0, bv[q]);
+        load_bc<TI, E>(static_cast<const TI *>(a.C) + bb * a.C_sb + g * a.C_sg + n0, cv[q]);
     }
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            dt_raw[q][k] = static_cast<const TI *>(a.dt)[bhead[q] + hh[k]];
+            const int64_t xo = bb64[q] * a.x_sb + hh[k] * a.x_sh + pp[k];
+            dt_raw[q][k] = static_cast<const TI *>(a.dt)[bb64[q] * a.dt_sb + hh[k]];
             // without a gate this reads x, and the value goes unused
-            z_raw[q][k] = static_cast<const TI *>(a.z ? a.z : a.x)[brow[q] + hp[k]];
+            z_raw[q][k] = a.z ? static_cast<const TI *>(a.z)[bb64[q] * a.z_sb + hh[k] * a.z_sh + pp[k]]
+                              : static_cast<const TI *>(a.x)[xo];
             if constexpr (COOP) {
                 // window sample v of the row, or x for v = 3
                 const int v = jl & 3;
-                const TI *src = v < 3 ? cwp[q] + hp[k] * HW + v : static_cast<const TI *>(a.x) + brow[q] + hp[k];
+                const TI *src = v < 3 ? cwp[q] + hp[k] * a.cs_sc + v : static_cast<const TI *>(a.x) + xo;
                 x_raw[q][k] = *src;
             } else {
-                x_raw[q][k] = static_cast<const TI *>(a.x)[brow[q] + hp[k]];
+                x_raw[q][k] = static_cast<const TI *>(a.x)[xo];
                 if constexpr (CW > 1) {
 #pragma unroll
                     for (int c = 0; c < HW; ++c)
-                        win[q][k][c] = cwp[q][hp[k] * HW + c];
+                        win[q][k][c] = cwp[q][hp[k] * a.cs_sc + c];
                 }
             }
         }
@@ -432,9 +435,9 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
                 // window's sample v: the value lane v + 1 loaded
                 const uint32_t nb = dpp_move_bits<DPP_QUAD_NEXT>(raw_bits(x_raw[q][k]));
                 if (ok && jl < 3)
-                    cwp[q][hp[k] * HW + jl] = from_bits<TI>(nb);
+                    cwp[q][hp[k] * a.cs_sc + jl] = from_bits<TI>(nb);
                 if (ok && jl == 0 && a.u_out)
-                    static_cast<TI *>(a.u_out)[brow[q] + hp[k]] = from_f32<TI>(u);
+                    static_cast<TI *>(a.u_out)[bb64[q] * a.u_sb + hh[k] * a.u_sh + pp[k]] = from_f32<TI>(u);
                 xv = u;
             } else if constexpr (CW > 0) {
                 float acc = cbias[k];
@@ -444,14 +447,14 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
                 acc = fmaf(tap[k][CW - 1], xv, acc);
                 const float u = silu_f32(acc);
                 if (ok && jl == 0) {  // the row's first lane shifts the window
-                    TI *w = cwp[q] + hp[k] * HW;
+                    TI *w = cwp[q] + hp[k] * a.cs_sc;
 #pragma unroll
                     for (int c = 0; c + 1 < CW - 1; ++c)
                         w[c] = win[q][k][c + 1];
                     if (CW > 1)
                         w[CW - 2] = x_raw[q][k];
                     if (a.u_out)
-                        static_cast<TI *>(a.u_out)[brow[q] + hp[k]] = from_f32<TI>(u);
+                        static_cast<TI *>(a.u_out)[bb64[q] * a.u_sb + hh[k] * a.u_sh + pp[k]] = from_f32<TI>(u);
                 }
                 xv = u;  // the update reads the float32 conv output
             }
@@ -483,16 +486,17 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
                     y = fmaf(Dh[k], xv, y);
                 if (a.z)
                     y *= silu_f32(to_f32(z_raw[q][k]));
-                static_cast<TI *>(a.out)[brow[q] + hp[k]] = from_f32<TI>(y);
+                static_cast<TI *>(a.out)[bb64[q] * a.o_sb + hh[k] * a.o_sh + pp[k]] = from_f32<TI>(y);
             }
         }
     }
 }
 
 // The interleaved map for a launch, if it applies: 32 bytes of state per lane
-// (two kilobyte accesses per wave), aligned 128-bit vectors, rows of
-// power-of-two size from 32 bytes to 1 KB, every wave's block inside one
-// group, and at least kIlvMinRows (request, row) pairs.  Below that the launch
+// (two kilobyte accesses per wave), aligned 128-bit vectors, dense (head,
+// row) rows within a slot, rows of power-of-two size from 32 bytes to 1 KB,
+// every wave's block inside one group, and at least kIlvMinRows (request,
+// row) pairs.  Below that the launch
 // is latency-bound and the blocked map, with half the rows per lane, was 4-5%
 // faster (Mamba-2 shapes at batch 8-16).  Returns log2(lanes per row), or -1.
 constexpr int64_t kIlvMinRows = int64_t(1) << 18;
@@ -501,7 +505,7 @@ static int ilv_lanes_log2(const SsuArgs &a)
 {
     const int rowbytes = a.dstate * StorageSize<TS>::value;
     if (!a.vec || a.states_per_lane * StorageSize<TS>::value != 32 || (rowbytes & (rowbytes - 1)) != 0 ||
-        rowbytes < 32 || rowbytes > 1024)
+        rowbytes < 32 || rowbytes > 1024 || a.st_sp != a.dstate || a.st_sh != (int64_t)a.headdim * a.dstate)
         return -1;
     int lg = 0;
     while ((16 << lg) < rowbytes)

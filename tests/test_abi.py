@@ -48,51 +48,90 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(9):
         assert lib.ssm_status_string(code)
     assert lib.ssm_status_string(99) == b"unknown status"
 
 
 FAKE = 0x10000  # aligned, never dereferenced
+F32, F16, BF16 = 0, 1, 2
+NULL, SHAPE, DTYPE, ALIGN, UNSUP, HIP, LAYOUT, OOR = 1, 2, 3, 4, 5, 6, 7, 8
+
+
+def T(ptr, dtype, shape, strides=None):
+    """An ssm_tensor: dense strides of `shape` unless given (ptr None = absent)."""
+    import state_space_model_causal_amd as ssm
+
+    if ptr is None:
+        return ssm.Tensor()
+    if strides is None:
+        strides, acc = [], 1
+        for n in reversed(shape):
+            strides.insert(0, acc)
+            acc *= n
+    st = list(strides) + [0] * (4 - len(strides))
+    t = ssm.Tensor()
+    t.data, t.dtype = ptr, dtype
+    for i in range(4):
+        t.stride[i] = st[i]
+    return t
 
 
 def conv(lib, **kw):
     a = dict(x=FAKE, w=FAKE, b=None, cs=None, idx=None, out=FAKE, batch=2, ch=8, L=16, W=4,
-             S=0, dt=1, init=0, silu=1)
+             S=0, dt=F16, wdt=F32, odt=None, init=0, silu=1, xs=None, os=None)
     a.update(kw)
-    return lib.ssm_causal_conv1d(a["x"], a["w"], a["b"], a["cs"], a["idx"], a["out"], a["batch"],
-                                 a["ch"], a["L"], a["W"], a["S"], a["dt"], a["init"], a["silu"], None)
+    sh = (a["batch"], a["ch"], a["L"])
+    return lib.ssm_causal_conv1d(
+        T(a["x"], a["dt"], sh, a["xs"]), T(a["w"], a["wdt"], (a["ch"], a["W"])),
+        T(a["b"], F32, (a["ch"],)), T(a["cs"], a["dt"], (a["S"], a["ch"], a["W"] - 1)), a["idx"],
+        T(a["out"], a["dt"] if a["odt"] is None else a["odt"], sh, a["os"]), a["batch"], a["ch"],
+        a["L"], a["W"], a["S"], a["init"], a["silu"], None)
 
 
 def scan(lib, **kw):
     a = dict(u=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, st=None,
-             idx=None, out=FAKE, batch=2, L=16, H=8, P=1, N=16, G=1, S=0, io=1, sd=0, aps=1, sp=1,
-             init=0)
+             idx=None, out=FAKE, batch=2, L=16, H=8, P=1, N=16, G=1, S=0, io=F16, sd=F32, bio=None,
+             aps=1, sp=1, init=0, Bs=None, us=None)
     a.update(kw)
-    return lib.ssm_selective_scan(a["u"], a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"],
-                                  a["z"], a["st"], a["idx"], a["out"], a["batch"], a["L"], a["H"],
-                                  a["P"], a["N"], a["G"], a["S"], a["io"], a["sd"], a["aps"],
-                                  a["sp"], a["init"], None)
+    Bt, L, H, P, N, G, io = a["batch"], a["L"], a["H"], a["P"], a["N"], a["G"], a["io"]
+    bio = io if a["bio"] is None else a["bio"]
+    return lib.ssm_selective_scan(
+        T(a["u"], io, (Bt, H * P, L), a["us"]), T(a["dt"], io, (Bt, H, L)),
+        T(a["bias"], F32, (H,)), T(a["A"], F32, (H, N) if a["aps"] else (H,)),
+        T(a["B"], bio, (Bt, G, N, L), a["Bs"]), T(a["C"], io, (Bt, G, N, L)), T(a["D"], F32, (H,)),
+        T(a["z"], io, (Bt, H * P, L)), T(a["st"], a["sd"], (a["S"], H, P, N)), a["idx"],
+        T(a["out"], io, (Bt, H * P, L)), Bt, L, H, P, N, G, a["S"], a["aps"], a["sp"], a["init"],
+        None)
+
+
+def _ssu_args(a):
+    Bt, H, P, N, G, io = a["batch"], a["H"], a["P"], a["N"], a["G"], a["io"]
+    return (T(a["st"], a["sd"], (a["S"], H, P, N), a["sts"]), a["idx"], T(a["x"], io, (Bt, H, P), a["xs"]),
+            T(a["dt"], io, (Bt, H)), T(a["bias"], F32, (H,)), T(a["A"], F32, (H, N) if a["aps"] else (H,)),
+            T(a["B"], io, (Bt, G, N)), T(a["C"], io, (Bt, G, N)), T(a["D"], F32, (H,)),
+            T(a["z"], io, (Bt, H, P)), T(a["out"], io, (Bt, H, P)), Bt, H, P, N, G, a["S"], a["aps"],
+            a["sp"])
+
+
+SSU = dict(st=FAKE, idx=None, x=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, z=None,
+           out=FAKE, batch=2, H=8, P=4, N=16, G=1, S=2, io=F16, sd=F32, aps=0, sp=1, sts=None, xs=None)
 
 
 def ssu(lib, **kw):
-    a = dict(st=FAKE, idx=None, x=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None,
-             z=None, out=FAKE, batch=2, H=8, P=4, N=16, G=1, S=2, io=1, sd=0, aps=0, sp=1)
+    a = dict(SSU)
     a.update(kw)
-    return lib.ssm_state_update(a["st"], a["idx"], a["x"], a["dt"], a["bias"], a["A"], a["B"],
-                                a["C"], a["D"], a["z"], a["out"], a["batch"], a["H"], a["P"],
-                                a["N"], a["G"], a["S"], a["io"], a["sd"], a["aps"], a["sp"], None)
-
-
-NULL, SHAPE, DTYPE, ALIGN, UNSUP = 1, 2, 3, 4, 5
+    return lib.ssm_state_update(*_ssu_args(a), None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL),
-    (dict(dt=7), DTYPE), (dict(batch=-1), SHAPE), (dict(ch=0), SHAPE), (dict(W=0), SHAPE),
+    (dict(dt=7), DTYPE), (dict(wdt=F16), DTYPE), (dict(odt=BF16), DTYPE),
+    (dict(batch=-1), SHAPE), (dict(ch=0), SHAPE), (dict(W=0), SHAPE),
     (dict(W=5), UNSUP), (dict(cs=FAKE, S=0), SHAPE), (dict(cs=FAKE, S=1, batch=2), SHAPE),
-    (dict(x=FAKE + 1), ALIGN), (dict(w=FAKE + 2, dt=1), ALIGN), (dict(idx=FAKE + 2), ALIGN),
-    (dict(batch=0), 0), (dict(L=0), 0),
+    (dict(x=FAKE + 1), ALIGN), (dict(w=FAKE + 2), ALIGN), (dict(idx=FAKE + 2), ALIGN),
+    (dict(xs=(256, 32, 2)), LAYOUT), (dict(os=(-128, 16, 1)), LAYOUT),
+    (dict(batch=0), 0), (dict(L=0), 0), (dict(batch=0, xs=(512, 32, 1)), 0),
 ])
 def test_conv_validation(lib, kw, code):
     assert conv(lib, **kw) == code
@@ -100,9 +139,11 @@ def test_conv_validation(lib, kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(u=None), NULL), (dict(A=None), NULL), (dict(B=None), NULL), (dict(out=None), NULL),
-    (dict(io=3), DTYPE), (dict(sd=-1), DTYPE), (dict(H=6, G=4), SHAPE), (dict(N=0), SHAPE),
-    (dict(N=257), UNSUP), (dict(P=0), SHAPE), (dict(st=FAKE, S=1), SHAPE),
-    (dict(u=FAKE + 1), ALIGN), (dict(st=FAKE + 2, S=4, sd=0), ALIGN), (dict(A=FAKE + 1), ALIGN),
+    (dict(io=3), DTYPE), (dict(sd=-1, st=FAKE, S=4), DTYPE), (dict(bio=BF16), DTYPE),
+    (dict(H=6, G=4), SHAPE), (dict(N=0), SHAPE), (dict(P=0), SHAPE), (dict(st=FAKE, S=1), SHAPE),
+    (dict(N=257), OOR),
+    (dict(u=FAKE + 1), ALIGN), (dict(st=FAKE + 2, S=4, sd=F32), ALIGN), (dict(A=FAKE + 1), ALIGN),
+    (dict(Bs=(256, 256, 16, 3)), LAYOUT), (dict(us=(128, -16, 1)), LAYOUT),
     (dict(batch=0), 0), (dict(L=0), 0),
 ])
 def test_scan_validation(lib, kw, code):
@@ -111,8 +152,9 @@ def test_scan_validation(lib, kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(st=None), NULL), (dict(x=None), NULL), (dict(C=None), NULL),
-    (dict(io=9), DTYPE), (dict(H=8, G=3), SHAPE), (dict(N=513), UNSUP), (dict(S=1), SHAPE),
-    (dict(S=0, idx=FAKE), SHAPE), (dict(x=FAKE + 1), ALIGN), (dict(st=FAKE + 2, sd=0), ALIGN),
+    (dict(io=9), DTYPE), (dict(H=8, G=3), SHAPE), (dict(N=513), OOR), (dict(S=1), SHAPE),
+    (dict(S=0, idx=FAKE), SHAPE), (dict(x=FAKE + 1), ALIGN), (dict(st=FAKE + 2, sd=F32), ALIGN),
+    (dict(sts=(512, 64, 16, 2)), LAYOUT), (dict(xs=(32, 4, 3)), LAYOUT),
     (dict(batch=0), 0),
 ])
 def test_ssu_validation(lib, kw, code):
@@ -129,21 +171,24 @@ def test_binding_refuses_cpu_tensors(lib):
 
 
 def dstep(lib, **kw):
-    a = dict(st=FAKE, cs=FAKE, idx=None, x=FAKE, w=FAKE, cb=None, W=4, dt=FAKE, bias=None, A=FAKE,
-             B=FAKE, C=FAKE, D=None, z=None, out=FAKE, uo=None, batch=2, H=8, P=4, N=16, G=1,
-             S=2, io=1, sd=0, aps=0, sp=1)
+    a = dict(SSU)
+    a.update(cs=FAKE, w=FAKE, cb=None, W=4, uo=None, csdt=None)
     a.update(kw)
-    return lib.ssm_decode_step(a["st"], a["cs"], a["idx"], a["x"], a["w"], a["cb"], a["W"],
-                               a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"], a["z"],
-                               a["out"], a["uo"], a["batch"], a["H"], a["P"], a["N"], a["G"],
-                               a["S"], a["io"], a["sd"], a["aps"], a["sp"], None)
+    Cn = a["H"] * a["P"]
+    args = list(_ssu_args(a))
+    st, idx, x = args[0], args[1], args[2]
+    rest = args[3:11]
+    return lib.ssm_decode_step(
+        st, T(a["cs"], a["io"] if a["csdt"] is None else a["csdt"], (a["S"], Cn, a["W"] - 1)), idx, x,
+        T(a["w"], F32, (Cn, a["W"])), T(a["cb"], F32, (Cn,)), a["W"], *rest,
+        T(a["uo"], a["io"], (a["batch"], a["H"], a["P"])), *args[11:], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(cs=None), NULL), (dict(w=None), NULL), (dict(st=None), NULL), (dict(W=3), UNSUP),
-    (dict(W=0), SHAPE), (dict(N=513), UNSUP), (dict(cs=FAKE + 1), ALIGN),
+    (dict(W=0), SHAPE), (dict(N=513), OOR), (dict(cs=FAKE + 1), ALIGN),
     (dict(uo=FAKE + 1), ALIGN), (dict(w=FAKE + 2), ALIGN), (dict(H=8, G=3), SHAPE),
-    (dict(batch=0), 0),
+    (dict(csdt=F32), DTYPE), (dict(batch=0), 0),
 ])
 def test_decode_step_validation(lib, kw, code):
     assert dstep(lib, **kw) == code
@@ -153,29 +198,33 @@ def ssu_ex(lib, cfg, **kw):
     import ctypes
     import state_space_model_causal_amd as ssm
 
-    a = dict(st=FAKE, idx=None, x=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None,
-             z=None, out=FAKE, batch=2, H=8, P=4, N=16, G=1, S=2, io=1, sd=0, aps=0, sp=1)
+    a = dict(SSU)
     a.update(kw)
     c = None if cfg is None else ctypes.byref(ssm.LaunchConfig(*cfg))
-    return lib.ssm_state_update_ex(a["st"], a["idx"], a["x"], a["dt"], a["bias"], a["A"], a["B"],
-                                   a["C"], a["D"], a["z"], a["out"], a["batch"], a["H"], a["P"],
-                                   a["N"], a["G"], a["S"], a["io"], a["sd"], a["aps"], a["sp"],
-                                   c, None)
+    return lib.ssm_state_update_ex(*_ssu_args(a), c, None)
 
 
 @pytest.mark.parametrize("cfg,kw", [
-    ((4, 256), dict(sd=1)),    # 4 states per lane only for a 4-byte cache
-    ((4, 256), dict(N=512)),   # a row of 128 lanes would not fit in a wave
-    ((32, 256), {}), ((8, 32), {}), ((16, 1024), {}), ((8, 96), {}), ((0, 0), {}),
+    ((4, 256), dict(sd=F16)),  # 4 states per lane only for a 4-byte cache
+    ((8, 32), {}), ((8, 96), {}), ((0, 0), {}), ((12, 256), {}), ((8, 320), {}),
 ])
 def test_state_update_ex_rejects_bad_geometry(lib, cfg, kw):
     assert ssu_ex(lib, cfg, **kw) == SHAPE
 
 
+@pytest.mark.parametrize("cfg,kw", [
+    ((32, 256), {}),           # more states per lane than the kernels hold in registers
+    ((16, 1024), {}),          # more lanes than the kernels' launch bound
+    ((4, 256), dict(N=512)),   # a row of 128 lanes would not fit in a wave
+])
+def test_state_update_ex_out_of_resources(lib, cfg, kw):
+    assert ssu_ex(lib, cfg, **kw) == OOR
+
+
 def test_state_update_ex_validates_like_the_plain_call(lib):
     # the override does not bypass the argument checks (none of these launch)
     assert ssu_ex(lib, (8, 256), st=None) == NULL
-    assert ssu_ex(lib, (8, 256), N=513) == UNSUP
+    assert ssu_ex(lib, (8, 256), N=513) == OOR
     assert ssu_ex(lib, (16, 64), batch=0) == 0
 
 
@@ -219,16 +268,19 @@ def test_tuned_table_entries_are_valid():
 
 def scan_ex(lib, algo, **kw):
     a = dict(u=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, st=None,
-             idx=None, out=FAKE, batch=2, L=64, H=4, P=64, N=128, G=1, S=0, io=2, sd=0, aps=0,
+             idx=None, out=FAKE, batch=2, L=64, H=4, P=64, N=128, G=1, S=0, io=BF16, sd=F32, aps=0,
              sp=1, init=0)
     a.update(kw)
-    return lib.ssm_selective_scan_ex(a["u"], a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"],
-                                     a["z"], a["st"], a["idx"], a["out"], a["batch"], a["L"],
-                                     a["H"], a["P"], a["N"], a["G"], a["S"], a["io"], a["sd"],
-                                     a["aps"], a["sp"], a["init"], algo, None)
+    Bt, L, H, P, N, G, io = a["batch"], a["L"], a["H"], a["P"], a["N"], a["G"], a["io"]
+    return lib.ssm_selective_scan_ex(
+        T(a["u"], io, (Bt, H * P, L)), T(a["dt"], io, (Bt, H, L)), T(a["bias"], F32, (H,)),
+        T(a["A"], F32, (H, N) if a["aps"] else (H,)), T(a["B"], io, (Bt, G, N, L)),
+        T(a["C"], io, (Bt, G, N, L)), T(a["D"], F32, (H,)), T(a["z"], io, (Bt, H * P, L)),
+        T(a["st"], a["sd"], (a["S"], H, P, N)), a["idx"], T(a["out"], io, (Bt, H * P, L)), Bt, L,
+        H, P, N, G, a["S"], a["aps"], a["sp"], a["init"], algo, None)
 
 
-@pytest.mark.parametrize("kw", [dict(aps=1, N=16), dict(io=1), dict(io=0), dict(N=96),
+@pytest.mark.parametrize("kw", [dict(aps=1, N=16), dict(io=F16), dict(io=F32), dict(N=96),
                                 dict(P=32), dict(L=60), dict(u=FAKE + 2)])
 def test_scan_chunked_refuses_unsupported_shapes(lib, kw):
     # the chunked form is asked for explicitly where it does not apply: the
@@ -239,3 +291,63 @@ def test_scan_chunked_refuses_unsupported_shapes(lib, kw):
 def test_scan_ex_rejects_unknown_algorithm(lib):
     assert scan_ex(lib, 7) == SHAPE
     assert scan_ex(lib, 2, batch=0) == 0
+
+
+def layer_desc(**kw):
+    import state_space_model_causal_amd as ssm
+
+    a = dict(d_model=64, d_inner=128, d_state=16, dt_rank=8, conv_width=4, norm_eps=1e-5,
+             norm_weight=FAKE, in_proj=FAKE, conv_weight=FAKE, conv_bias=None, x_proj=FAKE,
+             dt_proj=FAKE, dt_bias=None, A=FAKE, D=None, out_proj=FAKE)
+    a.update(kw)
+    return ssm.Mamba1Layer(*[a[f] for f, _ in ssm.Mamba1Layer._fields_])
+
+
+def layer(lib, desc=None, **kw):
+    import ctypes
+
+    a = dict(hidden=FAKE, cs=FAKE, st=FAKE, idx=None, batch=4, S=8, io=F16, sd=F32, hs=None,
+             sts=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    desc = desc or layer_desc()
+    return lib.ssm_mamba1_decode_layer(
+        ctypes.byref(desc), T(a["hidden"], a["io"], (a["batch"], desc.d_model), a["hs"]),
+        T(a["cs"], a["io"], (a["S"], desc.d_inner, desc.conv_width - 1)),
+        T(a["st"], a["sd"], (a["S"], desc.d_inner, 1, desc.d_state), a["sts"]), a["idx"],
+        a["batch"], a["S"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(st=FAKE + 2), ALIGN),               # misaligned f32 state: the last step's check
+    (dict(S=2), SHAPE),                       # implicit slots need nslots >= batch
+    (dict(sts=(2048, 16, 16, 2)), LAYOUT),    # state with a non-unit inner stride
+    (dict(sd=9), DTYPE), (dict(io=F32), UNSUP), (dict(hs=(64, 2)), LAYOUT),
+    (dict(ws=FAKE + 16), ALIGN), (dict(wsb=64), SHAPE),
+])
+def test_layer_checks_every_step_before_launching(lib, kw, code):
+    # Every step's arguments are checked before the first launch: with fake
+    # pointers and no GPU, any launch would come back as SSM_ERR_HIP (or
+    # fault), so the validation code itself shows that nothing ran and the
+    # conv cache (shifted by step 3) is untouched.
+    assert layer(lib, **kw) == code
+
+
+def test_layer_batch_zero_is_a_noop(lib):
+    assert layer(lib, batch=0) == 0
+
+
+def test_linear_and_rmsnorm_validation(lib):
+    f = lambda x=FAKE, w=FAKE, o=FAKE, M=4, N=16, K=32, xs=None, dt=F16: lib.ssm_linear(
+        T(x, dt, (M, K), xs), T(w, dt, (N, K)), T(None, dt, (M, N)), T(o, dt, (M, N)), M, N, K,
+        None, 0, None)
+    assert f(x=None) == NULL
+    assert f(dt=F32) == UNSUP
+    assert f(K=12) == SHAPE
+    assert f(xs=(36, 1)) == ALIGN      # rows of 72 bytes are not 16-byte multiples
+    assert f(xs=(64, 2)) == LAYOUT
+    assert f(M=0) == 0
+    g = lambda x=FAKE, o=FAKE, M=4, D=64, os=None: lib.ssm_rmsnorm(
+        T(x, F16, (M, D)), T(FAKE, F32, (D,)), T(o, F16, (M, D), os), M, D, 1e-5, None)
+    assert g(o=None) == NULL
+    assert g(os=(64, 3)) == LAYOUT
+    assert g(M=0) == 0
