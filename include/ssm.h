@@ -394,6 +394,31 @@ int ssm_mamba1_decode_layer(const ssm_mamba1_layer *layer, ssm_tensor hidden,
                             const int32_t *slot_idx, int batch, int nslots, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/*
+ * ssm_mamba1_decode_layer_noalloc -- ssm_mamba1_decode_layer for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same layer, the same kernels
+ * and the same results, with the workspace taken from a device array inside
+ * the library instead of a caller buffer.  The array is
+ * SSM_LAYER_SCRATCH_BYTES (64 MiB) per GPU, held from the first call on that
+ * GPU until the process ends; a layer and batch whose workspace
+ * (ssm_mamba1_decode_layer_workspace) exceeds it return
+ * SSM_ERR_OUT_OF_RESOURCES before anything is enqueued (the Mamba-2.8B layer
+ * fits for up to 687 requests).  Nothing is allocated, by this call or by
+ * the library: the first call on a GPU looks up that GPU's copy of the array
+ * (an SSM_ERR_HIP if the runtime cannot), later calls reuse it.  Every byte a
+ * call reads from the array was written earlier in the same call, so nothing
+ * needs clearing between calls; but all calls on one GPU share the one array,
+ * so calls that may overlap on a GPU (on different streams, or from several
+ * threads) race and must be serialised by the caller.  Other arguments and
+ * errors as in ssm_mamba1_decode_layer.
+ */
+#define SSM_LAYER_SCRATCH_BYTES (64 << 20)
+int ssm_mamba1_decode_layer_noalloc(const ssm_mamba1_layer *layer, ssm_tensor hidden,
+                                    ssm_tensor conv_state, ssm_tensor ssm_state,
+                                    const int32_t *slot_idx, int batch, int nslots,
+                                    void *stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *ssm_status_string(int status);
 

@@ -40,7 +40,8 @@ EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_selective_scan_ex", 
             "ssm_state_update_ex", "ssm_state_update_config",
             "ssm_decode_step", "ssm_causal_conv1d_varlen", "ssm_selective_scan_varlen",
             "ssm_linear", "ssm_linear_workspace", "ssm_rmsnorm", "ssm_mamba1_decode_layer",
-            "ssm_mamba1_decode_layer_workspace", "ssm_status_string", "ssm_abi_version")
+            "ssm_mamba1_decode_layer_workspace", "ssm_mamba1_decode_layer_noalloc",
+            "ssm_status_string", "ssm_abi_version")
 
 
 class Tensor(ctypes.Structure):
@@ -125,6 +126,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_mamba1_decode_layer_workspace.restype = Z
     lib.ssm_mamba1_decode_layer.argtypes = [P, T, T, T, P, I, I, P, Z, P]
     lib.ssm_mamba1_decode_layer.restype = I
+    lib.ssm_mamba1_decode_layer_noalloc.argtypes = [P, T, T, T, P, I, I, P]
+    lib.ssm_mamba1_decode_layer_noalloc.restype = I
     lib.ssm_status_string.argtypes = [I]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -408,7 +411,19 @@ def mamba1_decode_layer(layer, hidden, conv_state, ssm_state, slot_idx=None, wor
     return hidden
 
 
-__all__ = ["Tensor", "linear", "rmsnorm", "mamba1_layer", "mamba1_decode_layer", "Mamba1Layer",
+def mamba1_decode_layer_noalloc(layer, hidden, conv_state, ssm_state, slot_idx=None, stream=None):
+    """ssm_mamba1_decode_layer_noalloc: the decode layer with its workspace in
+    the library's per-GPU device array (no allocation by caller or library);
+    hidden [batch, d_model] updated in place."""
+    st = load_library().ssm_mamba1_decode_layer_noalloc(
+        ctypes.byref(layer), _tensor(hidden, "hidden"), _tensor(conv_state, "conv_state"),
+        _tensor(ssm_state, "ssm_state"), _ptr(slot_idx, "slot_idx", torch.int32), hidden.shape[0],
+        conv_state.shape[0], _stream(stream))
+    _check("ssm_mamba1_decode_layer_noalloc", st)
+    return hidden
+
+
+__all__ = ["Tensor", "linear", "mamba1_decode_layer_noalloc", "rmsnorm", "mamba1_layer", "mamba1_decode_layer", "Mamba1Layer",
            "causal_conv1d", "selective_scan", "state_update", "state_update_config",
            "LaunchConfig", "decode_step", "SCAN_AUTO", "SCAN_RECURRENT", "SCAN_CHUNKED",
            "causal_conv1d_varlen", "selective_scan_varlen", "load_library",

@@ -7,6 +7,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
+// Device memory of ssm_mamba1_decode_layer_noalloc: its workspace (the
+// layer's intermediates and split-K partial sums) lives here instead of in a
+// caller buffer.  Each GPU the library runs on holds its own copy, from the
+// first call on that GPU until the process ends.  Host code never uses this
+// name as an address: it looks up the device's copy with
+// hipGetSymbolAddress and keeps that pointer per device.
+static __device__ __align__(256) unsigned char scratch[SSM_LAYER_SCRATCH_BYTES];
+
 namespace {
 
 bool mfma_dtype(int d) { return d == SSM_F16 || d == SSM_BF16; }
@@ -316,6 +326,51 @@ int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, ssm_tensor hidden, ssm_te
     g.ld_residual = (int)hidden.stride[0];
     g.row_slot = slot_idx;
     return run_linear(g, M, Dm, Di, part, s);
+}
+
+namespace {
+
+// The scratch array's address on each device, looked up once per device.
+constexpr int kMaxDevices = 64;
+void *g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int scratch_of_current_device(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return SSM_ERR_HIP;
+    if (dev >= kMaxDevices)
+        return SSM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return SSM_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return SSM_OK;
+}
+
+} // namespace
+
+int ssm_mamba1_decode_layer_noalloc(const ssm_mamba1_layer *L, ssm_tensor hidden, ssm_tensor conv_state,
+                                    ssm_tensor ssm_state, const int32_t *slot_idx, int batch, int nslots,
+                                    void *stream)
+{
+    int st = check_layer(L, batch);
+    if (st != SSM_OK)
+        return st;
+    if (batch == 0)  // validated like the plain call, then a no-op
+        return ssm_mamba1_decode_layer(L, hidden, conv_state, ssm_state, slot_idx, 0, nslots, nullptr, 0, stream);
+    if (layer_ws(L, batch).total > (size_t)SSM_LAYER_SCRATCH_BYTES)
+        return SSM_ERR_OUT_OF_RESOURCES;
+    void *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != SSM_OK)
+        return st;
+    return ssm_mamba1_decode_layer(L, hidden, conv_state, ssm_state, slot_idx, batch, nslots, ws,
+                                   (size_t)SSM_LAYER_SCRATCH_BYTES, stream);
 }
 
 } // extern "C"

@@ -351,3 +351,19 @@ def test_linear_and_rmsnorm_validation(lib):
     assert g(o=None) == NULL
     assert g(os=(64, 3)) == LAYOUT
     assert g(M=0) == 0
+
+
+def test_noalloc_layer_scratch_limit(lib):
+    # the documented limit: the Mamba-2.8B layer's workspace fits the 64 MiB
+    # array up to 687 requests; beyond, the call is refused before any HIP call
+    import ctypes
+
+    desc = layer_desc(d_model=2560, d_inner=5120, d_state=16, dt_rank=160)
+    ws = lambda b: lib.ssm_mamba1_decode_layer_workspace(ctypes.byref(desc), b)
+    assert max(ws(b) for b in range(1, 688)) <= 64 << 20 < ws(688)
+    assert lib.ssm_mamba1_decode_layer_noalloc(
+        ctypes.byref(desc), T(FAKE, F16, (688, 2560)), T(FAKE, F16, (700, 5120, 3)),
+        T(FAKE, F32, (700, 5120, 1, 16)), None, 688, 700, None) == OOR
+    assert lib.ssm_mamba1_decode_layer_noalloc(
+        ctypes.byref(desc), T(FAKE, F16, (4, 2560)), T(FAKE, F16, (8, 5120, 3)),
+        T(FAKE, F32, (8, 5120, 1, 16)), None, 0, 8, None) == 0
