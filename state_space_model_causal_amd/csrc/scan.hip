@@ -263,6 +263,9 @@ void scan_kernel(ScanArgs a)
 
     for (int t0 = 0; t0 < hi; t0 += T) {
         const int tl = t0 + r * K;
+        // a tile whose every step lies in the sequence needs no masking
+        // (uniform over the workgroup; most tiles of a dense batch)
+        const bool full = lo == 0 && t0 + T <= hi;
         float dl[K], du[K], y[K];
         RawSteps<TI, K> rz;  // the gate's loads are issued with the others
         {
@@ -280,18 +283,27 @@ void scan_kernel(ScanArgs a)
                 load_steps<TI, VEC, K>(urow, tl, lo, hi, uu);
                 load_steps<TI, VEC, K>(dtrow, tl, lo, hi, dd);
             }
+            auto steps = [&](auto all_in) {
 #pragma unroll
-            for (int i = 0; i < K; ++i) {
-                const float v = dd[i] + bias_h;
-                const float spv = softplus_f32(v);
-                const bool in = tl + i >= lo && tl + i < hi;
-                // identity step outside the sequence (decay 1, input 0)
-                const float d = in ? (a.dt_softplus ? spv : v) : 0.0f;
-                const float uv = in ? uu[i] : 0.0f;
-                dl[i] = d;
-                du[i] = d * uv;
-                y[i] = D_h * uv;
-            }
+                for (int i = 0; i < K; ++i) {
+                    const float v = dd[i] + bias_h;
+                    const float spv = softplus_f32(v);
+                    float d = a.dt_softplus ? spv : v, uv = uu[i];
+                    if constexpr (!decltype(all_in)::value) {
+                        // identity step outside the sequence (decay 1, input 0)
+                        const bool in = tl + i >= lo && tl + i < hi;
+                        d = in ? d : 0.0f;
+                        uv = in ? uv : 0.0f;
+                    }
+                    dl[i] = d;
+                    du[i] = d * uv;
+                    y[i] = D_h * uv;
+                }
+            };
+            if (full)
+                steps(std::true_type{});
+            else
+                steps(std::false_type{});
         }
         float sdl = 0.0f;
 #pragma unroll
@@ -317,20 +329,26 @@ void scan_kernel(ScanArgs a)
 
         for (int n0 = 0; n0 < N; n0 += NC) {
             __syncthreads();  // previous chunk's readers are done with the LDS tiles
+            const bool bc_full = full && n0 + NC <= N;  // no state or step out of range
             for (int m = tid; m < NC * T / E; m += 256) {
                 const int nl = m / (T / E), tc = (m % (T / E)) * E;
                 const int n = n0 + nl, t = t0 + tc;
                 float vb[E], vc[E];
                 if constexpr (VEC) {
-                    // clamped address, unconditional load, then select
-                    const bool ok = n < N && t < hi;
-                    load_vec_cached<TI, E>(Bg + (ok ? n * a.B_sn + t : 0), vb);
-                    load_vec_cached<TI, E>(Cg + (ok ? n * a.C_sn + t : 0), vc);
+                    if (bc_full) {
+                        load_vec_cached<TI, E>(Bg + n * a.B_sn + t, vb);
+                        load_vec_cached<TI, E>(Cg + n * a.C_sn + t, vc);
+                    } else {
+                        // clamped address, unconditional load, then select
+                        const bool ok = n < N && t < hi;
+                        load_vec_cached<TI, E>(Bg + (ok ? n * a.B_sn + t : 0), vb);
+                        load_vec_cached<TI, E>(Cg + (ok ? n * a.C_sn + t : 0), vc);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const bool in = ok && t + e >= lo && t + e < hi;
-                        vb[e] = in ? vb[e] : 0.0f;
-                        vc[e] = in ? vc[e] : 0.0f;
+                        for (int e = 0; e < E; ++e) {
+                            const bool in = ok && t + e >= lo && t + e < hi;
+                            vb[e] = in ? vb[e] : 0.0f;
+                            vc[e] = in ? vc[e] : 0.0f;
+                        }
                     }
                 } else {
 #pragma unroll

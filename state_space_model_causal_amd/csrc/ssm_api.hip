@@ -555,6 +555,11 @@ int prepare_ssu(SsuArgs &a, const ssm_tensor &state, const int32_t *slot_idx, co
             rows16(A, a_per_state ? 2 : 1, a_per_state ? as2 : as1);
     a.requests_per_lane = rb;
     a.conv_width = 0;
+    // a request's x / z / out rows are addressed with 32-bit offsets
+    const int64_t hmax = (int64_t)nheads - 1;
+    if (hmax * a.x_sh + headdim > INT32_MAX || hmax * a.z_sh + headdim > INT32_MAX ||
+        hmax * a.o_sh + headdim > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
     return SSM_OK;
 }
 
@@ -585,6 +590,8 @@ int prepare_decode_conv(SsuArgs &a, const ssm_tensor &conv_state, const ssm_tens
     a.u_sb = st(u_out, 0);
     a.u_sh = st(u_out, 1);
     a.conv_width = conv_width;
+    if ((int64_t)(a.nheads - 1) * a.u_sh + a.headdim > INT32_MAX)
+        return SSM_ERR_UNSUPPORTED;
     return SSM_OK;
 }
 

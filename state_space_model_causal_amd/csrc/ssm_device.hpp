@@ -173,13 +173,13 @@ __device__ __forceinline__ float log1p_unit(float e)
     return fmaf(log2_hw(w), kLn2, c);
 }
 
-// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^{-|v|}); for v > 20 the
-// second term is below 2.1e-9 and v alone is returned.  Branch-free.
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^{-|v|}).  Branch-free
+// and without a cutoff: for v > 16.7 the second term is below half an ulp of
+// v, so the sum rounds to v by itself; v = +inf gives inf, v = -inf gives 0.
 __device__ __forceinline__ float softplus_f32(float v)
 {
     const float e = exp2_hw(-fabsf(v) * kLog2e);
-    const float r = fmaxf(v, 0.0f) + log1p_unit(e);
-    return v > 20.0f ? v : r;
+    return fmaxf(v, 0.0f) + log1p_unit(e);
 }
 
 // SiLU(v) = v / (1 + e^{-v}).

@@ -374,6 +374,9 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
     TS *sp[RB];
     TI *cwp[RB];
     int64_t bb64[RB];
+    // the row's element offset within a request's x / z / out / u_out rows
+    // (32-bit: the host checks that a request's rows fit), formed where used
+    auto rowoff = [&](int k, int64_t sh) { return hh[k] * (int)sh + pp[k]; };
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
         const int b = (int)blockIdx.y * RB + q;
@@ -396,18 +399,17 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
     for (int q = 0; q < RB; ++q) {
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const int64_t xo = bb64[q] * a.x_sb + hh[k] * a.x_sh + pp[k];
-            dt_raw[q][k] = static_cast<const TI *>(a.dt)[bb64[q] * a.dt_sb + hh[k]];
+            const TI *xq = static_cast<const TI *>(a.x) + bb64[q] * a.x_sb;  // uniform
+            dt_raw[q][k] = (static_cast<const TI *>(a.dt) + bb64[q] * a.dt_sb)[hh[k]];
             // without a gate this reads x, and the value goes unused
-            z_raw[q][k] = a.z ? static_cast<const TI *>(a.z)[bb64[q] * a.z_sb + hh[k] * a.z_sh + pp[k]]
-                              : static_cast<const TI *>(a.x)[xo];
+            z_raw[q][k] = a.z ? (static_cast<const TI *>(a.z) + bb64[q] * a.z_sb)[rowoff(k, a.z_sh)] : xq[rowoff(k, a.x_sh)];
             if constexpr (COOP) {
                 // window sample v of the row, or x for v = 3
                 const int v = jl & 3;
-                const TI *src = v < 3 ? cwp[q] + hp[k] * a.cs_sc + v : static_cast<const TI *>(a.x) + xo;
+                const TI *src = v < 3 ? cwp[q] + hp[k] * a.cs_sc + v : xq + rowoff(k, a.x_sh);
                 x_raw[q][k] = *src;
             } else {
-                x_raw[q][k] = static_cast<const TI *>(a.x)[xo];
+                x_raw[q][k] = xq[rowoff(k, a.x_sh)];
                 if constexpr (CW > 1) {
 #pragma unroll
                     for (int c = 0; c < HW; ++c)
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
                 if (ok && jl < 3)
                     cwp[q][hp[k] * a.cs_sc + jl] = from_bits<TI>(nb);
                 if (ok && jl == 0 && a.u_out)
-                    static_cast<TI *>(a.u_out)[bb64[q] * a.u_sb + hh[k] * a.u_sh + pp[k]] = from_f32<TI>(u);
+                    (static_cast<TI *>(a.u_out) + bb64[q] * a.u_sb)[rowoff(k, a.u_sh)] = from_f32<TI>(u);
                 xv = u;
             } else if constexpr (CW > 0) {
                 float acc = cbias[k];
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
                     if (CW > 1)
                         w[CW - 2] = x_raw[q][k];
                     if (a.u_out)
-                        static_cast<TI *>(a.u_out)[bb64[q] * a.u_sb + hh[k] * a.u_sh + pp[k]] = from_f32<TI>(u);
+                        (static_cast<TI *>(a.u_out) + bb64[q] * a.u_sb)[rowoff(k, a.u_sh)] = from_f32<TI>(u);
                 }
                 xv = u;  // the update reads the float32 conv output
             }
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
                     y = fmaf(Dh[k], xv, y);
                 if (a.z)
                     y *= silu_f32(to_f32(z_raw[q][k]));
-                static_cast<TI *>(a.out)[bb64[q] * a.o_sb + hh[k] * a.o_sh + pp[k]] = from_f32<TI>(y);
+                (static_cast<TI *>(a.out) + bb64[q] * a.o_sb)[rowoff(k, a.o_sh)] = from_f32<TI>(y);
             }
         }
     }
