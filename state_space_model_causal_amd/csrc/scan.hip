@@ -265,7 +265,7 @@ void scan_kernel(ScanArgs a)
         const int tl = t0 + r * K;
         // a tile whose every step lies in the sequence needs no masking
         // (uniform over the workgroup; most tiles of a dense batch)
-        const bool full = lo == 0 && t0 + T <= hi;
+        const bool full = t0 >= lo && t0 + T <= hi;
         float dl[K], du[K], y[K];
         RawSteps<TI, K> rz;  // the gate's loads are issued with the others
         {

@@ -15,6 +15,9 @@ from __future__ import annotations
 import numpy as np
 
 RTOL = {"f32": 1e-5, "f16": 3e-3, "bf16": 3e-3}
+# every check's statistics, in order (written out at the end of a test session
+# when SSM_PARITY_STATS names a file; see tests/conftest.py)
+RECORD = []
 _MANT_EMIN = {"f32": (23, -126), "f16": (10, -14), "bf16": (7, -126)}
 
 
@@ -55,6 +58,7 @@ def check(got, want, scale, rtol: float, dtype: str, what: str) -> dict:
         "max_rel": float(np.max(err[big] / np.abs(o[big]))) if big.any() else 0.0,
         "normwise": float(np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-300)) if o.size else 0.0,
     }
+    RECORD.append({"what": what, "dtype": dtype, "rtol": rtol, **stats})
     if not ok.all():
         bad = np.argwhere(~ok)
         lines = []

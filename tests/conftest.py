@@ -17,3 +17,18 @@ def oracle():
     import oracle as _oracle
     _oracle.build(force=False)
     return _oracle
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # the parity statistics of every element-wise check (max error over the
+    # tolerance, max relative error, normwise error), for the record
+    path = os.environ.get("SSM_PARITY_STATS")
+    if not path:
+        return
+    from tests._parity import RECORD
+
+    if RECORD:
+        import json
+
+        with open(path, "w") as f:
+            json.dump(RECORD, f, indent=0)

@@ -140,3 +140,35 @@ def test_decode_layer_parity(dev, ssm, oracle, label, kw, pad):
     d_inner = wf["in_proj"].shape[0] // 2
     check(gcs[:, :, -1], stages["x"][live], xs[live][:, :d_inner], 3e-3, kw["io"],
           f"layer {label} conv window")
+
+
+def test_decode_layer_batch245_sampled_rows(dev, ssm, oracle):
+    """The layer at the size the benchmark runs (Mamba-2.8B dimensions, 245
+    requests from a 512-slot cache, f16 I/O, f32 state), every fifth request
+    padded.  The requests are independent, so the oracle runs only a sample
+    of them (with their slots) and each sampled row is compared in full."""
+    from oracle import layer
+
+    t = W.mamba1_layer(seed=13, device=dev, batch=245, nslots=512, io="f16", state="f32")
+    idx = t["slot_idx"].clone()
+    idx[::5] = -1
+    h0, cs0, ss0 = t["hidden"].clone(), t["conv_state"].clone(), t["ssm_state"].clone()
+    desc = ssm.mamba1_layer(t["w"], eps=1e-5)
+    ssm.mamba1_decode_layer(desc, t["hidden"], t["conv_state"], t["ssm_state"], slot_idx=idx)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    rows = np.array([0, 1, 2, 77, 128, 200, 243, 244])  # 0 and 200 are padded
+    wf = {k: f(v) for k, v in t["w"].items()}
+    o, s, cs, ss, sss = layer.mamba1_decode_layer(wf, f(h0)[rows], f(cs0), f(ss0), idx_np[rows],
+                                                  eps=1e-5, round_kind=oracle.F16)
+    check(f(t["hidden"])[rows], o, s, 3e-3, "f16", "layer b245 hidden (sampled rows)")
+    named = idx_np[rows][idx_np[rows] >= 0]
+    check(f(t["ssm_state"])[named], ss[named], sss[named], 3e-3, "f32", "layer b245 state (sampled slots)")
+    np.testing.assert_array_equal(f(t["conv_state"])[named][:, :, :-1], f(cs0)[named][:, :, 1:])
+    # padded requests: hidden rows untouched
+    pad = np.nonzero(idx_np < 0)[0]
+    np.testing.assert_array_equal(f(t["hidden"])[pad], f(h0)[pad])
+    # slots no request names: untouched
+    others = np.setdiff1d(np.arange(512), idx_np[idx_np >= 0])
+    np.testing.assert_array_equal(f(t["ssm_state"])[others], f(ss0)[others])
+    np.testing.assert_array_equal(f(t["conv_state"])[others], f(cs0)[others])
