@@ -105,10 +105,11 @@ struct ChunkLoads {
     bf16 dt;             // dt of step t0 + lane, as stored (wave 0 widens it when staging)
 };
 
+// The B (or C) part of a chunk's loads: unit u of the chunk is a pair of
+// states and 8 steps.
 template <int N>
-__device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, const bf16 *Bg, const bf16 *Cg,
-                                           int64_t bsn, int64_t csn, const bf16 *urow, const bf16 *zrow,
-                                           const bf16 *dtrow, int tid, int w, int l, int lq, int nh)
+__device__ __forceinline__ void load_pairs(u32x4 (&v0)[ChunkLoads<N>::UNITS], u32x4 (&v1)[ChunkLoads<N>::UNITS],
+                                           int t0, int L, const bf16 *G, int64_t sn, int tid)
 {
 #pragma unroll
     for (int k = 0; k < ChunkLoads<N>::UNITS; ++k) {
@@ -116,11 +117,16 @@ __device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, cons
         const int n = 2 * (u >> 3), tv = u & 7;
         const int t = t0 + 8 * tv;
         const int tc = t < L ? t : 0;  // clamped; zeroed when staged
-        c.b0[k] = *reinterpret_cast<const u32x4 *>(Bg + n * bsn + tc);
-        c.b1[k] = *reinterpret_cast<const u32x4 *>(Bg + (n + 1) * bsn + tc);
-        c.c0[k] = *reinterpret_cast<const u32x4 *>(Cg + n * csn + tc);
-        c.c1[k] = *reinterpret_cast<const u32x4 *>(Cg + (n + 1) * csn + tc);
+        v0[k] = *reinterpret_cast<const u32x4 *>(G + n * sn + tc);
+        v1[k] = *reinterpret_cast<const u32x4 *>(G + (n + 1) * sn + tc);
     }
+}
+
+// The rest of a chunk's loads: u, z and dt.
+template <int N>
+__device__ __forceinline__ void load_rows(ChunkLoads<N> &c, int t0, int L, const bf16 *urow, const bf16 *zrow,
+                                          const bf16 *dtrow, int l, int lq, int nh)
+{
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const int t = t0 + 32 * kk + 8 * lq;
@@ -143,6 +149,16 @@ __device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, cons
         const int t = t0 + l;
         c.dt = dtrow[t < L ? t : t0];
     }
+}
+
+template <int N>
+__device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, const bf16 *Bg, const bf16 *Cg,
+                                           int64_t bsn, int64_t csn, const bf16 *urow, const bf16 *zrow,
+                                           const bf16 *dtrow, int tid, int l, int lq, int nh)
+{
+    load_pairs<N>(c.b0, c.b1, t0, L, Bg, bsn, tid);
+    load_pairs<N>(c.c0, c.c1, t0, L, Cg, csn, tid);
+    load_rows<N>(c, t0, L, urow, zrow, dtrow, l, lq, nh);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     }
 
     ChunkLoads<N> cur;
-    load_chunk<N>(cur, 0, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, w, l, lq, nh);
+    load_chunk<N>(cur, 0, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, l, lq, nh);
 
     for (int t0 = 0; t0 < L; t0 += SQ) {
         // ---- stage the chunk (its loads were issued one chunk earlier)
@@ -254,9 +270,12 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         const uint2 xo[2] = {cur.xo[0], cur.xo[1]}, zo[2] = {cur.zo[0], cur.zo[1]};
         __syncthreads();
 
-        // ---- the next chunk's loads, in flight during this chunk's work
-        if (t0 + SQ < L)
-            load_chunk<N>(cur, t0 + SQ, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, w, l, lq, nh);
+        // ---- the next chunk's loads, in flight during this chunk's work;
+        // issued in three parts between the phases below, so that no wave
+        // stalls on a full load queue for the whole chunk's worth at once
+        const bool more = t0 + SQ < L;
+        if (more)
+            load_pairs<N>(cur.c0, cur.c1, t0 + SQ, L, Cg, a.C_sn, tid);
 
         // ---- carried state over this wave's half of the states:
         // yc[st] = sum_{n in half} C_s[n] H[p][n]; the state as MFMA operands
@@ -294,6 +313,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             *reinterpret_cast<f32x4_t *>(&s_x[partner][0][l][0]) = nh ? yc[0] : yc[2];
             *reinterpret_cast<f32x4_t *>(&s_x[partner][1][l][0]) = nh ? yc[1] : yc[3];
         }
+
+        if (more)
+            load_pairs<N>(cur.b0, cur.b1, t0 + SQ, L, Bg, a.B_sn, tid);
 
         // ---- masked decay matrix M[s][r] = (C_s.B_r) exp(L_s - L_r) delta_r
         // for r <= s: rows s in [16 pw, 16 pw + 16), r tiles 2 nh, 2 nh + 1
@@ -333,6 +355,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 *reinterpret_cast<bf16x4_t *>(&s_ml[s * LDQ + r0]) = ml;
             }
         }
+
+        if (more)
+            load_rows<N>(cur, t0 + SQ, L, urow, zrow, dtrow, l, lq, nh);
 
         // ---- state update of this wave's half: H <- exp(L_last) H +
         // sum_r B_r (w_r X_r)^T, w_r = exp(L_last - L_r) delta_r on this
