@@ -181,7 +181,10 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     __shared__ __align__(16) __bf16 s_mh[SQ * LDQ];  // masked decay matrix M[s][r], high part
     __shared__ __align__(16) __bf16 s_ml[SQ * LDQ];  // and remainder
     __shared__ __align__(16) float s_x[SNW][2][64][4];  // C.H halves for the partner wave
-    __shared__ float s_d[SQ], s_L[SQ], s_eL[SQ], s_w[SQ], s_etot[1];
+    // e^{L} is read after the second barrier, by the outputs; it is kept per
+    // chunk parity so that the next chunk's staging (which no barrier
+    // separates from this chunk's outputs) does not overwrite it
+    __shared__ float s_d[SQ], s_L[SQ], s_eL[2][SQ], s_w[SQ], s_etot[1];
 
     const int L = a.seqlen, P = a.headdim, H = a.nheads;
     const int npb = P / SPB;
@@ -224,26 +227,34 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         hacc[q] = v;
     }
 
+    // the two upper tiles of M that the outputs read, (0, 1) and (2, 3), stay
+    // zero; every other tile they read is computed in each chunk
+    {
+        const int tile = tid >> 8, e = tid & 255;
+        const int s = 32 * tile + (e >> 4), r = 32 * tile + 16 + (e & 15);
+        s_mh[s * LDQ + r] = (__bf16)0.0f;
+        s_ml[s * LDQ + r] = (__bf16)0.0f;
+    }
+
     ChunkLoads<N> cur;
     load_chunk<N>(cur, 0, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, l, lq, nh);
 
     for (int t0 = 0; t0 < L; t0 += SQ) {
-        // ---- stage the chunk (its loads were issued one chunk earlier)
+        const int par = (t0 / SQ) & 1;
+        // ---- stage the chunk (its loads were issued one chunk earlier).
+        // The previous chunk's readers of the staged B, C, delta, L and w
+        // all sit before its second barrier, so no barrier is needed here.
         if (w == 0) {
             const bool ok = t0 + l < L;
             const float v = to_f32(cur.dt) + bias;
             const float sp = softplus_f32(v);
             const float d = ok ? (a.dt_softplus ? sp : v) : 0.0f;  // identity step past the end
-            float cum = d * A2;  // log2 of this step's decay, summed over the chunk
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float up = __shfl_up(cum, o, 64);
-                cum += (l >= o) ? up : 0.0f;
-            }
-            const float tot = __shfl(cum, 63, 64);
+            // log2 of the decay over the chunk's steps up to this one
+            const float cum = wave_prefix_sum(d * A2);
+            const float tot = lane_value(cum, 63);
             s_d[l] = d;
             s_L[l] = cum;
-            s_eL[l] = exp2_hw(cum);
+            s_eL[par][l] = exp2_hw(cum);
             s_w[l] = exp2_hw(tot - cum) * d;
             if (l == 0)
                 s_etot[0] = exp2_hw(tot);
@@ -318,41 +329,42 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             load_pairs<N>(cur.b0, cur.b1, t0 + SQ, L, Bg, a.B_sn, tid);
 
         // ---- masked decay matrix M[s][r] = (C_s.B_r) exp(L_s - L_r) delta_r
-        // for r <= s: rows s in [16 pw, 16 pw + 16), r tiles 2 nh, 2 nh + 1
+        // for r <= s, over its 10 lower-triangle 16 x 16 tiles (st, rt).  The
+        // tiles are dealt so that waves w and w + 4 (which share a SIMD) hold
+        // at most 3 between them: one byte per (wave, tile), st in the high
+        // nibble and rt in the low one, 0xff for none
         {
-            const int s = 16 * pw + l16;
-            const float Ls = s_L[s];
+            const uint64_t deal = w < 4 ? 0xff22ff2011103300ull : 0xff32ff21ff31ff30ull;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int rt = 2 * nh + i;
-                float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (rt <= pw) {
+                const int code = (int)((deal >> (8 * (2 * pw + i))) & 0xffu);
+                if (code != 0xff) {
+                    const int st = code >> 4, rt = code & 15;
+                    const int s = 16 * st + l16;
                     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int kk = 0; kk < N / 32; ++kk) {
                         const int nb = 32 * kk + 8 * lq;
                         const bf16x8_t av = col8_tr(s_bn, LDQ, nb, nb + 4, 16 * rt, l16);
-                        const bf16x8_t bv = col8_tr(s_cn, LDQ, nb, nb + 4, 16 * pw, l16);
+                        const bf16x8_t bv = col8_tr(s_cn, LDQ, nb, nb + 4, 16 * st, l16);
                         acc = mma(av, bv, acc);
                     }
+                    const float Ls = s_L[s];
                     const int r0 = 16 * rt + 4 * lq;
                     const float4 Lr = *reinterpret_cast<const float4 *>(&s_L[r0]);
                     const float4 dr = *reinterpret_cast<const float4 *>(&s_d[r0]);
                     const float lr[4] = {Lr.x, Lr.y, Lr.z, Lr.w}, dv[4] = {dr.x, dr.y, dr.z, dr.w};
+                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                    bf16x4_t mh, ml;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        m[j] = (r0 + j <= s) ? acc[j] * exp2_hw(Ls - lr[j]) * dv[j] : 0.0f;
+                    for (int j = 0; j < 4; ++j) {
+                        const float m = (r0 + j <= s) ? acc[j] * exp2_hw(Ls - lr[j]) * dv[j] : 0.0f;
+                        mh[j] = (__bf16)m;
+                        ml[j] = (__bf16)(m - (float)mh[j]);
+                    }
+                    *reinterpret_cast<bf16x4_t *>(&s_mh[s * LDQ + r0]) = mh;
+                    *reinterpret_cast<bf16x4_t *>(&s_ml[s * LDQ + r0]) = ml;
                 }
-                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                bf16x4_t mh, ml;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    mh[j] = (__bf16)m[j];
-                    ml[j] = (__bf16)(m[j] - (float)mh[j]);
-                }
-                const int r0 = 16 * rt + 4 * lq;
-                *reinterpret_cast<bf16x4_t *>(&s_mh[s * LDQ + r0]) = mh;
-                *reinterpret_cast<bf16x4_t *>(&s_ml[s * LDQ + r0]) = ml;
             }
         }
 
@@ -410,7 +422,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             const int s0 = 16 * st + 4 * lq;
             const int t = t0 + s0;
             if (t < L) {  // L % 4 == 0: the 4 steps are all in or all out
-                const float4 eL = *reinterpret_cast<const float4 *>(&s_eL[s0]);
+                const float4 eL = *reinterpret_cast<const float4 *>(&s_eL[par][s0]);
                 const float el[4] = {eL.x, eL.y, eL.z, eL.w};
                 const float xv[4] = {bf_lo(xo[i].x), bf_hi(xo[i].x), bf_lo(xo[i].y), bf_hi(xo[i].y)};
                 const float zv[4] = {bf_lo(zo[i].x), bf_hi(zo[i].x), bf_lo(zo[i].y), bf_hi(zo[i].y)};
@@ -429,7 +441,6 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 *reinterpret_cast<uint2 *>(orow + t) = ov;
             }
         }
-        __syncthreads();  // the next chunk overwrites the staged tiles
     }
 
     if (srow) {

@@ -199,6 +199,8 @@ enum : int {
     DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
     DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
     DPP_QUAD_NEXT = 0xF9,  // quad_perm [1,2,3,3]: lane i of a quad reads lane min(i+1, 3)
+    DPP_ROW_BCAST15 = 0x142,  // lane 15 of each row to every lane of the next row
+    DPP_ROW_BCAST31 = 0x143,  // lane 31 to every lane of rows 2 and 3
 };
 
 // Read `src` from another lane of the same 16-lane row; lanes whose source
@@ -224,6 +226,26 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_move_bits(uint32_t src)
 {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)src, CTRL, 0xf, 0xf, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: a Hillis-Steele scan in
+// each 16-lane row, then the row totals added by the two row broadcasts
+// (rows 1 and 3 take the total of the row before; rows 2 and 3 that of
+// rows 0-1).  No LDS round trip.
+__device__ __forceinline__ float wave_prefix_sum(float v)
+{
+    v += dpp_move_zero<DPP_ROW_SHR1>(v);
+    v += dpp_move_zero<DPP_ROW_SHR2>(v);
+    v += dpp_move_zero<DPP_ROW_SHR4>(v);
+    v += dpp_move_zero<DPP_ROW_SHR8>(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPP_ROW_BCAST15, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPP_ROW_BCAST31, 0xc, 0xf, false));
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
 // ---------------------------------------------------------------- block order
