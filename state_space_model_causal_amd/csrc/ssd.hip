@@ -33,6 +33,8 @@
 // one wave's vector work overlap the other's matrix work.  HBM traffic: u,
 // dt, z, B, C read once (B and C from L2 for every head of a group), out
 // written once, the state read and written once.
+#include <algorithm>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -117,8 +119,12 @@ __device__ __forceinline__ void load_pairs(u32x4 (&v0)[ChunkLoads<N>::UNITS], u3
         const int n = 2 * (u >> 3), tv = u & 7;
         const int t = t0 + 8 * tv;
         const int tc = t < L ? t : 0;  // clamped; zeroed when staged
-        v0[k] = *reinterpret_cast<const u32x4 *>(G + n * sn + tc);
-        v1[k] = *reinterpret_cast<const u32x4 *>(G + (n + 1) * sn + tc);
+        // byte offsets from the workgroup's base (32-bit: the host checks the
+        // extent), so that the loads take the scalar base + vector offset form
+        const uint32_t o0 = 2u * (uint32_t)(n * (int)sn + tc), o1 = o0 + 2u * (uint32_t)sn;
+        const char *g = reinterpret_cast<const char *>(G);
+        v0[k] = *reinterpret_cast<const u32x4 *>(g + o0);
+        v1[k] = *reinterpret_cast<const u32x4 *>(g + o1);
     }
 }
 
@@ -466,8 +472,12 @@ static hipError_t launch_ssd_ts(const ScanArgs &a, hipStream_t stream)
 
 bool ssd_supported(const ScanArgs &a)
 {
+    // B and C are addressed by 32-bit byte offsets from each (request, group)
+    // base
+    const int64_t span = (int64_t)2 * ((int64_t)(a.dstate - 1) * std::max(a.B_sn, a.C_sn) + a.seqlen);
     return !a.cu_seqlens && !a.a_per_state && a.io_dtype == 2 && a.vec &&
-           (a.dstate == 64 || a.dstate == 128 || a.dstate == 256) && a.headdim % SPB == 0;
+           (a.dstate == 64 || a.dstate == 128 || a.dstate == 256) && a.headdim % SPB == 0 &&
+           span < ((int64_t)1 << 32);
 }
 
 hipError_t launch_ssd(const ScanArgs &a, hipStream_t stream)
