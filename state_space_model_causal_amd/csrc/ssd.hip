@@ -331,6 +331,17 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             *reinterpret_cast<f32x4_t *>(&s_x[partner][1][l][0]) = nh ? yc[1] : yc[3];
         }
 
+        // the gate of this wave's outputs, computed here where the matrix
+        // work of the other waves hides it (1 without z)
+        float gz[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float zv[4] = {bf_lo(zo[i].x), bf_hi(zo[i].x), bf_lo(zo[i].y), bf_hi(zo[i].y)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                gz[i][j] = zrow ? silu_f32(zv[j]) : 1.0f;
+        }
+
         if (more)
             load_pairs<N>(cur.b0, cur.b1, t0 + SQ, L, Bg, a.B_sn, tid);
 
@@ -431,15 +442,12 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 const float4 eL = *reinterpret_cast<const float4 *>(&s_eL[par][s0]);
                 const float el[4] = {eL.x, eL.y, eL.z, eL.w};
                 const float xv[4] = {bf_lo(xo[i].x), bf_hi(xo[i].x), bf_lo(xo[i].y), bf_hi(xo[i].y)};
-                const float zv[4] = {bf_lo(zo[i].x), bf_hi(zo[i].x), bf_lo(zo[i].y), bf_hi(zo[i].y)};
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const f32x4_t mine = i ? (nh ? yc[3] : yc[1]) : (nh ? yc[2] : yc[0]);
-                    float v = y[j] + el[j] * (mine[j] + other[j]) + Dh * xv[j];
-                    if (zrow)
-                        v *= silu_f32(zv[j]);
-                    o[j] = v;
+                    const float v = y[j] + el[j] * (mine[j] + other[j]) + Dh * xv[j];
+                    o[j] = v * gz[i][j];
                 }
                 uint2 ov;
                 ov.x = (uint32_t)from_f32<bf16>(o[0]).bits | ((uint32_t)from_f32<bf16>(o[1]).bits << 16);
