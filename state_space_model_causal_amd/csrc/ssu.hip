@@ -391,7 +391,7 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
         bb64[q] = bb;
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
-            load_vec_cached<TS, E>(sp[q] + hp[k] * N, hs[q][k]);
+            load_vec<TS, E>(sp[q] + hp[k] * N, hs[q][k]);
         load_bc<TI, E>(static_cast<const TI *>(a.B) + bb * a.B_sb + g * a.B_sg + n0, bv[q]);
         load_bc<TI, E>(static_cast<const TI *>(a.C) + bb * a.C_sb + g * a.C_sg + n0, cv[q]);
     }
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(512) void ssu_ilv_kernel(SsuArgs a)
                 }
             }
             if (ok)
-                store_vec_cached<TS, E>(sp[q] + hp[k] * N, hn);
+                store_vec<TS, E>(sp[q] + hp[k] * N, hn);
             for (int o = lpr >> 1; o > 0; o >>= 1)
                 y += __shfl_xor(y, o, 64);
             if (ok && jl == 0) {
