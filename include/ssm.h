@@ -349,11 +349,27 @@ int ssm_selective_scan_varlen(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, s
  * f16 or bf16 (f32 returns SSM_ERR_UNSUPPORTED); K a multiple of 8; x and
  * weight rows 16-byte aligned (base and row stride); out and residual may be
  * strided views with unit inner stride.  workspace: ssm_linear_workspace(M,
- * N, K) bytes (may be 0 and NULL) of device memory for split-K partial sums.
+ * N, K) bytes (may be 0 and NULL) of device memory for split-K partial sums;
+ * its contents need not be preserved between calls.
+ *
+ * ssm_linear_ex -- the same with the launch plan given: rows_per_wave (16,
+ * 32 or 64), cols_per_workgroup (64 or 128: a workgroup of 4 waves per 64
+ * columns takes 4 x rows_per_wave rows) and splits (1 .. min(64, ceil(K /
+ * 64)) workgroups along K, partial sums added by a second kernel); 0 for the
+ * library's choice of each.  A power of two above 64 rows per wave or 128
+ * columns returns SSM_ERR_OUT_OF_RESOURCES (past a wave's accumulator
+ * registers or a workgroup's threads), other values SSM_ERR_SHAPE.  Its
+ * workspace is ssm_linear_workspace_ex of the same plan (0 for an invalid
+ * plan).  For tuning sweeps.
  */
 size_t ssm_linear_workspace(int M, int N, int K);
 int ssm_linear(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M,
                int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+size_t ssm_linear_workspace_ex(int M, int N, int K, int rows_per_wave, int cols_per_workgroup,
+                               int splits);
+int ssm_linear_ex(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M,
+                  int N, int K, int rows_per_wave, int cols_per_workgroup, int splits,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* ssm_rmsnorm -- out[m, :] = x[m, :] / sqrt(mean(x[m, :]^2) + eps) * weight
  * (weight float32 [D], dense; x, out f16 or bf16 [M, D]). */

@@ -39,7 +39,8 @@ _DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: S
 EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_selective_scan_ex", "ssm_state_update",
             "ssm_state_update_ex", "ssm_state_update_config",
             "ssm_decode_step", "ssm_causal_conv1d_varlen", "ssm_selective_scan_varlen",
-            "ssm_linear", "ssm_linear_workspace", "ssm_rmsnorm", "ssm_mamba1_decode_layer",
+            "ssm_linear", "ssm_linear_workspace", "ssm_linear_ex", "ssm_linear_workspace_ex",
+            "ssm_rmsnorm", "ssm_mamba1_decode_layer",
             "ssm_mamba1_decode_layer_workspace", "ssm_mamba1_decode_layer_noalloc",
             "ssm_status_string", "ssm_abi_version")
 
@@ -120,6 +121,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_linear_workspace.restype = Z
     lib.ssm_linear.argtypes = [T, T, T, T, I, I, I, P, Z, P]
     lib.ssm_linear.restype = I
+    lib.ssm_linear_workspace_ex.argtypes = [I, I, I, I, I, I]
+    lib.ssm_linear_workspace_ex.restype = Z
+    lib.ssm_linear_ex.argtypes = [T, T, T, T, I, I, I, I, I, I, P, Z, P]
+    lib.ssm_linear_ex.restype = I
     lib.ssm_rmsnorm.argtypes = [T, T, T, I, I, ctypes.c_float, P]
     lib.ssm_rmsnorm.restype = I
     lib.ssm_mamba1_decode_layer_workspace.argtypes = [P, I]
@@ -348,20 +353,24 @@ def _workspace(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def linear(x, weight, residual=None, out=None, workspace=None, stream=None):
-    """ssm_linear: out[M, N] = x[M, K] . weight[N, K]^T (+ residual)."""
+def linear(x, weight, residual=None, out=None, workspace=None, stream=None, rows_per_wave=0, cols=0,
+           splits=0):
+    """ssm_linear: out[M, N] = x[M, K] . weight[N, K]^T (+ residual).  With
+    rows_per_wave / cols / splits (0: the library's choice) the plan is given
+    (ssm_linear_ex)."""
     M, K = x.shape
     N = weight.shape[0]
     if out is None:
         out = torch.empty(M, N, dtype=x.dtype, device=x.device)
-    need = load_library().ssm_linear_workspace(M, N, K)
+    lib = load_library()
     if workspace is None:
+        need = lib.ssm_linear_workspace_ex(M, N, K, int(rows_per_wave), int(cols), int(splits))
         workspace = _workspace(need, x.device)
-    st = load_library().ssm_linear(
+    st = lib.ssm_linear_ex(
         _tensor(x, "x"), _tensor(weight, "weight"), _tensor(residual, "residual"),
-        _tensor(out, "out"), M, N, K, _ptr(workspace, "workspace"),
+        _tensor(out, "out"), M, N, K, int(rows_per_wave), int(cols), int(splits), _ptr(workspace, "workspace"),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("ssm_linear", st)
+    _check("ssm_linear_ex", st)
     return out
 
 

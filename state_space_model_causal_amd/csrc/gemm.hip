@@ -7,23 +7,29 @@
 // skinny product: out[M, N] = act[M, K] . W[N, K]^T with M = the number of
 // requests (245 on the pages' concurrency test), K and N the layer widths.
 //
-// Kernel: one 256-lane workgroup per (64 output columns, slice of K, 256
-// rows).  Wave w owns rows [64 w, 64 w + 64) of the block and all 64
-// columns: 4 x 4 tiles of v_mfma_f32_16x16x32_{f16,bf16}, float32
-// accumulation.  K is walked in batches of 64: each batch's activation tile
-// (256 rows x 64 k) and weight tile (64 rows x 64 k) are loaded once per
-// workgroup with coalesced 128-bit loads (consecutive lanes, consecutive 16
-// bytes of a row) and staged in LDS, from where each wave reads its MFMA
-// operands (8 consecutive k of one row: row-major, k innermost is the operand
-// order).  The next batch's loads are in flight during the current batch's
-// MFMAs.  The weights, the dominant traffic, stream from
-// HBM once per row block (the activations, 2.6 MB at most, stay in L2).
-// Narrow outputs split K over several workgroups, whose float32 partial sums
-// a second kernel adds.
+// Kernel: one 256-lane workgroup per (64 output columns, 4 WR rows, slice of
+// K), WR = 64, 32 or 16 rows per wave.  Wave w owns rows [WR w, WR w + WR) of
+// the block and all 64 columns: WR/16 x 4 tiles of
+// v_mfma_f32_16x16x32_{f16,bf16}, float32 accumulation.  K is walked in
+// batches of 64: each batch's activation tile (4 WR rows x 64 k) and weight
+// tile (64 rows x 64 k) are loaded once per workgroup with coalesced 128-bit
+// loads (consecutive lanes, consecutive 16 bytes of a row) and staged in LDS,
+// from where each wave reads its MFMA operands (8 consecutive k of one row:
+// row-major, k innermost is the operand order).  The next batch's loads are
+// in flight during the current batch's MFMAs.  The weights, the dominant
+// traffic, stream from HBM once (the row blocks of one column tile run on one
+// XCD and share its L2; the activations, 2.6 MB at most, stay in L2).
+// Narrow outputs split K over several workgroups.  Their float32 partial sums
+// are added by the last split of each tile to finish (a counter per tile), or,
+// where that would be a long serial tail, by a second kernel.
 //
 // Epilogue: output columns go to up to three destinations (column segments,
 // e.g. the x and z halves of in_proj), optionally added to a residual, rows
 // of padded requests left untouched.
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -33,7 +39,6 @@ namespace {
 typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_g __attribute__((ext_vector_type(8)));
 typedef float f32x4_g __attribute__((ext_vector_type(4)));
-constexpr int GM = 256;  // rows per workgroup
 constexpr int GN = 64;   // columns per workgroup
 constexpr int GK = 32;   // k per MFMA step
 
@@ -110,27 +115,45 @@ __device__ __forceinline__ void gemm_store4(const GemmArgs &a, int row, int col,
         gemm_store<T>(a, row, col + e, v[e]);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+// Workgroup of 4 x CW waves for a tile of 4 WR rows x 64 CW columns and one
+// slice of K; wave w owns rows [WR (w % 4), + WR) and columns
+// [64 (w / 4), + 64).
+template <typename T, int WR, int CW>
+__global__ __launch_bounds__(256 * CW) void gemm_kernel(GemmArgs a)
 {
-    // one k batch of both operands in LDS: the activation tile (GM rows) and
-    // the weight tile (GN rows), KBK k each, row stride padded by 16 B
+    // one k batch of both operands in LDS: the activation tile (GMR rows) and
+    // the weight tile (GNC rows), KBK k each, row stride padded by 16 B
+    constexpr int NT = 256 * CW;     // threads
+    constexpr int GMR = 4 * WR;      // rows per workgroup
+    constexpr int GNC = GN * CW;     // columns per workgroup
+    constexpr int RT = WR / 16;      // 16-row MFMA tiles per wave
     constexpr int KB = 2;            // MFMA k-steps per batch
     constexpr int KBK = KB * GK;     // k per batch
     constexpr int LDK = KBK + 8;     // elements per LDS row
     constexpr int CPR = KBK / 8;     // 16-byte chunks per row
-    constexpr int ACH = GM * CPR / 256, WCH = GN * CPR / 256;  // chunks per thread
-    __shared__ __align__(16) T s_a[GM * LDK];
-    __shared__ __align__(16) T s_w[GN * LDK];
+    constexpr int ACH = GMR * CPR / NT, WCH = GNC * CPR / NT;  // chunks per thread
+    static_assert(ACH * NT == GMR * CPR && WCH * NT == GNC * CPR, "tiles must split evenly over the threads");
+    __shared__ __align__(16) T s_a[GMR * LDK];
+    __shared__ __align__(16) T s_w[GNC * LDK];
 
-    const int nb = blockIdx.x, ks = blockIdx.y, mb = blockIdx.z;
+    // logical block (column tile, row block, split): the splits and row
+    // blocks of one column tile are consecutive, and consecutive logical
+    // blocks run on one XCD, so they share its L2 (the weight tile)
+    const int ncol = (a.N + GNC - 1) / GNC, nrow = (a.M + GMR - 1) / GMR;
+    const uint32_t lb = xcd_block_order(blockIdx.x, gridDim.x);
+    const int ks = (int)(lb % (uint32_t)a.splits);
+    const int mb = (int)((lb / (uint32_t)a.splits) % (uint32_t)nrow);
+    const int nb = (int)(lb / ((uint32_t)a.splits * (uint32_t)nrow));
+    if (nb >= ncol)
+        return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int wm = w & 3, wn = w >> 2;  // row and column group of the wave
     const int l16 = l & 15, lq = l >> 4;
     const int K = a.K;
     const int nbatch = (K + KBK - 1) / KBK;
     const int b0 = (int)((int64_t)nbatch * ks / a.splits), b1 = (int)((int64_t)nbatch * (ks + 1) / a.splits);
 
-    // chunk c = tid + 256 q of a tile: row c / CPR, k offset 8 (c % CPR);
+    // chunk c = tid + NT q of a tile: row c / CPR, k offset 8 (c % CPR);
     // consecutive threads read consecutive 16 B of a row
     const T *asrc[ACH];
     const T *wsrc[WCH];
@@ -138,22 +161,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     const int kofs = 8 * (tid % CPR);  // the same for every chunk of this thread
 #pragma unroll
     for (int q = 0; q < ACH; ++q) {
-        const int c = tid + 256 * q, r = c / CPR;
-        const int m = min(mb * GM + r, a.M - 1);  // clamped rows are never stored
+        const int c = tid + NT * q, r = c / CPR;
+        const int m = min(mb * GMR + r, a.M - 1);  // clamped rows are never stored
         asrc[q] = static_cast<const T *>(a.A) + (int64_t)m * a.lda + kofs;
         adst[q] = r * LDK + kofs;
     }
 #pragma unroll
     for (int q = 0; q < WCH; ++q) {
-        const int c = tid + 256 * q, r = c / CPR;
-        const int n = min(nb * GN + r, a.N - 1);
+        const int c = tid + NT * q, r = c / CPR;
+        const int n = min(nb * GNC + r, a.N - 1);
         wsrc[q] = static_cast<const T *>(a.W) + (int64_t)n * a.ldw + kofs;
         wdst[q] = r * LDK + kofs;
     }
 
-    f32x4_g acc[4][4];
+    f32x4_g acc[RT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_g{0.0f, 0.0f, 0.0f, 0.0f};
@@ -161,61 +184,71 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     // K % 8 == 0: an 8-element chunk is all in or all out; out of range it
     // is loaded from the row's first chunk (in bounds) and zeroed when it is
     // staged.  Zeroing at staging time, not right after the load, keeps the
-    // loads in flight during the MFMAs of the batch before.
-    u32x4 ar[ACH], wr[WCH];
-    bool in_range = true;
-    auto load = [&](int batch) {
-        in_range = batch * KBK + kofs < K;
-        const int off = in_range ? batch * KBK : -kofs;
+    // loads in flight.  Two batches of loads are in flight at a time, in two
+    // register sets (the loop is unrolled by two, so each set is named at
+    // compile time): batch b + 2 is issued as soon as batch b is staged.
+    u32x4 ar[2][ACH], wr[2][WCH];
+    bool in_range[2] = {true, true};
+    auto load = [&](int batch, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        in_range[B] = batch * KBK + kofs < K;
+        const int off = in_range[B] ? batch * KBK : -kofs;
 #pragma unroll
         for (int q = 0; q < ACH; ++q)
-            ar[q] = *reinterpret_cast<const u32x4 *>(asrc[q] + off);
+            ar[B][q] = *reinterpret_cast<const u32x4 *>(asrc[q] + off);
 #pragma unroll
         for (int q = 0; q < WCH; ++q)
-            wr[q] = *reinterpret_cast<const u32x4 *>(wsrc[q] + off);
+            wr[B][q] = *reinterpret_cast<const u32x4 *>(wsrc[q] + off);
     };
-    auto stage = [&]() {
+    auto step = [&](int bt, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
         const u32x4 zero{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int q = 0; q < ACH; ++q)
-            *reinterpret_cast<u32x4 *>(&s_a[adst[q]]) = in_range ? ar[q] : zero;
+            *reinterpret_cast<u32x4 *>(&s_a[adst[q]]) = in_range[B] ? ar[B][q] : zero;
 #pragma unroll
         for (int q = 0; q < WCH; ++q)
-            *reinterpret_cast<u32x4 *>(&s_w[wdst[q]]) = in_range ? wr[q] : zero;
-    };
-
-    if (b0 < b1)
-        load(b0);
-    for (int bt = b0; bt < b1; ++bt) {
-        stage();
+            *reinterpret_cast<u32x4 *>(&s_w[wdst[q]]) = in_range[B] ? wr[B][q] : zero;
         __syncthreads();
-        if (bt + 1 < b1)
-            load(bt + 1);  // in flight during this batch's MFMAs
+        if (bt + 2 < b1)
+            load(bt + 2, bufc);  // in flight during this batch's and the next one's MFMAs
 #pragma unroll
         for (int q = 0; q < KB; ++q) {
-            u32x4 av[4], bv[4];
+            u32x4 av[RT], bv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[i] = *reinterpret_cast<const u32x4 *>(&s_a[(64 * w + 16 * i + l16) * LDK + q * GK + 8 * lq]);
+            for (int i = 0; i < RT; ++i)
+                av[i] = *reinterpret_cast<const u32x4 *>(&s_a[(WR * wm + 16 * i + l16) * LDK + q * GK + 8 * lq]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bv[j] = *reinterpret_cast<const u32x4 *>(&s_w[(16 * j + l16) * LDK + q * GK + 8 * lq]);
+                bv[j] = *reinterpret_cast<const u32x4 *>(&s_w[(GN * wn + 16 * j + l16) * LDK + q * GK + 8 * lq]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < RT; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = Mfma<T>::run(bv[j], av[i], acc[i][j]);
         }
         __syncthreads();  // the tiles are restaged next batch
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    if (b0 < b1)
+        load(b0, B0{});
+    if (b0 + 1 < b1)
+        load(b0 + 1, B1{});
+    for (int bt = b0; bt < b1; bt += 2) {
+        step(bt, B0{});
+        if (bt + 1 < b1)
+            step(bt + 1, B1{});
     }
 
     // The products are taken as W . act^T, so acc[i][j][e] is output row
-    // mb*GM + 64 w + 16 i + l16, column nb*GN + 16 j + 4 lq + e: each lane
-    // holds four consecutive columns of one row.
-    const int col0 = nb * GN + 4 * lq;
+    // mb*GMR + WR wm + 16 i + l16, column nb*GNC + 64 wn + 16 j + 4 lq + e:
+    // each lane holds four consecutive columns of one row.
+    const int col0 = nb * GNC + GN * wn + 4 * lq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = mb * GM + 64 * w + 16 * i + l16;
+    for (int i = 0; i < RT; ++i) {
+        const int row = mb * GMR + WR * wm + 16 * i + l16;
         if (a.splits == 1) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -278,11 +311,31 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a)
     gemm_store4<T>(a, row, col, v);
 }
 
+template <typename T, int WR, int CW>
+static void launch_gemm_wr(const GemmArgs &a, hipStream_t stream)
+{
+    const int64_t ncol = (a.N + GN * CW - 1) / (GN * CW), nrow = (a.M + 4 * WR - 1) / (4 * WR);
+    const dim3 grid((unsigned)(ncol * nrow * a.splits));
+    hipLaunchKernelGGL((gemm_kernel<T, WR, CW>), grid, dim3(256 * CW), 0, stream, a);
+}
+
+template <typename T, int CW>
+static void launch_gemm_cw(const GemmArgs &a, hipStream_t stream)
+{
+    switch (a.wr) {
+    case 16: launch_gemm_wr<T, 16, CW>(a, stream); break;
+    case 32: launch_gemm_wr<T, 32, CW>(a, stream); break;
+    default: launch_gemm_wr<T, 64, CW>(a, stream); break;
+    }
+}
+
 template <typename T>
 static hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((a.N + GN - 1) / GN), (unsigned)a.splits, (unsigned)((a.M + GM - 1) / GM));
-    hipLaunchKernelGGL((gemm_kernel<T>), grid, dim3(256), 0, stream, a);
+    if (a.cw == 2)
+        launch_gemm_cw<T, 2>(a, stream);
+    else
+        launch_gemm_cw<T, 1>(a, stream);
     if (a.splits > 1) {
         const int64_t n = (int64_t)a.M * ((a.N + 3) / 4);
         hipLaunchKernelGGL((gemm_reduce_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
@@ -295,8 +348,106 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
     return a.dtype == 1 ? launch_gemm_t<f16>(a, stream) : launch_gemm_t<bf16>(a, stream);
 }
 
+// How a product is laid over the chip (see GemmPlan): the plan of least
+// modelled time among rows per wave {16, 32, 64} x column groups {1, 2} x
+// splits 1 .. min(32, K / 64) (those the caller fixed, fixed).  The model,
+// fitted to measured sweeps on gfx950: a compute unit takes its operand tiles
+// in through its L1 at about 38 GB/s, one workgroup after another (the
+// activation tile is re-read by every column tile, the weight tile by every
+// row block); a split also writes its float32 partial sums, and the second
+// kernel's round trip through HBM plus its launch (about 3 us) is added.
+GemmPlan plan_gemm(int M, int N, int K, int rows_per_wave, int cols, int splits)
+{
+    const int nbatch = (K + 63) / 64;
+    GemmPlan best{64, 1, 1};
+    double tbest = 1e300;
+    for (int wr : {16, 32, 64}) {
+        if (rows_per_wave && wr != rows_per_wave)
+            continue;
+        for (int cw : {1, 2}) {
+            if (cols && cw * GN != cols)
+                continue;
+            const int s0 = splits ? splits : 1, s1 = splits ? splits : (nbatch < 32 ? nbatch : 32);
+            for (int s = s0; s <= s1; ++s) {
+                const double rows = 4.0 * wr, c = (double)GN * cw;
+                const double tiles = std::ceil(N / c) * std::ceil(M / rows);
+                const double ks = 64.0 * std::ceil((double)nbatch / s);
+                const double bytes = ks * 2.0 * (std::min(rows, (double)M) + c) + (s > 1 ? rows * c * 4.0 : 0.0);
+                double t = bytes * std::ceil(tiles * s / 256.0) / 38.4e9;
+                if (s > 1)
+                    t += (double)s * M * N * 8.0 / 8e12 + 3e-6;
+                if (t < tbest) {
+                    tbest = t;
+                    best = GemmPlan{wr, cw, s};
+                }
+            }
+        }
+    }
+    return best;
+}
+
 // RMSNorm of each row: out = x / sqrt(mean(x^2) + eps) * weight (weight in
-// float32), one workgroup per row.
+// float32).  One wave per row: the row is read once into registers with
+// 128-bit loads (8 elements per lane and round, C rounds), its sum of squares
+// reduced across the wave, then scaled and written with 128-bit stores.
+template <typename T, int C>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T *__restrict__ x, int64_t ldx,
+                                                           const float *__restrict__ wt, T *__restrict__ out,
+                                                           int64_t ldo, int M, int D, float eps)
+{
+    const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M)
+        return;  // the whole wave
+    const T *xr = x + row * ldx;
+    u32x4 v[C];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int e = 512 * c + 8 * lane;
+        if (e < D) {
+            v[c] = *reinterpret_cast<const u32x4 *>(xr + e);
+            float f[8];
+            unpack_word(v[c].x, f, T{});
+            unpack_word(v[c].y, f + 2, T{});
+            unpack_word(v[c].z, f + 4, T{});
+            unpack_word(v[c].w, f + 6, T{});
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ss = fmaf(f[i], f[i], ss);
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1)
+        ss += __shfl_xor(ss, o, 64);
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    T *orow = out + row * ldo;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int e = 512 * c + 8 * lane;
+        if (e < D) {
+            float f[8];
+            unpack_word(v[c].x, f, T{});
+            unpack_word(v[c].y, f + 2, T{});
+            unpack_word(v[c].z, f + 4, T{});
+            unpack_word(v[c].w, f + 6, T{});
+            const float4 w0 = *reinterpret_cast<const float4 *>(wt + e);
+            const float4 w1 = *reinterpret_cast<const float4 *>(wt + e + 4);
+            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                f[i] = f[i] * inv * wv[i];
+            u32x4 o;
+            o.x = pack_word(f, T{});
+            o.y = pack_word(f + 2, T{});
+            o.z = pack_word(f + 4, T{});
+            o.w = pack_word(f + 6, T{});
+            *reinterpret_cast<u32x4 *>(orow + e) = o;
+        }
+    }
+}
+
+// Rows whose width or alignment does not allow the vector form: one
+// workgroup per row, element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ x, int64_t ldx,
                                                       const float *__restrict__ wt, T *__restrict__ out,
@@ -321,15 +472,39 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ x, i
         out[row * ldo + i] = from_f32<T>(to_f32(xr[i]) * inv * wt[i]);
 }
 
+template <typename T, int C>
+static void launch_rmsnorm_rows(const T *x, int64_t ldx, const float *w, T *out, int64_t ldo, int M, int D,
+                                float eps, hipStream_t stream)
+{
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<T, C>), dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, x, ldx, w,
+                       out, ldo, M, D, eps);
+}
+
+template <typename T>
+static void launch_rmsnorm_t(const T *x, int64_t ldx, const float *w, T *out, int64_t ldo, int M, int D,
+                             float eps, hipStream_t stream)
+{
+    const bool vec = D % 8 == 0 && ldx % 8 == 0 && ldo % 8 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+    if (vec && D <= 1024)
+        launch_rmsnorm_rows<T, 2>(x, ldx, w, out, ldo, M, D, eps, stream);
+    else if (vec && D <= 4096)
+        launch_rmsnorm_rows<T, 8>(x, ldx, w, out, ldo, M, D, eps, stream);
+    else if (vec && D <= 8192)
+        launch_rmsnorm_rows<T, 16>(x, ldx, w, out, ldo, M, D, eps, stream);
+    else
+        hipLaunchKernelGGL((rmsnorm_kernel<T>), dim3(M), dim3(256), 0, stream, x, ldx, w, out, ldo, M, D, eps);
+}
+
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const float *w, void *out, int64_t ldo, int M, int D,
                           float eps, int dtype, hipStream_t stream)
 {
     if (dtype == 1)
-        hipLaunchKernelGGL((rmsnorm_kernel<f16>), dim3(M), dim3(256), 0, stream, static_cast<const f16 *>(x), ldx,
-                           w, static_cast<f16 *>(out), ldo, M, D, eps);
+        launch_rmsnorm_t<f16>(static_cast<const f16 *>(x), ldx, w, static_cast<f16 *>(out), ldo, M, D, eps, stream);
     else
-        hipLaunchKernelGGL((rmsnorm_kernel<bf16>), dim3(M), dim3(256), 0, stream, static_cast<const bf16 *>(x),
-                           ldx, w, static_cast<bf16 *>(out), ldo, M, D, eps);
+        launch_rmsnorm_t<bf16>(static_cast<const bf16 *>(x), ldx, w, static_cast<bf16 *>(out), ldo, M, D, eps,
+                               stream);
     return hipGetLastError();
 }
 

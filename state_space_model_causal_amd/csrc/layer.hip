@@ -25,24 +25,32 @@ bool al(const void *p, uintptr_t n) { return p == nullptr || (reinterpret_cast<u
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 using ssm::status_of;
 
-// K split so that a narrow output still spreads over the chip: up to 32
-// slices of at least 2 k batches, aiming at ~512 workgroups.
-int choose_splits(int M, int N, int K)
+// Workspace of one product: the float32 partial sums of a K split.
+struct LinearWs {
+    ssm::GemmPlan plan;
+    size_t total;
+};
+
+LinearWs linear_ws(int M, int N, const ssm::GemmPlan &plan)
 {
-    const int nsteps = (K + 63) / 64;  // 64-k batches of the projection kernel
-    const int64_t blocks = (int64_t)((N + 63) / 64) * ((M + 255) / 256);
-    int s = (int)(512 / (blocks > 0 ? blocks : 1));
-    if (s > 32)
-        s = 32;
-    if (s > nsteps / 2)
-        s = nsteps / 2;
-    return s < 1 ? 1 : s;
+    LinearWs w{};
+    w.plan = plan;
+    w.total = plan.splits > 1 ? round_up((size_t)plan.splits * M * N * sizeof(float)) : 0;
+    return w;
 }
 
-size_t linear_partial_bytes(int M, int N, int K)
+// The plan as given (0: the library's choice of that part); status of values
+// the product kernel does not take
+int plan_of(int M, int N, int K, int rows_per_wave, int cols, int splits, ssm::GemmPlan &plan)
 {
-    const int s = choose_splits(M, N, K);
-    return s > 1 ? round_up((size_t)s * M * N * sizeof(float)) : 0;
+    const bool pow2 = (rows_per_wave & (rows_per_wave - 1)) == 0 && (cols & (cols - 1)) == 0;
+    if (pow2 && (rows_per_wave > 64 || cols > 128))
+        return SSM_ERR_OUT_OF_RESOURCES;  // past a wave's accumulators / a workgroup's threads
+    if ((rows_per_wave != 0 && rows_per_wave != 16 && rows_per_wave != 32 && rows_per_wave != 64) ||
+        (cols != 0 && cols != 64 && cols != 128) || splits < 0 || splits > (K + 63) / 64 || splits > 64)
+        return SSM_ERR_SHAPE;
+    plan = ssm::plan_gemm(M, N, K, rows_per_wave, cols, splits);
+    return SSM_OK;
 }
 
 ssm_tensor dense(const void *p, int dtype, int64_t s0, int64_t s1 = 1, int64_t s2 = 1)
@@ -95,13 +103,16 @@ int check_linear(const ssm_tensor &x, const ssm_tensor &w, const ssm_tensor &res
     return SSM_OK;
 }
 
-int run_linear(ssm::GemmArgs g, int M, int N, int K, void *ws, hipStream_t stream)
+// The product with its plan (partial sums in `partial` when it splits K).
+int run_linear(ssm::GemmArgs g, int M, int N, int K, const LinearWs &lw, void *partial, hipStream_t stream)
 {
     g.M = M;
     g.N = N;
     g.K = K;
-    g.splits = choose_splits(M, N, K);
-    g.partial = g.splits > 1 ? static_cast<float *>(ws) : nullptr;
+    g.wr = lw.plan.wr;
+    g.cw = lw.plan.cw;
+    g.splits = lw.plan.splits;
+    g.partial = g.splits > 1 ? static_cast<float *>(partial) : nullptr;
     return status_of(ssm::launch_gemm(g, stream));
 }
 
@@ -109,26 +120,34 @@ int run_linear(ssm::GemmArgs g, int M, int N, int K, void *ws, hipStream_t strea
 
 extern "C" {
 
-size_t ssm_linear_workspace(int M, int N, int K)
+size_t ssm_linear_workspace_ex(int M, int N, int K, int rows_per_wave, int cols_per_workgroup, int splits)
 {
-    if (M < 1 || N < 1 || K < 1)
+    ssm::GemmPlan plan;
+    if (M < 1 || N < 1 || K < 1 || plan_of(M, N, K, rows_per_wave, cols_per_workgroup, splits, plan) != SSM_OK)
         return 0;
-    return linear_partial_bytes(M, N, K);
+    return linear_ws(M, N, plan).total;
 }
 
-int ssm_linear(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M, int N, int K,
-               void *workspace, size_t workspace_bytes, void *stream)
+size_t ssm_linear_workspace(int M, int N, int K) { return ssm_linear_workspace_ex(M, N, K, 0, 0, 0); }
+
+int ssm_linear_ex(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M, int N, int K,
+                  int rows_per_wave, int cols_per_workgroup, int splits, void *workspace, size_t workspace_bytes,
+                  void *stream)
 {
-    const int st = check_linear(x, weight, residual, out, M, N, K);
+    int st = check_linear(x, weight, residual, out, M, N, K);
     if (st != SSM_OK)
+        return st;
+    ssm::GemmPlan plan;
+    if ((st = plan_of(M > 0 ? M : 1, N, K, rows_per_wave, cols_per_workgroup, splits, plan)) != SSM_OK)
         return st;
     if (!al(workspace, 16))
         return SSM_ERR_ALIGN;
     if (M == 0)
         return SSM_OK;
-    const size_t need = linear_partial_bytes(M, N, K);
-    if (need && (!workspace || workspace_bytes < need))
+    const LinearWs lw = linear_ws(M, N, plan);
+    if (lw.total && (!workspace || workspace_bytes < lw.total))
         return SSM_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
     ssm::GemmArgs g{};
     g.A = x.data;
     g.lda = (int)x.stride[0];
@@ -139,7 +158,13 @@ int ssm_linear(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor 
     g.nseg = 1;
     g.residual = residual.data;
     g.ld_residual = residual.data ? (int)residual.stride[0] : 0;
-    return run_linear(g, M, N, K, workspace, static_cast<hipStream_t>(stream));
+    return run_linear(g, M, N, K, lw, workspace, s);
+}
+
+int ssm_linear(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M, int N, int K,
+               void *workspace, size_t workspace_bytes, void *stream)
+{
+    return ssm_linear_ex(x, weight, residual, out, M, N, K, 0, 0, 0, workspace, workspace_bytes, stream);
 }
 
 int ssm_rmsnorm(ssm_tensor x, ssm_tensor weight, ssm_tensor out, int M, int D, float eps, void *stream)
@@ -169,6 +194,7 @@ int ssm_rmsnorm(ssm_tensor x, ssm_tensor weight, ssm_tensor out, int M, int D, f
 // Workspace of one decode layer: the intermediates of the batch, each
 // 256-byte aligned, then the largest split-K partial buffer.
 struct LayerWs {
+    LinearWs in, xp, dtp, out;  // the four products
     size_t hn, x, z, u, dtl, B, C, dt, y, partial, total;
 };
 
@@ -187,14 +213,15 @@ static LayerWs layer_ws(const ssm_mamba1_layer *L, int batch)
     w.C = o; o += round_up(M * L->d_state * e);
     w.dt = o; o += round_up(M * L->d_inner * e);
     w.y = o; o += round_up(M * L->d_inner * e);
+    const int b = batch, R = L->dt_rank, N2 = L->dt_rank + 2 * L->d_state;
+    w.in = linear_ws(b, 2 * L->d_inner, ssm::plan_gemm(b, 2 * L->d_inner, L->d_model));
+    w.xp = linear_ws(b, N2, ssm::plan_gemm(b, N2, L->d_inner));
+    w.dtp = linear_ws(b, L->d_inner, ssm::plan_gemm(b, L->d_inner, R));
+    w.out = linear_ws(b, L->d_model, ssm::plan_gemm(b, L->d_model, L->d_inner));
+    size_t p = 0;
+    for (const LinearWs *lw : {&w.in, &w.xp, &w.dtp, &w.out})
+        p = lw->total > p ? lw->total : p;
     w.partial = o;
-    size_t p = linear_partial_bytes(batch, 2 * L->d_inner, L->d_model);
-    const size_t p2 = linear_partial_bytes(batch, L->dt_rank + 2 * L->d_state, L->d_inner);
-    const size_t p3 = linear_partial_bytes(batch, L->d_inner, L->dt_rank);
-    const size_t p4 = linear_partial_bytes(batch, L->d_model, L->d_inner);
-    if (p2 > p) p = p2;
-    if (p3 > p) p = p3;
-    if (p4 > p) p = p4;
     w.total = o + p;
     return w;
 }
@@ -281,7 +308,7 @@ int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, ssm_tensor hidden, ssm_te
     g.seg[0] = ssm::GemmSeg{x, Di, 0, Di};
     g.seg[1] = ssm::GemmSeg{z, Di, Di, Di};
     g.nseg = 2;
-    if ((st = run_linear(g, M, 2 * Di, Dm, part, s)) != SSM_OK)
+    if ((st = run_linear(g, M, 2 * Di, Dm, w.in, part, s)) != SSM_OK)
         return st;
     // 3. conv update + SiLU of x (the request's window in its slot)
     if ((st = status_of(ssm::launch_conv(ca, s))) != SSM_OK)
@@ -297,7 +324,7 @@ int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, ssm_tensor hidden, ssm_te
     g.seg[1] = ssm::GemmSeg{Bm, N, R, N};
     g.seg[2] = ssm::GemmSeg{Cm, N, R + N, N};
     g.nseg = 3;
-    if ((st = run_linear(g, M, R + 2 * N, Di, part, s)) != SSM_OK)
+    if ((st = run_linear(g, M, R + 2 * N, Di, w.xp, part, s)) != SSM_OK)
         return st;
     // 5. dt_proj -> dt (its bias goes in with the softplus of the update)
     g = ssm::GemmArgs{};
@@ -308,7 +335,7 @@ int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, ssm_tensor hidden, ssm_te
     g.ldw = R;
     g.seg[0] = ssm::GemmSeg{dt, Di, 0, Di};
     g.nseg = 1;
-    if ((st = run_linear(g, M, Di, R, part, s)) != SSM_OK)
+    if ((st = run_linear(g, M, Di, R, w.dtp, part, s)) != SSM_OK)
         return st;
     // 6. selective state update
     if ((st = status_of(ssm::launch_ssu(sa, s))) != SSM_OK)
@@ -325,7 +352,7 @@ int ssm_mamba1_decode_layer(const ssm_mamba1_layer *L, ssm_tensor hidden, ssm_te
     g.residual = hidden.data;
     g.ld_residual = (int)hidden.stride[0];
     g.row_slot = slot_idx;
-    return run_linear(g, M, Dm, Di, part, s);
+    return run_linear(g, M, Dm, Di, w.out, part, s);
 }
 
 namespace {

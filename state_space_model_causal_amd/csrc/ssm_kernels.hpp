@@ -135,6 +135,8 @@ struct GemmArgs {
     const void *W;           // [N, ldw], row-major
     int lda, ldw, M, N, K;
     int dtype;               // 1 f16, 2 bf16
+    int wr;                  // rows per wave: 16, 32 or 64
+    int cw;                  // column groups of 64 per workgroup (1 or 2; 4 waves each)
     int splits;              // K split over this many workgroups
     float *partial;          // [splits, M, N] float32 when splits > 1
     GemmSeg seg[3];
@@ -143,6 +145,14 @@ struct GemmArgs {
     int ld_residual;
     const int32_t *row_slot; // optional: rows with a negative entry are not written
 };
+// How a product is laid over the chip: rows per wave, column groups of 64
+// (a workgroup of 4 cw waves takes 4 wr rows x 64 cw columns) and K splits
+// (their float32 partial sums added by a second kernel).
+struct GemmPlan {
+    int wr, cw, splits;
+};
+// (rows_per_wave, cols, splits: 0 for the library's choice)
+GemmPlan plan_gemm(int M, int N, int K, int rows_per_wave = 0, int cols = 0, int splits = 0);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const float *w, void *out, int64_t ldo, int M, int D,
                           float eps, int dtype, hipStream_t stream);

@@ -63,6 +63,53 @@ def test_linear_parity(dev, ssm, M, N, K, dt, res):
     check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", f"linear {M}x{N}x{K}")
 
 
+# every plan the product kernel takes: rows per wave x columns per workgroup
+# x splits (partials added by the reduce kernel); ragged rows and columns,
+# N % 4 != 0
+PLAN_SHAPES = [(245, 10240, 2560), (245, 2560, 5120), (77, 200, 1000), (130, 70, 512)]
+PLANS = [(wr, c, sp) for wr in (16, 32, 64) for c in (64, 128) for sp in (1, 3, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", PLAN_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in PLAN_SHAPES])
+def test_linear_every_plan(dev, ssm, M, N, K):
+    """Each plan against the oracle on the same inputs, twice (bit-identical)."""
+    from oracle import layer
+
+    lib = ssm.load_library()
+    g = torch.Generator(device=dev).manual_seed(M + N + K)
+    x = torch.randn(M, K, generator=g, device=dev).to(torch.float16)
+    w = (torch.randn(N, K, generator=g, device=dev) / K ** 0.5).to(torch.float16)
+    r = torch.randn(M, N, generator=g, device=dev).to(torch.float16)
+    o, s = layer.linear(f(x), f(w), residual=f(r))
+    for wr, c, sp in PLANS:
+        need = lib.ssm_linear_workspace_ex(M, N, K, wr, c, sp)
+        ws = torch.full((max(need, 16) // 4,), -1, dtype=torch.int32, device=dev)
+        outs = []
+        for rep in range(2):
+            outs.append(ssm.linear(x, w, residual=r, workspace=ws, rows_per_wave=wr, cols=c, splits=sp))
+            torch.cuda.synchronize()
+            check(outs[-1], o, s, 3e-3, "f16", f"linear {M}x{N}x{K} wr={wr} cols={c} splits={sp} call {rep}")
+        assert torch.equal(outs[0], outs[1]), f"wr={wr} cols={c} splits={sp}: repeated call differs"
+
+
+def test_linear_plan_validation(dev, ssm):
+    lib = ssm.load_library()
+    assert lib.ssm_linear_workspace_ex(245, 2560, 5120, 128, 0, 0) == 0
+    assert lib.ssm_linear_workspace_ex(245, 2560, 5120, 48, 0, 0) == 0
+    assert lib.ssm_linear_workspace_ex(245, 2560, 5120, 0, 96, 0) == 0
+    assert lib.ssm_linear_workspace_ex(245, 2560, 5120, 0, 0, 81) == 0  # more splits than 64-k batches
+    x = torch.zeros(8, 64, dtype=torch.float16, device=dev)
+    w = torch.zeros(16, 64, dtype=torch.float16, device=dev)
+    out = torch.zeros(8, 16, dtype=torch.float16, device=dev)
+    T = ssm._tensor
+    code = {v: k for k, v in ssm.STATUS.items()}
+    call = lambda wr, c, sp: lib.ssm_linear_ex(T(x, "x"), T(w, "w"), T(None, "r"), T(out, "o"), 8, 16, 64,
+                                               wr, c, sp, None, 0, None)
+    assert call(128, 0, 0) == code["SSM_ERR_OUT_OF_RESOURCES"]
+    assert call(0, 256, 0) == code["SSM_ERR_OUT_OF_RESOURCES"]
+    assert call(16, 64, 2) == code["SSM_ERR_SHAPE"]  # more splits than the one 64-k batch
+
+
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
 def test_linear_unaligned_output(dev, ssm, dt):
     """An output (and residual) only 2-byte aligned: the main kernel's stores
@@ -84,17 +131,37 @@ def test_linear_unaligned_output(dev, ssm, dt):
     check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", "linear unaligned")
 
 
+# widths: one round of 128-bit loads per lane (520: a partial second round),
+# the 2.8B model's 2560, the largest vector width, and widths that take the
+# element-wise kernel (not a multiple of 8; past the vector form's limit)
+@pytest.mark.parametrize("D", [520, 2560, 8192, 100, 8200])
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
-def test_rmsnorm_parity(dev, ssm, dt):
+def test_rmsnorm_parity(dev, ssm, dt, D):
     from oracle import layer
 
     g = torch.Generator(device=dev).manual_seed(3)
-    x = (torch.randn(37, 2560, generator=g, device=dev) * 3).to(dt)
-    w = torch.rand(2560, generator=g, device=dev) + 0.5
+    x = (torch.randn(37, D, generator=g, device=dev) * 3).to(dt)
+    w = torch.rand(D, generator=g, device=dev) + 0.5
     out = ssm.rmsnorm(x, w, eps=1e-5)
     torch.cuda.synchronize()
     o, s = layer.rmsnorm(f(x), f(w), 1e-5)
-    check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", "rmsnorm")
+    check(out, o, s, 3e-3, "f16" if dt == torch.float16 else "bf16", f"rmsnorm D={D}")
+
+
+def test_rmsnorm_strided_rows(dev, ssm):
+    """Rows 4 elements apart from 8-aligned (the element-wise kernel) and a
+    view of every other row (the vector kernel), against the oracle."""
+    from oracle import layer
+
+    g = torch.Generator(device=dev).manual_seed(4)
+    w = torch.rand(512, generator=g, device=dev) + 0.5
+    for ld, rows in ((516, slice(None)), (1024, slice(None, None, 2))):
+        base = (torch.randn(21, ld, generator=g, device=dev) * 2).to(torch.float16)
+        x = base[:, :512] if rows == slice(None) else base.view(-1, 512)[rows]
+        out = ssm.rmsnorm(x, w, eps=1e-6)
+        torch.cuda.synchronize()
+        o, s = layer.rmsnorm(f(x), f(w), 1e-6)
+        check(out, o, s, 3e-3, "f16", f"rmsnorm ld={ld}")
 
 
 LAYER_CASES = [
