@@ -74,7 +74,7 @@ KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp", "ssm_kernels.
                   "conv1d_decode": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "conv1d_varlen": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "selective_scan_varlen": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
-                  "chunked_scan": ["ssd.hip", "ssm_kernels.hpp"],
+                  "chunked_scan": ["ssd.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "layer_decode": ["gemm.hip", "layer.hip", "conv1d.hip", "ssu.hip", "ssm_device.hpp",
                                    "ssm_kernels.hpp"]}
 # rocprofv3 kernel names of each headline kernel

@@ -13,7 +13,10 @@ reads their CSV output and writes the summaries under profiles/:
                batch of each shape;
   copy_*       the same two counters on a plain 1 GiB device copy, which
                calibrates them to bytes;
-  sq           SQ and GRBM counters of the selective scan (VALU issue).
+  sq           SQ and GRBM counters of the selective scan (VALU issue);
+  ssd          SQ, GRBM and L1->L2 request counters of the chunked Mamba-2
+               prefill (matrix-core work, LDS, the B/C stream into the L1s);
+  copy_l2      the L1->L2 read requests of the 1 GiB copy (bytes per request).
 """
 from __future__ import annotations
 
@@ -27,6 +30,8 @@ import bench
 
 SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES "
                "SQ_WAVE_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
+SSD_COUNTERS = ("SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_LDS "
+                "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE TCP_TCC_READ_REQ_sum")
 HEADLINE_LABELS = {"conv1d_prefill": "conv_rows_kernel", "selective_scan": "scan_kernel",
                    "decode_step": "ssu_"}
 
@@ -49,6 +54,9 @@ def profile_commands(out):
                                   cmd="python -u bench.py --copy-calibration")),
         ("sq", pmc.format(c=SQ_COUNTERS, o=out, n="sq",
                           cmd=f"{b} --only prefill --eager --timed-replays 1 --steps 3 --warmup 1")),
+        ("ssd", pmc.format(c=SSD_COUNTERS, o=out, n="ssd", cmd=f"{b} --only chunked --eager --timed-replays 1")),
+        ("copy_l2", pmc.format(c="TCP_TCC_READ_REQ_sum", o=out, n="copy_l2",
+                               cmd="python -u bench.py --copy-calibration")),
     ]
 
 
@@ -271,6 +279,38 @@ def summarize_profile(out):
                    "fetch_factor": f_factor, "write_factor": w_factor, "points": recs,
                    "commands": [cmds["trace"], cmds["ssu_fetch"], cmds["ssu_write"]]}, f, indent=1)
     _write("mamba2_state_update_kernels.md", S)
+
+    # ------------------------------------ chunked Mamba-2 prefill counters
+    ssd_glob = glob.glob(f"{out}/ssd/**/*counter_collection.csv", recursive=True) + \
+        glob.glob(f"{out}/ssd/*counter_collection.csv")
+    if ssd_glob:
+        cl2, _ = _mean_counters(_counters(_one(f"{out}/copy_l2/*counter_collection.csv")),
+                                lambda n: "copyBuffer" in n)
+        req_bytes = copy_bytes / cl2["TCP_TCC_READ_REQ_sum"] if cl2.get("TCP_TCC_READ_REQ_sum") else None
+        dc, ndc = _mean_counters(_counters(ssd_glob[0]), lambda nm: _library(nm) and "ssd_kernel" in nm)
+        ch = cfgs.get("chunked_prefill") or {}
+        ssd_us = _stat([d for ds in bym.get("chunked_prefill", {}).values() for d in ds])[1] \
+            if "chunked_prefill" in bym else None
+        flops = dc.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        cyc = dc.get("GRBM_GUI_ACTIVE", 0.0) / bench.N_XCD
+        l2l1 = dc.get("TCP_TCC_READ_REQ_sum", 0.0) * req_bytes if req_bytes else None
+        alg = ch.get("bytes")
+        rec = {"kernel": "chunked_prefill (ssd_kernel)",
+               "kernel_source_sha": bench.kernel_source_sha(bench.KERNEL_SOURCES["chunked_scan"]),
+               "counters": dc, "dispatches": ndc, "avg_launch_us_trace": ssd_us,
+               "mfma_flops_per_launch": flops,
+               "mfma_tflops_at_trace_time": flops / (ssd_us * 1e-6) / 1e12 if ssd_us else None,
+               "frac_of_bf16_dense_peak": flops / (ssd_us * 1e-6) / (bench.MFMA_BF16_PEAK_TFLOPS * 1e12)
+               if ssd_us else None,
+               "mfma_busy_per_simd_cycle": dc.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * bench.N_SIMD)
+               if cyc else None,
+               "valu_busy": dc.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (cyc * bench.N_SIMD) if cyc else None,
+               "lds_bank_conflict_per_cu_cycle": dc.get("SQ_LDS_BANK_CONFLICT", 0.0) / (cyc * 256) if cyc else None,
+               "l1_to_l2_read_bytes": l2l1, "bytes_per_l1_read_request": req_bytes,
+               "algorithmic_hbm_bytes": alg,
+               "commands": [cmds["ssd"], cmds["copy_l2"], cmds["trace"]]}
+        with open(os.path.join(bench.PROFILES, "mamba2_chunked_prefill_counters.json"), "w") as f:
+            json.dump(rec, f, indent=1)
 
     # ----------------------------------------- the other workloads' traces
     for labels, title, fname, rec in (
