@@ -146,7 +146,8 @@ int ssm_selective_scan(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, ssm_tens
  *         SSM_SCAN_CHUNKED: the chunked matrix form on the matrix cores.
  * The chunked form needs one decay per head (a_per_state == 0), bf16 I/O,
  * dstate 64, 128 or 256, headdim a multiple of 64, seqlen a multiple of 8,
- * 16-byte aligned rows and a dense [.., headdim, dstate] state slot;
+ * 16-byte aligned rows, B and C (request, group) planes spanning less than
+ * 4 GiB, and a dense [.., headdim, dstate] state slot;
  * otherwise SSM_SCAN_CHUNKED returns SSM_ERR_UNSUPPORTED.  SSM_SCAN_AUTO
  * takes it whenever it applies.  The chunked form computes the same
  * recurrence: over a chunk of steps with one scalar decay per step, the state

@@ -269,19 +269,22 @@ def test_tuned_table_entries_are_valid():
 def scan_ex(lib, algo, **kw):
     a = dict(u=FAKE, dt=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, st=None,
              idx=None, out=FAKE, batch=2, L=64, H=4, P=64, N=128, G=1, S=0, io=BF16, sd=F32, aps=0,
-             sp=1, init=0)
+             sp=1, init=0, bs=None)
     a.update(kw)
     Bt, L, H, P, N, G, io = a["batch"], a["L"], a["H"], a["P"], a["N"], a["G"], a["io"]
     return lib.ssm_selective_scan_ex(
         T(a["u"], io, (Bt, H * P, L)), T(a["dt"], io, (Bt, H, L)), T(a["bias"], F32, (H,)),
-        T(a["A"], F32, (H, N) if a["aps"] else (H,)), T(a["B"], io, (Bt, G, N, L)),
+        T(a["A"], F32, (H, N) if a["aps"] else (H,)), T(a["B"], io, (Bt, G, N, L), a["bs"]),
         T(a["C"], io, (Bt, G, N, L)), T(a["D"], F32, (H,)), T(a["z"], io, (Bt, H * P, L)),
         T(a["st"], a["sd"], (a["S"], H, P, N)), a["idx"], T(a["out"], io, (Bt, H * P, L)), Bt, L,
         H, P, N, G, a["S"], a["aps"], a["sp"], a["init"], algo, None)
 
 
+# (the last case: B's states 2^25 elements apart, so a (request, group) plane
+# spans more than the chunked kernel's 32-bit byte offsets reach)
 @pytest.mark.parametrize("kw", [dict(aps=1, N=16), dict(io=F16), dict(io=F32), dict(N=96),
-                                dict(P=32), dict(L=60), dict(u=FAKE + 2)])
+                                dict(P=32), dict(L=60), dict(u=FAKE + 2),
+                                dict(bs=(128 << 25, 128 << 25, 1 << 25, 1))])
 def test_scan_chunked_refuses_unsupported_shapes(lib, kw):
     # the chunked form is asked for explicitly where it does not apply: the
     # call fails before anything is launched (fake pointers are never touched)
