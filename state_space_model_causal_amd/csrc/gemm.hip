@@ -7,21 +7,22 @@
 // skinny product: out[M, N] = act[M, K] . W[N, K]^T with M = the number of
 // requests (245 on the pages' concurrency test), K and N the layer widths.
 //
-// Kernel: one 256-lane workgroup per (64 output columns, 4 WR rows, slice of
-// K), WR = 64, 32 or 16 rows per wave.  Wave w owns rows [WR w, WR w + WR) of
-// the block and all 64 columns: WR/16 x 4 tiles of
-// v_mfma_f32_16x16x32_{f16,bf16}, float32 accumulation.  K is walked in
-// batches of 64: each batch's activation tile (4 WR rows x 64 k) and weight
-// tile (64 rows x 64 k) are loaded once per workgroup with coalesced 128-bit
-// loads (consecutive lanes, consecutive 16 bytes of a row) and staged in LDS,
-// from where each wave reads its MFMA operands (8 consecutive k of one row:
-// row-major, k innermost is the operand order).  The next batch's loads are
-// in flight during the current batch's MFMAs.  The weights, the dominant
-// traffic, stream from HBM once (the row blocks of one column tile run on one
-// XCD and share its L2; the activations, 2.6 MB at most, stay in L2).
-// Narrow outputs split K over several workgroups.  Their float32 partial sums
-// are added by the last split of each tile to finish (a counter per tile), or,
-// where that would be a long serial tail, by a second kernel.
+// Kernel: one workgroup of 4 CW waves per (64 CW output columns, 4 WR rows,
+// slice of K), WR = 64, 32 or 16 rows per wave and CW = 1 or 2 column groups.
+// Wave w owns rows [WR (w % 4), + WR) of the block and the 64 columns of
+// group w / 4: WR/16 x 4 tiles of v_mfma_f32_16x16x32_{f16,bf16}, float32
+// accumulation.  K is walked in batches of 64: each batch's activation tile
+// (4 WR rows x 64 k) and weight tile (64 CW rows x 64 k) are loaded once per
+// workgroup with coalesced 128-bit loads (consecutive lanes, consecutive 16
+// bytes of a row) and staged in LDS, from where each wave reads its MFMA
+// operands (8 consecutive k of one row: row-major, k innermost is the operand
+// order).  Two batches' loads are in flight during the MFMAs.  The weights,
+// the dominant traffic, stream from HBM once (the row blocks of one column
+// tile run on one XCD and share its L2; the activations, 2.6 MB at most, stay
+// in L2).
+// Narrow outputs split K over several workgroups, whose float32 partial sums
+// a second kernel adds.  The plan (rows per wave, columns per workgroup,
+// splits) comes from plan_gemm's traffic model.
 //
 // Epilogue: output columns go to up to three destinations (column segments,
 // e.g. the x and z halves of in_proj), optionally added to a residual, rows

@@ -29,10 +29,12 @@
 // stages B and C in LDS as stored ([state][step]; the operands that need them
 // transposed use gfx950's transpose reads), builds the masked decay matrix
 // once for all waves, then every wave computes its share of the outputs and
-// updates its part of the state.  Two waves per SIMD let
-// one wave's vector work overlap the other's matrix work.  HBM traffic: u,
-// dt, z, B, C read once (B and C from L2 for every head of a group), out
-// written once, the state read and written once.
+// updates its part of the state.  Two waves per SIMD let one wave's vector
+// work overlap the other's matrix work.  The next chunk's loads are issued in
+// three parts between the phases, and two barriers per chunk suffice (the
+// staged tiles' last readers precede the second).  HBM traffic: u, dt, z, B,
+// C read once (B and C from L2 for every head of a group), out written once,
+// the state read and written once.
 #include <algorithm>
 
 #include "ssm_device.hpp"
