@@ -368,6 +368,10 @@ int ssm_linear(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor 
                int N, int K, void *workspace, size_t workspace_bytes, void *stream);
 size_t ssm_linear_workspace_ex(int M, int N, int K, int rows_per_wave, int cols_per_workgroup,
                                int splits);
+/* The plan ssm_linear takes for a shape (each output may be NULL);
+ * SSM_ERR_SHAPE for M, N < 1 or K < 8. */
+int ssm_linear_plan(int M, int N, int K, int *rows_per_wave, int *cols_per_workgroup,
+                    int *splits);
 int ssm_linear_ex(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M,
                   int N, int K, int rows_per_wave, int cols_per_workgroup, int splits,
                   void *workspace, size_t workspace_bytes, void *stream);

@@ -39,7 +39,7 @@ _DTYPE_CODE = {torch.float32: SSM_F32, torch.float16: SSM_F16, torch.bfloat16: S
 EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_selective_scan_ex", "ssm_state_update",
             "ssm_state_update_ex", "ssm_state_update_config",
             "ssm_decode_step", "ssm_causal_conv1d_varlen", "ssm_selective_scan_varlen",
-            "ssm_linear", "ssm_linear_workspace", "ssm_linear_ex", "ssm_linear_workspace_ex",
+            "ssm_linear", "ssm_linear_workspace", "ssm_linear_ex", "ssm_linear_workspace_ex", "ssm_linear_plan",
             "ssm_rmsnorm", "ssm_mamba1_decode_layer",
             "ssm_mamba1_decode_layer_workspace", "ssm_mamba1_decode_layer_noalloc",
             "ssm_status_string", "ssm_abi_version")
@@ -125,6 +125,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_linear_workspace_ex.restype = Z
     lib.ssm_linear_ex.argtypes = [T, T, T, T, I, I, I, I, I, I, P, Z, P]
     lib.ssm_linear_ex.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.ssm_linear_plan.argtypes = [I, I, I, IP, IP, IP]
+    lib.ssm_linear_plan.restype = I
     lib.ssm_rmsnorm.argtypes = [T, T, T, I, I, ctypes.c_float, P]
     lib.ssm_rmsnorm.restype = I
     lib.ssm_mamba1_decode_layer_workspace.argtypes = [P, I]
@@ -374,6 +377,15 @@ def linear(x, weight, residual=None, out=None, workspace=None, stream=None, rows
     return out
 
 
+def linear_plan(M, N, K):
+    """ssm_linear_plan: (rows per wave, columns per workgroup, splits) that
+    ssm_linear takes for the shape."""
+    r, c, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check("ssm_linear_plan", load_library().ssm_linear_plan(M, N, K, ctypes.byref(r), ctypes.byref(c),
+                                                             ctypes.byref(s)))
+    return r.value, c.value, s.value
+
+
 def rmsnorm(x, weight, eps=1e-5, out=None, stream=None):
     """ssm_rmsnorm over the last dimension of x [M, D]."""
     M, D = x.shape
@@ -432,7 +444,7 @@ def mamba1_decode_layer_noalloc(layer, hidden, conv_state, ssm_state, slot_idx=N
     return hidden
 
 
-__all__ = ["Tensor", "linear", "mamba1_decode_layer_noalloc", "rmsnorm", "mamba1_layer", "mamba1_decode_layer", "Mamba1Layer",
+__all__ = ["Tensor", "linear", "linear_plan", "mamba1_decode_layer_noalloc", "rmsnorm", "mamba1_layer", "mamba1_decode_layer", "Mamba1Layer",
            "causal_conv1d", "selective_scan", "state_update", "state_update_config",
            "LaunchConfig", "decode_step", "SCAN_AUTO", "SCAN_RECURRENT", "SCAN_CHUNKED",
            "causal_conv1d_varlen", "selective_scan_varlen", "load_library",

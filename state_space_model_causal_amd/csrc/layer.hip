@@ -130,6 +130,20 @@ size_t ssm_linear_workspace_ex(int M, int N, int K, int rows_per_wave, int cols_
 
 size_t ssm_linear_workspace(int M, int N, int K) { return ssm_linear_workspace_ex(M, N, K, 0, 0, 0); }
 
+int ssm_linear_plan(int M, int N, int K, int *rows_per_wave, int *cols_per_workgroup, int *splits)
+{
+    if (M < 1 || N < 1 || K < 8)
+        return SSM_ERR_SHAPE;
+    const ssm::GemmPlan plan = ssm::plan_gemm(M, N, K);
+    if (rows_per_wave)
+        *rows_per_wave = plan.wr;
+    if (cols_per_workgroup)
+        *cols_per_workgroup = 64 * plan.cw;
+    if (splits)
+        *splits = plan.splits;
+    return SSM_OK;
+}
+
 int ssm_linear_ex(ssm_tensor x, ssm_tensor weight, ssm_tensor residual, ssm_tensor out, int M, int N, int K,
                   int rows_per_wave, int cols_per_workgroup, int splits, void *workspace, size_t workspace_bytes,
                   void *stream)

@@ -356,6 +356,23 @@ def test_linear_and_rmsnorm_validation(lib):
     assert g(M=0) == 0
 
 
+def test_linear_plan_query(lib):
+    # the plan ssm_linear takes, reported on the host; its workspace is the
+    # one ssm_linear asks for, and every reported plan is one ssm_linear_ex takes
+    import ctypes
+
+    import state_space_model_causal_amd as ssm
+
+    for M, N, K in ((245, 10240, 2560), (245, 192, 5120), (245, 5120, 160), (245, 2560, 5120),
+                    (1, 64, 32), (7, 100, 40), (300, 130, 264)):
+        wr, c, sp = ssm.linear_plan(M, N, K)
+        assert wr in (16, 32, 64) and c in (64, 128) and 1 <= sp <= min(32, (K + 63) // 64)
+        assert lib.ssm_linear_workspace_ex(M, N, K, wr, c, sp) == lib.ssm_linear_workspace(M, N, K)
+    out = ctypes.c_int()
+    assert lib.ssm_linear_plan(0, 64, 32, None, None, None) == SHAPE
+    assert lib.ssm_linear_plan(4, 64, 4, ctypes.byref(out), None, None) == SHAPE
+
+
 def test_noalloc_layer_scratch_limit(lib):
     # the documented limit: the Mamba-2.8B layer's workspace fits the 64 MiB
     # array up to 687 requests; beyond, the call is refused before any HIP call
