@@ -13,7 +13,9 @@ reads their CSV output and writes the summaries under profiles/:
                batch of each shape;
   copy_*       the same two counters on a plain 1 GiB device copy, which
                calibrates them to bytes;
-  sq           SQ and GRBM counters of the selective scan (VALU issue);
+  sq           SQ and GRBM counters of the headline kernels (VALU issue of the
+               scan, and how much of the conv's and the decode step's time
+               their vector work fills);
   ssd          SQ, GRBM and L1->L2 request counters of the chunked Mamba-2
                prefill (matrix-core work, LDS, the B/C stream into the L1s);
   copy_l2      the L1->L2 read requests of the 1 GiB copy (bytes per request).
@@ -53,7 +55,7 @@ def profile_commands(out):
         ("copy_write", pmc.format(c="WRITE_SIZE", o=out, n="copy_write",
                                   cmd="python -u bench.py --copy-calibration")),
         ("sq", pmc.format(c=SQ_COUNTERS, o=out, n="sq",
-                          cmd=f"{b} --only prefill --eager --timed-replays 1 --steps 3 --warmup 1")),
+                          cmd=f"{b} --only headline --eager --timed-replays 1 --steps 3 --warmup 1")),
         ("ssd", pmc.format(c=SSD_COUNTERS, o=out, n="ssd", cmd=f"{b} --only chunked --eager --timed-replays 1")),
         ("copy_l2", pmc.format(c="TCP_TCC_READ_REQ_sum", o=out, n="copy_l2",
                                cmd="python -u bench.py --copy-calibration")),
@@ -244,6 +246,22 @@ def summarize_profile(out):
         with open(os.path.join(bench.PROFILES, "selective_scan_counters.json"), "w") as f:
             json.dump({"kernel": "selective_scan", "kernel_source_sha": scan_sha,
                        "counters": sc, "dispatches": nsc, "command": cmds["sq"]}, f, indent=1)
+    # the other two headline kernels from the same pass: how much of their
+    # (memory-bound) time their vector work fills
+    others = {}
+    for k, sym in (("conv1d_prefill", "conv_rows_kernel"), ("decode_step", "ssu_")):
+        oc, noc = _mean_counters(sq, lambda nm, sym=sym: _library(nm) and sym in nm)
+        k_us = _stat([d for nm, ds in bym.get(k, {}).items() if sym in nm for d in ds])[1] if k in bym else None
+        vi = bench.valu_issue(oc, k_us) if oc else None
+        if vi:
+            others[k] = {"kernel_source_sha": kern.get(k, {}).get("kernel_source_sha"), "counters": oc,
+                         "dispatches": noc, "avg_launch_us_trace": k_us, **vi}
+            L.append(f"- {k}: {oc['SQ_INSTS_VALU'] / max(oc.get('SQ_WAVES', 1), 1):.0f} VALU instructions per wave; "
+                     f"VALU issue {vi.get('frac_at_counted_clock', float('nan')):.3f} of the SIMD cycles, "
+                     f"busy {vi.get('valu_busy', float('nan')):.3f} (mean over {noc} dispatches)")
+    if others:
+        with open(os.path.join(bench.PROFILES, "headline_valu_counters.json"), "w") as f:
+            json.dump({"kernels": others, "command": cmds["sq"]}, f, indent=1)
     _write("mamba1_layer_step_kernels.md", L)
 
     # --------------------------------------------- Mamba-2 state updates
