@@ -54,15 +54,26 @@ __device__ __forceinline__ f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// x = hi + lo with hi, lo in bfloat16 (relative error of the pair ~2^-16)
+// a = ha + la and b = hb + lb with the four parts in bfloat16 (relative
+// error of a pair ~2^-16): the high parts are a and b rounded (one packed
+// conversion), the remainders are exact in float32 before their own rounding
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    hi = pk_bf16(a, b);
+    // the low half moved up by a byte permute (a shift there is rewritten
+    // into a second conversion of a alone)
+    const float ha = __uint_as_float(__builtin_amdgcn_perm(0u, hi, 0x01000c0cu));
+    lo = pk_bf16(a - ha, b - __uint_as_float(hi & 0xffff0000u));
+}
+
 __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8_t &hi, bf16x8_t &lo)
 {
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)x[i];
-        hi[i] = h;
-        lo[i] = (__bf16)(x[i] - (float)h);
-    }
+    for (int i = 0; i < 4; ++i)
+        split_pair(x[2 * i], x[2 * i + 1], h[i], l[i]);
+    hi = __builtin_bit_cast(bf16x8_t, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8_t, u32x4{l[0], l[1], l[2], l[3]});
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8_t, w); }
@@ -297,8 +308,10 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             load_pairs<N>(cur.c0, cur.c1, t0 + SQ, L, Cg, a.C_sn, tid);
 
         // ---- carried state over this wave's half of the states:
-        // yc[st] = sum_{n in half} C_s[n] H[p][n]; the state as MFMA operands
-        // (high and low parts) in the order the accumulators hold it
+        // yc[k] = sum_{n in half} C_s[n] H[p][n] over the steps s of row tile
+        // st = (k + 2 (1 - nh)) % 4: the partner's two output tiles first
+        // (k = 0, 1), then this wave's own (k = 2, 3); the state as MFMA
+        // operands (high and low parts) in the order the accumulators hold it
         f32x4_t yc[4];
         {
             bf16x8_t hh[NTH / 2], hl[NTH / 2];
@@ -313,7 +326,8 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 split_bf16(hv, hh[q2], hl[q2]);
             }
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int k = 0; k < 4; ++k) {
+                const int st = (k + 2 * (1 - nh)) & 3;
                 f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int q2 = 0; q2 < NTH / 2; ++q2) {
@@ -325,12 +339,11 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                     acc = mma(cv, hh[q2], acc);
                     acc = mma(cv, hl[q2], acc);
                 }
-                yc[st] = acc;
+                yc[k] = acc;
             }
-            // the partner needs this half for its output row tiles (selects,
-            // not a register array indexed at run time)
-            *reinterpret_cast<f32x4_t *>(&s_x[partner][0][l][0]) = nh ? yc[0] : yc[2];
-            *reinterpret_cast<f32x4_t *>(&s_x[partner][1][l][0]) = nh ? yc[1] : yc[3];
+            // the partner needs this half for its output row tiles
+            *reinterpret_cast<f32x4_t *>(&s_x[partner][0][l][0]) = yc[0];
+            *reinterpret_cast<f32x4_t *>(&s_x[partner][1][l][0]) = yc[1];
         }
 
         // the gate of this wave's outputs, computed here where the matrix
@@ -340,8 +353,12 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         for (int i = 0; i < 2; ++i) {
             const float zv[4] = {bf_lo(zo[i].x), bf_hi(zo[i].x), bf_lo(zo[i].y), bf_hi(zo[i].y)};
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
                 gz[i][j] = zrow ? silu_f32(zv[j]) : 1.0f;
+                // pinned here: left alone, the compiler sinks the gate into
+                // the output phase, where nothing overlaps it
+                asm volatile("" ::"v"(gz[i][j]));
+            }
         }
 
         if (more)
@@ -373,16 +390,15 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                     const float4 Lr = *reinterpret_cast<const float4 *>(&s_L[r0]);
                     const float4 dr = *reinterpret_cast<const float4 *>(&s_d[r0]);
                     const float lr[4] = {Lr.x, Lr.y, Lr.z, Lr.w}, dv[4] = {dr.x, dr.y, dr.z, dr.w};
-                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                    bf16x4_t mh, ml;
+                    float m[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float m = (r0 + j <= s) ? acc[j] * exp2_hw(Ls - lr[j]) * dv[j] : 0.0f;
-                        mh[j] = (__bf16)m;
-                        ml[j] = (__bf16)(m - (float)mh[j]);
-                    }
-                    *reinterpret_cast<bf16x4_t *>(&s_mh[s * LDQ + r0]) = mh;
-                    *reinterpret_cast<bf16x4_t *>(&s_ml[s * LDQ + r0]) = ml;
+                    for (int j = 0; j < 4; ++j)
+                        m[j] = (r0 + j <= s) ? acc[j] * exp2_hw(Ls - lr[j]) * dv[j] : 0.0f;
+                    uint32_t mh[2], ml[2];
+                    split_pair(m[0], m[1], mh[0], ml[0]);
+                    split_pair(m[2], m[3], mh[1], ml[1]);
+                    *reinterpret_cast<uint2 *>(&s_mh[s * LDQ + r0]) = uint2{mh[0], mh[1]};
+                    *reinterpret_cast<uint2 *>(&s_ml[s * LDQ + r0]) = uint2{ml[0], ml[1]};
                 }
             }
         }
@@ -447,14 +463,11 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const f32x4_t mine = i ? (nh ? yc[3] : yc[1]) : (nh ? yc[2] : yc[0]);
+                    const f32x4_t mine = yc[2 + i];
                     const float v = y[j] + el[j] * (mine[j] + other[j]) + Dh * xv[j];
                     o[j] = v * gz[i][j];
                 }
-                uint2 ov;
-                ov.x = (uint32_t)from_f32<bf16>(o[0]).bits | ((uint32_t)from_f32<bf16>(o[1]).bits << 16);
-                ov.y = (uint32_t)from_f32<bf16>(o[2]).bits | ((uint32_t)from_f32<bf16>(o[3]).bits << 16);
-                *reinterpret_cast<uint2 *>(orow + t) = ov;
+                *reinterpret_cast<uint2 *>(orow + t) = uint2{pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
             }
         }
     }

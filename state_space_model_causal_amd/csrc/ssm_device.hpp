@@ -29,18 +29,21 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 // v_cvt_f16_f32 rounds to nearest even in the default mode.
 template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }
-// Round to nearest even on the bit pattern; NaN stays a quiet NaN.
+// Round to nearest even: gfx950 converts in hardware (v_cvt_pk_bf16_f32,
+// which keeps NaNs NaN and, with float32 denormals on, rounds denormals too).
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v)
 {
-    uint32_t u = __float_as_uint(v);
     bf16 r;
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-        r.bits = (uint16_t)((u >> 16) | 0x40u);
-    } else {
-        u += 0x7fffu + ((u >> 16) & 1u);
-        r.bits = (uint16_t)(u >> 16);
-    }
+    r.bits = __builtin_bit_cast(uint16_t, (__bf16)v);
     return r;
+}
+
+// Two floats rounded to bf16 in one conversion, a in the low half.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Unpack one 32-bit word holding 1 (f32) or 2 (f16/bf16) elements.
@@ -66,10 +69,7 @@ __device__ __forceinline__ uint32_t pack_word(const float *src, f16)
     c.h[1] = (f16)src[1];
     return c.u;
 }
-__device__ __forceinline__ uint32_t pack_word(const float *src, bf16)
-{
-    return (uint32_t)from_f32<bf16>(src[0]).bits | ((uint32_t)from_f32<bf16>(src[1]).bits << 16);
-}
+__device__ __forceinline__ uint32_t pack_word(const float *src, bf16) { return pk_bf16(src[0], src[1]); }
 
 template <typename T> struct PerWord { static constexpr int value = 4 / StorageSize<T>::value; };
 

@@ -420,6 +420,45 @@ def test_softplus_step_accuracy(dev, ssm, oracle, io):
     assert not bad.any(), (f(dt).ravel()[bad][:5], got[bad][:5], want[bad][:5])
 
 
+def _bf16_rounding_cases(rng, n):
+    """float32 bit patterns that exercise round-to-nearest-even into bfloat16:
+    exact ties (odd and even), one below and one above a tie, subnormals,
+    values that round up to infinity, random patterns, and +-inf and NaN."""
+    top = rng.integers(0, 1 << 16, n, dtype=np.uint64)
+    top = np.where((top & 0x7f80) == 0x7f80, top & 0x807f, top)  # finite
+    low = np.array([0x8000, 0x7fff, 0x8001, 0x0000], dtype=np.uint64)[np.arange(n) % 4]
+    bits = (top << 16) | low
+    sub = rng.integers(1, 1 << 23, n // 8, dtype=np.uint64)  # float32 subnormals
+    bits[: n // 8] = sub | (np.uint64(0x80000000) * (sub & 1))
+    bits[n // 8: n // 4] = rng.integers(0, 0x7f800000, n // 8, dtype=np.uint64)
+    bits[-6:] = [0x7f7fffff, 0xff7f8000, 0x7f800000, 0xff800000, 0x7fc00001, 0xffa00000]
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def test_bf16_state_rounding_is_rne(dev, ssm, oracle):
+    """The stored bfloat16 state is the float32 state rounded to nearest even,
+    bit for bit.  A one-step scan with step size 1, B = 1 and a decay of 0
+    (A = -1e30) leaves exactly u in the state, so the cache holds
+    round(u) over the crafted patterns; NaN stays NaN."""
+    n, N = 4096, 16
+    u_np = _bf16_rounding_cases(np.random.default_rng(5), n)
+    u = torch.from_numpy(u_np.copy()).view(1, n, 1).to(dev)
+    dt = torch.ones(1, n, 1, dtype=torch.float32, device=dev)
+    A = torch.full((n, N), -1e30, dtype=torch.float32, device=dev)
+    Bm = torch.ones(1, 1, N, 1, dtype=torch.float32, device=dev)
+    Cm = torch.zeros(1, 1, N, 1, dtype=torch.float32, device=dev)
+    state = torch.zeros(1, n, 1, N, dtype=torch.bfloat16, device=dev)
+    slot = torch.zeros(1, dtype=torch.int32, device=dev)
+    ssm.selective_scan(u, dt, A, Bm, Cm, dt_softplus=False, ssm_state=state, slot_idx=slot)
+    torch.cuda.synchronize()
+    got = state.float().cpu().numpy().reshape(n, N).astype(np.float64)
+    want = oracle.round_to(u_np.astype(np.float64), 2)
+    nan = np.isnan(want)
+    assert (np.isnan(got[nan]).all()), "NaN not kept"
+    ok = got[~nan] == want[~nan][:, None]
+    assert ok.all(), (u_np[~nan][~ok.all(1)][:5], got[~nan][~ok.all(1)][:5, 0], want[~nan][~ok.all(1)][:5])
+
+
 # ------------------------------------------------------- fused decode step
 DECODE_CASES = [
     ("m1_f16_f32state", dict(seqlen=1, nheads=300, dstate=16, io="f16", state="f32", batch=7,
