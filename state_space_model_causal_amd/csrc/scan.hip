@@ -12,8 +12,10 @@
 //     All 16 channels belong to one (request, group), so they share one B/C
 //     stream, which is staged once per tile in LDS and read by all of them.
 //   * The sequence is walked in tiles of 16 K timesteps; lane r of a channel
-//     owns timesteps [K r, K r + K) of the tile (K = 16 for dense batches,
-//     8 for packed ones; one to four 128-bit loads of u, dt and z).
+//     owns timesteps [K r, K r + K) of the tile (K = 16: 128-bit loads of u,
+//     dt and z).  In packed batches each sequence ends in shorter tiles
+//     (K = 8, then 4: 64-bit loads for 2-byte types), so that it pads its
+//     last tile by fewer than 64 steps.
 //   * For each state n, every lane reduces its K steps to one affine map
 //     h -> a*h + b (a = product of decays, b = local state from zero), the 16
 //     maps of a row are combined by an inclusive Hillis-Steele scan with DPP
@@ -34,8 +36,7 @@ namespace ssm {
 
 namespace {
 constexpr int R = 16;        // lanes per channel
-constexpr int KD = 16;       // timesteps per lane per tile: dense batches
-constexpr int KP = 8;        // packed batches (half the padding at each sequence's last tile)
+constexpr int KD = 16;       // timesteps per lane per tile (the last tiles of a packed sequence: 8, 4)
 constexpr int CPB = 256 / R; // channels per workgroup
 constexpr int NC = 16;       // states per LDS chunk of B/C
 } // namespace
@@ -74,13 +75,16 @@ __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, i
     }
 }
 
-// Raw 128-bit loads of timesteps [tl, tl+K) of one row (VEC rows only),
-// issued back to back; widen() converts them once they are needed.
+// Raw vector loads of timesteps [tl, tl+K) of one row (VEC rows only),
+// issued back to back; widen() converts them once they are needed.  A lane's
+// K steps are 128-bit vectors, or one 64-bit vector when they are narrower
+// (4 steps of a 2-byte type).
 template <typename TI, int K>
 struct RawSteps {
-    static constexpr int E = 16 / StorageSize<TI>::value;
+    static constexpr int VB = K * StorageSize<TI>::value >= 16 ? 16 : K * StorageSize<TI>::value;
+    static constexpr int E = VB / StorageSize<TI>::value;  // elements per vector
     static constexpr int NV = K / E;
-    u32x4 w[NV];
+    u32x4 w[NV];  // a 64-bit vector in .x and .y
     bool ok[NV];
 };
 
@@ -91,7 +95,13 @@ __device__ __forceinline__ void load_raw(RawSteps<TI, K> &r, const TI *__restric
     for (int v = 0; v < RawSteps<TI, K>::NV; ++v) {
         const int off = tl + v * RawSteps<TI, K>::E;
         r.ok[v] = off < hi;
-        r.w[v] = *reinterpret_cast<const u32x4 *>(row + (r.ok[v] ? off : 0));
+        const TI *p = row + (r.ok[v] ? off : 0);
+        if constexpr (RawSteps<TI, K>::VB == 16) {
+            r.w[v] = *reinterpret_cast<const u32x4 *>(p);
+        } else {
+            const uint2 q = *reinterpret_cast<const uint2 *>(p);
+            r.w[v] = u32x4{q.x, q.y, 0u, 0u};
+        }
     }
 }
 
@@ -108,8 +118,10 @@ __device__ __forceinline__ void widen(const RawSteps<TI, K> &r, float (&dst)[K])
         float part[E];
         unpack_word(r.w[v].x, &part[0 * PW], TI{});
         unpack_word(r.w[v].y, &part[1 * PW], TI{});
-        unpack_word(r.w[v].z, &part[2 * PW], TI{});
-        unpack_word(r.w[v].w, &part[3 * PW], TI{});
+        if constexpr (RawSteps<TI, K>::VB == 16) {
+            unpack_word(r.w[v].z, &part[2 * PW], TI{});
+            unpack_word(r.w[v].w, &part[3 * PW], TI{});
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e)
             dst[v * E + e] = part[e];
@@ -122,8 +134,8 @@ __device__ __forceinline__ void widen(const RawSteps<TI, K> &r, float (&dst)[K])
 template <typename TI, bool VEC, int K>
 __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int lo, int hi, const float (&src)[K])
 {
-    constexpr int E = 16 / StorageSize<TI>::value;
     if constexpr (VEC) {
+        constexpr int E = RawSteps<TI, K>::E, PW = PerWord<TI>::value;
 #pragma unroll
         for (int v = 0; v < K / E; ++v) {
             const int off = tl + v * E;
@@ -132,7 +144,10 @@ __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int lo
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     part[e] = src[v * E + e];
-                store_vec_cached<TI, E>(row + off, part);
+                if constexpr (RawSteps<TI, K>::VB == 16)
+                    store_vec_cached<TI, E>(row + off, part);
+                else
+                    *reinterpret_cast<uint2 *>(row + off) = uint2{pack_word(&part[0], TI{}), pack_word(&part[PW], TI{})};
             } else if (off + E > lo && off < hi) {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
@@ -150,13 +165,11 @@ __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int lo
 
 // Register budget: with 16 steps per lane the float16 vector paths (except
 // per-state decays over several state chunks) fit three waves per SIMD (at
-// most 168 VGPRs) without spilling, and the other variants are allowed two;
-// 8 steps per lane take about half the registers of the per-step arrays.
-template <typename TI, bool VEC, bool A_PER_STATE, bool ONE_CHUNK, int K>
+// most 168 VGPRs) without spilling, and the other variants are allowed two.
+template <typename TI, bool VEC, bool A_PER_STATE, bool ONE_CHUNK>
 constexpr int scan_waves_per_simd()
 {
-    return (std::is_same<TI, f16>::value && VEC && (ONE_CHUNK || !A_PER_STATE)) ? (K == KP ? 5 : 3)
-                                                                                    : (K == KP ? 3 : 2);
+    return (std::is_same<TI, f16>::value && VEC && (ONE_CHUNK || !A_PER_STATE)) ? 3 : 2;
 }
 
 // Packed batches of at most 256 sequences: the sequence of rank r when the
@@ -188,18 +201,17 @@ __device__ __forceinline__ int packed_seq_of_rank(const int32_t *__restrict__ cu
     return s_pick;
 }
 
-template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK, int K>
+template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK, bool PACKED>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, VEC, A_PER_STATE, ONE_CHUNK, K>())))
+__attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, VEC, A_PER_STATE, ONE_CHUNK>())))
 void scan_kernel(ScanArgs a)
 {
-    constexpr int T = R * K;  // timesteps per tile
-    constexpr int E = 16 / StorageSize<TI>::value;
+    constexpr int E = 16 / StorageSize<TI>::value;  // elements per 128-bit vector
     // B/C chunk in a lane-interleaved layout: the float4 holding timesteps
-    // [16r + 4q, 16r + 4q + 4) of local state nl sits at (nl*(K/4) + q)*R + r,
+    // [K r + 4q, K r + 4q + 4) of local state nl sits at (nl*(K/4) + q)*R + r,
     // so the 16 lanes of a row read 16 consecutive float4s (no bank conflict).
-    __shared__ float4 lds_b[NC * T / 4];
-    __shared__ float4 lds_c[NC * T / 4];
+    __shared__ float4 lds_b[NC * R * KD / 4];
+    __shared__ float4 lds_c[NC * R * KD / 4];
     // per channel and state: the state entering the current tile (the carry)
     // and A*log2(e); lane 0 of the row reads and rewrites the carry once per
     // tile, all 16 lanes read A*log2(e) (an LDS broadcast)
@@ -219,10 +231,9 @@ void scan_kernel(ScanArgs a)
     const int bg = (int)(lb / nblk_g);
     const int g = bg % a.ngroups;
     int b = bg / a.ngroups;
-    if constexpr (K == KP) {
-        // packed batches (the only ones with 8 steps per lane): the longest
-        // sequences' workgroups start first, so the longest walks do not
-        // begin late and leave the chip idle at the end
+    if constexpr (PACKED) {
+        // the longest sequences' workgroups start first, so the longest walks
+        // do not begin late and leave the chip idle at the end
         if (a.batch <= 256)
             b = packed_seq_of_rank(a.cu_seqlens, a.batch, L, b);
     }
@@ -261,7 +272,10 @@ void scan_kernel(ScanArgs a)
             lds_a2[ch][n] = a.A[h * a.A_sh + n] * kLog2e;
     }
 
-    for (int t0 = 0; t0 < hi; t0 += T) {
+    // One tile: 16 lanes x K steps per channel, starting at column t0.
+    auto tile = [&](auto kc, const int t0) {
+        constexpr int K = decltype(kc)::value;
+        constexpr int T = R * K;  // timesteps per tile
         const int tl = t0 + r * K;
         // a tile whose every step lies in the sequence needs no masking
         // (uniform over the workgroup; most tiles of a dense batch)
@@ -448,6 +462,22 @@ void scan_kernel(ScanArgs a)
         }
         if (active)
             store_steps<TI, VEC, K>(orow, tl, lo, hi, y);
+    };
+    if constexpr (PACKED) {
+        // Each sequence pads its last tile to a tile boundary.  Tiles of 16
+        // steps per lane while more than 3/4 of one remains, then of 8 while
+        // more than 64 steps remain, then one of 4: under 64 padded steps
+        // per sequence, and the dense per-step cost for the rest.
+        int t0 = 0;
+        for (; hi - t0 > 3 * R * KD / 4; t0 += R * KD)
+            tile(std::integral_constant<int, KD>{}, t0);
+        for (; hi - t0 > R * 4; t0 += R * 8)
+            tile(std::integral_constant<int, 8>{}, t0);
+        if (t0 < hi)
+            tile(std::integral_constant<int, 4>{}, t0);
+    } else {
+        for (int t0 = 0; t0 < hi; t0 += R * KD)
+            tile(std::integral_constant<int, KD>{}, t0);
     }
     __syncthreads();
     if (srow && active)
@@ -458,20 +488,16 @@ void scan_kernel(ScanArgs a)
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC>
 static void launch_scan_v(const ScanArgs &a, dim3 grid, hipStream_t stream)
 {
-    // Packed batches take 8 steps per lane: each sequence pads its last tile
-    // to a tile boundary, and halving the tile halves that waste (packed
-    // 16-sequence Mamba-1 prefill 281 -> 261 us).  Dense batches keep 16,
-    // whose lane scan costs less per step (227 vs 238 us).
     if (a.cu_seqlens) {
         if (a.dstate <= NC)
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, KP>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, true>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, KP>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, true>), grid, dim3(256), 0, stream, a);
     } else {
         if (a.dstate <= NC)
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, KD>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, false>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, KD>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, false>), grid, dim3(256), 0, stream, a);
     }
 }
 
