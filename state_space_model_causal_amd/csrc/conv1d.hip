@@ -10,7 +10,9 @@
 //
 // Dense prefill, 16-byte aligned rows (the common case): two rows per
 // 256-lane workgroup, each lane one 128-bit chunk of each row per tile plus
-// the few samples in front of it, no LDS and no barriers (conv_rows_kernel).
+// the few samples in front of it (from the previous lane, by DPP), no LDS
+// and no barriers (conv_rows_kernel).  The first tile's loads are issued
+// before the rows' parameters are fetched.
 // Other dense rows: one workgroup per (b, c) row walks the row in tiles of
 // 256*E samples staged in LDS with their W-1 history (conv_prefill_kernel).
 // Either way HBM traffic is x read once, out written once, and the row's
@@ -118,9 +120,10 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
 // barriers.  A workgroup takes RPW rows; per tile, each lane takes E samples
 // of each of its rows (one 128-bit load per row, all issued before any
 // arithmetic, so RPW loads are in flight per lane) and, for the taps that
-// reach in front of them, the 4 samples before (an 8- or 16-byte load of its
-// neighbour's samples, already in cache).  The first chunk of a row takes
-// the row's history instead (the slot's cache or zeros).  Lane 0 reads the
+// reach in front of them, the 4 samples before: the end of the previous
+// lane's chunk, moved by a DPP wave shift (the first lane of each wave loads
+// them).  The first chunk of a row takes the row's history instead (the
+// slot's cache or zeros).  Lane 0 reads the
 // histories before its first chunk and writes the rows' new tails after the
 // walk, so the two accesses to a cache slot are ordered within one lane.
 template <typename T, int W, int RPW, bool MASKED = false>
@@ -135,23 +138,76 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
     const int64_t nrows = (int64_t)a.batch * a.channels;
     const int tid = threadIdx.x, L = a.seqlen;
 
+    // the rows' first tile is requested before anything else: its addresses
+    // need only the kernel arguments, while the slot, the taps and the
+    // history are further loads, whose latency then overlaps the tile's
+    // row = b*channels + c, uniform over the workgroup: one division for the
+    // first row (32-bit where the rows allow: a 64-bit one is a long scalar
+    // sequence in front of every load), the next rows by stepping c
+    int64_t b0 = 0;
+    int c0 = 0;
+    if (row0 < nrows) {
+        if (nrows <= (int64_t)UINT32_MAX) {
+            const uint32_t q = (uint32_t)row0 / (uint32_t)a.channels;
+            b0 = q;
+            c0 = (int)((uint32_t)row0 - q * (uint32_t)a.channels);
+        } else {
+            b0 = row0 / a.channels;
+            c0 = (int)(row0 % a.channels);
+        }
+    }
+    const T *xr[RPW];
+    int64_t rb[RPW];
+    int rc[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        int64_t b = 0;
+        int c = 0;
+        if (row0 + r < nrows) {  // rows past the end read row 0 and store nothing
+            b = b0;
+            c = c0 + r;
+            for (; c >= a.channels; c -= a.channels)
+                ++b;
+        }
+        rb[r] = b;
+        rc[r] = c;
+        xr[r] = static_cast<const T *>(a.x) + b * a.x_sb + c * a.x_sc;
+    }
+    // the samples in front of a chunk are the end of the previous lane's
+    // chunk: moved from it within the wave; the first lane of a wave loads
+    // them (they belong to the previous wave or tile)
+    const bool first = (tid & 63) == 0;
+    u32x4 raw[RPW];
+    Prev praw[RPW];
+    auto issue = [&](int t0) {
+        const int t = t0 + tid * E;
+        const int tc = t < L ? t : 0;
+        const int tp = tc > 0 ? tc - PW : 0;  // clamped; sample 0 takes the history
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            // x is streamed once: non-temporal (41.9 -> 35.7 us per call on
+            // the 4 x 5120 x 2048 f16 prefill)
+            raw[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr[r] + tc));
+            if (first)
+                praw[r] = *reinterpret_cast<const Prev *>(xr[r] + tp);
+        }
+    };
+    issue(0);
+
     float w[RPW][W], bias[RPW], hist[RPW][PW];
     bool live[RPW];
-    const T *xr[RPW];
     T *orow[RPW];
     T *cs[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-        const int64_t row = row0 + r;  // b*channels + c, uniform over the workgroup
-        const int64_t rr = row < nrows ? row : 0;
-        const int b = (int)(rr / a.channels), c = (int)(rr % a.channels);
-        const int slot = a.slot_idx ? a.slot_idx[b] : b;
-        live[r] = row < nrows && slot >= 0;  // padded request: untouched
+        const int64_t b = rb[r];
+        const int c = rc[r];
+        const int slot = a.slot_idx ? a.slot_idx[b] : (int)b;
+        live[r] = row0 + r < nrows && slot >= 0;  // padded request: untouched
 #pragma unroll
         for (int k = 0; k < W; ++k)
             w[r][k] = a.weight[c * a.w_sc + k];
         bias[r] = a.bias ? a.bias[c] : 0.0f;
-        xr[r] = static_cast<const T *>(a.x) + b * a.x_sb + c * a.x_sc;
         orow[r] = static_cast<T *>(a.out) + b * a.o_sb + c * a.o_sc;
         cs[r] = (a.conv_state && slot >= 0) ? static_cast<T *>(a.conv_state) + slot * a.cs_ss + c * a.cs_sc
                                             : nullptr;
@@ -170,16 +226,19 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
         const int t = t0 + tid * E;
         const bool tin = t < L;  // L % E == 0: a chunk is all in or all out
         const int tc = tin ? t : 0;
-        const int tp = tc > 0 ? tc - PW : 0;  // clamped; sample 0 takes the history
-        u32x4 raw[RPW];
-        Prev praw[RPW];
+        if (t0 > 0)
+            issue(t0);
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            // x is streamed once: non-temporal (41.9 -> 35.7 us per call on
-            // the 4 x 5120 x 2048 f16 prefill); the few samples in front come
-            // from the neighbour's chunk, through the cache
-            raw[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr[r] + tc));
-            praw[r] = *reinterpret_cast<const Prev *>(xr[r] + tp);
+            Prev nb;
+            if constexpr (PB == 16) {
+                nb = u32x4{dpp_move_bits<DPP_WAVE_SHR1>(raw[r].x), dpp_move_bits<DPP_WAVE_SHR1>(raw[r].y),
+                           dpp_move_bits<DPP_WAVE_SHR1>(raw[r].z), dpp_move_bits<DPP_WAVE_SHR1>(raw[r].w)};
+            } else {
+                nb = uint2{dpp_move_bits<DPP_WAVE_SHR1>(raw[r].z), dpp_move_bits<DPP_WAVE_SHR1>(raw[r].w)};
+            }
+            if (!first)
+                praw[r] = nb;
         }
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {

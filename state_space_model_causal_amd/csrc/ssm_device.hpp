@@ -201,6 +201,7 @@ enum : int {
     DPP_QUAD_NEXT = 0xF9,  // quad_perm [1,2,3,3]: lane i of a quad reads lane min(i+1, 3)
     DPP_ROW_BCAST15 = 0x142,  // lane 15 of each row to every lane of the next row
     DPP_ROW_BCAST31 = 0x143,  // lane 31 to every lane of rows 2 and 3
+    DPP_WAVE_SHR1 = 0x138,    // lane i reads lane i-1 of the wave (lane 0: bound_ctrl)
 };
 
 // Read `src` from another lane of the same 16-lane row; lanes whose source
