@@ -383,7 +383,9 @@ void scan_kernel(ScanArgs a)
                 }
             }
             __syncthreads();
-#pragma unroll 1
+            // four states per pass: 196.6 against 199.1 us one at a time
+            // (2: 197.2, 8: 198.0) on the Mamba-1 2.8B prefill
+#pragma unroll 4
             for (int nl = 0; nl < NC; ++nl) {
                 if (n0 + nl >= N)
                     break;
