@@ -85,8 +85,10 @@ KERNEL_SYMBOLS = {"conv1d_prefill": "conv_rows_kernel", "selective_scan": "scan_
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # 200 timed steps (about 55 ms) after 50 warm-up steps: a 50-step window
+    # right after start-up read 1-2% slow against later windows
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="target duration of each CPU oracle sample (one core, all cores)")
