@@ -116,34 +116,55 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvArgs a)
         cs[tid] = from_f32<T>(hist[tid]);  // exact: the values came from T
 }
 
-// Dense prefill with rows of whole 16-byte vectors: no LDS and no
-// barriers.  A workgroup takes RPW rows; per tile, each lane takes E samples
-// of each of its rows (one 128-bit load per row, all issued before any
-// arithmetic, so RPW loads are in flight per lane) and, for the taps that
-// reach in front of them, the 4 samples before: the end of the previous
-// lane's chunk, moved by a DPP wave shift (the first lane of each wave loads
-// them).  The first chunk of a row takes the row's history instead (the
-// slot's cache or zeros).  Lane 0 reads the
-// histories before its first chunk and writes the rows' new tails after the
-// walk, so the two accesses to a cache slot are ordered within one lane.
-template <typename T, int W, int RPW, bool MASKED = false>
-__device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t row0,
-                                               const int *pads = nullptr, int npad = 0)
-{
-    constexpr int E = 16 / StorageSize<T>::value;  // samples per 128-bit access
-    constexpr int H = W - 1;
-    constexpr int PW = 4;                           // samples loaded in front of a chunk (>= H)
-    constexpr int PB = PW * StorageSize<T>::value;  // their bytes: 8 or 16
+// The rows of a workgroup's walk and the loads of their current tile, from
+// the first loads (rows_begin, which a caller can issue early) to the
+// compute (conv_rows_walk).
+template <typename T, int RPW>
+struct RowTiles {
+    static constexpr int E = 16 / StorageSize<T>::value;  // samples per 128-bit access
+    static constexpr int PW = 4;                          // samples loaded in front of a chunk (>= W-1)
+    static constexpr int PB = PW * StorageSize<T>::value;  // their bytes: 8 or 16
     using Prev = typename std::conditional<PB == 16, u32x4, uint2>::type;
-    const int64_t nrows = (int64_t)a.batch * a.channels;
-    const int tid = threadIdx.x, L = a.seqlen;
+    const T *xr[RPW];
+    int64_t rb[RPW];
+    int rc[RPW];
+    u32x4 raw[RPW];
+    Prev praw[RPW];
+};
 
-    // the rows' first tile is requested before anything else: its addresses
-    // need only the kernel arguments, while the slot, the taps and the
-    // history are further loads, whose latency then overlaps the tile's
-    // row = b*channels + c, uniform over the workgroup: one division for the
-    // first row (32-bit where the rows allow: a 64-bit one is a long scalar
-    // sequence in front of every load), the next rows by stepping c
+// Issue the loads of tile t0 of the rows.  The samples in front of a chunk
+// are the end of the previous lane's chunk, moved from it within the wave
+// (conv_rows_walk); the first lane of a wave loads them (they belong to the
+// previous wave or tile).
+template <typename T, int RPW>
+__device__ __forceinline__ void rows_issue(RowTiles<T, RPW> &rt, int L, int t0)
+{
+    using RT = RowTiles<T, RPW>;
+    const int tid = threadIdx.x;
+    const int t = t0 + tid * RT::E;
+    const int tc = t < L ? t : 0;
+    const int tp = tc > 0 ? tc - RT::PW : 0;  // clamped; sample 0 takes the history
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        // x is streamed once: non-temporal (41.9 -> 35.7 us per call on
+        // the 4 x 5120 x 2048 f16 prefill)
+        rt.raw[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rt.xr[r] + tc));
+        if ((tid & 63) == 0)
+            rt.praw[r] = *reinterpret_cast<const typename RT::Prev *>(rt.xr[r] + tp);
+    }
+}
+
+// The rows row0 .. row0 + RPW - 1 (row = b*channels + c, uniform over the
+// workgroup) and the loads of their first tile, requested before anything
+// else: the addresses need only the kernel arguments, while the slot, the
+// taps and the history are further loads, whose latency then overlaps the
+// tile's.  One division for the first row (32-bit where the rows allow: a
+// 64-bit one is a long scalar sequence in front of every load), the next
+// rows by stepping c.
+template <typename T, int RPW>
+__device__ __forceinline__ void rows_begin(RowTiles<T, RPW> &rt, const ConvArgs &a, const int64_t row0)
+{
+    const int64_t nrows = (int64_t)a.batch * a.channels;
     int64_t b0 = 0;
     int c0 = 0;
     if (row0 < nrows) {
@@ -156,9 +177,6 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
             c0 = (int)(row0 % a.channels);
         }
     }
-    const T *xr[RPW];
-    int64_t rb[RPW];
-    int rc[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
         int64_t b = 0;
@@ -169,30 +187,40 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
             for (; c >= a.channels; c -= a.channels)
                 ++b;
         }
-        rb[r] = b;
-        rc[r] = c;
-        xr[r] = static_cast<const T *>(a.x) + b * a.x_sb + c * a.x_sc;
+        rt.rb[r] = b;
+        rt.rc[r] = c;
+        rt.xr[r] = static_cast<const T *>(a.x) + b * a.x_sb + c * a.x_sc;
     }
-    // the samples in front of a chunk are the end of the previous lane's
-    // chunk: moved from it within the wave; the first lane of a wave loads
-    // them (they belong to the previous wave or tile)
+    rows_issue<T, RPW>(rt, a.seqlen, 0);
+}
+
+// Dense prefill with rows of whole 16-byte vectors: no LDS and no
+// barriers.  A workgroup takes RPW rows (rows_begin has issued their first
+// tile); per tile, each lane takes E samples of each of its rows (one
+// 128-bit load per row, all issued before any arithmetic, so RPW loads are
+// in flight per lane) and, for the taps that reach in front of them, the 4
+// samples before: the end of the previous lane's chunk, moved by a DPP wave
+// shift (the first lane of each wave loads them).  The first chunk of a row
+// takes the row's history instead (the slot's cache or zeros).  Lane 0
+// reads the histories before its first chunk and writes the rows' new tails
+// after the walk, so the two accesses to a cache slot are ordered within
+// one lane.
+template <typename T, int W, int RPW, bool MASKED = false>
+__device__ __forceinline__ void conv_rows_walk(RowTiles<T, RPW> &rt, const ConvArgs &a, const int64_t row0,
+                                               const int *pads = nullptr, int npad = 0)
+{
+    using RT = RowTiles<T, RPW>;
+    constexpr int E = RT::E;
+    constexpr int H = W - 1;
+    constexpr int PW = RT::PW;
+    constexpr int PB = RT::PB;
+    using Prev = typename RT::Prev;
+    const int64_t nrows = (int64_t)a.batch * a.channels;
+    const int tid = threadIdx.x, L = a.seqlen;
     const bool first = (tid & 63) == 0;
-    u32x4 raw[RPW];
-    Prev praw[RPW];
-    auto issue = [&](int t0) {
-        const int t = t0 + tid * E;
-        const int tc = t < L ? t : 0;
-        const int tp = tc > 0 ? tc - PW : 0;  // clamped; sample 0 takes the history
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            // x is streamed once: non-temporal (41.9 -> 35.7 us per call on
-            // the 4 x 5120 x 2048 f16 prefill)
-            raw[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr[r] + tc));
-            if (first)
-                praw[r] = *reinterpret_cast<const Prev *>(xr[r] + tp);
-        }
-    };
-    issue(0);
+    const T *const *xr = rt.xr;
+    u32x4 *raw = rt.raw;
+    Prev *praw = rt.praw;
 
     float w[RPW][W], bias[RPW], hist[RPW][PW];
     bool live[RPW];
@@ -200,8 +228,8 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
     T *cs[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-        const int64_t b = rb[r];
-        const int c = rc[r];
+        const int64_t b = rt.rb[r];
+        const int c = rt.rc[r];
         const int slot = a.slot_idx ? a.slot_idx[b] : (int)b;
         live[r] = row0 + r < nrows && slot >= 0;  // padded request: untouched
 #pragma unroll
@@ -227,7 +255,7 @@ __device__ __forceinline__ void conv_rows_walk(const ConvArgs &a, const int64_t 
         const bool tin = t < L;  // L % E == 0: a chunk is all in or all out
         const int tc = tin ? t : 0;
         if (t0 > 0)
-            issue(t0);
+            rows_issue<T, RPW>(rt, L, t0);
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             Prev nb;
@@ -550,11 +578,20 @@ __global__ __launch_bounds__(256) void conv_varlen_kernel(ConvArgs a)
 template <typename T, int W, int RPW>
 __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
 {
-    constexpr int E = 16 / StorageSize<T>::value;
     constexpr int H = W - 1;
     constexpr int HS = H > 0 ? H : 1;
     const int tid = threadIdx.x, nseq = a.batch, Tn = a.seqlen;
     const ConvArgs pa = a;  // the packed-batch arguments
+    // the dense walk's view: each packed channel row as one request with no
+    // history; its first tile is requested before the table is read (if the
+    // table turns out not to suit the walk, those values go unused)
+    ConvArgs da = a;
+    da.batch = 1;
+    da.slot_idx = nullptr;
+    da.conv_state = nullptr;
+    da.has_initial_state = 0;
+    RowTiles<T, RPW> rt;
+    rows_begin<T, RPW>(rt, da, row0);
     // lane t <= nseq: entry t of the table (lane t < nseq: sequence t)
     constexpr int kPadCap = 8;  // padded sequences the dense walk stores around
     __shared__ int s_pads[2 * kPadCap];
@@ -585,16 +622,39 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
         }
         __syncthreads();
     }
-    if (plain || masked) {
-        a.batch = 1;
-        a.slot_idx = nullptr;
-        a.conv_state = nullptr;
-        a.has_initial_state = 0;
-        if (plain)
-            conv_rows_walk<T, W, RPW>(a, row0);
-        else
-            conv_rows_walk<T, W, RPW, true>(a, row0, s_pads, npad);
+
+    // One lane per (sequence, row) then redoes the sequence's first W-1
+    // outputs and writes its cache tail.  Its inputs (the cached history,
+    // the first and the last H samples) do not depend on the walk's outputs:
+    // they are requested now, so their latency overlaps the walk's.
+    const int tb = min(max(cb, 0), Tn);
+    const int te = min(max(ce, tb), Tn);
+    const int len = te - tb;
+    const bool fix = H > 0 && tid < nseq && slot >= 0 && len > 0;
+    T hraw[RPW][HS], xb[RPW][HS], xe[RPW][HS];
+    if (fix) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int64_t c = min(row0 + r, (int64_t)pa.channels - 1);  // rows past the end: unused
+            const T *cs = pa.conv_state ? static_cast<const T *>(pa.conv_state) + slot * pa.cs_ss + c * pa.cs_sc
+                                        : nullptr;
+            const T *xr = static_cast<const T *>(pa.x) + c * pa.x_sc + tb;
+            // every sample from an in-bounds address, issued together
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
+                hraw[r][k] = cs ? cs[k] : from_f32<T>(0.0f);
+                xb[r][k] = xr[min(k, len - 1)];
+                xe[r][k] = xr[max(len - H + k, 0)];
+            }
+        }
+    }
+
+    if (plain) {
+        conv_rows_walk<T, W, RPW>(rt, da, row0);
+    } else if (masked) {
+        conv_rows_walk<T, W, RPW, true>(rt, da, row0, s_pads, npad);
     } else {
+        constexpr int E = 16 / StorageSize<T>::value;
         constexpr int TILE = 256 * E;
         const int ntiles = (Tn + TILE - 1) / TILE;
         for (int r = 0; r < RPW; ++r) {
@@ -614,12 +674,7 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
     // rewrites a start: vmcnt(0), expcnt and lgkmcnt left free
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (tid >= nseq || slot < 0)
-        return;
-    const int tb = min(max(cb, 0), Tn);
-    const int te = min(max(ce, tb), Tn);
-    const int len = te - tb;
-    if (len == 0)
+    if (!fix)
         return;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -627,22 +682,12 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
         if (c >= pa.channels)
             break;
         T *cs = pa.conv_state ? static_cast<T *>(pa.conv_state) + slot * pa.cs_ss + c * pa.cs_sc : nullptr;
-        const T *xr = static_cast<const T *>(pa.x) + c * pa.x_sc + tb;
-        // every sample the lane needs, from in-bounds addresses, issued
-        // together: the cached history, the first and the last H samples
-        T hraw[HS], xb[HS], xe[HS];
-#pragma unroll
-        for (int k = 0; k < H; ++k) {
-            hraw[k] = cs ? cs[k] : from_f32<T>(0.0f);
-            xb[k] = xr[min(k, len - 1)];
-            xe[k] = xr[max(len - H + k, 0)];
-        }
         if (plain || masked) {
             float hx[2 * HS];  // history || the first H samples (zeros past the end)
 #pragma unroll
             for (int k = 0; k < H; ++k) {
-                hx[k] = init ? to_f32(hraw[k]) : 0.0f;
-                hx[H + k] = k < len ? to_f32(xb[k]) : 0.0f;
+                hx[k] = init ? to_f32(hraw[r][k]) : 0.0f;
+                hx[H + k] = k < len ? to_f32(xb[r][k]) : 0.0f;
             }
             float w[W];
 #pragma unroll
@@ -667,12 +712,12 @@ __device__ __forceinline__ void conv_rows_packed(ConvArgs a, const int64_t row0)
                 const int tau = len - H + k;  // step of the k-th kept sample
                 T v = from_f32<T>(0.0f);      // before the sequence, with no history
                 if (tau >= 0) {
-                    v = xe[k];
+                    v = xe[r][k];
                 } else if (init) {
 #pragma unroll
                     for (int m = 0; m < H; ++m)
                         if (m == H + tau)
-                            v = hraw[m];
+                            v = hraw[r][m];
                 }
                 cs[k] = v;
             }
@@ -684,10 +729,13 @@ template <typename T, int W, int RPW, bool VARLEN>
 __global__ __launch_bounds__(256) void conv_rows_kernel(ConvArgs a)
 {
     const int64_t row0 = (int64_t)xcd_block_order(blockIdx.x, gridDim.x) * RPW;
-    if constexpr (VARLEN)
+    if constexpr (VARLEN) {
         conv_rows_packed<T, W, RPW>(a, row0);
-    else
-        conv_rows_walk<T, W, RPW>(a, row0);
+    } else {
+        RowTiles<T, RPW> rt;
+        rows_begin<T, RPW>(rt, a, row0);
+        conv_rows_walk<T, W, RPW>(rt, a, row0);
+    }
 }
 
 
