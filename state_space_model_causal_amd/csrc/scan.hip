@@ -13,9 +13,10 @@
 //     stream, which is staged once per tile in LDS and read by all of them.
 //   * The sequence is walked in tiles of 16 K timesteps; lane r of a channel
 //     owns timesteps [K r, K r + K) of the tile (K = 16: 128-bit loads of u,
-//     dt and z).  In packed batches each sequence ends in shorter tiles
-//     (K = 8, then 4: 64-bit loads for 2-byte types), so that it pads its
-//     last tile by fewer than 64 steps.
+//     dt and z).  In packed batches, and in dense rows whose length is not
+//     a multiple of 256, each sequence ends in shorter tiles (K = 8, then 4:
+//     64-bit loads for 2-byte types), so that it pads its last tile by fewer
+//     than 64 steps.
 //   * For each state n, every lane reduces its K steps to one affine map
 //     h -> a*h + b (a = product of decays, b = local state from zero), the 16
 //     maps of a row are combined by an inclusive Hillis-Steele scan with DPP
@@ -201,7 +202,13 @@ __device__ __forceinline__ int packed_seq_of_rank(const int32_t *__restrict__ cu
     return s_pick;
 }
 
-template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK, bool PACKED>
+// Walks: WALK_DENSE, tiles of 16 steps per lane; WALK_LADDER, the same
+// ending in tiles of 8 and 4 steps per lane (dense rows whose length is not
+// a multiple of 256); WALK_PACKED, the ladder over the sequences of a packed
+// batch, longest first.
+enum { WALK_DENSE = 0, WALK_LADDER = 1, WALK_PACKED = 2 };
+
+template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK, int WALK>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, VEC, A_PER_STATE, ONE_CHUNK>())))
 void scan_kernel(ScanArgs a)
@@ -231,7 +238,7 @@ void scan_kernel(ScanArgs a)
     const int bg = (int)(lb / nblk_g);
     const int g = bg % a.ngroups;
     int b = bg / a.ngroups;
-    if constexpr (PACKED) {
+    if constexpr (WALK == WALK_PACKED) {
         // the longest sequences' workgroups start first, so the longest walks
         // do not begin late and leave the chip idle at the end
         if (a.batch <= 256)
@@ -465,7 +472,7 @@ void scan_kernel(ScanArgs a)
         if (active)
             store_steps<TI, VEC, K>(orow, tl, lo, hi, y);
     };
-    if constexpr (PACKED) {
+    if constexpr (WALK != WALK_DENSE) {
         // Each sequence pads its last tile to a tile boundary.  Tiles of 16
         // steps per lane while more than 3/4 of one remains, then of 8 while
         // more than 64 steps remain, then one of 4: under 64 padded steps
@@ -487,20 +494,24 @@ void scan_kernel(ScanArgs a)
             srow[n] = from_f32<TS>(lds_carry[ch][n]);
 }
 
+template <typename TI, typename TS, bool A_PER_STATE, bool VEC, int WALK>
+static void launch_scan_w(const ScanArgs &a, dim3 grid, hipStream_t stream)
+{
+    if (a.dstate <= NC)
+        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, WALK>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, WALK>), grid, dim3(256), 0, stream, a);
+}
+
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC>
 static void launch_scan_v(const ScanArgs &a, dim3 grid, hipStream_t stream)
 {
-    if (a.cu_seqlens) {
-        if (a.dstate <= NC)
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, true>), grid, dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, true>), grid, dim3(256), 0, stream, a);
-    } else {
-        if (a.dstate <= NC)
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, true, false>), grid, dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((scan_kernel<TI, TS, A_PER_STATE, VEC, false, false>), grid, dim3(256), 0, stream, a);
-    }
+    if (a.cu_seqlens)
+        launch_scan_w<TI, TS, A_PER_STATE, VEC, WALK_PACKED>(a, grid, stream);
+    else if (a.seqlen % (R * KD) != 0)
+        launch_scan_w<TI, TS, A_PER_STATE, VEC, WALK_LADDER>(a, grid, stream);
+    else
+        launch_scan_w<TI, TS, A_PER_STATE, VEC, WALK_DENSE>(a, grid, stream);
 }
 
 template <typename TI, typename TS>
