@@ -140,6 +140,14 @@ SCAN_CASES = [
                            random_slots=True, batch=3), dict(init=True, pad=3)),
     ("m2_bf16_L4096_N256", dict(io="bf16", state="f32", seqlen=4096, nheads=1, headdim=16,
                                 dstate=256, a_per_state=False, index_sensitive=True), {}),
+    # 16-byte rows whose length is not a multiple of 256 end in 8- and 4-step
+    # tiles (64-bit loads and stores for 2-byte types)
+    ("m1_f16_L264_vec_ladder", dict(io="f16", seqlen=264, nheads=24, batch=2, index_sensitive=True,
+                                    nslots=3, random_slots=True), dict(init=True)),
+    ("m1_bf16_L136_vec_ladder", dict(io="bf16", seqlen=136, nheads=16, batch=2, index_sensitive=True), {}),
+    ("m1_f32_L40_vec_ladder", dict(io="f32", seqlen=40, nheads=12, batch=3, index_sensitive=True), {}),
+    ("m2_f16_L408_vec_ladder", dict(io="f16", state="f32", seqlen=408, nheads=4, headdim=8, dstate=16,
+                                    ngroups=2, a_per_state=False, index_sensitive=True), {}),
 ]
 
 
