@@ -203,10 +203,10 @@ __device__ __forceinline__ int packed_seq_of_rank(const int32_t *__restrict__ cu
 }
 
 // Walks: WALK_DENSE, tiles of 16 steps per lane; WALK_LADDER, the same
-// ending in tiles of 8 and 4 steps per lane (dense rows whose length is not
-// a multiple of 256); WALK_PACKED, the ladder over the sequences of a packed
-// batch, longest first.
-enum { WALK_DENSE = 0, WALK_LADDER = 1, WALK_PACKED = 2 };
+// ending in tiles of 8 and 4 steps per lane, for packed batches (their
+// sequences handed out longest first) and for dense rows whose length is not
+// a multiple of 256.
+enum { WALK_DENSE = 0, WALK_LADDER = 1 };
 
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC, bool ONE_CHUNK, int WALK>
 __global__ __launch_bounds__(256)
@@ -238,10 +238,11 @@ void scan_kernel(ScanArgs a)
     const int bg = (int)(lb / nblk_g);
     const int g = bg % a.ngroups;
     int b = bg / a.ngroups;
-    if constexpr (WALK == WALK_PACKED) {
-        // the longest sequences' workgroups start first, so the longest walks
-        // do not begin late and leave the chip idle at the end
-        if (a.batch <= 256)
+    if constexpr (WALK == WALK_LADDER) {
+        // packed batches: the longest sequences' workgroups start first, so
+        // the longest walks do not begin late and leave the chip idle at the
+        // end
+        if (a.cu_seqlens && a.batch <= 256)
             b = packed_seq_of_rank(a.cu_seqlens, a.batch, L, b);
     }
     const SeqSpan sp = seq_span(a.cu_seqlens, a.has_init_seq, b, L, a.has_initial_state);
@@ -506,9 +507,7 @@ static void launch_scan_w(const ScanArgs &a, dim3 grid, hipStream_t stream)
 template <typename TI, typename TS, bool A_PER_STATE, bool VEC>
 static void launch_scan_v(const ScanArgs &a, dim3 grid, hipStream_t stream)
 {
-    if (a.cu_seqlens)
-        launch_scan_w<TI, TS, A_PER_STATE, VEC, WALK_PACKED>(a, grid, stream);
-    else if (a.seqlen % (R * KD) != 0)
+    if (a.cu_seqlens || a.seqlen % (R * KD) != 0)
         launch_scan_w<TI, TS, A_PER_STATE, VEC, WALK_LADDER>(a, grid, stream);
     else
         launch_scan_w<TI, TS, A_PER_STATE, VEC, WALK_DENSE>(a, grid, stream);
