@@ -481,7 +481,7 @@ def measure_tiny(ssm, W, dev, timer, mark):
 
 
 SSU_SHAPES = [
-    # (config, name, factory, ngroups, caches, batches, judged batches)
+    # (config, name, factory, ngroups, caches, batches, batches the HBM target applies to)
     (3, "m2_ssu_hd64_n128", "m2_ssu_64", (1, 8), ("f16", "f32"), (1, 16, 256, 1024), (256, 1024)),
     (4, "m2_ssu_hd128_n256", "m2_ssu_128", (1,), ("bf16", "f32"), (1, 8, 64, 512), (512,)),
 ]
@@ -494,7 +494,7 @@ def measure_ssu_points(ssm, W, dev, timer, mark, headline_only=False):
     replays of max(10, sets) launches."""
     import torch
     points = []
-    for cfg, name, fac, groups, caches, batches, judged in SSU_SHAPES:
+    for cfg, name, fac, groups, caches, batches, target_batches in SSU_SHAPES:
         factory = getattr(W, fac)
         for G in groups:
             for cache in caches:
@@ -532,8 +532,8 @@ def measure_ssu_points(ssm, W, dev, timer, mark, headline_only=False):
                           "batch": Bt, "effective_batch": Bt * spec.nheads, "us": us, "bytes": b,
                           "GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
                           "rotation_sets": R, "launches_per_graph": launches, "label": label,
-                          "judged": Bt in judged,
-                          "target_met": (gbps / HBM_PEAK_GBPS >= TARGET_HBM_FRAC) if Bt in judged else None}
+                          "target_batch": Bt in target_batches,
+                          "target_met": (gbps / HBM_PEAK_GBPS >= TARGET_HBM_FRAC) if Bt in target_batches else None}
                     log(f"{label}: {us:.1f} us, {gbps:.0f} GB/s")
                     points.append(pt)
                     del t, out, sets
@@ -881,7 +881,7 @@ def main():
               if k in ("selective_scan", "decode_step", "state_update")}
     if configs:
         for pt in configs["m2_state_update"]:
-            if pt["judged"]:
+            if pt["target_batch"]:
                 target[pt["label"]] = pt["target_met"]
 
     cpu = None
