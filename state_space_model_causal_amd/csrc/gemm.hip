@@ -12,11 +12,15 @@
 // Wave w owns rows [WR (w % 4), + WR) of the block and the 64 columns of
 // group w / 4: WR/16 x 4 tiles of v_mfma_f32_16x16x32_{f16,bf16}, float32
 // accumulation.  K is walked in batches of 64: each batch's activation tile
-// (4 WR rows x 64 k) and weight tile (64 CW rows x 64 k) are loaded once per
-// workgroup with coalesced 128-bit loads (consecutive lanes, consecutive 16
-// bytes of a row) and staged in LDS, from where each wave reads its MFMA
-// operands (8 consecutive k of one row: row-major, k innermost is the operand
-// order).  Two batches' loads are in flight during the MFMAs.  The weights,
+// (4 WR rows x 64 k) and weight tile (64 CW rows x 64 k) are copied once per
+// workgroup from global memory straight into LDS by global_load_lds_dwordx4
+// (each wave instruction fills 1 KB, 8 rows of 128 bytes), from where each
+// wave reads its MFMA operands (8 consecutive k of one row: row-major, k
+// innermost is the operand order).  A ring of three LDS stages keeps two
+// batches in flight during the MFMAs.  A wave reads all of a batch's operands
+// before it issues the next copy: the compiler waits for every copy in flight
+// before an LDS read that may touch one, and only for copies into other
+// stages can it tell that none does.  The weights,
 // the dominant traffic, stream from HBM once (the row blocks of one column
 // tile run on one XCD and share its L2; the activations, 2.6 MB at most, stay
 // in L2).
@@ -118,28 +122,33 @@ __device__ __forceinline__ void gemm_store4(const GemmArgs &a, int row, int col,
 
 // Workgroup of 4 x CW waves for a tile of 4 WR rows x 64 CW columns and one
 // slice of K; wave w owns rows [WR (w % 4), + WR) and columns
-// [64 (w / 4), + 64).
+// [64 (w / 4), + 64).  Each batch of 64 k is copied from global memory
+// straight into LDS (global_load_lds_dwordx4: no registers, no LDS stores
+// of its own), in a ring of three stages so that two batches are in flight
+// while one is multiplied.  A row of a stage is 128 bytes, its 16-byte
+// chunk c stored at position c ^ (row & 7): an operand read (one chunk of 16
+// consecutive rows) spreads over eight bank groups instead of one.
+typedef __attribute__((address_space(3))) void lds_void_t;
 template <typename T, int WR, int CW>
 __global__ __launch_bounds__(256 * CW) void gemm_kernel(GemmArgs a)
 {
-    // one k batch of both operands in LDS: the activation tile (GMR rows) and
-    // the weight tile (GNC rows), KBK k each, row stride padded by 16 B
-    constexpr int NT = 256 * CW;     // threads
+    constexpr int NW = 4 * CW;       // waves
     constexpr int GMR = 4 * WR;      // rows per workgroup
     constexpr int GNC = GN * CW;     // columns per workgroup
     constexpr int RT = WR / 16;      // 16-row MFMA tiles per wave
     constexpr int KB = 2;            // MFMA k-steps per batch
-    constexpr int KBK = KB * GK;     // k per batch
-    constexpr int LDK = KBK + 8;     // elements per LDS row
-    constexpr int CPR = KBK / 8;     // 16-byte chunks per row
-    constexpr int ACH = GMR * CPR / NT, WCH = GNC * CPR / NT;  // chunks per thread
-    static_assert(ACH * NT == GMR * CPR && WCH * NT == GNC * CPR, "tiles must split evenly over the threads");
-    __shared__ __align__(16) T s_a[GMR * LDK];
-    __shared__ __align__(16) T s_w[GNC * LDK];
+    constexpr int KBK = KB * GK;     // k per batch (64)
+    constexpr int ABLK = GMR * 8 / 64, WBLK = GNC * 8 / 64;  // 1 KB blocks per tile
+    constexpr int AJ = ABLK / NW, WJ = WBLK / NW;             // DMA instructions per wave and tile
+    static_assert(AJ * NW == ABLK && WJ * NW == WBLK, "tiles must split evenly over the waves");
+    static_assert(sizeof(T) == 2, "2-byte operands");
+    __shared__ __align__(16) T sA0[GMR * KBK];
+    __shared__ __align__(16) T sA1[GMR * KBK];
+    __shared__ __align__(16) T sA2[GMR * KBK];
+    __shared__ __align__(16) T sW0[GNC * KBK];
+    __shared__ __align__(16) T sW1[GNC * KBK];
+    __shared__ __align__(16) T sW2[GNC * KBK];
 
-    // logical block (column tile, row block, split): the splits and row
-    // blocks of one column tile are consecutive, and consecutive logical
-    // blocks run on one XCD, so they share its L2 (the weight tile)
     const int ncol = (a.N + GNC - 1) / GNC, nrow = (a.M + GMR - 1) / GMR;
     const uint32_t lb = xcd_block_order(blockIdx.x, gridDim.x);
     const int ks = (int)(lb % (uint32_t)a.splits);
@@ -148,32 +157,47 @@ __global__ __launch_bounds__(256 * CW) void gemm_kernel(GemmArgs a)
     if (nb >= ncol)
         return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int wm = w & 3, wn = w >> 2;  // row and column group of the wave
+    const int wm = w & 3, wn = w >> 2;
     const int l16 = l & 15, lq = l >> 4;
     const int K = a.K;
     const int nbatch = (K + KBK - 1) / KBK;
     const int b0 = (int)((int64_t)nbatch * ks / a.splits), b1 = (int)((int64_t)nbatch * (ks + 1) / a.splits);
 
-    // chunk c = tid + NT q of a tile: row c / CPR, k offset 8 (c % CPR);
-    // consecutive threads read consecutive 16 B of a row
-    const T *asrc[ACH];
-    const T *wsrc[WCH];
-    int adst[ACH], wdst[WCH];
-    const int kofs = 8 * (tid % CPR);  // the same for every chunk of this thread
+    // lane l of DMA block bI: row bI*8 + l/8, stored chunk position l%8,
+    // which holds global chunk (l%8) ^ (row & 7)
+    const T *asrc[AJ];
+    const T *wsrc[WJ];
+    int achk[AJ], wchk[WJ];
 #pragma unroll
-    for (int q = 0; q < ACH; ++q) {
-        const int c = tid + NT * q, r = c / CPR;
-        const int m = min(mb * GMR + r, a.M - 1);  // clamped rows are never stored
-        asrc[q] = static_cast<const T *>(a.A) + (int64_t)m * a.lda + kofs;
-        adst[q] = r * LDK + kofs;
+    for (int j = 0; j < AJ; ++j) {
+        const int r = (j * NW + w) * 8 + (l >> 3);
+        achk[j] = 8 * ((l & 7) ^ (r & 7));
+        asrc[j] = static_cast<const T *>(a.A) + (int64_t)min(mb * GMR + r, a.M - 1) * a.lda;
     }
 #pragma unroll
-    for (int q = 0; q < WCH; ++q) {
-        const int c = tid + NT * q, r = c / CPR;
-        const int n = min(nb * GNC + r, a.N - 1);
-        wsrc[q] = static_cast<const T *>(a.W) + (int64_t)n * a.ldw + kofs;
-        wdst[q] = r * LDK + kofs;
+    for (int j = 0; j < WJ; ++j) {
+        const int r = (j * NW + w) * 8 + (l >> 3);
+        wchk[j] = 8 * ((l & 7) ^ (r & 7));
+        wsrc[j] = static_cast<const T *>(a.W) + (int64_t)min(nb * GNC + r, a.N - 1) * a.ldw;
     }
+    // the DMA written out: the compiler then does not count it among the LDS
+    // writes it must drain before every LDS read; its completion is waited
+    // for explicitly (vmcnt) before each batch's barrier
+    auto dma16 = [&](const T *g, T *ldst) {
+        __builtin_amdgcn_global_load_lds((const void *)g, (lds_void_t *)ldst, 16, 0, 0);
+    };
+    auto issue = [&](int batch, T *sA, T *sW) {
+#pragma unroll
+        for (int j = 0; j < AJ; ++j) {
+            const int k = batch * KBK + achk[j];
+            dma16(asrc[j] + (k < K ? k : 0), sA + (j * NW + w) * 512);
+        }
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            const int k = batch * KBK + wchk[j];
+            dma16(wsrc[j] + (k < K ? k : 0), sW + (j * NW + w) * 512);
+        }
+    };
 
     f32x4_g acc[RT][4];
 #pragma unroll
@@ -182,65 +206,58 @@ __global__ __launch_bounds__(256 * CW) void gemm_kernel(GemmArgs a)
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_g{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // K % 8 == 0: an 8-element chunk is all in or all out; out of range it
-    // is loaded from the row's first chunk (in bounds) and zeroed when it is
-    // staged.  Zeroing at staging time, not right after the load, keeps the
-    // loads in flight.  Two batches of loads are in flight at a time, in two
-    // register sets (the loop is unrolled by two, so each set is named at
-    // compile time): batch b + 2 is issued as soon as batch b is staged.
-    u32x4 ar[2][ACH], wr[2][WCH];
-    bool in_range[2] = {true, true};
-    auto load = [&](int batch, auto bufc) {
-        constexpr int B = decltype(bufc)::value;
-        in_range[B] = batch * KBK + kofs < K;
-        const int off = in_range[B] ? batch * KBK : -kofs;
-#pragma unroll
-        for (int q = 0; q < ACH; ++q)
-            ar[B][q] = *reinterpret_cast<const u32x4 *>(asrc[q] + off);
-#pragma unroll
-        for (int q = 0; q < WCH; ++q)
-            wr[B][q] = *reinterpret_cast<const u32x4 *>(wsrc[q] + off);
-    };
-    auto step = [&](int bt, auto bufc) {
-        constexpr int B = decltype(bufc)::value;
+    auto step = [&](int bt, const T *sA, const T *sW, T *nA, T *nW) {
+        if (bt + 1 < b1)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (AJ + WJ));  // batch bt has landed (bt + 1 may be in flight)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_s_barrier();
+        // every operand of this batch read out of LDS before the DMA of batch
+        // bt + 2 is issued: the compiler then finds no DMA in flight to an
+        // LDS array these reads may touch, and adds no wait of its own
+        const bool partial = (bt + 1) * KBK > K;
         const u32x4 zero{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int q = 0; q < ACH; ++q)
-            *reinterpret_cast<u32x4 *>(&s_a[adst[q]]) = in_range[B] ? ar[B][q] : zero;
-#pragma unroll
-        for (int q = 0; q < WCH; ++q)
-            *reinterpret_cast<u32x4 *>(&s_w[wdst[q]]) = in_range[B] ? wr[B][q] : zero;
-        __syncthreads();
-        if (bt + 2 < b1)
-            load(bt + 2, bufc);  // in flight during this batch's and the next one's MFMAs
+        u32x4 av[KB][RT], bv[KB][4];
 #pragma unroll
         for (int q = 0; q < KB; ++q) {
-            u32x4 av[RT], bv[4];
+            const int kc = 4 * q + lq;  // 16-byte chunk of the batch
+            const bool kin = !partial || bt * KBK + 8 * kc < K;
 #pragma unroll
-            for (int i = 0; i < RT; ++i)
-                av[i] = *reinterpret_cast<const u32x4 *>(&s_a[(WR * wm + 16 * i + l16) * LDK + q * GK + 8 * lq]);
+            for (int i = 0; i < RT; ++i) {
+                const int row = WR * wm + 16 * i + l16;
+                av[q][i] = *reinterpret_cast<const u32x4 *>(&sA[row * KBK + 8 * (kc ^ (row & 7))]);
+                if (partial)
+                    av[q][i] = kin ? av[q][i] : zero;
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bv[j] = *reinterpret_cast<const u32x4 *>(&s_w[(GN * wn + 16 * j + l16) * LDK + q * GK + 8 * lq]);
+            for (int j = 0; j < 4; ++j) {
+                const int row = GN * wn + 16 * j + l16;
+                bv[q][j] = *reinterpret_cast<const u32x4 *>(&sW[row * KBK + 8 * (kc ^ (row & 7))]);
+                if (partial)
+                    bv[q][j] = kin ? bv[q][j] : zero;
+            }
+        }
+        if (bt + 2 < b1)
+            issue(bt + 2, nA, nW);
+#pragma unroll
+        for (int q = 0; q < KB; ++q)
 #pragma unroll
             for (int i = 0; i < RT; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = Mfma<T>::run(bv[j], av[i], acc[i][j]);
-        }
-        __syncthreads();  // the tiles are restaged next batch
+                    acc[i][j] = Mfma<T>::run(bv[q][j], av[q][i], acc[i][j]);
     };
 
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
     if (b0 < b1)
-        load(b0, B0{});
+        issue(b0, sA0, sW0);
     if (b0 + 1 < b1)
-        load(b0 + 1, B1{});
-    for (int bt = b0; bt < b1; bt += 2) {
-        step(bt, B0{});
+        issue(b0 + 1, sA1, sW1);
+    for (int bt = b0; bt < b1; bt += 3) {
+        step(bt, sA0, sW0, sA2, sW2);
         if (bt + 1 < b1)
-            step(bt + 1, B1{});
+            step(bt + 1, sA1, sW1, sA0, sW0);
+        if (bt + 2 < b1)
+            step(bt + 2, sA2, sW2, sA1, sW1);
     }
 
     // The products are taken as W . act^T, so acc[i][j][e] is output row
