@@ -73,6 +73,19 @@ VARLEN_CASES = [
     # tile with the start-aware code, a barrier between tiles
     ("m1_f16_10_padded_3_tiles", dict(io="f16", state="f32", nheads=8, nslots=24, seed=26),
      W.varlen_lengths(26, 20, 5000), [0, 2, 3, 4, 6, 8, 10, 12, 16, 18]),  # total 5000 (vec)
+    # packed rows of several conv tiles (2048 f16 or 1024 f32 columns):
+    # sequences that start one or two columns before a tile's end, so that
+    # their first width-1 outputs span two tiles, with and without a
+    # history; one that starts on a tile boundary; and a padded sequence
+    # next to them
+    ("m1_f16_starts_at_tile_edges", dict(io="f16", state="f32", nheads=8, nslots=8, seed=28),
+     [5, 2042, 3, 1, 2045, 8], None),                                # total 4104 (vec)
+    ("m1_f16_start_before_edge_padded", dict(io="f16", state="f16", nheads=6, nslots=8, seed=29),
+     [6, 2040, 700, 6], 3),                                          # total 2752 (vec)
+    ("m1_f32_start_at_tile_edge", dict(io="f32", state="f32", nheads=6, nslots=8, seed=30),
+     [1021, 1, 4, 900, 2], None),                                    # total 1928 (vec)
+    ("m1_bf16_w2_start_at_tile_edge", dict(io="bf16", state="f32", nheads=4, width=2, nslots=8, seed=31),
+     [2047, 2, 7, 2000], 0),                                         # total 4056 (vec)
     # more sequences than the conv kernel stages in LDS (its global-table path)
     ("m1_f16_300_seqs", dict(io="f16", state="f32", nheads=8, nslots=320, seed=19),
      [0, 3] + W.varlen_lengths(19, 298, 2395), None),                    # total 2398
