@@ -506,7 +506,7 @@ int prepare_ssu(SsuArgs &a, const ssm_tensor &state, const int32_t *slot_idx, co
         ++lg;
     const int64_t nrows = (int64_t)batch * nheads * headdim;
     const int rb = ssu_requests_per_lane(batch, headdim);
-    if (((((int64_t)nheads * headdim) << lg) + 63) / 64 > INT32_MAX || (batch + rb - 1) / rb > 65535)
+    if (((((int64_t)nheads * headdim) << lg) + 63) / 64 > INT32_MAX)
         return SSM_ERR_UNSUPPORTED;
     a = SsuArgs{};
     a.state = state.data;

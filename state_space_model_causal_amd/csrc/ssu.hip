@@ -24,6 +24,9 @@
 // no barriers.  V and the workgroup size (64 to 512 lanes) are chosen per
 // shape on the host, from a table tuned on gfx950 or a heuristic, or given by
 // the caller.
+#include <algorithm>
+#include <type_traits>
+
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
 
@@ -626,13 +629,54 @@ static hipError_t launch_ssu_s(const SsuArgs &a, hipStream_t stream)
     }
 }
 
-hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream)
+static hipError_t launch_ssu_one(const SsuArgs &a, hipStream_t stream)
 {
     switch (a.state_dtype) {
     case 0: return launch_ssu_s<float>(a, stream);
     case 1: return launch_ssu_s<f16>(a, stream);
     default: return launch_ssu_s<bf16>(a, stream);
     }
+}
+
+template <typename P>
+static P *advance(P *p, int64_t elems, int elem_bytes)
+{
+    using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+    return p ? reinterpret_cast<P *>(reinterpret_cast<C *>(p) + elems * elem_bytes) : p;
+}
+
+// The request groups of a launch sit on the grid's y dimension (at most
+// 65535 of them); a larger batch is launched in consecutive parts of that
+// many groups, each with its request rows, and (without a slot table) its
+// state and conv-cache rows, offset to its first request.
+hipError_t launch_ssu(const SsuArgs &a, hipStream_t stream)
+{
+    const int64_t per = (int64_t)65535 * a.requests_per_lane;
+    if (a.batch <= per)
+        return launch_ssu_one(a, stream);
+    const int io = a.io_dtype == 0 ? 4 : 2, sd = a.state_dtype == 0 ? 4 : 2;
+    for (int64_t b0 = 0; b0 < a.batch; b0 += per) {
+        SsuArgs c = a;
+        c.batch = (int)std::min<int64_t>(per, a.batch - b0);
+        c.nrows = (int64_t)c.batch * a.nheads * a.headdim;
+        c.x = advance(a.x, b0 * a.x_sb, io);
+        c.dt = advance(a.dt, b0 * a.dt_sb, io);
+        c.B = advance(a.B, b0 * a.B_sb, io);
+        c.C = advance(a.C, b0 * a.C_sb, io);
+        c.z = advance(a.z, b0 * a.z_sb, io);
+        c.out = advance(a.out, b0 * a.o_sb, io);
+        c.u_out = advance(a.u_out, b0 * a.u_sb, io);
+        if (a.slot_idx) {
+            c.slot_idx = a.slot_idx + b0;
+        } else {  // slot = request
+            c.state = advance(a.state, b0 * a.st_ss, sd);
+            c.conv_state = advance(a.conv_state, b0 * a.cs_ss, io);
+        }
+        const hipError_t e = launch_ssu_one(c, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 } // namespace ssm

@@ -280,8 +280,10 @@ def run_ssu(ssm, oracle, dev, spec, opts, label, t=None):
     idx = _pad(t["slot_idx"], opts.get("pad", 0))
     st0 = t["ssm_state"].clone()
     out0 = torch.full_like(t["x"], 3.0)
+    # without a table the slot of request b is b (the arange the oracle takes)
     out = ssm.state_update(t["ssm_state"], t["x"], t["dt"], t["A"], t["B"], t["C"], D=D, z=z,
-                           dt_bias=bias, slot_idx=idx, out=out0.clone())
+                           dt_bias=bias, slot_idx=None if opts.get("no_table") else idx,
+                           out=out0.clone())
     torch.cuda.synchronize()
     idx_np = idx.cpu().numpy()
     o, s, st, sts = oracle.state_update(
@@ -510,7 +512,8 @@ def run_decode_step(ssm, oracle, spec, t, opts, label):
     u_out = torch.full_like(t["x"], 9.0)
     out = ssm.decode_step(t["ssm_state"], t["conv_state"], t["x"], t["conv_w"], t["dt"], t["A"],
                           t["B"], t["C"], conv_bias=t["conv_b"], D=D, z=z, dt_bias=bias,
-                          slot_idx=idx, out=out0.clone(), u_out=u_out)
+                          slot_idx=None if opts.get("no_table") else idx, out=out0.clone(),
+                          u_out=u_out)
     torch.cuda.synchronize()
     idx_np = idx.cpu().numpy()
     Bt, Cn = spec.batch, spec.channels
@@ -544,6 +547,29 @@ def run_decode_step(ssm, oracle, spec, t, opts, label):
 def test_decode_step_parity(dev, ssm, oracle, label, kw, opts):
     spec = W.tiny(**kw)
     run_decode_step(ssm, oracle, spec, W.make(spec, dev), opts, label)
+
+
+# Batches whose request groups (one or two requests per lane) exceed the
+# grid's y dimension (65535): the update is launched in parts of that many
+# groups; without a slot table each part's state and conv-cache rows start at
+# its first request.
+BIG_BATCH_CASES = [
+    ("m1_two_per_lane_table", dict(seqlen=1, nheads=2, dstate=16, io="f16", state="f32",
+                                   batch=140001, nslots=140007, random_slots=True,
+                                   index_sensitive=True), dict(pad=7)),
+    ("m1_two_per_lane_no_table", dict(seqlen=1, nheads=2, dstate=16, io="f32", state="f32",
+                                      batch=131075, index_sensitive=True), dict(no_table=True)),
+    ("m2_one_per_lane_no_table", dict(seqlen=1, nheads=1, headdim=4, dstate=16, io="bf16",
+                                      state="bf16", a_per_state=False, batch=65539,
+                                      index_sensitive=True), dict(no_table=True)),
+]
+
+
+@pytest.mark.parametrize("label,kw,opts", BIG_BATCH_CASES, ids=[c[0] for c in BIG_BATCH_CASES])
+def test_state_update_and_decode_step_past_grid_limit(dev, ssm, oracle, label, kw, opts):
+    spec = W.tiny(**kw)
+    run_ssu(ssm, oracle, dev, spec, opts, label + " ssu")
+    run_decode_step(ssm, oracle, spec, W.make(spec, dev), opts, label + " decode")
 
 
 def test_decode_step_chain_matches_prefill(dev, ssm, oracle):
