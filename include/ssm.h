@@ -102,7 +102,8 @@ typedef struct ssm_tensor {
  *
  * seqlen == 1 with has_initial_state is the decode update (one output, window
  * shifted by one); prefill writes the tail a later decode step starts from.
- * Limits: 1 <= width <= 4 (else SSM_ERR_UNSUPPORTED).
+ * Limits: 1 <= width <= 4 and batch*channels <= 2^31-1 (else
+ * SSM_ERR_UNSUPPORTED).
  */
 int ssm_causal_conv1d(ssm_tensor x, ssm_tensor weight, ssm_tensor bias, ssm_tensor conv_state,
                       const int32_t *slot_idx, ssm_tensor out, int batch, int channels,
@@ -302,6 +303,7 @@ int ssm_decode_step(ssm_tensor state, ssm_tensor conv_state, const int32_t *slot
  *   x, out      io dtype [channels, total_len]
  *   other arguments as in ssm_causal_conv1d; the conv cache of each sequence
  *   receives the last width-1 samples of its history || its samples.
+ *   Limit: channels <= 65535 (else SSM_ERR_UNSUPPORTED).
  */
 int ssm_causal_conv1d_varlen(ssm_tensor x, ssm_tensor weight, ssm_tensor bias,
                              ssm_tensor conv_state, const int32_t *slot_idx,
