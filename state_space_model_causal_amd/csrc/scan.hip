@@ -14,9 +14,9 @@
 //   * The sequence is walked in tiles of 16 K timesteps; lane r of a channel
 //     owns timesteps [K r, K r + K) of the tile (K = 16: 128-bit loads of u,
 //     dt and z).  In packed batches, and in dense rows whose length is not
-//     a multiple of 256, each sequence ends in shorter tiles (K = 8, then 4:
-//     64-bit loads for 2-byte types), so that it pads its last tile by fewer
-//     than 64 steps.
+//     a multiple of 256, each sequence ends in shorter tiles (K = 8, then at
+//     most one each of K = 4, 2 and 1, with 8-, 4- and 2-byte loads for
+//     2-byte types), so that it pads its last tile by fewer than 16 steps.
 //   * For each state n, every lane reduces its K steps to one affine map
 //     h -> a*h + b (a = product of decays, b = local state from zero), the 16
 //     maps of a row are combined by an inclusive Hillis-Steele scan with DPP
@@ -54,7 +54,7 @@ template <typename TI, bool VEC, int K>
 __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, int lo, int hi, float (&dst)[K])
 {
     constexpr int E = 16 / StorageSize<TI>::value;
-    if constexpr (VEC) {
+    if constexpr (VEC && K >= E) {
         // a vector that starts before hi ends inside the row (rows are a
         // multiple of 8 long and 16-byte aligned), and column 0 is a valid vector
 #pragma unroll
@@ -78,8 +78,8 @@ __device__ __forceinline__ void load_steps(const TI *__restrict__ row, int tl, i
 
 // Raw vector loads of timesteps [tl, tl+K) of one row (VEC rows only),
 // issued back to back; widen() converts them once they are needed.  A lane's
-// K steps are 128-bit vectors, or one 64-bit vector when they are narrower
-// (4 steps of a 2-byte type).
+// K steps are 128-bit vectors, or one narrower vector (8, 4 or 2 bytes) when
+// they take less than 16 bytes.
 template <typename TI, int K>
 struct RawSteps {
     static constexpr int VB = K * StorageSize<TI>::value >= 16 ? 16 : K * StorageSize<TI>::value;
@@ -99,9 +99,13 @@ __device__ __forceinline__ void load_raw(RawSteps<TI, K> &r, const TI *__restric
         const TI *p = row + (r.ok[v] ? off : 0);
         if constexpr (RawSteps<TI, K>::VB == 16) {
             r.w[v] = *reinterpret_cast<const u32x4 *>(p);
-        } else {
+        } else if constexpr (RawSteps<TI, K>::VB == 8) {
             const uint2 q = *reinterpret_cast<const uint2 *>(p);
             r.w[v] = u32x4{q.x, q.y, 0u, 0u};
+        } else if constexpr (RawSteps<TI, K>::VB == 4) {
+            r.w[v] = u32x4{*reinterpret_cast<const uint32_t *>(p), 0u, 0u, 0u};
+        } else {
+            r.w[v] = u32x4{(uint32_t)*reinterpret_cast<const uint16_t *>(p), 0u, 0u, 0u};
         }
     }
 }
@@ -116,9 +120,10 @@ __device__ __forceinline__ void widen(const RawSteps<TI, K> &r, float (&dst)[K])
     constexpr int E = RawSteps<TI, K>::E, PW = PerWord<TI>::value;
 #pragma unroll
     for (int v = 0; v < RawSteps<TI, K>::NV; ++v) {
-        float part[E];
+        float part[4 * PW];
         unpack_word(r.w[v].x, &part[0 * PW], TI{});
-        unpack_word(r.w[v].y, &part[1 * PW], TI{});
+        if constexpr (RawSteps<TI, K>::VB >= 8)
+            unpack_word(r.w[v].y, &part[1 * PW], TI{});
         if constexpr (RawSteps<TI, K>::VB == 16) {
             unpack_word(r.w[v].z, &part[2 * PW], TI{});
             unpack_word(r.w[v].w, &part[3 * PW], TI{});
@@ -141,14 +146,18 @@ __device__ __forceinline__ void store_steps(TI *__restrict__ row, int tl, int lo
         for (int v = 0; v < K / E; ++v) {
             const int off = tl + v * E;
             if (off >= lo && off + E <= hi) {
-                float part[E];
+                float part[E < PW ? PW : E];
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     part[e] = src[v * E + e];
                 if constexpr (RawSteps<TI, K>::VB == 16)
                     store_vec_cached<TI, E>(row + off, part);
-                else
+                else if constexpr (RawSteps<TI, K>::VB == 8)
                     *reinterpret_cast<uint2 *>(row + off) = uint2{pack_word(&part[0], TI{}), pack_word(&part[PW], TI{})};
+                else if constexpr (RawSteps<TI, K>::VB == 4)
+                    *reinterpret_cast<uint32_t *>(row + off) = pack_word(&part[0], TI{});
+                else
+                    row[off] = from_f32<TI>(part[0]);
             } else if (off + E > lo && off < hi) {
 #pragma unroll
                 for (int e = 0; e < E; ++e)
@@ -203,7 +212,7 @@ __device__ __forceinline__ int packed_seq_of_rank(const int32_t *__restrict__ cu
 }
 
 // Walks: WALK_DENSE, tiles of 16 steps per lane; WALK_LADDER, the same
-// ending in tiles of 8 and 4 steps per lane, for packed batches (their
+// ending in tiles of 8, 4, 2 and 1 steps per lane, for packed batches (their
 // sequences handed out longest first) and for dense rows whose length is not
 // a multiple of 256.
 enum { WALK_DENSE = 0, WALK_LADDER = 1 };
@@ -385,7 +394,9 @@ void scan_kernel(ScanArgs a)
 #pragma unroll
                 for (int e4 = 0; e4 < E / 4; ++e4) {
                     const int tt = tc + 4 * e4;
-                    const int idx = (nl * (K / 4) + (tt % K) / 4) * R + tt / K;
+                    // tiles of fewer than 4 steps per lane: the state's T steps
+                    // in order (a lane reads its K consecutive floats)
+                    const int idx = K >= 4 ? (nl * (K / 4) + (tt % K) / 4) * R + tt / K : (nl * T + tt) / 4;
                     lds_b[idx] = make_float4(vb[4 * e4], vb[4 * e4 + 1], vb[4 * e4 + 2], vb[4 * e4 + 3]);
                     lds_c[idx] = make_float4(vc[4 * e4], vc[4 * e4 + 1], vc[4 * e4 + 2], vc[4 * e4 + 3]);
                 }
@@ -399,12 +410,22 @@ void scan_kernel(ScanArgs a)
                     break;
                 const int n = n0 + nl;
                 float Bv[K], Cv[K];
+                if constexpr (K >= 4) {
 #pragma unroll
-                for (int q = 0; q < K / 4; ++q) {
-                    const float4 vb = lds_b[(nl * (K / 4) + q) * R + r];
-                    const float4 vc = lds_c[(nl * (K / 4) + q) * R + r];
-                    Bv[4 * q] = vb.x; Bv[4 * q + 1] = vb.y; Bv[4 * q + 2] = vb.z; Bv[4 * q + 3] = vb.w;
-                    Cv[4 * q] = vc.x; Cv[4 * q + 1] = vc.y; Cv[4 * q + 2] = vc.z; Cv[4 * q + 3] = vc.w;
+                    for (int q = 0; q < K / 4; ++q) {
+                        const float4 vb = lds_b[(nl * (K / 4) + q) * R + r];
+                        const float4 vc = lds_c[(nl * (K / 4) + q) * R + r];
+                        Bv[4 * q] = vb.x; Bv[4 * q + 1] = vb.y; Bv[4 * q + 2] = vb.z; Bv[4 * q + 3] = vb.w;
+                        Cv[4 * q] = vc.x; Cv[4 * q + 1] = vc.y; Cv[4 * q + 2] = vc.z; Cv[4 * q + 3] = vc.w;
+                    }
+                } else {
+                    const float *fb = reinterpret_cast<const float *>(lds_b) + nl * T + r * K;
+                    const float *fc = reinterpret_cast<const float *>(lds_c) + nl * T + r * K;
+#pragma unroll
+                    for (int i = 0; i < K; ++i) {
+                        Bv[i] = fb[i];
+                        Cv[i] = fc[i];
+                    }
                 }
                 const float cin = lds_carry[ch][n];
                 const float carry = (r == 0) ? cin : 0.0f;
@@ -476,15 +497,25 @@ void scan_kernel(ScanArgs a)
     if constexpr (WALK != WALK_DENSE) {
         // Each sequence pads its last tile to a tile boundary.  Tiles of 16
         // steps per lane while more than 3/4 of one remains, then of 8 while
-        // more than 64 steps remain, then one of 4: under 64 padded steps
-        // per sequence, and the dense per-step cost for the rest.
+        // more than 64 steps remain, then at most one each of 4, 2 and 1
+        // (64, 32 and 16 steps), each taken while more than half of it
+        // remains: under 16 padded steps per sequence, and the dense
+        // per-step cost for the rest.
         int t0 = 0;
         for (; hi - t0 > 3 * R * KD / 4; t0 += R * KD)
             tile(std::integral_constant<int, KD>{}, t0);
         for (; hi - t0 > R * 4; t0 += R * 8)
             tile(std::integral_constant<int, 8>{}, t0);
-        if (t0 < hi)
+        if (hi - t0 > R * 2) {
             tile(std::integral_constant<int, 4>{}, t0);
+            t0 += R * 4;
+        }
+        if (hi - t0 > R) {
+            tile(std::integral_constant<int, 2>{}, t0);
+            t0 += R * 2;
+        }
+        if (t0 < hi)
+            tile(std::integral_constant<int, 1>{}, t0);
     } else {
         for (int t0 = 0; t0 < hi; t0 += R * KD)
             tile(std::integral_constant<int, KD>{}, t0);
