@@ -145,7 +145,7 @@ int ssm_selective_scan(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, ssm_tens
  *   algo  SSM_SCAN_AUTO: the library's choice;
  *         SSM_SCAN_RECURRENT: the step-by-step recurrence (any shape);
  *         SSM_SCAN_CHUNKED: the chunked matrix form on the matrix cores.
- * The chunked form needs one decay per head (a_per_state == 0), bf16 I/O,
+ * The chunked form needs one decay per head (a_per_state == 0), f16 or bf16 I/O,
  * dstate 64, 128 or 256, headdim a multiple of 64, seqlen a multiple of 8,
  * 16-byte aligned rows, B and C (request, group) planes spanning less than
  * 4 GiB, and a dense [.., headdim, dstate] state slot;
@@ -154,10 +154,13 @@ int ssm_selective_scan(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, ssm_tens
  * recurrence: over a chunk of steps with one scalar decay per step, the state
  * recursion unrolls into products of small matrices (decay-weighted C.B^T
  * within the chunk, C times the carried state, and the decay-weighted B
- * times u for the next state), which run on MFMA with float32 accumulation;
- * operands that are not exact in bf16 are split into two bf16 parts (about
- * 16 significant bits per product).  Other arguments as in
- * ssm_selective_scan.
+ * times u for the next state), which run on MFMA with float32 accumulation.
+ * With bf16 I/O, operands that are not exact in bf16 are split into two bf16
+ * parts (about 16 significant bits per product).  With f16 I/O, C.B^T runs on
+ * the f16 instruction, u is split exactly into two bf16 parts for the bf16
+ * decay matrix, and the carried state and the weighted u are split into two
+ * f16 parts under a power-of-two scale per row (about 22 bits).  Other
+ * arguments as in ssm_selective_scan.
  */
 #define SSM_SCAN_AUTO 0
 #define SSM_SCAN_RECURRENT 1

@@ -36,6 +36,7 @@
 // C read once (B and C from L2 for every head of a group), out written once,
 // the state read and written once.
 #include <algorithm>
+#include <type_traits>
 
 #include "ssm_device.hpp"
 #include "ssm_kernels.hpp"
@@ -78,6 +79,67 @@ __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8_t &hi, bf
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8_t, w); }
 
+// f16 I/O: the f16 matrix instruction of the same shape and lane layout
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8_t as_f16x8(u32x4 w) { return __builtin_bit_cast(f16x8_t, w); }
+__device__ __forceinline__ f32x4_t mma16(f16x8_t a, f16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// The product of two operands exact in the I/O type (B and C as stored).
+template <typename TI>
+__device__ __forceinline__ f32x4_t mma_io(u32x4 a, u32x4 b, f32x4_t c)
+{
+    if constexpr (std::is_same<TI, f16>::value)
+        return mma16(as_f16x8(a), as_f16x8(b), c);
+    else
+        return mma(as_bf16x8(a), as_bf16x8(b), c);
+}
+
+// 8 values of the I/O type (raw bits) as floats
+template <typename TI>
+__device__ __forceinline__ void widen8(u32x4 w, float (&x)[8])
+{
+    unpack_word(w.x, &x[0], TI{});
+    unpack_word(w.y, &x[2], TI{});
+    unpack_word(w.z, &x[4], TI{});
+    unpack_word(w.w, &x[6], TI{});
+}
+
+// A power of two s, and 1/s, that bring m (>= 0) into [2^13, 2^14): the
+// scale under which float32 values of magnitude <= m split into f16 high and
+// low parts without overflow, with 22 significant bits for the largest
+// (exponents clamped to the normal range; a zero m gives the largest s).
+__device__ __forceinline__ void pow2_scale(float m, float &s, float &inv)
+{
+    const int be = (__float_as_int(m) >> 23) & 0xff;  // m = f 2^(be-126), f in [0.5, 1)
+    int k = 14 - (be - 126);
+    k = k < -126 ? -126 : (k > 126 ? 126 : k);
+    s = __int_as_float((k + 127) << 23);
+    inv = __int_as_float((127 - k) << 23);
+}
+
+// x s = hi + lo with hi and lo in f16 (|x s| <= 2^14)
+__device__ __forceinline__ void split_f16(const float (&x)[8], float s, f16x8_t &hi, f16x8_t &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float v = x[i] * s;
+        const _Float16 h = (_Float16)v;
+        hi[i] = h;
+        lo[i] = (_Float16)(v - (float)h);
+    }
+}
+
+// the largest value over the 4 lanes that share lane % 16 (the lanes that
+// hold one column of an MFMA operand or result)
+__device__ __forceinline__ float col_max4(float m)
+{
+    m = fmaxf(m, __shfl_xor(m, 16));
+    return fmaxf(m, __shfl_xor(m, 32));
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -97,12 +159,12 @@ __device__ __forceinline__ uint2 ds_read_tr(const __bf16 *p)
 // column c0 + (lane % 16) of a row-major LDS tile with row stride ld: the
 // k-operand of one lane of v_mfma_f32_16x16x32_bf16 from the natural layout.
 // n0 and c0 may differ between the lane's 16-lane groups.
-__device__ __forceinline__ bf16x8_t col8_tr(const __bf16 *tile, int ld, int n0, int n0b, int c0, int l16)
+__device__ __forceinline__ u32x4 col8_tr(const __bf16 *tile, int ld, int n0, int n0b, int c0, int l16)
 {
     const int i = l16 >> 2, a = l16 & 3;
     const uint2 lo = ds_read_tr(tile + (n0 + i) * ld + c0 + 4 * a);
     const uint2 hi = ds_read_tr(tile + (n0b + i) * ld + c0 + 4 * a);
-    return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
 constexpr int SNW = 8;           // waves per workgroup
@@ -110,25 +172,25 @@ constexpr int STHREADS = 64 * SNW;
 
 // Global data of one chunk, loaded a chunk ahead (registers) so that the
 // loads of chunk c+1 are in flight while chunk c is computed.
-template <int N>
+template <typename TI, int N>
 struct ChunkLoads {
     static constexpr int NUNITS = (N / 2) * (SQ / 8);  // (pair of states, 8 steps)
     static constexpr int UNITS = (NUNITS + STHREADS - 1) / STHREADS;
     u32x4 b0[UNITS], b1[UNITS], c0[UNITS], c1[UNITS];
     u32x4 x[2];          // X[p][t0 + 32 kk + 8 lq .. +8)
     uint2 xo[2], zo[2];  // u and z at steps t0 + 16 st + 4 lq .. +4, this wave's 2 row tiles
-    bf16 dt;             // dt of step t0 + lane, as stored (wave 0 widens it when staging)
+    TI dt;               // dt of step t0 + lane, as stored (wave 0 widens it when staging)
 };
 
 // The B (or C) part of a chunk's loads: unit u of the chunk is a pair of
 // states and 8 steps.
-template <int N>
-__device__ __forceinline__ void load_pairs(u32x4 (&v0)[ChunkLoads<N>::UNITS], u32x4 (&v1)[ChunkLoads<N>::UNITS],
-                                           int t0, int L, const bf16 *G, int64_t sn, int tid)
+template <typename TI, int N>
+__device__ __forceinline__ void load_pairs(u32x4 (&v0)[(ChunkLoads<TI, N>::UNITS)], u32x4 (&v1)[(ChunkLoads<TI, N>::UNITS)],
+                                           int t0, int L, const TI *G, int64_t sn, int tid)
 {
 #pragma unroll
-    for (int k = 0; k < ChunkLoads<N>::UNITS; ++k) {
-        const int u = min(tid + STHREADS * k, ChunkLoads<N>::NUNITS - 1);
+    for (int k = 0; k < ChunkLoads<TI, N>::UNITS; ++k) {
+        const int u = min(tid + STHREADS * k, ChunkLoads<TI, N>::NUNITS - 1);
         const int n = 2 * (u >> 3), tv = u & 7;
         const int t = t0 + 8 * tv;
         const int tc = t < L ? t : 0;  // clamped; zeroed when staged
@@ -142,9 +204,9 @@ __device__ __forceinline__ void load_pairs(u32x4 (&v0)[ChunkLoads<N>::UNITS], u3
 }
 
 // The rest of a chunk's loads: u, z and dt.
-template <int N>
-__device__ __forceinline__ void load_rows(ChunkLoads<N> &c, int t0, int L, const bf16 *urow, const bf16 *zrow,
-                                          const bf16 *dtrow, int l, int lq, int nh)
+template <typename TI, int N>
+__device__ __forceinline__ void load_rows(ChunkLoads<TI, N> &c, int t0, int L, const TI *urow, const TI *zrow,
+                                          const TI *dtrow, int l, int lq, int nh)
 {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -156,7 +218,7 @@ __device__ __forceinline__ void load_rows(ChunkLoads<N> &c, int t0, int L, const
     // every load issued before it (the whole chunk).  Without a gate the z
     // load reads u, and the value goes unused; every wave loads dt (wave 0
     // uses it).
-    const bf16 *zsrc = zrow ? zrow : urow;
+    const TI *zsrc = zrow ? zrow : urow;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int t = t0 + 16 * (2 * nh + i) + 4 * lq;
@@ -170,14 +232,14 @@ __device__ __forceinline__ void load_rows(ChunkLoads<N> &c, int t0, int L, const
     }
 }
 
-template <int N>
-__device__ __forceinline__ void load_chunk(ChunkLoads<N> &c, int t0, int L, const bf16 *Bg, const bf16 *Cg,
-                                           int64_t bsn, int64_t csn, const bf16 *urow, const bf16 *zrow,
-                                           const bf16 *dtrow, int tid, int l, int lq, int nh)
+template <typename TI, int N>
+__device__ __forceinline__ void load_chunk(ChunkLoads<TI, N> &c, int t0, int L, const TI *Bg, const TI *Cg,
+                                           int64_t bsn, int64_t csn, const TI *urow, const TI *zrow,
+                                           const TI *dtrow, int tid, int l, int lq, int nh)
 {
-    load_pairs<N>(c.b0, c.b1, t0, L, Bg, bsn, tid);
-    load_pairs<N>(c.c0, c.c1, t0, L, Cg, csn, tid);
-    load_rows<N>(c, t0, L, urow, zrow, dtrow, l, lq, nh);
+    load_pairs<TI, N>(c.b0, c.b1, t0, L, Bg, bsn, tid);
+    load_pairs<TI, N>(c.c0, c.c1, t0, L, Cg, csn, tid);
+    load_rows<TI, N>(c, t0, L, urow, zrow, dtrow, l, lq, nh);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -187,7 +249,7 @@ __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 
 // and half of the states, n-tiles [NT/2 (w/4), NT/2 (w/4 + 1)); the two
 // waves of a row block exchange their halves of C.H through LDS and each
 // writes half of the chunk's output rows (row tiles 2 (w/4) and 2 (w/4) + 1).
-template <typename TS, int N>
+template <typename TI, typename TS, int N>
 __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 {
     constexpr int LDQ = SQ + 8;  // row stride of the natural B and C tiles and of M
@@ -221,12 +283,13 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     const int partner = pw + 4 * (1 - nh);
     const int p = pb * SPB + 16 * pw + l16;   // this lane's row of headdim
     const int64_t c = (int64_t)h * P + p;  // channel
-    const bf16 *urow = static_cast<const bf16 *>(a.u) + b * a.u_sb + c * a.u_sc;
-    const bf16 *zrow = a.z ? static_cast<const bf16 *>(a.z) + b * a.z_sb + c * a.z_sc : nullptr;
-    bf16 *orow = static_cast<bf16 *>(a.out) + b * a.o_sb + c * a.o_sc;
-    const bf16 *dtrow = static_cast<const bf16 *>(a.dt) + b * a.dt_sb + h * a.dt_sh;
-    const bf16 *Bg = static_cast<const bf16 *>(a.B) + b * a.B_sb + g * a.B_sg;
-    const bf16 *Cg = static_cast<const bf16 *>(a.C) + b * a.C_sb + g * a.C_sg;
+    constexpr bool F16 = std::is_same<TI, f16>::value;
+    const TI *urow = static_cast<const TI *>(a.u) + b * a.u_sb + c * a.u_sc;
+    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + b * a.z_sb + c * a.z_sc : nullptr;
+    TI *orow = static_cast<TI *>(a.out) + b * a.o_sb + c * a.o_sc;
+    const TI *dtrow = static_cast<const TI *>(a.dt) + b * a.dt_sb + h * a.dt_sh;
+    const TI *Bg = static_cast<const TI *>(a.B) + b * a.B_sb + g * a.B_sg;
+    const TI *Cg = static_cast<const TI *>(a.C) + b * a.C_sb + g * a.C_sg;
     TS *srow = a.state ? static_cast<TS *>(a.state) + slot * a.st_ss + h * a.st_sh + p * a.st_sp : nullptr;
 
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
@@ -255,8 +318,8 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         s_ml[s * LDQ + r] = (__bf16)0.0f;
     }
 
-    ChunkLoads<N> cur;
-    load_chunk<N>(cur, 0, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, l, lq, nh);
+    ChunkLoads<TI, N> cur;
+    load_chunk<TI, N>(cur, 0, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, l, lq, nh);
 
     for (int t0 = 0; t0 < L; t0 += SQ) {
         const int par = (t0 / SQ) & 1;
@@ -279,9 +342,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 s_etot[0] = exp2_hw(tot);
         }
 #pragma unroll
-        for (int k = 0; k < ChunkLoads<N>::UNITS; ++k) {
+        for (int k = 0; k < ChunkLoads<TI, N>::UNITS; ++k) {
             const int u = tid + STHREADS * k;
-            if (u < ChunkLoads<N>::NUNITS) {
+            if (u < ChunkLoads<TI, N>::NUNITS) {
                 const int n = 2 * (u >> 3), tv = u & 7;
                 const bool ok = t0 + 8 * tv < L;  // L % 8 == 0: a vector is all in or all out
                 const u32x4 z4 = {0u, 0u, 0u, 0u};
@@ -293,11 +356,23 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                 *reinterpret_cast<u32x4 *>(&s_cn[(n + 1) * LDQ + 8 * tv]) = c1;
             }
         }
-        bf16x8_t xk[2];
+        u32x4 xk[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            xk[kk] = as_bf16x8(t0 + 32 * kk + 8 * lq < L ? cur.x[kk] : u32x4{0u, 0u, 0u, 0u});
+            xk[kk] = t0 + 32 * kk + 8 * lq < L ? cur.x[kk] : u32x4{0u, 0u, 0u, 0u};
         const uint2 xo[2] = {cur.xo[0], cur.xo[1]}, zo[2] = {cur.zo[0], cur.zo[1]};
+        // f16 I/O: X as the sum of two bf16 parts (exact: an f16 value's 11
+        // significant bits fit in a rounded bf16 and its remainder), the
+        // operand the bf16 decay matrix multiplies
+        bf16x8_t xkh[2], xkl[2];
+        if constexpr (F16) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float xf[8];
+                widen8<TI>(xk[kk], xf);
+                split_bf16(xf, xkh[kk], xkl[kk]);
+            }
+        }
         __syncthreads();
 
         // ---- the next chunk's loads, in flight during this chunk's work;
@@ -305,7 +380,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         // stalls on a full load queue for the whole chunk's worth at once
         const bool more = t0 + SQ < L;
         if (more)
-            load_pairs<N>(cur.c0, cur.c1, t0 + SQ, L, Cg, a.C_sn, tid);
+            load_pairs<TI, N>(cur.c0, cur.c1, t0 + SQ, L, Cg, a.C_sn, tid);
 
         // ---- carried state over this wave's half of the states:
         // yc[k] = sum_{n in half} C_s[n] H[p][n] over the steps s of row tile
@@ -314,32 +389,72 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         // operands (high and low parts) in the order the accumulators hold it
         f32x4_t yc[4];
         {
-            bf16x8_t hh[NTH / 2], hl[NTH / 2];
+            if constexpr (F16) {
+                // the f16 instruction takes C as stored; the state is split
+                // into f16 parts under a power-of-two scale per row p (this
+                // lane's column of every state tile), so no part overflows,
+                // and the products are scaled back
+                float m = 0.0f;
 #pragma unroll
-            for (int q2 = 0; q2 < NTH / 2; ++q2) {
-                float hv[8];
+                for (int q = 0; q < NTH; ++q)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    hv[i] = hacc[2 * q2][i];
-                    hv[4 + i] = hacc[2 * q2 + 1][i];
-                }
-                split_bf16(hv, hh[q2], hl[q2]);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int st = (k + 2 * (1 - nh)) & 3;
-                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                    for (int i = 0; i < 4; ++i)
+                        m = fmaxf(m, fabsf(hacc[q][i]));
+                float hsc, hinv;
+                pow2_scale(col_max4(m), hsc, hinv);
+                f16x8_t hh[NTH / 2], hl[NTH / 2];
 #pragma unroll
                 for (int q2 = 0; q2 < NTH / 2; ++q2) {
-                    const int kk = (NTH / 2) * nh + q2;  // 32-state step
-                    // C_s[n] for s = 16 st + l16 and the states of hh's order:
-                    // n = 32 kk + 4 lq + i and 32 kk + 16 + 4 lq + i
-                    const int nc = 32 * kk + 4 * lq;
-                    const bf16x8_t cv = col8_tr(s_cn, LDQ, nc, nc + 16, 16 * st, l16);
-                    acc = mma(cv, hh[q2], acc);
-                    acc = mma(cv, hl[q2], acc);
+                    float hv[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        hv[i] = hacc[2 * q2][i];
+                        hv[4 + i] = hacc[2 * q2 + 1][i];
+                    }
+                    split_f16(hv, hsc, hh[q2], hl[q2]);
                 }
-                yc[k] = acc;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int st = (k + 2 * (1 - nh)) & 3;
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int q2 = 0; q2 < NTH / 2; ++q2) {
+                        const int kk = (NTH / 2) * nh + q2;
+                        const int nc = 32 * kk + 4 * lq;
+                        const f16x8_t cv = as_f16x8(col8_tr(s_cn, LDQ, nc, nc + 16, 16 * st, l16));
+                        acc = mma16(cv, hh[q2], acc);
+                        acc = mma16(cv, hl[q2], acc);
+                    }
+                    yc[k] = acc * hinv;
+                }
+            } else {
+                bf16x8_t hh[NTH / 2], hl[NTH / 2];
+#pragma unroll
+                for (int q2 = 0; q2 < NTH / 2; ++q2) {
+                    float hv[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        hv[i] = hacc[2 * q2][i];
+                        hv[4 + i] = hacc[2 * q2 + 1][i];
+                    }
+                    split_bf16(hv, hh[q2], hl[q2]);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int st = (k + 2 * (1 - nh)) & 3;
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int q2 = 0; q2 < NTH / 2; ++q2) {
+                        const int kk = (NTH / 2) * nh + q2;  // 32-state step
+                        // C_s[n] for s = 16 st + l16 and the states of hh's order:
+                        // n = 32 kk + 4 lq + i and 32 kk + 16 + 4 lq + i
+                        const int nc = 32 * kk + 4 * lq;
+                        const bf16x8_t cv = as_bf16x8(col8_tr(s_cn, LDQ, nc, nc + 16, 16 * st, l16));
+                        acc = mma(cv, hh[q2], acc);
+                        acc = mma(cv, hl[q2], acc);
+                    }
+                    yc[k] = acc;
+                }
             }
             // the partner needs this half for its output row tiles
             *reinterpret_cast<f32x4_t *>(&s_x[partner][0][l][0]) = yc[0];
@@ -351,7 +466,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         float gz[2][4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const float zv[4] = {bf_lo(zo[i].x), bf_hi(zo[i].x), bf_lo(zo[i].y), bf_hi(zo[i].y)};
+            float zv[4];
+            unpack_word(zo[i].x, &zv[0], TI{});
+            unpack_word(zo[i].y, &zv[2], TI{});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 gz[i][j] = zrow ? silu_f32(zv[j]) : 1.0f;
@@ -362,7 +479,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         }
 
         if (more)
-            load_pairs<N>(cur.b0, cur.b1, t0 + SQ, L, Bg, a.B_sn, tid);
+            load_pairs<TI, N>(cur.b0, cur.b1, t0 + SQ, L, Bg, a.B_sn, tid);
 
         // ---- masked decay matrix M[s][r] = (C_s.B_r) exp(L_s - L_r) delta_r
         // for r <= s, over its 10 lower-triangle 16 x 16 tiles (st, rt).  The
@@ -381,9 +498,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 #pragma unroll
                     for (int kk = 0; kk < N / 32; ++kk) {
                         const int nb = 32 * kk + 8 * lq;
-                        const bf16x8_t av = col8_tr(s_bn, LDQ, nb, nb + 4, 16 * rt, l16);
-                        const bf16x8_t bv = col8_tr(s_cn, LDQ, nb, nb + 4, 16 * st, l16);
-                        acc = mma(av, bv, acc);
+                        const u32x4 av = col8_tr(s_bn, LDQ, nb, nb + 4, 16 * rt, l16);
+                        const u32x4 bv = col8_tr(s_cn, LDQ, nb, nb + 4, 16 * st, l16);
+                        acc = mma_io<TI>(av, bv, acc);
                     }
                     const float Ls = s_L[s];
                     const int r0 = 16 * rt + 4 * lq;
@@ -404,37 +521,72 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         }
 
         if (more)
-            load_rows<N>(cur, t0 + SQ, L, urow, zrow, dtrow, l, lq, nh);
+            load_rows<TI, N>(cur, t0 + SQ, L, urow, zrow, dtrow, l, lq, nh);
 
         // ---- state update of this wave's half: H <- exp(L_last) H +
         // sum_r B_r (w_r X_r)^T, w_r = exp(L_last - L_r) delta_r on this
         // lane's X (exact B is the other operand)
         {
             const float etot = s_etot[0];
-            bf16x8_t xwh[2], xwl[2];
+            float xw[2][8];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const float4 w0 = *reinterpret_cast<const float4 *>(&s_w[32 * kk + 8 * lq]);
                 const float4 w1 = *reinterpret_cast<const float4 *>(&s_w[32 * kk + 8 * lq + 4]);
                 const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-                float xw[8];
+                float xf[8];
+                widen8<TI>(xk[kk], xf);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    xw[i] = (float)xk[kk][i] * wv[i];
-                split_bf16(xw, xwh[kk], xwl[kk]);
+                    xw[kk][i] = xf[i] * wv[i];
             }
+            if constexpr (F16) {
+                // B as stored on the f16 instruction; the weighted X split into
+                // f16 parts under a power-of-two scale per row p (this lane's
+                // column), the products scaled back as they join the state
+                float m = 0.0f;
 #pragma unroll
-            for (int q = 0; q < NTH; ++q) {
-                const int nt = NTH * nh + q;
-                f32x4_t acc = hacc[q] * etot;
+                for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8_t braw = *reinterpret_cast<const bf16x8_t *>(
-                        &s_bn[(16 * nt + l16) * LDQ + 32 * kk + 8 * lq]);
-                    acc = mma(braw, xwh[kk], acc);
-                    acc = mma(braw, xwl[kk], acc);
+                    for (int i = 0; i < 8; ++i)
+                        m = fmaxf(m, fabsf(xw[kk][i]));
+                float wsc, winv;
+                pow2_scale(col_max4(m), wsc, winv);
+                f16x8_t xwh[2], xwl[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    split_f16(xw[kk], wsc, xwh[kk], xwl[kk]);
+#pragma unroll
+                for (int q = 0; q < NTH; ++q) {
+                    const int nt = NTH * nh + q;
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const f16x8_t braw = as_f16x8(*reinterpret_cast<const u32x4 *>(
+                            &s_bn[(16 * nt + l16) * LDQ + 32 * kk + 8 * lq]));
+                        acc = mma16(braw, xwh[kk], acc);
+                        acc = mma16(braw, xwl[kk], acc);
+                    }
+                    hacc[q] = hacc[q] * etot + acc * winv;
                 }
-                hacc[q] = acc;
+            } else {
+                bf16x8_t xwh[2], xwl[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    split_bf16(xw[kk], xwh[kk], xwl[kk]);
+#pragma unroll
+                for (int q = 0; q < NTH; ++q) {
+                    const int nt = NTH * nh + q;
+                    f32x4_t acc = hacc[q] * etot;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const bf16x8_t braw = *reinterpret_cast<const bf16x8_t *>(
+                            &s_bn[(16 * nt + l16) * LDQ + 32 * kk + 8 * lq]);
+                        acc = mma(braw, xwh[kk], acc);
+                        acc = mma(braw, xwl[kk], acc);
+                    }
+                    hacc[q] = acc;
+                }
             }
         }
         __syncthreads();  // M and the C.H halves visible
@@ -450,8 +602,14 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                     &s_mh[(16 * st + l16) * LDQ + 32 * kk + 8 * lq]);
                 const bf16x8_t ml = *reinterpret_cast<const bf16x8_t *>(
                     &s_ml[(16 * st + l16) * LDQ + 32 * kk + 8 * lq]);
-                y = mma(mh, xk[kk], y);
-                y = mma(ml, xk[kk], y);
+                if constexpr (F16) {
+                    y = mma(mh, xkh[kk], y);
+                    y = mma(mh, xkl[kk], y);
+                    y = mma(ml, xkh[kk], y);
+                } else {
+                    y = mma(mh, as_bf16x8(xk[kk]), y);
+                    y = mma(ml, as_bf16x8(xk[kk]), y);
+                }
             }
             const f32x4_t other = *reinterpret_cast<const f32x4_t *>(&s_x[w][i][l][0]);
             const int s0 = 16 * st + 4 * lq;
@@ -459,7 +617,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             if (t < L) {  // L % 4 == 0: the 4 steps are all in or all out
                 const float4 eL = *reinterpret_cast<const float4 *>(&s_eL[par][s0]);
                 const float el[4] = {eL.x, eL.y, eL.z, eL.w};
-                const float xv[4] = {bf_lo(xo[i].x), bf_hi(xo[i].x), bf_lo(xo[i].y), bf_hi(xo[i].y)};
+                float xv[4];
+                unpack_word(xo[i].x, &xv[0], TI{});
+                unpack_word(xo[i].y, &xv[2], TI{});
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -467,7 +627,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                     const float v = y[j] + el[j] * (mine[j] + other[j]) + Dh * xv[j];
                     o[j] = v * gz[i][j];
                 }
-                *reinterpret_cast<uint2 *>(orow + t) = uint2{pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
+                *reinterpret_cast<uint2 *>(orow + t) = uint2{pack_word(&o[0], TI{}), pack_word(&o[2], TI{})};
             }
         }
     }
@@ -481,16 +641,26 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     }
 }
 
-template <typename TS>
+template <typename TI, typename TS>
 static hipError_t launch_ssd_ts(const ScanArgs &a, hipStream_t stream)
 {
     const dim3 grid((unsigned)((int64_t)a.batch * a.nheads * (a.headdim / SPB)));
     switch (a.dstate) {
-    case 64: hipLaunchKernelGGL((ssd_kernel<TS, 64>), grid, dim3(STHREADS), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((ssd_kernel<TS, 128>), grid, dim3(STHREADS), 0, stream, a); break;
-    default: hipLaunchKernelGGL((ssd_kernel<TS, 256>), grid, dim3(STHREADS), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((ssd_kernel<TI, TS, 64>), grid, dim3(STHREADS), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((ssd_kernel<TI, TS, 128>), grid, dim3(STHREADS), 0, stream, a); break;
+    default: hipLaunchKernelGGL((ssd_kernel<TI, TS, 256>), grid, dim3(STHREADS), 0, stream, a); break;
     }
     return hipGetLastError();
+}
+
+template <typename TI>
+static hipError_t launch_ssd_t(const ScanArgs &a, hipStream_t stream)
+{
+    switch (a.state_dtype) {
+    case 0: return launch_ssd_ts<TI, float>(a, stream);
+    case 1: return launch_ssd_ts<TI, f16>(a, stream);
+    default: return launch_ssd_ts<TI, bf16>(a, stream);
+    }
 }
 
 bool ssd_supported(const ScanArgs &a)
@@ -498,18 +668,14 @@ bool ssd_supported(const ScanArgs &a)
     // B and C are addressed by 32-bit byte offsets from each (request, group)
     // base
     const int64_t span = (int64_t)2 * ((int64_t)(a.dstate - 1) * std::max(a.B_sn, a.C_sn) + a.seqlen);
-    return !a.cu_seqlens && !a.a_per_state && a.io_dtype == 2 && a.vec &&
+    return !a.cu_seqlens && !a.a_per_state && (a.io_dtype == 1 || a.io_dtype == 2) && a.vec &&
            (a.dstate == 64 || a.dstate == 128 || a.dstate == 256) && a.headdim % SPB == 0 &&
            span < ((int64_t)1 << 32);
 }
 
 hipError_t launch_ssd(const ScanArgs &a, hipStream_t stream)
 {
-    switch (a.state_dtype) {
-    case 0: return launch_ssd_ts<float>(a, stream);
-    case 1: return launch_ssd_ts<f16>(a, stream);
-    default: return launch_ssd_ts<bf16>(a, stream);
-    }
+    return a.io_dtype == 1 ? launch_ssd_t<f16>(a, stream) : launch_ssd_t<bf16>(a, stream);
 }
 
 } // namespace ssm

@@ -1,12 +1,15 @@
 """GPU parity of the chunked (matrix-core) Mamba-2 prefill against the float64
 oracle's recurrence, and against the step-by-step kernel on the same inputs.
 
-The chunked form applies to one decay per head, bf16 I/O, dstate 64/128/256,
-headdim a multiple of 64 and seqlen a multiple of 8.  Cases span one chunk and
-many, a ragged last chunk (seqlen not a multiple of 64), several workgroups
-per head (headdim 128), groups, initial states in every cache dtype, padded
-requests and the optional arguments.  Tolerance: the bf16 I/O bar of
-tests/_parity.py (3e-3 of the magnitude scale plus half an ulp).
+The chunked form applies to one decay per head, f16 or bf16 I/O, dstate
+64/128/256, headdim a multiple of 64 and seqlen a multiple of 8.  Cases span
+one chunk and many, a ragged last chunk (seqlen not a multiple of 64), several
+workgroups per head (headdim 128), groups, initial states in every cache
+dtype, padded requests and the optional arguments, each with both I/O types;
+with f16 I/O also a carried state beyond f16's range and values far below 1
+(the f16 parts of the state and the weighted u are taken under per-row
+power-of-two scales).  Tolerance: the 16-bit I/O bar of tests/_parity.py
+(3e-3 of the magnitude scale plus half an ulp).
 """
 import numpy as np
 import pytest
@@ -49,6 +52,13 @@ SSD_CASES = [
      dict(z=False, D=False, bias=False)),
     ("N64_no_softplus", dict(seqlen=96, nheads=2, headdim=64, dstate=64), dict(softplus=False)),
     ("N256_G4_L2048", dict(seqlen=2048, nheads=4, headdim=64, dstate=256, ngroups=4), {}),
+    # magnitudes: a carried state of up to ~10^5 (its f16 parts need the
+    # scale) with u x 100 and C x 10^-2 (so that the outputs stay within
+    # f16); then values around 10^-3 and a state around 10^-6
+    ("N128_large_state", dict(seqlen=256, nheads=2, headdim=64, dstate=128),
+     dict(init=True, state_scale=3e4, x_scale=100.0, c_scale=1e-2)),
+    ("N64_small_values", dict(seqlen=128, nheads=2, headdim=64, dstate=64),
+     dict(init=True, state_scale=1e-6, x_scale=1e-3)),
 ]
 
 
@@ -56,6 +66,12 @@ def _run(ssm, oracle, dev, spec, opts, label, algo):
     t = W.make(spec, dev)
     if not opts.get("softplus", True):
         t["dt"].abs_().add_(0.01)
+    if opts.get("state_scale"):
+        t["ssm_state"].mul_(opts["state_scale"])
+    if opts.get("x_scale"):
+        t["x"].mul_(opts["x_scale"])
+    if opts.get("c_scale"):
+        t["C"].mul_(opts["c_scale"])
     u = t["x"]
     z = t["z"] if opts.get("z", True) else None
     D = t["D"] if opts.get("D", True) else None
@@ -86,17 +102,19 @@ def _run(ssm, oracle, dev, spec, opts, label, algo):
     return out, t["ssm_state"]
 
 
+@pytest.mark.parametrize("io", ["bf16", "f16"])
 @pytest.mark.parametrize("label,kw,opts", SSD_CASES, ids=[c[0] for c in SSD_CASES])
-def test_chunked_scan_parity(dev, ssm, oracle, label, kw, opts):
-    spec = W.tiny(io="bf16", a_per_state=False, index_sensitive=True,
+def test_chunked_scan_parity(dev, ssm, oracle, label, kw, opts, io):
+    spec = W.tiny(io=io, a_per_state=False, index_sensitive=True,
                   **{**dict(state="f32"), **kw})
-    _run(ssm, oracle, dev, spec, opts, label, ssm.SCAN_CHUNKED)
+    _run(ssm, oracle, dev, spec, opts, f"{label} {io}", ssm.SCAN_CHUNKED)
 
 
-def test_auto_takes_the_chunked_form(dev, ssm):
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_auto_takes_the_chunked_form(dev, ssm, io):
     # the library's choice for a supported shape equals the explicit request,
     # bit for bit (same kernel)
-    spec = W.tiny(io="bf16", a_per_state=False, seqlen=128, nheads=2, headdim=64, dstate=128,
+    spec = W.tiny(io=io, a_per_state=False, seqlen=128, nheads=2, headdim=64, dstate=128,
                   index_sensitive=True)
     t = W.make(spec, dev)
     outs = []
@@ -109,9 +127,11 @@ def test_auto_takes_the_chunked_form(dev, ssm):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
-def test_chunked_and_recurrent_agree(dev, ssm):
-    # the two algorithms on the same inputs: within the bf16 bar of each other
-    spec = W.tiny(io="bf16", a_per_state=False, seqlen=640, nheads=2, headdim=128, dstate=256,
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_chunked_and_recurrent_agree(dev, ssm, io):
+    # the two algorithms on the same inputs: within the 16-bit I/O bar of
+    # each other
+    spec = W.tiny(io=io, a_per_state=False, seqlen=640, nheads=2, headdim=128, dstate=256,
                   index_sensitive=True, state="f32")
     t = W.make(spec, dev)
     res = {}
