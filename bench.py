@@ -594,9 +594,19 @@ def measure_chunked(ssm, W, dev, timer, mark):
 
     with mark("chunked_prefill"):
         us = timer.time(run)
+    # the same shape with f16 I/O (also the chunked form)
+    del sets[:]
+    for k in range(2):
+        t = W.make(W.m2_prefill(state="f32", io="f16", seed=spec.seed + 100 * k), dev)
+        t["out"] = torch.empty_like(t["x"])
+        sets.append(t)
+    with mark("chunked_prefill_f16"):
+        us16 = timer.time(run)
+    del sets[:]
     b = W.algorithmic_bytes(spec)["scan"]
     useful = W.chunked_mfma_flops(spec)
     issued = chunked_issued_mfma_flops(spec)
+    issued16 = chunked_issued_mfma_flops(spec, f16_io=True)
     return {"workload": "Mamba-2 prefill, 2 requests x L 4096, 64 heads, headdim 128, dstate 256, "
                         "1 group, bf16 I/O, f32 state to a 1024-slot cache, chunks of 64",
             "us": us, "tokens_per_s": spec.batch * spec.seqlen / (us * 1e-6),
@@ -611,18 +621,24 @@ def measure_chunked(ssm, W, dev, timer, mark):
             "issued_TFLOPs": issued / (us * 1e-6) / 1e12,
             "useful_frac_bf16_peak": useful / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "issued_frac_bf16_peak": issued / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "f16_io": {"us": us16, "tokens_per_s": spec.batch * spec.seqlen / (us16 * 1e-6),
+                       "GBps": b / (us16 * 1e-6) / 1e9,
+                       "frac_hbm_peak": b / (us16 * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                       "issued_mfma_flops": issued16,
+                       "issued_frac_16bit_peak": issued16 / (us16 * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
             "kernel_source_sha": kernel_source_sha(KERNEL_SOURCES["chunked_scan"])}
 
 
-def chunked_issued_mfma_flops(spec, chunk=64, rows=64):
+def chunked_issued_mfma_flops(spec, chunk=64, rows=64, f16_io=False):
     """Matrix work the chunked Mamba-2 kernel issues, per (request, head, 64
-    rows of headdim) workgroup and chunk of 64 steps, in 16x16x32 bf16 MFMAs
-    (16384 flops each): C times the carried state, split operand (4 step tiles
-    x dstate/32 x 2 x 4 row tiles); the masked C B^T on the 10 causal tiles of
-    16 (10 x dstate/32); the state update, split operand (dstate/16 x 2 x 2 x
-    4 row tiles); the outputs, split operand (12 x 4 row tiles)."""
+    rows of headdim) workgroup and chunk of 64 steps, in 16x16x32 MFMAs of a
+    16-bit type (16384 flops each): C times the carried state, split operand
+    (4 step tiles x dstate/32 x 2 x 4 row tiles); the masked C B^T on the 10
+    causal tiles of 16 (10 x dstate/32); the state update, split operand
+    (dstate/16 x 2 x 2 x 4 row tiles); the outputs, split operand (12 x 4 row
+    tiles; with f16 I/O 18 x 4, u being split as well)."""
     N = spec.dstate
-    per = 4 * (N // 32) * 2 * 4 + 10 * (N // 32) + (N // 16) * 2 * 2 * 4 + 12 * 4
+    per = 4 * (N // 32) * 2 * 4 + 10 * (N // 32) + (N // 16) * 2 * 2 * 4 + (18 if f16_io else 12) * 4
     wgs = spec.batch * spec.nheads * (spec.headdim // rows)
     chunks = (spec.seqlen + chunk - 1) // chunk
     return float(wgs * chunks * per * 16384)

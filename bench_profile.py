@@ -305,7 +305,9 @@ def summarize_profile(out):
         cl2, _ = _mean_counters(_counters(_one(f"{out}/copy_l2/*counter_collection.csv")),
                                 lambda n: "copyBuffer" in n)
         req_bytes = copy_bytes / cl2["TCP_TCC_READ_REQ_sum"] if cl2.get("TCP_TCC_READ_REQ_sum") else None
-        dc, ndc = _mean_counters(_counters(ssd_glob[0]), lambda nm: _library(nm) and "ssd_kernel" in nm)
+        # the bf16-I/O kernel (the counter pass also runs the f16-I/O one)
+        dc, ndc = _mean_counters(_counters(ssd_glob[0]),
+                                 lambda nm: _library(nm) and "ssd_kernelINS_4bf16" in nm)
         ch = cfgs.get("chunked_prefill") or {}
         ssd_us = _stat([d for ds in bym.get("chunked_prefill", {}).values() for d in ds])[1] \
             if "chunked_prefill" in bym else None
@@ -334,7 +336,8 @@ def summarize_profile(out):
     for labels, title, fname, rec in (
             (["tiny_conv1d", "tiny_scan", "tiny_pair"], "tiny Mamba-1 prefill (f32, L 64, d_inner 128)",
              "mamba1_tiny_prefill_kernels.md", cfgs.get("tiny_prefill")),
-            (["chunked_prefill"], "chunked Mamba-2 prefill on MFMA", "mamba2_chunked_prefill_kernels.md",
+            (["chunked_prefill", "chunked_prefill_f16"], "chunked Mamba-2 prefill on MFMA (bf16, then f16 I/O)",
+             "mamba2_chunked_prefill_kernels.md",
              cfgs.get("chunked_prefill")),
             (["varlen_conv1d", "varlen_scan"], "packed variable-length prefill (Mamba-1 2.8B layer)",
              "mamba1_varlen_prefill_kernels.md", cfgs.get("varlen_prefill")),
