@@ -307,7 +307,8 @@ def summarize_profile(out):
         req_bytes = copy_bytes / cl2["TCP_TCC_READ_REQ_sum"] if cl2.get("TCP_TCC_READ_REQ_sum") else None
         # the bf16-I/O kernel (the counter pass also runs the f16-I/O one)
         dc, ndc = _mean_counters(_counters(ssd_glob[0]),
-                                 lambda nm: _library(nm) and "ssd_kernelINS_4bf16" in nm)
+                                 lambda nm: _library(nm) and ("ssd_kernel<ssm::bf16" in nm or
+                                                              "ssd_kernelINS_4bf16" in nm))
         ch = cfgs.get("chunked_prefill") or {}
         ssd_us = _stat([d for ds in bym.get("chunked_prefill", {}).values() for d in ds])[1] \
             if "chunked_prefill" in bym else None
