@@ -182,35 +182,6 @@ constexpr int scan_waves_per_simd()
     return (std::is_same<TI, f16>::value && VEC && (ONE_CHUNK || !A_PER_STATE)) ? 3 : 2;
 }
 
-// Packed batches of at most 256 sequences: the sequence of rank r when the
-// sequences are sorted by length, longest first (ties by index).  Every
-// workgroup derives the same order from the table, so the ranks form a
-// permutation whatever the table holds.  Call from every lane.
-__device__ __forceinline__ int packed_seq_of_rank(const int32_t *__restrict__ cu, int nseq, int L, int r)
-{
-    __shared__ int s_len[256];
-    __shared__ int s_pick;
-    const int tid = threadIdx.x;
-    int len = 0;
-    if (tid < nseq) {
-        const int lo = min(max(cu[tid], 0), L);
-        len = min(max(cu[tid + 1], lo), L) - lo;
-        s_len[tid] = len;
-    }
-    __syncthreads();
-    if (tid < nseq) {
-        int rank = 0;
-        for (int j = 0; j < nseq; ++j) {
-            const int lj = s_len[j];
-            rank += (lj > len || (lj == len && j < tid)) ? 1 : 0;
-        }
-        if (rank == r)
-            s_pick = tid;
-    }
-    __syncthreads();
-    return s_pick;
-}
-
 // Walks: WALK_DENSE, tiles of 16 steps per lane; WALK_LADDER, the same
 // ending in tiles of 8, 4, 2 and 1 steps per lane, for packed batches (their
 // sequences handed out longest first) and for dense rows whose length is not

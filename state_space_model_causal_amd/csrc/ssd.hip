@@ -267,15 +267,27 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     // separates from this chunk's outputs) does not overwrite it
     __shared__ float s_d[SQ], s_L[SQ], s_eL[2][SQ], s_w[SQ], s_etot[1];
 
-    const int L = a.seqlen, P = a.headdim, H = a.nheads;
+    const int P = a.headdim, H = a.nheads;
     const int npb = P / SPB;
     const int pb = blockIdx.x % npb;
     const int bh = blockIdx.x / npb;
-    const int h = bh % H, b = bh / H;
+    const int h = bh % H;
+    int b = bh / H;
+    // packed batches: the longest sequences' workgroups start first
+    if (a.cu_seqlens && a.batch <= 256)
+        b = packed_seq_of_rank(a.cu_seqlens, a.batch, a.seqlen, b);
     const int g = h / a.heads_per_group;
     const int slot = a.slot_idx ? a.slot_idx[b] : b;
     if (slot < 0)
         return;  // padded request (uniform over the workgroup)
+    // the request's columns: the whole rows of a dense batch; in a packed
+    // batch the sequence's columns, walked from the 16-byte vector holding
+    // its first one, with the columns of its neighbours as identity steps
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.has_init_seq, b, a.seqlen, a.has_initial_state);
+    if (sp.len == 0)
+        return;
+    const int lo = sp.begin % 8, hi = lo + sp.len;  // the walk covers columns [0, hi), the sequence [lo, hi)
+    const int64_t col0 = sp.begin - lo, blk = sp.block;
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int l16 = l & 15, lq = l >> 4;
@@ -284,12 +296,12 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     const int p = pb * SPB + 16 * pw + l16;   // this lane's row of headdim
     const int64_t c = (int64_t)h * P + p;  // channel
     constexpr bool F16 = std::is_same<TI, f16>::value;
-    const TI *urow = static_cast<const TI *>(a.u) + b * a.u_sb + c * a.u_sc;
-    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + b * a.z_sb + c * a.z_sc : nullptr;
-    TI *orow = static_cast<TI *>(a.out) + b * a.o_sb + c * a.o_sc;
-    const TI *dtrow = static_cast<const TI *>(a.dt) + b * a.dt_sb + h * a.dt_sh;
-    const TI *Bg = static_cast<const TI *>(a.B) + b * a.B_sb + g * a.B_sg;
-    const TI *Cg = static_cast<const TI *>(a.C) + b * a.C_sb + g * a.C_sg;
+    const TI *urow = static_cast<const TI *>(a.u) + blk * a.u_sb + c * a.u_sc + col0;
+    const TI *zrow = a.z ? static_cast<const TI *>(a.z) + blk * a.z_sb + c * a.z_sc + col0 : nullptr;
+    TI *orow = static_cast<TI *>(a.out) + blk * a.o_sb + c * a.o_sc + col0;
+    const TI *dtrow = static_cast<const TI *>(a.dt) + blk * a.dt_sb + h * a.dt_sh + col0;
+    const TI *Bg = static_cast<const TI *>(a.B) + blk * a.B_sb + g * a.B_sg + col0;
+    const TI *Cg = static_cast<const TI *>(a.C) + blk * a.C_sb + g * a.C_sg + col0;
     TS *srow = a.state ? static_cast<TS *>(a.state) + slot * a.st_ss + h * a.st_sh + p * a.st_sp : nullptr;
 
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
 #pragma unroll
     for (int q = 0; q < NTH; ++q) {
         f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (srow && a.has_initial_state) {
+        if (srow && sp.init) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 v[j] = to_f32(srow[16 * (NTH * nh + q) + 4 * lq + j]);
@@ -319,15 +331,15 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
     }
 
     ChunkLoads<TI, N> cur;
-    load_chunk<TI, N>(cur, 0, L, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, l, lq, nh);
+    load_chunk<TI, N>(cur, 0, hi, Bg, Cg, a.B_sn, a.C_sn, urow, zrow, dtrow, tid, l, lq, nh);
 
-    for (int t0 = 0; t0 < L; t0 += SQ) {
+    for (int t0 = 0; t0 < hi; t0 += SQ) {
         const int par = (t0 / SQ) & 1;
         // ---- stage the chunk (its loads were issued one chunk earlier).
         // The previous chunk's readers of the staged B, C, delta, L and w
         // all sit before its second barrier, so no barrier is needed here.
         if (w == 0) {
-            const bool ok = t0 + l < L;
+            const bool ok = t0 + l >= lo && t0 + l < hi;
             const float v = to_f32(cur.dt) + bias;
             const float sp = softplus_f32(v);
             const float d = ok ? (a.dt_softplus ? sp : v) : 0.0f;  // identity step past the end
@@ -346,7 +358,10 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             const int u = tid + STHREADS * k;
             if (u < ChunkLoads<TI, N>::NUNITS) {
                 const int n = 2 * (u >> 3), tv = u & 7;
-                const bool ok = t0 + 8 * tv < L;  // L % 8 == 0: a vector is all in or all out
+                // a vector past the end is zeroed (rows are a multiple of 8
+                // long); the steps of the first vector before the sequence
+                // take a zero step size (no decay, no input)
+                const bool ok = t0 + 8 * tv < hi;
                 const u32x4 z4 = {0u, 0u, 0u, 0u};
                 const u32x4 b0 = ok ? cur.b0[k] : z4, b1 = ok ? cur.b1[k] : z4;
                 const u32x4 c0 = ok ? cur.c0[k] : z4, c1 = ok ? cur.c1[k] : z4;
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         u32x4 xk[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            xk[kk] = t0 + 32 * kk + 8 * lq < L ? cur.x[kk] : u32x4{0u, 0u, 0u, 0u};
+            xk[kk] = t0 + 32 * kk + 8 * lq < hi ? cur.x[kk] : u32x4{0u, 0u, 0u, 0u};
         const uint2 xo[2] = {cur.xo[0], cur.xo[1]}, zo[2] = {cur.zo[0], cur.zo[1]};
         // f16 I/O: X as the sum of two bf16 parts (exact: an f16 value's 11
         // significant bits fit in a rounded bf16 and its remainder), the
@@ -378,9 +393,9 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         // ---- the next chunk's loads, in flight during this chunk's work;
         // issued in three parts between the phases below, so that no wave
         // stalls on a full load queue for the whole chunk's worth at once
-        const bool more = t0 + SQ < L;
+        const bool more = t0 + SQ < hi;
         if (more)
-            load_pairs<TI, N>(cur.c0, cur.c1, t0 + SQ, L, Cg, a.C_sn, tid);
+            load_pairs<TI, N>(cur.c0, cur.c1, t0 + SQ, hi, Cg, a.C_sn, tid);
 
         // ---- carried state over this wave's half of the states:
         // yc[k] = sum_{n in half} C_s[n] H[p][n] over the steps s of row tile
@@ -479,7 +494,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         }
 
         if (more)
-            load_pairs<TI, N>(cur.b0, cur.b1, t0 + SQ, L, Bg, a.B_sn, tid);
+            load_pairs<TI, N>(cur.b0, cur.b1, t0 + SQ, hi, Bg, a.B_sn, tid);
 
         // ---- masked decay matrix M[s][r] = (C_s.B_r) exp(L_s - L_r) delta_r
         // for r <= s, over its 10 lower-triangle 16 x 16 tiles (st, rt).  The
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
         }
 
         if (more)
-            load_rows<TI, N>(cur, t0 + SQ, L, urow, zrow, dtrow, l, lq, nh);
+            load_rows<TI, N>(cur, t0 + SQ, hi, urow, zrow, dtrow, l, lq, nh);
 
         // ---- state update of this wave's half: H <- exp(L_last) H +
         // sum_r B_r (w_r X_r)^T, w_r = exp(L_last - L_r) delta_r on this
@@ -614,7 +629,7 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
             const f32x4_t other = *reinterpret_cast<const f32x4_t *>(&s_x[w][i][l][0]);
             const int s0 = 16 * st + 4 * lq;
             const int t = t0 + s0;
-            if (t < L) {  // L % 4 == 0: the 4 steps are all in or all out
+            if (t + 4 > lo && t < hi) {  // some of the 4 steps lie in the sequence
                 const float4 eL = *reinterpret_cast<const float4 *>(&s_eL[par][s0]);
                 const float el[4] = {eL.x, eL.y, eL.z, eL.w};
                 float xv[4];
@@ -627,7 +642,14 @@ __global__ __launch_bounds__(STHREADS) void ssd_kernel(ScanArgs a)
                     const float v = y[j] + el[j] * (mine[j] + other[j]) + Dh * xv[j];
                     o[j] = v * gz[i][j];
                 }
-                *reinterpret_cast<uint2 *>(orow + t) = uint2{pack_word(&o[0], TI{}), pack_word(&o[2], TI{})};
+                if (t >= lo && t + 4 <= hi) {
+                    *reinterpret_cast<uint2 *>(orow + t) = uint2{pack_word(&o[0], TI{}), pack_word(&o[2], TI{})};
+                } else {  // a sequence's end: its own columns only
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (t + j >= lo && t + j < hi)
+                            orow[t + j] = from_f32<TI>(o[j]);
+                }
             }
         }
     }
@@ -668,7 +690,7 @@ bool ssd_supported(const ScanArgs &a)
     // B and C are addressed by 32-bit byte offsets from each (request, group)
     // base
     const int64_t span = (int64_t)2 * ((int64_t)(a.dstate - 1) * std::max(a.B_sn, a.C_sn) + a.seqlen);
-    return !a.cu_seqlens && !a.a_per_state && (a.io_dtype == 1 || a.io_dtype == 2) && a.vec &&
+    return !a.a_per_state && (a.io_dtype == 1 || a.io_dtype == 2) && a.vec &&
            (a.dstate == 64 || a.dstate == 128 || a.dstate == 256) && a.headdim % SPB == 0 &&
            span < ((int64_t)1 << 32);
 }

@@ -262,4 +262,33 @@ __device__ __forceinline__ uint32_t xcd_block_order(uint32_t i, uint32_t nblocks
     return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Packed batches of at most 256 sequences: the sequence of rank r when the
+// sequences are sorted by length, longest first (ties by index).  Every
+// workgroup derives the same order from the table, so the ranks form a
+// permutation whatever the table holds.  Call from every lane.
+__device__ __forceinline__ int packed_seq_of_rank(const int32_t *__restrict__ cu, int nseq, int L, int r)
+{
+    __shared__ int s_len[256];
+    __shared__ int s_pick;
+    const int tid = threadIdx.x;
+    int len = 0;
+    if (tid < nseq) {
+        const int lo = min(max(cu[tid], 0), L);
+        len = min(max(cu[tid + 1], lo), L) - lo;
+        s_len[tid] = len;
+    }
+    __syncthreads();
+    if (tid < nseq) {
+        int rank = 0;
+        for (int j = 0; j < nseq; ++j) {
+            const int lj = s_len[j];
+            rank += (lj > len || (lj == len && j < tid)) ? 1 : 0;
+        }
+        if (rank == r)
+            s_pick = tid;
+    }
+    __syncthreads();
+    return s_pick;
+}
+
 } // namespace ssm

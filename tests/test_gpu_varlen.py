@@ -86,6 +86,18 @@ VARLEN_CASES = [
      [1021, 1, 4, 900, 2], None),                                    # total 1928 (vec)
     ("m1_bf16_w2_start_at_tile_edge", dict(io="bf16", state="f32", nheads=4, width=2, nslots=8, seed=31),
      [2047, 2, 7, 2000], 0),                                         # total 4056 (vec)
+    # Mamba-2 shapes that take the chunked matrix form (16-bit I/O, headdim a
+    # multiple of 64, dstate 64/128/256): sequences shorter than a chunk, a
+    # vector or a step, starting mid-vector, padded and empty ones
+    ("m2_bf16_hd64_N128_chunked", dict(io="bf16", state="f32", nheads=2, headdim=64, dstate=128,
+                                       a_per_state=False, nslots=8, seed=32),
+     [100, 3, 0, 517, 64, 9, 307], 1),                                 # total 1000 (vec)
+    ("m2_f16_hd128_N256_chunked", dict(io="f16", state="bf16", nheads=1, headdim=128, dstate=256,
+                                       a_per_state=False, nslots=6, seed=33),
+     [1, 130, 64, 7, 598], None),                                      # total 800 (vec)
+    ("m2_f16_hd64_N64_G2_chunked", dict(io="f16", state="f16", nheads=4, headdim=64, dstate=64,
+                                        ngroups=2, a_per_state=False, nslots=9, seed=34),
+     [65, 0, 2, 127, 8, 70], 2),                                       # total 272 (vec)
     # more sequences than the conv kernel stages in LDS (its global-table path)
     ("m1_f16_300_seqs", dict(io="f16", state="f32", nheads=8, nslots=320, seed=19),
      [0, 3] + W.varlen_lengths(19, 298, 2395), None),                    # total 2398
@@ -179,6 +191,32 @@ def test_varlen_equal_lengths_match_dense_kernels(dev, ssm, io):
     assert bool(((ov - od).abs() <= tol).all())
     sv, sd = st_v.double(), st_d.double()
     assert bool(((sv - sd).abs() <= 1e-5 * sd.abs().max()).all())
+
+
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_varlen_mamba2_chunked_matches_dense(dev, ssm, io):
+    # packed sequences of one length (a multiple of 8, so every sequence
+    # starts on a vector) walk the same chunks as the dense call: the chunked
+    # Mamba-2 scan gives the same bits either way
+    spec = W.tiny(io=io, state="f32", nheads=2, headdim=64, dstate=128, a_per_state=False,
+                  nslots=6, seed=35)
+    L, nseq = 264, 3
+    t = W.make_varlen(spec, [L] * nseq, dev, init_every=1)
+    cu, idx = t["cu_seqlens"], t["slot_idx"]
+    st_v, st_d = t["ssm_state"].clone(), t["ssm_state"].clone()
+    o_v = ssm.selective_scan_varlen(t["x"], t["dt"], t["A"], t["B"], t["C"], cu, D=t["D"], z=t["z"],
+                                    dt_bias=t["dt_bias"], ssm_state=st_v, slot_idx=idx,
+                                    has_initial_state=t["has_init"])
+
+    def dense(a):  # [rows..., nseq*L] -> [nseq, rows..., L]
+        return torch.stack(a.split(L, dim=-1)).contiguous()
+
+    o_d = ssm.selective_scan(dense(t["x"]), dense(t["dt"]), t["A"], dense(t["B"]), dense(t["C"]),
+                             D=t["D"], z=dense(t["z"]), dt_bias=t["dt_bias"], ssm_state=st_d,
+                             slot_idx=idx, has_initial_state=True, algo=ssm.SCAN_CHUNKED)
+    torch.cuda.synchronize()
+    assert torch.equal(dense(o_v), o_d)
+    assert torch.equal(st_v, st_d)
 
 
 def test_varlen_all_empty_is_noop(dev, ssm):
