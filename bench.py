@@ -602,6 +602,26 @@ def measure_chunked(ssm, W, dev, timer, mark):
         sets.append(t)
     with mark("chunked_prefill_f16"):
         us16 = timer.time(run)
+    # continuous batching: the 8192 tokens as 16 packed sequences of mixed
+    # lengths (every other one continuing from its slot), bf16 I/O
+    del sets[:]
+    lengths = W.varlen_lengths(VARLEN_SEED, VARLEN_NSEQ, VARLEN_TOKENS)
+    vspec = W.m2_prefill(state="f32", width=4)
+    for k in range(2):
+        t = W.make_varlen(W.m2_prefill(state="f32", width=4, seed=spec.seed + 200 + k), lengths, dev)
+        t["out"] = torch.empty_like(t["x"])
+        sets.append(t)
+
+    def run_packed(i):
+        t = sets[i % 2]
+        ssm.selective_scan_varlen(t["x"], t["dt"], t["A"], t["B"], t["C"], t["cu_seqlens"], D=t["D"],
+                                  z=t["z"], dt_bias=t["dt_bias"], ssm_state=t["ssm_state"],
+                                  slot_idx=t["slot_idx"], has_initial_state=t["has_init"], out=t["out"])
+
+    with mark("chunked_prefill_packed"):
+        usp = timer.time(run_packed)
+    n_init = int(sets[0]["has_init"].sum().item())
+    bp = W.varlen_bytes(vspec, lengths, n_init)["scan"]
     del sets[:]
     b = W.algorithmic_bytes(spec)["scan"]
     useful = W.chunked_mfma_flops(spec)
@@ -626,6 +646,11 @@ def measure_chunked(ssm, W, dev, timer, mark):
                        "frac_hbm_peak": b / (us16 * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                        "issued_mfma_flops": issued16,
                        "issued_frac_16bit_peak": issued16 / (us16 * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+            "packed": {"workload": f"{VARLEN_NSEQ} packed sequences, {VARLEN_TOKENS} tokens, mixed lengths "
+                                   "(log-uniform), every other one continuing from its slot; same heads, "
+                                   "bf16 I/O",
+                       "lengths": lengths, "us": usp, "tokens_per_s": VARLEN_TOKENS / (usp * 1e-6),
+                       "bytes": bp, "GBps": bp / (usp * 1e-6) / 1e9},
             "kernel_source_sha": kernel_source_sha(KERNEL_SOURCES["chunked_scan"])}
 
 

@@ -337,7 +337,8 @@ def summarize_profile(out):
     for labels, title, fname, rec in (
             (["tiny_conv1d", "tiny_scan", "tiny_pair"], "tiny Mamba-1 prefill (f32, L 64, d_inner 128)",
              "mamba1_tiny_prefill_kernels.md", cfgs.get("tiny_prefill")),
-            (["chunked_prefill", "chunked_prefill_f16"], "chunked Mamba-2 prefill on MFMA (bf16, then f16 I/O)",
+            (["chunked_prefill", "chunked_prefill_f16", "chunked_prefill_packed"],
+             "chunked Mamba-2 prefill on MFMA (bf16, f16 I/O, then 16 packed sequences)",
              "mamba2_chunked_prefill_kernels.md",
              cfgs.get("chunked_prefill")),
             (["varlen_conv1d", "varlen_scan"], "packed variable-length prefill (Mamba-1 2.8B layer)",
