@@ -305,10 +305,17 @@ def summarize_profile(out):
         cl2, _ = _mean_counters(_counters(_one(f"{out}/copy_l2/*counter_collection.csv")),
                                 lambda n: "copyBuffer" in n)
         req_bytes = copy_bytes / cl2["TCP_TCC_READ_REQ_sum"] if cl2.get("TCP_TCC_READ_REQ_sum") else None
-        # the bf16-I/O kernel (the counter pass also runs the f16-I/O one)
-        dc, ndc = _mean_counters(_counters(ssd_glob[0]),
-                                 lambda nm: _library(nm) and ("ssd_kernel<ssm::bf16" in nm or
-                                                              "ssd_kernelINS_4bf16" in nm))
+        # the dense bf16-I/O prefill: the pass then runs the f16-I/O one and
+        # the packed batch (the same bf16 kernel), so only the bf16
+        # dispatches in front of the first f16 one are taken
+        disp, dense = _counters(ssd_glob[0]), collections.OrderedDict()
+        for did, (nm, d) in disp.items():
+            if not (_library(nm) and "ssd_kernel" in nm):
+                continue
+            if not ("ssd_kernel<ssm::bf16" in nm or "ssd_kernelINS_4bf16" in nm):
+                break
+            dense[did] = (nm, d)
+        dc, ndc = _mean_counters(dense, lambda nm: True)
         ch = cfgs.get("chunked_prefill") or {}
         ssd_us = _stat([d for ds in bym.get("chunked_prefill", {}).values() for d in ds])[1] \
             if "chunked_prefill" in bym else None
