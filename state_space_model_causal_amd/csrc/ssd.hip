@@ -14,16 +14,24 @@
 //     Y[s,p]  = sum_{r<=s} C_s.B_r exp(L_s - L_r) delta_r X[r,p]     (within)
 //             + exp(L_s) sum_n C_s[n] H[p,n]                           (carried)
 //     H'[p,n] = exp(L_Q-1) H[p,n] + sum_r exp(L_Q-1 - L_r) delta_r B_r[n] X[r,p]
-// where H is the state entering the chunk.  All four contractions (C^T B over
+// where H is the state entering the chunk.  The four contractions (C^T B over
 // states, the masked decay matrix times X, C times H^T, and B times the
-// weighted X) run on v_mfma_f32_16x16x32_bf16.  Each product has one operand
-// that is exact in bfloat16 (B or C, stored in bf16, or X) and one float32
-// operand (the masked decay matrix, the carried state, the weighted X), which
-// is split into a bf16 high part and a bf16 remainder, so every product keeps
-// about 16 significant bits; the accumulation is float32.
+// weighted X) run on the 16x16x32 matrix instructions with float32
+// accumulation, each product keeping one operand exact:
+//   * bf16 I/O: all on v_mfma_f32_16x16x32_bf16; B, C and X are exact, and
+//     the float32 operand (the masked decay matrix, the carried state, the
+//     weighted X) is split into a bf16 high part and a bf16 remainder (about
+//     16 significant bits per product).
+//   * f16 I/O: C^T B on v_mfma_f32_16x16x32_f16 (exact products); X split
+//     exactly into two bf16 parts against the bf16 decay matrix; C and B as
+//     stored on the f16 instruction against the carried state and the
+//     weighted X, split into f16 parts under a power-of-two scale per row p
+//     (no part overflows; about 22 significant bits), scaled back afterwards.
 //
 // Work decomposition: one 512-lane workgroup per (request, head, 64 rows of
-// headdim).  Each wave owns 16 rows and half of the states: its part of the
+// headdim); in a packed batch the request is a sequence, walked from the
+// 16-byte vector holding its first column, its neighbours' columns being
+// identity steps (zero step size), the longest sequences first.  Each wave owns 16 rows and half of the states: its part of the
 // state (dstate/2 x 16, float32) stays in MFMA accumulators for the whole
 // sequence, which is walked in chunks of 64 steps.  Per chunk the workgroup
 // stages B and C in LDS as stored ([state][step]; the operands that need them
