@@ -320,7 +320,11 @@ int ssm_causal_conv1d_varlen(ssm_tensor x, ssm_tensor weight, ssm_tensor bias,
  *   dt          io dtype [nheads, total_len]
  *   B, C        io dtype [ngroups, dstate, total_len]
  *   other arguments as in ssm_selective_scan; each sequence's final state goes
- *   to its slot.
+ *   to its slot.  A sequence is walked from the 16-byte vector that holds its
+ *   first column, and the neighbouring columns it meets there and in its
+ *   last vector enter as identity steps (zero step size, zero-weighted
+ *   products): they must hold finite values.  Mamba-2 shapes with f16 or
+ *   bf16 I/O take the chunked form (as in ssm_selective_scan_ex).
  */
 int ssm_selective_scan_varlen(ssm_tensor u, ssm_tensor dt, ssm_tensor dt_bias, ssm_tensor A,
                               ssm_tensor B, ssm_tensor C, ssm_tensor D, ssm_tensor z,
