@@ -147,9 +147,11 @@ def test_mamba2_ssu_hd64_batches(dev, ssm, oracle, batch):
               sample=tuple(sorted({0, batch - 1})))
 
 
-@pytest.mark.parametrize("state", ["bf16", "f32"])
-def test_mamba2_prefill_full(dev, ssm, oracle, state):
-    spec = W.m2_prefill(state=state)
+@pytest.mark.parametrize("io,state", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f32")])
+def test_mamba2_prefill_full(dev, ssm, oracle, io, state):
+    # the chunked form at the full hd128/N256, L 4096, batch 2 size, with
+    # bf16 and f16 I/O: sampled heads and rows against the oracle
+    spec = W.m2_prefill(state=state, io=io)
     t = W.make(spec, dev)
     out = ssm.selective_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              dt_bias=t["dt_bias"], ssm_state=t["ssm_state"],
@@ -166,10 +168,10 @@ def test_mamba2_prefill_full(dev, ssm, oracle, state):
             f(t["x"][b:b + 1, ch]), f(t["dt"][b:b + 1, hi]), f(t["A"][hi]), f(t["B"][b:b + 1]),
             f(t["C"][b:b + 1]), D=f(t["D"][hi]), z=f(t["z"][b:b + 1, ch]),
             dt_bias=f(t["dt_bias"][hi]), state=np.zeros((1, len(heads), len(rows), spec.dstate)))
-        check(out[b:b + 1, ch], o, so, RTOL[spec.io], spec.io, f"m2 prefill out b={b}")
+        check(out[b:b + 1, ch], o, so, RTOL[spec.io], spec.io, f"m2 prefill {io} out b={b}")
         slot = int(t["slot_idx"][b])
         gst = t["ssm_state"][slot][hi][:, pi]
-        check(gst, st[0], sts[0], RTOL[spec.io], spec.state, f"m2 prefill state b={b}")
+        check(gst, st[0], sts[0], RTOL[spec.io], spec.state, f"m2 prefill {io} state b={b}")
 
 
 def test_mamba1_decode_step_fused_full(dev, ssm, oracle):
