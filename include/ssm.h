@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum ssm_dtype {
     SSM_F32 = 0,
@@ -448,6 +448,40 @@ int ssm_mamba1_decode_layer_noalloc(const ssm_mamba1_layer *layer, ssm_tensor hi
                                     ssm_tensor conv_state, ssm_tensor ssm_state,
                                     const int32_t *slot_idx, int batch, int nslots,
                                     void *stream);
+
+/*
+ * ssm_group_begin / ssm_group_end -- a launch group: calls made between the
+ * two on `stream` by this host thread are declared independent of each other
+ * (no call reads or writes what another writes), so the library may run them
+ * together.  This is the serving step of a batch that holds requests in
+ * prefill and requests in decode, each with its own cache slot (the
+ * per-request state cache of InfiniLM-Rust PR #48, section 3.1, under the
+ * concurrent requests of its section 4.2): one prefill scan and one decode
+ * step of the kinds below go out as ONE kernel launch, the decode step's
+ * workgroups after the scan's, so that they run in the slots the scan's last
+ * round of workgroups leaves free.
+ *
+ *   Taken together: an ssm_selective_scan without packed sequences that
+ *   takes the recurrence, with f16 or bf16 io, an f32 state cache, per-state
+ *   decays (Mamba-1), dstate <= 16 and seqlen a multiple of 256; and an
+ *   ssm_decode_step with the same io dtype, an f32 state cache, per-state
+ *   decays and conv_width 4 whose state rows the interleaved map takes
+ *   (dstate 8 to 256 in powers of two, at least 2^18 (request, channel)
+ *   rows, two requests per lane).  Such a call is validated when made (its
+ *   errors are returned then) and held until its partner arrives or the
+ *   group ends; every other call launches at once.  A held call's launch
+ *   status is returned by the call or ssm_group_end that launches it.  The
+ *   values computed are the same, bit for bit, as those of the calls made
+ *   outside a group.
+ *
+ *   The caller keeps every buffer of a held call alive and unchanged until
+ *   ssm_group_end has returned (pointers are held, not contents).  Groups do
+ *   not nest: ssm_group_begin with a group open, and ssm_group_end without
+ *   one or with another stream, return SSM_ERR_UNSUPPORTED.  Host-side only:
+ *   the group allocates nothing and is usable under stream capture.
+ */
+int ssm_group_begin(void *stream);
+int ssm_group_end(void *stream);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *ssm_status_string(int status);

@@ -24,6 +24,7 @@ contiguous.  Layouts (time innermost for prefill):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -42,6 +43,7 @@ EXPORTED = ("ssm_causal_conv1d", "ssm_selective_scan", "ssm_selective_scan_ex", 
             "ssm_linear", "ssm_linear_workspace", "ssm_linear_ex", "ssm_linear_workspace_ex", "ssm_linear_plan",
             "ssm_rmsnorm", "ssm_mamba1_decode_layer",
             "ssm_mamba1_decode_layer_workspace", "ssm_mamba1_decode_layer_noalloc",
+            "ssm_group_begin", "ssm_group_end",
             "ssm_status_string", "ssm_abi_version")
 
 
@@ -136,6 +138,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_mamba1_decode_layer.restype = I
     lib.ssm_mamba1_decode_layer_noalloc.argtypes = [P, T, T, T, P, I, I, P]
     lib.ssm_mamba1_decode_layer_noalloc.restype = I
+    lib.ssm_group_begin.argtypes = [P]
+    lib.ssm_group_begin.restype = I
+    lib.ssm_group_end.argtypes = [P]
+    lib.ssm_group_end.restype = I
     lib.ssm_status_string.argtypes = [I]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -302,6 +308,22 @@ def decode_step(state, conv_state, x, conv_weight, dt, A, B, C, conv_bias=None, 
         int(bool(dt_softplus)), _stream(stream))
     _check("ssm_decode_step", st)
     return out
+
+
+@contextlib.contextmanager
+def launch_group(stream=None):
+    """ssm_group_begin / ssm_group_end around a block of independent calls on
+    `stream` (default: the current stream): a Mamba-1 prefill scan and a
+    fused decode step of the kinds ssm.h lists run as one launch, with the
+    same results as the calls made one after the other.  Buffers of the calls
+    must stay alive until the block has ended."""
+    s = _stream(stream)
+    _check("ssm_group_begin", load_library().ssm_group_begin(s))
+    try:
+        yield
+    finally:
+        st = load_library().ssm_group_end(s)
+    _check("ssm_group_end", st)
 
 
 def causal_conv1d_varlen(x, weight, cu_seqlens, bias=None, conv_state=None, slot_idx=None,

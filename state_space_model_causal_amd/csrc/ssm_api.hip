@@ -275,6 +275,57 @@ int conv_call(const ssm_tensor &x, const ssm_tensor &weight, const ssm_tensor &b
     return status_of(ssm::launch_conv(a, static_cast<hipStream_t>(stream)));
 }
 
+// The open launch group of this host thread (ssm_group_begin / _end): at
+// most one held scan and one held decode step of the kinds the mixed kernel
+// takes; a held pair goes out as one mixed launch as soon as both are there.
+struct LaunchGroup {
+    bool open = false;
+    void *stream = nullptr;
+    bool has_scan = false, has_decode = false;
+    ssm::ScanArgs scan;
+    ssm::SsuArgs decode;
+};
+thread_local LaunchGroup g_group;
+
+// A scan handed to the open group: true when the group now holds it or has
+// launched it with its held decode step (*st = that launch's status); false
+// when the caller launches it itself.
+bool group_take_scan(const ssm::ScanArgs &a, void *stream, int *st)
+{
+    LaunchGroup &g = g_group;
+    if (!g.open || g.stream != stream || !ssm::mixed_scan_ok(a))
+        return false;
+    if (g.has_decode && ssm::mixed_pair_ok(a, g.decode)) {
+        g.has_decode = false;
+        *st = status_of(ssm::launch_mixed(a, g.decode, static_cast<hipStream_t>(stream)));
+        return true;
+    }
+    if (g.has_scan)
+        return false;
+    g.scan = a;
+    g.has_scan = true;
+    *st = SSM_OK;
+    return true;
+}
+
+bool group_take_decode(const ssm::SsuArgs &a, void *stream, int *st)
+{
+    LaunchGroup &g = g_group;
+    if (!g.open || g.stream != stream || !ssm::mixed_decode_ok(a))
+        return false;
+    if (g.has_scan && ssm::mixed_pair_ok(g.scan, a)) {
+        g.has_scan = false;
+        *st = status_of(ssm::launch_mixed(g.scan, a, static_cast<hipStream_t>(stream)));
+        return true;
+    }
+    if (g.has_decode)
+        return false;
+    g.decode = a;
+    g.has_decode = true;
+    *st = SSM_OK;
+    return true;
+}
+
 int scan_call(const ssm_tensor &u, const ssm_tensor &dt, const ssm_tensor &dt_bias, const ssm_tensor &A,
               const ssm_tensor &B, const ssm_tensor &C, const ssm_tensor &D, const ssm_tensor &z,
               const ssm_tensor &ssm_state, const int32_t *slot_idx, const int32_t *cu_seqlens,
@@ -295,6 +346,9 @@ int scan_call(const ssm_tensor &u, const ssm_tensor &dt, const ssm_tensor &dt_bi
         return SSM_OK;
     if (chunked && algo != SSM_SCAN_RECURRENT)
         return status_of(ssm::launch_ssd(a, static_cast<hipStream_t>(stream)));
+    int st;
+    if (group_take_scan(a, stream, &st))
+        return st;
     return status_of(ssm::launch_scan(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -655,7 +709,38 @@ int ssm_decode_step(ssm_tensor state, ssm_tensor conv_state, const int32_t *slot
     SSM_TRY(ssm::prepare_decode_conv(a, conv_state, conv_weight, conv_bias, u_out, conv_width));
     if (batch == 0)
         return SSM_OK;
+    int st;
+    if (group_take_decode(a, stream, &st))
+        return st;
     return status_of(ssm::launch_ssu(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_group_begin(void *stream)
+{
+    LaunchGroup &g = g_group;
+    if (g.open)
+        return SSM_ERR_UNSUPPORTED;
+    g = LaunchGroup();
+    g.open = true;
+    g.stream = stream;
+    return SSM_OK;
+}
+
+int ssm_group_end(void *stream)
+{
+    LaunchGroup &g = g_group;
+    if (!g.open || g.stream != stream)
+        return SSM_ERR_UNSUPPORTED;
+    int st = SSM_OK;
+    if (g.has_scan)
+        st = status_of(ssm::launch_scan(g.scan, static_cast<hipStream_t>(stream)));
+    if (g.has_decode) {
+        const int s2 = status_of(ssm::launch_ssu(g.decode, static_cast<hipStream_t>(stream)));
+        if (st == SSM_OK)
+            st = s2;
+    }
+    g = LaunchGroup();
+    return st;
 }
 
 } // extern "C"

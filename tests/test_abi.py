@@ -387,3 +387,15 @@ def test_noalloc_layer_scratch_limit(lib):
     assert lib.ssm_mamba1_decode_layer_noalloc(
         ctypes.byref(desc), T(FAKE, F16, (4, 2560)), T(FAKE, F16, (8, 5120, 3)),
         T(FAKE, F32, (8, 5120, 1, 16)), None, 0, 8, None) == 0
+
+
+def test_launch_group_state_errors(lib):
+    # host-side only: no device call is made by begin, or by an end with
+    # nothing held
+    s, other = 0x1000, 0x2000  # stream handles are only compared
+    assert lib.ssm_group_end(s) == 5            # no open group: SSM_ERR_UNSUPPORTED
+    assert lib.ssm_group_begin(s) == 0
+    assert lib.ssm_group_begin(s) == 5          # groups do not nest
+    assert lib.ssm_group_end(other) == 5        # the group's stream only
+    assert lib.ssm_group_end(s) == 0
+    assert lib.ssm_group_end(s) == 5            # closed

@@ -1,0 +1,185 @@
+"""GPU tests of the launch group (ssm_group_begin / ssm_group_end): a
+Mamba-1 prefill scan and an independent fused decode step made inside one
+group run as one mixed launch.  Their results must be the same, bit for bit,
+as those of the two calls made one after the other (the standalone calls are
+checked against the float64 oracle at the same sizes in the full-size
+tests); a sample of the grouped prefill is also checked against the oracle
+here.  Also: a group holding one call, calls the mixed kernel does not take,
+either order of the pair, and graph replays of a captured group.
+
+Workloads: the Mamba-1 2.8B layer prefill (batch 4, L 2048, d_inner 5120,
+d_state 16, f16 I/O, f32 state; also bf16 I/O and batch 1, L 256) and the
+245-request decode step from a 512-slot cache.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests._parity import RTOL, check, to_f64 as f
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import state_space_model_causal_amd as m
+
+    m.load_library()
+    return m
+
+
+def _sets(pspec, dspec, dev):
+    p = W.make(pspec, dev)
+    p["u"] = torch.zeros_like(p["x"])
+    p["out"] = torch.zeros_like(p["x"])
+    d = W.make(dspec, dev)
+    d["out"] = torch.zeros_like(d["x"])
+    return p, d
+
+
+def _clone(t):
+    return {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+
+
+def _scan(ssm, p):
+    ssm.selective_scan(p["u"], p["dt"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                       dt_bias=p["dt_bias"], ssm_state=p["ssm_state"], slot_idx=p["slot_idx"],
+                       has_initial_state=False, out=p["out"])
+
+
+def _decode(ssm, d):
+    ssm.decode_step(d["ssm_state"], d["conv_state"], d["x"], d["conv_w"], d["dt"], d["A"],
+                    d["B"], d["C"], conv_bias=d["conv_b"], D=d["D"], z=d["z"],
+                    dt_bias=d["dt_bias"], slot_idx=d["slot_idx"], out=d["out"])
+
+
+def _conv(ssm, p):
+    ssm.causal_conv1d(p["x"], p["conv_w"], p["conv_b"], conv_state=p["conv_state"],
+                      slot_idx=p["slot_idx"], out=p["u"], has_initial_state=False)
+
+
+def _same(a, b, what):
+    for k in ("out", "ssm_state", "conv_state"):
+        assert torch.equal(a[k], b[k]), f"{what}: {k} differs"
+
+
+@pytest.mark.parametrize("io,batch,seqlen,order", [
+    ("f16", 4, 2048, "scan_first"),
+    ("f16", 4, 2048, "decode_first"),
+    ("bf16", 4, 2048, "scan_first"),
+    ("f16", 1, 256, "scan_first"),
+])
+def test_group_matches_separate_calls(ssm, io, batch, seqlen, order):
+    dev = torch.device("cuda:0")
+    print(f"group io={io} batch={batch} L={seqlen} {order}", flush=True)
+    pspec = W.prefill(io=io, batch=batch, seqlen=seqlen)
+    dspec = W.decode(io=io)
+    p, d = _sets(pspec, dspec, dev)
+    _conv(ssm, p)
+    p2, d2 = _clone(p), _clone(d)
+    _scan(ssm, p)
+    _decode(ssm, d)
+    with ssm.launch_group():
+        if order == "scan_first":
+            _scan(ssm, p2)
+            _decode(ssm, d2)
+        else:
+            _decode(ssm, d2)
+            _scan(ssm, p2)
+    torch.cuda.synchronize()
+    _same(p, p2, "prefill")
+    _same(d, d2, "decode")
+
+
+def test_group_prefill_matches_oracle(ssm, oracle):
+    dev = torch.device("cuda:0")
+    pspec, dspec = W.prefill(), W.decode()
+    p, d = _sets(pspec, dspec, dev)
+    _conv(ssm, p)
+    torch.cuda.synchronize()
+    with ssm.launch_group():
+        _scan(ssm, p)
+        _decode(ssm, d)
+    torch.cuda.synchronize()
+    chans = np.array([0, 1, 15, 16, 2047, 5119])
+    ci = torch.as_tensor(chans, device=dev)
+    for b in (0, pspec.batch - 1):
+        uo, _, _ = oracle.causal_conv1d(f(p["x"][b:b + 1, ci]), f(p["conv_w"][ci]),
+                                        f(p["conv_b"][ci]), None, None)
+        uo = oracle.round_to(uo, oracle.F16)  # the scan reads u stored in f16
+        o, so, st, sts = oracle.selective_scan(
+            uo, f(p["dt"][b:b + 1, ci]), f(p["A"][ci]), f(p["B"][b:b + 1]),
+            f(p["C"][b:b + 1]), D=f(p["D"][ci]), z=f(p["z"][b:b + 1, ci]),
+            dt_bias=f(p["dt_bias"][ci]), state=np.zeros((1, len(chans), 1, 16)))
+        check(p["out"][b:b + 1, ci], o, so, RTOL["f16"], "f16", f"grouped scan out b={b}")
+        slot = int(p["slot_idx"][b])
+        check(p["ssm_state"][slot, ci], st[0], sts[0], RTOL["f16"], "f32", f"grouped state b={b}")
+
+
+def test_group_single_and_unmixable_calls(ssm):
+    dev = torch.device("cuda:0")
+    # a scan alone, a decode step alone, and a pair the mixed kernel does not
+    # take (rows of 300 steps) each run as their own launches
+    for name, pspec, use_p, use_d in [
+            ("scan alone", W.prefill(batch=2, seqlen=512), True, False),
+            ("decode alone", W.prefill(batch=1, seqlen=256), False, True),
+            ("ragged scan", W.prefill(batch=2, seqlen=300), True, True)]:
+        print(f"group {name}", flush=True)
+        p, d = _sets(pspec, W.decode(), dev)
+        _conv(ssm, p)
+        p2, d2 = _clone(p), _clone(d)
+        if use_p:
+            _scan(ssm, p)
+        if use_d:
+            _decode(ssm, d)
+        with ssm.launch_group():
+            if use_p:
+                _scan(ssm, p2)
+            if use_d:
+                _decode(ssm, d2)
+        torch.cuda.synchronize()
+        _same(p, p2, name)
+        _same(d, d2, name)
+
+
+def test_group_graph_replays(ssm):
+    """A captured group replayed three times, with eager work and a
+    synchronization between replays, against three grouped eager steps."""
+    dev = torch.device("cuda:0")
+    p, d = _sets(W.prefill(), W.decode(), dev)
+    _conv(ssm, p)
+    p2, d2 = _clone(p), _clone(d)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            with ssm.launch_group():
+                _scan(ssm, p2)
+                _decode(ssm, d2)
+    torch.cuda.synchronize()
+    for r in range(3):
+        with ssm.launch_group():
+            _scan(ssm, p)
+            _decode(ssm, d)
+        g.replay()
+        torch.cuda.synchronize()
+        p2["x"].add_(0)  # eager work between replays
+        torch.cuda.synchronize()
+        _same(p, p2, f"replay {r}")
+        _same(d, d2, f"replay {r}")
+
+
+def test_group_errors(ssm):
+    s = torch.cuda.current_stream()
+    lib = ssm.load_library()
+    assert lib.ssm_group_end(s.cuda_stream) == 5           # no open group
+    assert lib.ssm_group_begin(s.cuda_stream) == 0
+    assert lib.ssm_group_begin(s.cuda_stream) == 5         # groups do not nest
+    other = torch.cuda.Stream()
+    assert lib.ssm_group_end(other.cuda_stream) == 5       # another stream
+    assert lib.ssm_group_end(s.cuda_stream) == 0
