@@ -8,6 +8,10 @@ One step = one pass of the whole path over one batch of synthetic input:
   decode   one token for 245 concurrent requests gathered from a 512-slot cache
            (conv cache fp16 [512,5120,3], state cache fp32 [512,5120,16]): the
            conv update fused with the selective state update.
+The prefill and decode requests hold separate cache slots, so the step makes
+the scan and the decode step in one launch group: they run as one mixed
+launch whose decode workgroups follow the scan's and fill the slots its last
+round of workgroups leaves free (--serial-step: three separate launches).
 Inputs are resident in HBM before the timed region.  Independent buffer sets
 are rotated between launches so that no launch re-reads what the previous one
 left in the 256 MB Infinity Cache.
@@ -67,16 +71,18 @@ GRAPH_LAUNCHES, WARM_REPLAYS, TIMED_REPLAYS = 10, 5, 100
 ROTATION_BYTES = 512e6          # 2x the Infinity Cache
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"selective_scan": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
-                  "state_update": ["ssu.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
-                  "decode_step": ["ssu.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+KERNEL_SOURCES = {"selective_scan": ["scan.hip", "scan_body.hpp", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "state_update": ["ssu.hip", "ssu_body.hpp", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "decode_step": ["ssu.hip", "ssu_body.hpp", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "mixed_scan_decode": ["ssu.hip", "scan_body.hpp", "ssu_body.hpp", "ssm_device.hpp",
+                                        "ssm_kernels.hpp"],
                   "conv1d_prefill": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "conv1d_decode": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "conv1d_varlen": ["conv1d.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
-                  "selective_scan_varlen": ["scan.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
+                  "selective_scan_varlen": ["scan.hip", "scan_body.hpp", "ssm_device.hpp", "ssm_kernels.hpp"],
                   "chunked_scan": ["ssd.hip", "ssm_device.hpp", "ssm_kernels.hpp"],
-                  "layer_decode": ["gemm.hip", "layer.hip", "conv1d.hip", "ssu.hip", "ssm_device.hpp",
-                                   "ssm_kernels.hpp"]}
+                  "layer_decode": ["gemm.hip", "layer.hip", "conv1d.hip", "ssu.hip", "ssu_body.hpp",
+                                   "ssm_device.hpp", "ssm_kernels.hpp"]}
 # rocprofv3 kernel names of each headline kernel
 KERNEL_SYMBOLS = {"conv1d_prefill": "conv_rows_kernel", "selective_scan": "scan_kernel",
                   "decode_step": "ssu_"}
@@ -104,6 +110,9 @@ def parse():
     p.add_argument("--only", choices=["headline", "prefill", "decode", "varlen", "layer", "chunked",
                                       "ssu", "ssu-headline", "tiny"], default=None,
                    help="run one part only (for profiling)")
+    p.add_argument("--serial-step", action="store_true",
+                   help="launch the step's prefill scan and decode step one after the other "
+                        "instead of as one launch group")
     p.add_argument("--unfused-decode", action="store_true",
                    help="decode with the separate conv-update and state-update calls instead "
                         "of the fused decode step")
@@ -333,13 +342,19 @@ def measure_headline(ssm, W, dev, args, timer, mark):
         host = {"prefill": {k: v.cpu() for k, v in psets[0].items()},
                 "decode": {k: v.cpu() for k, v in dsets[0].items()}}
 
+    # the prefill's scan and the decode step touch disjoint buffers: made in
+    # one launch group they run as one mixed launch (the decode's workgroups
+    # after the scan's)
+    grouped = bool(psets and dsets and fused and not args.serial_step)
+
     def step(i):
         if psets:
-            t = psets[i % NP]
-            run_conv_prefill(ssm, t)
-            run_scan_prefill(ssm, t)
-        if dsets:
-            run_decode(ssm, dsets[i % ND], dspec, fused)
+            run_conv_prefill(ssm, psets[i % NP])
+        with (ssm.launch_group() if grouped else contextlib.nullcontext()):
+            if psets:
+                run_scan_prefill(ssm, psets[i % NP])
+            if dsets:
+                run_decode(ssm, dsets[i % ND], dspec, fused)
 
     # the step: W eager warm-up steps, then a graph of G steps replayed
     # (5 warm replays), then exactly K steps timed
@@ -402,6 +417,17 @@ def measure_headline(ssm, W, dev, args, timer, mark):
                     D=dsets[i % ND]["D"], z=dsets[i % ND]["z"], dt_bias=dsets[i % ND]["dt_bias"],
                     slot_idx=dsets[i % ND]["slot_idx"], out=dsets[i % ND]["out"]))
             kernels["state_update"] = {"bytes": dbytes["ssu"], "us": us}
+    mixed = None
+    if grouped:
+        def run_mixed(i):
+            with ssm.launch_group():
+                run_scan_prefill(ssm, psets[i % NP])
+                run_decode(ssm, dsets[i % ND], dspec, True)
+        with mark("mixed_scan_decode"):
+            us = timer.time(run_mixed)
+        mixed = {"us": us, "bytes": pbytes["scan"] + fused_bytes,
+                 "GBps": (pbytes["scan"] + fused_bytes) / (us * 1e-6) / 1e9,
+                 "kernel_source_sha": kernel_source_sha(KERNEL_SOURCES["mixed_scan_decode"])}
     for k, v in kernels.items():
         v["kernel_source_sha"] = kernel_source_sha(KERNEL_SOURCES[k])
         v["GBps"] = v["bytes"] / (v["us"] * 1e-6) / 1e9
@@ -418,6 +444,7 @@ def measure_headline(ssm, W, dev, args, timer, mark):
     del psets, dsets
     torch.cuda.empty_cache()
     return {"ms_per_step": ms_per_step, "step_graph": G, "wall_s_timed": t_wall,
+            "grouped": grouped, "mixed_launch": mixed,
             "step_bytes": step_bytes, "kernels": kernels,
             "decode_us": dec_us, "fused": fused,
             "decode_tokens_per_s": dspec.batch / (dec_us * 1e-6) if dec_us else None,
@@ -958,6 +985,9 @@ def main():
                        "d_state": dspec.dstate, "fused_conv_update": head["fused"]},
             "step_bytes": head["step_bytes"],
             "buffer_sets": {"prefill": 3, "decode": 3},
+            "step_launches": ("conv1d; then the scan and the decode step as one mixed launch "
+                              "(a launch group: the decode's workgroups after the scan's)"
+                              if head["grouped"] else "conv1d, scan, decode step one after the other"),
             "timing": ("eager launches" if args.eager else
                        f"HIP graph of {head['step_graph']} steps, {WARM_REPLAYS} warm replays, "
                        f"{args.steps // head['step_graph']} timed replays"),
@@ -967,6 +997,7 @@ def main():
         "decode_tokens_per_s": head["decode_tokens_per_s"],
         "kernels": kernels,
         "kernel_sum_us": head["kernel_sum_us"],
+        "mixed_launch": head["mixed_launch"],
         "roofline": roofline,
         "target_met": target,
         "cpu_baseline": cpu,

@@ -35,7 +35,7 @@ SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VA
 SSD_COUNTERS = ("SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_LDS "
                 "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE TCP_TCC_READ_REQ_sum")
 HEADLINE_LABELS = {"conv1d_prefill": "conv_rows_kernel", "selective_scan": "scan_kernel",
-                   "decode_step": "ssu_"}
+                   "decode_step": "ssu_", "mixed_scan_decode": "mixed_kernel"}
 
 
 def profile_commands(out):
@@ -170,7 +170,9 @@ def summarize_profile(out):
     ranges = _markers(_one(f"{out}/trace/*marker_api_trace.csv"))
     bym = _by_marker(trace_rows, ranges)
     line = _json_line(f"{out}/trace.log", '"metric"')
-    kern = line.get("kernels", {})
+    kern = dict(line.get("kernels", {}))
+    if line.get("mixed_launch"):  # the step's scan + decode step as one launch
+        kern["mixed_scan_decode"] = line["mixed_launch"]
     cfgs = line.get("configs") or {}
 
     # ---------------------------------------------------------- headline
