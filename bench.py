@@ -736,7 +736,30 @@ def measure_varlen(ssm, W, dev, timer, mark):
     with mark("varlen_scan"):
         su = timer.time(scan)
     tot = cu + su
+    # the packed scan beside the 245-request decode step of other requests:
+    # one after the other, and as one launch group (one mixed launch)
+    dspec = W.decode()
+    dsets = _decode_sets(W, dev, dspec, 2)
+
+    def serial(i):
+        scan(i)
+        run_decode(ssm, dsets[i % 2], dspec, True)
+
+    def grouped(i):
+        with ssm.launch_group():
+            scan(i)
+            run_decode(ssm, dsets[i % 2], dspec, True)
+
+    with mark("varlen_scan_decode_serial"):
+        ser = timer.time(serial)
+    with mark("varlen_scan_decode_grouped"):
+        grp = timer.time(grouped)
+    del dsets
     return {
+        "scan_and_decode_step": {"serial_us": ser, "grouped_us": grp,
+                                 "note": "the packed scan and a 245-request decode step from a "
+                                         "512-slot cache (other requests), one after the other "
+                                         "vs one launch group (one mixed launch)"},
         "workload": f"{VARLEN_NSEQ} packed sequences, {VARLEN_TOKENS} tokens, mixed lengths "
                     "(log-uniform), every other one continuing from its slot; Mamba-1 2.8B "
                     "layer (d_inner 5120, d_state 16, conv 4, f16 io / f32 state)",

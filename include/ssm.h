@@ -461,9 +461,9 @@ int ssm_mamba1_decode_layer_noalloc(const ssm_mamba1_layer *layer, ssm_tensor hi
  * workgroups after the scan's, so that they run in the slots the scan's last
  * round of workgroups leaves free.
  *
- *   Taken together: an ssm_selective_scan without packed sequences that
- *   takes the recurrence, with f16 or bf16 io, an f32 state cache, per-state
- *   decays (Mamba-1), dstate <= 16 and seqlen a multiple of 256; and an
+ *   Taken together: an ssm_selective_scan or ssm_selective_scan_varlen
+ *   that takes the recurrence, with f16 or bf16 io, an f32 state cache,
+ *   per-state decays (Mamba-1) and dstate <= 16; and an
  *   ssm_decode_step with the same io dtype, an f32 state cache, per-state
  *   decays and conv_width 4 whose state rows the interleaved map takes
  *   (dstate 8 to 256 in powers of two, at least 2^18 (request, channel)

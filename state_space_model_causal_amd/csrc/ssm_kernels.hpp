@@ -187,10 +187,10 @@ int prepare_decode_conv(SsuArgs &a, const ssm_tensor &conv_state, const ssm_tens
                         const ssm_tensor &conv_bias, const ssm_tensor &u_out, int conv_width);
 int status_of(hipError_t e);
 
-// The mixed launch (ssu.hip): a dense prefill scan and an independent fused
+// The mixed launch (ssu.hip): a prefill scan and an independent fused
 // decode step in one grid.  mixed_scan_ok / mixed_decode_ok: the kinds it is
 // built for (f16 or bf16 I/O, f32 state, per-state decays, 128-bit rows; a
-// Mamba-1 scan of dstate <= 16 over rows of a multiple of 256 steps; the
+// Mamba-1 scan of dstate <= 16, dense or packed; the
 // decode step's interleaved map with the shared conv, two requests per lane);
 // mixed_pair_ok: both, with one io dtype, within one grid.
 bool mixed_scan_ok(const ScanArgs &s);

@@ -185,7 +185,7 @@ static hipError_t launch_ssu_one(const SsuArgs &a, hipStream_t stream)
 bool mixed_scan_ok(const ScanArgs &s)
 {
     return (s.io_dtype == 1 || s.io_dtype == 2) && s.state_dtype == 0 && s.a_per_state && s.vec &&
-           s.dstate <= NC && !s.cu_seqlens && s.seqlen % (R * KD) == 0;
+           s.dstate <= NC;
 }
 
 bool mixed_decode_ok(const SsuArgs &d)
@@ -195,13 +195,13 @@ bool mixed_decode_ok(const SsuArgs &d)
            d.batch <= 65535 * 2 && ilv_lanes_log2<float>(d) >= 2;
 }
 
-template <typename TI>
+template <typename TI, int WALK>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd<TI, true, true, true>())))
 void mixed_kernel(ScanArgs s, SsuArgs d, uint32_t nscan, uint32_t dx)
 {
     if (blockIdx.x < nscan) {
-        scan_body<TI, float, true, true, true, WALK_DENSE>(s, blockIdx.x, nscan);
+        scan_body<TI, float, true, true, true, WALK>(s, blockIdx.x, nscan);
         return;
     }
     const uint32_t w = blockIdx.x - nscan;  // uniform: the request group and wave block
@@ -232,10 +232,20 @@ hipError_t launch_mixed(const ScanArgs &s, const SsuArgs &d0, hipStream_t stream
     const int cpg = s.heads_per_group * s.headdim;
     const uint32_t nscan = (uint32_t)((int64_t)s.batch * s.ngroups * ((cpg + CPB - 1) / CPB));
     const dim3 grid(nscan + dx * dy);
-    if (s.io_dtype == 1)
-        hipLaunchKernelGGL((mixed_kernel<f16>), grid, dim3(256), 0, stream, s, d, nscan, dx);
-    else
-        hipLaunchKernelGGL((mixed_kernel<bf16>), grid, dim3(256), 0, stream, s, d, nscan, dx);
+    // the scan's walk as in its own launch: the ladder of shorter end tiles
+    // for packed batches and rows of other lengths
+    const bool ladder = s.cu_seqlens || s.seqlen % (R * KD) != 0;
+    if (s.io_dtype == 1) {
+        if (ladder)
+            hipLaunchKernelGGL((mixed_kernel<f16, WALK_LADDER>), grid, dim3(256), 0, stream, s, d, nscan, dx);
+        else
+            hipLaunchKernelGGL((mixed_kernel<f16, WALK_DENSE>), grid, dim3(256), 0, stream, s, d, nscan, dx);
+    } else {
+        if (ladder)
+            hipLaunchKernelGGL((mixed_kernel<bf16, WALK_LADDER>), grid, dim3(256), 0, stream, s, d, nscan, dx);
+        else
+            hipLaunchKernelGGL((mixed_kernel<bf16, WALK_DENSE>), grid, dim3(256), 0, stream, s, d, nscan, dx);
+    }
     return hipGetLastError();
 }
 

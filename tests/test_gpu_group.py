@@ -121,12 +121,14 @@ def test_group_prefill_matches_oracle(ssm, oracle):
 
 def test_group_single_and_unmixable_calls(ssm):
     dev = torch.device("cuda:0")
-    # a scan alone, a decode step alone, and a pair the mixed kernel does not
-    # take (rows of 300 steps) each run as their own launches
+    # a scan alone and a decode step alone run as their own launches; rows of
+    # 300 steps take the mixed kernel's ladder walk; an f32-I/O scan is not
+    # taken (both calls launch on their own)
     for name, pspec, use_p, use_d in [
             ("scan alone", W.prefill(batch=2, seqlen=512), True, False),
             ("decode alone", W.prefill(batch=1, seqlen=256), False, True),
-            ("ragged scan", W.prefill(batch=2, seqlen=300), True, True)]:
+            ("ragged scan (ladder walk)", W.prefill(batch=2, seqlen=300), True, True),
+            ("f32 scan (not taken)", W.prefill(io="f32", batch=1, seqlen=512), True, True)]:
         print(f"group {name}", flush=True)
         p, d = _sets(pspec, W.decode(), dev)
         _conv(ssm, p)
@@ -183,3 +185,37 @@ def test_group_errors(ssm):
     other = torch.cuda.Stream()
     assert lib.ssm_group_end(other.cuda_stream) == 5       # another stream
     assert lib.ssm_group_end(s.cuda_stream) == 0
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_group_packed_scan_matches_separate_calls(ssm, io):
+    """The packed variable-length scan (16 sequences, 8192 tokens, every other
+    one continuing from its slot) and the decode step in one group."""
+    dev = torch.device("cuda:0")
+    print(f"group packed io={io}", flush=True)
+    lengths = W.varlen_lengths(7, 16, 8192)
+    p = W.make_varlen(W.prefill(io=io, nslots=512, seed=40), lengths, dev)
+    p["out"] = torch.zeros_like(p["x"])
+    p["u"] = torch.zeros_like(p["x"])
+    ssm.causal_conv1d_varlen(p["x"], p["conv_w"], p["cu_seqlens"], bias=p["conv_b"],
+                             conv_state=p["conv_state"], slot_idx=p["slot_idx"],
+                             has_initial_state=p["has_init"], out=p["u"])
+    d = W.make(W.decode(io=io), dev)
+    d["out"] = torch.zeros_like(d["x"])
+    p2, d2 = _clone(p), _clone(d)
+
+    def scan(t):
+        ssm.selective_scan_varlen(t["u"], t["dt"], t["A"], t["B"], t["C"], t["cu_seqlens"],
+                                  D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                                  ssm_state=t["ssm_state"], slot_idx=t["slot_idx"],
+                                  has_initial_state=t["has_init"], out=t["out"])
+
+    scan(p)
+    _decode(ssm, d)
+    with ssm.launch_group():
+        _decode(ssm, d2)
+        scan(p2)
+    torch.cuda.synchronize()
+    for k in ("out", "ssm_state"):
+        assert torch.equal(p[k], p2[k]), f"packed {k} differs"
+    _same(d, d2, "decode")
